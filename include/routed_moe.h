@@ -1,0 +1,298 @@
+/*
+ * routed_moe.h -- C ABI of the routed Mixture-of-Experts layer executed over a
+ * bounded GPU expert cache shared by every MoE layer (AMD MI355X, gfx950).
+ *
+ * Per MoE layer the method runs: router softmax/top-k; a lookup from the
+ * logical (layer, expert) id to a cache slot with LRU update; token permutation
+ * by expert; the SwiGLU expert FFN on resident slots; a gate-weighted combine.
+ * Misses are either filled over PCIe from a pinned host expert pool or run on
+ * host CPU cores, split by q* = m * B_P / B_H.
+ *
+ * Sources, cited by page title and section:
+ *   [FT-KR] FreeToken paper summary, discuss.pytorch.kr ("FreeToken: ...
+ *           Edge-Serving에 대한 연구").
+ *   [FT-CN] FreeToken reading notes, qqtang-code.github.io ("论文精读 ·
+ *           FreeToken: 边缘原生的 MoE 服务系统").
+ *   [SPARK] "Luce Spark" expert-offload post, molayo1419.me.
+ *
+ * Conventions for every call:
+ *  - Every call returns moe_status (0 = MOE_OK, negative = error) unless noted.
+ *    No C++ exception crosses this boundary.  moe_last_error() gives the text
+ *    of the last error on a context.
+ *  - "device" pointers are HIP device allocations on the context's device; "host"
+ *    pointers are CPU memory.  The caller owns every pointer it passes in (inputs,
+ *    outputs, router weights, slot arena, a registered host pool) and must keep it
+ *    alive while the context may use it.  The library owns the residency tables,
+ *    work lists, pinned staging, a copy stream, events and the CPU worker pool.
+ *  - Calls on one context must be serialised by the caller.  Work is enqueued on
+ *    the stream argument (a hipStream_t; NULL = the null stream).  Calls that need
+ *    a host decision (fills, CPU branch, resize) synchronise on that stream.
+ *  - Device-side faults surface as MOE_EHIP at the next synchronising call.
+ *  - Tokens are rows: x is [T, hidden] row-major in the activation format; y is
+ *    [T, hidden] fp32.  topk_idx / topk_w / slot_idx are [T, top_k] row-major.
+ */
+#ifndef ROUTED_MOE_H
+#define ROUTED_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+
+typedef struct moe_ctx moe_ctx;
+typedef void* moe_stream_t; /* hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,  /* bad argument, shape or size */
+  MOE_ENOMEM = -2,  /* allocation failed */
+  MOE_EHIP = -3,    /* HIP runtime error (includes device faults) */
+  MOE_ESTATE = -4,  /* call-order violation (e.g. decode without lookup, resize in prefill) */
+  MOE_ENOPIN = -5,  /* the host pool is not page-locked: only MOE_MODE_CPU can use it */
+  MOE_ENOTSUP = -6  /* combination not supported */
+} moe_status;
+
+/* Expert weight formats of a pool record (see moe_record_bytes for the layout). */
+typedef enum {
+  MOE_WFMT_F32 = 0,  /* fp32 gate | up | down */
+  MOE_WFMT_BF16 = 1, /* bf16 gate | up | down */
+  MOE_WFMT_FP4 = 2   /* e2m1 codes + one bf16 scale per 32 elements along each row */
+} moe_wfmt;
+
+typedef enum { MOE_AFMT_F32 = 0, MOE_AFMT_BF16 = 1 } moe_afmt;
+
+/*
+ * Backend modes ([FT-KR] usage section: --moe-backend fused|offload|cpu|hybrid):
+ *  FUSED   every record is resident; slot = key; no cache.
+ *  OFFLOAD LRU cache; every miss is filled over PCIe (capped by evictable slots).
+ *  CPU     LRU cache for hits; every miss runs on the host CPU.
+ *  HYBRID  misses split by q* between fills and the CPU.
+ */
+typedef enum { MOE_MODE_FUSED = 0, MOE_MODE_OFFLOAD = 1, MOE_MODE_CPU = 2, MOE_MODE_HYBRID = 3 } moe_mode;
+
+/* Trace record kinds: hit, fill, CPU execution, prefill full-layer buffer. */
+typedef enum { MOE_KIND_HIT = 0, MOE_KIND_FILL = 1, MOE_KIND_CPU = 2, MOE_KIND_BUF = 3 } moe_kind;
+
+#define MOE_FLAG_PROFILE 1 /* time the FFN kernels with HIP events (moe_get_stats) */
+
+typedef struct {
+  int32_t n_layers, n_experts, top_k, hidden, inter; /* L, E, k, H, I */
+  int32_t wfmt;        /* moe_wfmt */
+  int32_t afmt;        /* moe_afmt */
+  int32_t renorm;      /* 0: gates are the softmax over all E; 1: renormalised over the k chosen */
+  int32_t max_tokens;  /* largest T any call will pass */
+  int32_t mode;        /* moe_mode */
+  uint64_t bw_pcie;    /* B_P, bytes/s (host -> device expert transfer) */
+  uint64_t bw_host;    /* B_H, bytes/s (host CPU expert processing) */
+  int32_t cpu_threads; /* CPU branch threads; 0 = every CPU in the process affinity mask */
+  int32_t flags;       /* MOE_FLAG_* */
+} moe_config;
+
+/* One record per distinct routed key of a layer step, in first-appearance order
+ * over (token, rank) pairs.  slot = -1 for CPU; evicted = key that lost the slot, or -1. */
+typedef struct {
+  int32_t key, kind, slot, evicted;
+} moe_trace_rec;
+
+/* Counters returned by lookups (all int32). */
+enum { MOE_CNT_HIT = 0, MOE_CNT_FILL = 1, MOE_CNT_CPU = 2, MOE_CNT_EVICT = 3 };
+
+typedef struct {
+  uint64_t decode_calls, prefill_calls, lookups;
+  uint64_t hits, fills, cpu_experts, evictions;
+  uint64_t fill_bytes;            /* bytes copied host -> slot arena */
+  double phase1_ms, phase2_ms;    /* summed kernel time (MOE_FLAG_PROFILE) */
+  uint64_t phase1_launches, phase2_launches;
+  uint64_t phase1_bytes, phase2_bytes; /* algorithmic weight + activation bytes of those launches */
+  double gemm1_ms, gemm2_ms;      /* prefill grouped GEMMs (MOE_FLAG_PROFILE) */
+  uint64_t gemm1_launches, gemm2_launches;
+  double gemm_flops;              /* algorithmic flops of those launches: 2 * pairs * 3 * H * I */
+  double copy_ms;                 /* prefill whole-layer copies (MOE_FLAG_PROFILE) */
+  uint64_t copy_bytes;
+  double cpu_ms;                  /* host CPU branch wall time */
+} moe_stats;
+
+/* ---- context ---------------------------------------------------------- */
+
+/* Create a context on the current HIP device.  Validates the shape: top_k <= n_experts <= 1024,
+ * hidden % 64 == 0 and inter % 64 == 0 (FP4 also needs multiples of 32 along rows), max_tokens >= 1. */
+MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out);
+MOE_API moe_status moe_destroy(moe_ctx* ctx);
+/* Text of the last error on ctx (never NULL; "" when none).  Valid until the next call on ctx. */
+MOE_API const char* moe_last_error(const moe_ctx* ctx);
+
+/*
+ * Bytes S of one expert record, the unit of every fill and of the host pool.
+ * A slot holds every tensor of one (layer, expert) pair ([FT-KR] "FreeToken의 설계"),
+ * so one record moves one expert.  Layout (row-major, W_gate/W_up [I,H], W_down [H,I]):
+ *   F32 / BF16: [gate | up | down], element size 4 / 2
+ *   FP4:        [gate codes I*H/2 | up codes | down codes H*I/2 | gate scales I*H/32 bf16 |
+ *                up scales | down scales]; element 2i of a row is the low nibble of byte i;
+ *                one scale per 32 consecutive elements of a row (the reduction dimension);
+ *                w = e2m1(code) * scale.
+ * Returns -1 for an invalid config.  Pure host function.
+ */
+MOE_API int64_t moe_record_bytes(const moe_config* cfg);
+
+/* ---- host expert pool (the source of truth) ---------------------------- */
+
+/*
+ * Allocate a page-locked host pool of n_records records owned by the library (freed by
+ * moe_destroy) and return its host address.  Key lE+e lives in record (lE+e) % n_records, so
+ * n_records = L*E is the full pool ([FT-KR] "FreeToken의 설계": the CPU-resident pool holds
+ * every routed expert; "전문가 뱅크와 FTW 포맷": banks are indexed by lE+e).  The caller fills
+ * the records before the first lookup.  The memory is allocated page-locked and then filled:
+ * registering already-filled memory is not used (see the design notes).
+ */
+MOE_API moe_status moe_pool_alloc(moe_ctx* ctx, int64_t n_records, void** host_pool);
+
+/*
+ * Use caller-owned host memory as the pool (same record indexing as moe_pool_alloc).
+ * pinned = 1 promises the memory is page-locked (e.g. from hipHostMalloc); with pinned = 0 the
+ * pool is pageable and only MOE_MODE_CPU may run on it (MOE_ENOPIN otherwise): every routed
+ * expert then runs on the host, as in the pages' pure-CPU fallback ([FT-KR] "전문가 뱅크와
+ * FTW 포맷", last paragraph).
+ */
+MOE_API moe_status moe_pool_register(moe_ctx* ctx, void* host_pool, int64_t n_records, int32_t pinned);
+
+/*
+ * Bind the router weights and the slot arena.
+ *  router_w: device fp32 [L, E, H].  arena: device memory of arena_bytes >= n_slots * S.
+ *  n_slots:  cache slots.  MOE_MODE_FUSED needs n_slots >= L*E (slot = key; fill it with
+ *            moe_fused_load).  Other modes: 0 <= n_slots <= 4096.
+ * Resets the cache to empty (cold start: [FT-KR] "탄력적 메모리 관리" -- no warm-up).
+ */
+MOE_API moe_status moe_bind(moe_ctx* ctx, const float* router_w, void* arena, size_t arena_bytes,
+                            int32_t n_slots);
+
+/* FUSED mode: copy every pool record into arena slot = key (enqueued on stream). */
+MOE_API moe_status moe_fused_load(moe_ctx* ctx, moe_stream_t stream);
+
+/* Set B_P and B_H (bytes/s) used by the q* split from now on. */
+MOE_API moe_status moe_set_bandwidths(moe_ctx* ctx, uint64_t bw_pcie, uint64_t bw_host);
+
+/* Change the backend mode between steps (not FUSED <-> cached: that needs a new bind). */
+MOE_API moe_status moe_set_mode(moe_ctx* ctx, int32_t mode);
+
+/* ---- the hot path ------------------------------------------------------ */
+
+/*
+ * Router logits and top-k for T tokens of `layer` ([FT-KR] "decode 공동 설계": the router and
+ * the cache lookup run on the GPU).
+ *   z[t,e] = sum_h x[t,h] * W_r[layer][e,h] + logit_bias[t,e]      (fp32)
+ *   topk_idx[t,:] = the k largest z[t,:], highest first, ties to the lower expert index
+ *   topk_w[t,j]   = softmax(z[t,:])[topk_idx[t,j]]   (renorm = 1: divided by their sum)
+ * x: device [T,H] (afmt); logit_bias: device fp32 [T,E] or NULL; logits_out: device fp32
+ * [T,E] or NULL; topk_idx: device int32 [T,k]; topk_w: device fp32 [T,k].  1 <= T <= max_tokens.
+ */
+MOE_API moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
+                             float* logits_out, int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+
+/* The top-k and gate step of moe_route alone, on given device fp32 logits [T,E]. */
+MOE_API moe_status moe_topk(moe_ctx* ctx, const float* logits, int32_t T, int32_t* topk_idx, float* topk_w,
+                            moe_stream_t stream);
+
+/*
+ * One layer step of the cache control ([FT-KR] "CUDA Graph와 공존하는 LRU 캐시"; [FT-CN] 05
+ * Implementation): dedupe the routed experts, classify them against the residency table, derive
+ * q from the integer bandwidths (same formula as qstar_split), choose the q least recently used
+ * evictable slots in one pass, admit the fills, refresh recency, and rewrite ids.
+ *   topk_idx: device int32 [T,k] experts of `layer`.
+ *   slot_idx: device int32 [T,k] out: slot >= 0 for GPU execution, or -1-c for entry c of the
+ *             step's CPU list.
+ *   trace:    device moe_trace_rec [min(T*k, E)] or NULL (one record per distinct key).
+ *   counts:   device int32 [4] or NULL: hits, fills, CPU experts, evictions of occupied slots.
+ * Asynchronous.  Queues the step's fill and CPU work lists for the next moe_ffn_decode of the
+ * same layer.  In FUSED mode every key is a hit at slot = key and nothing changes.
+ */
+MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* topk_idx, int32_t T,
+                                       int32_t* slot_idx, moe_trace_rec* trace, int32_t* counts,
+                                       moe_stream_t stream);
+
+/*
+ * Decode expert FFN for the work of the last lookup on `layer` ([FT-KR] "측정된 대역폭이 분할을
+ * 결정합니다": the CPU branch starts first; the GPU then copies the fills and evaluates the
+ * resident set G = H u F; the two partial sums are added exactly):
+ *   y[t] = sum_{j in G, rank order} w[t,j] FFN_{slot}(x_t) + sum_{j in C, rank order} w[t,j] FFN_key(x_t)
+ * with FFN(x) = W_down (silu(W_gate x) * (W_up x)).  x: device [T,H]; topk_idx, topk_w, slot_idx
+ * as given to / returned by the lookup; y: device fp32 [T,H].  Needs T * H <= 16384 (decode
+ * batches); use moe_ffn_prefill for longer inputs.  Synchronises the stream when the step has
+ * fills or CPU work (the fill list is read on the host), then enqueues the GPU work.
+ */
+MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
+                                  const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);
+
+/*
+ * Prefill over layers 0..L-1 in ascending order ([FT-KR] "전층 이중 버퍼링"; [FT-CN] 04 Design,
+ * mechanism 1).  moe_prefill_begin reserves two full-layer buffers (slots [0,E) and [E,2E)) from
+ * the shared pool when n_slots >= 2E and starts copying layers 0 and 1 on the library's copy
+ * stream; otherwise prefill loads experts on demand.  moe_ffn_prefill(layer) waits for its layer's
+ * copy, routes nothing itself (topk_idx / topk_w come from moe_route), permutes the token-expert
+ * pairs by slot, runs the grouped SwiGLU GEMMs, combines into y (device fp32 [T,H]) and queues the
+ * copy of layer+2 into the buffer it frees.  trace (device, [min(T*k,E)] per round) and counts
+ * (device int32 [4]) are optional.  moe_prefill_end returns the buffers to the pool with their
+ * contents: the last two layers survive to seed decode.
+ */
+MOE_API moe_status moe_prefill_begin(moe_ctx* ctx, moe_stream_t stream);
+MOE_API moe_status moe_ffn_prefill(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
+                                   const float* topk_w, float* y, moe_trace_rec* trace, int32_t* counts,
+                                   moe_stream_t stream);
+MOE_API moe_status moe_prefill_end(moe_ctx* ctx, moe_stream_t stream);
+
+/*
+ * Token permutation by expert slot (a step of moe_ffn_prefill, exported on its own):
+ *   perm[i]     pair index p = t*k + j of the i-th GPU pair, stably ordered by (slot, p)
+ *   offsets[g]  first position of group g; offsets[n_groups] = number of GPU pairs
+ *   group_slot[g] slot of group g, ascending
+ * slot_idx: device int32 [T,k] (negative entries are not GPU pairs and are left out).
+ * perm: device int32 [T*k]; offsets: device int32 [T*k+1]; group_slot: device int32 [T*k];
+ * n_groups: device int32 [1].  Asynchronous.
+ */
+MOE_API moe_status moe_permute(moe_ctx* ctx, const int32_t* slot_idx, int32_t T, int32_t* perm, int32_t* offsets,
+                               int32_t* group_slot, int32_t* n_groups, moe_stream_t stream);
+
+/*
+ * Rebuild the cache for n_slots' slots at a safe point, without touching the host pool
+ * ([FT-KR] "탄력적 메모리 관리").  Shrinking keeps the n_slots' most recently used entries,
+ * packed into slots 0..n_slots'-1 in ascending old-slot order (recency kept); growing adds empty
+ * slots.  new_arena = NULL resizes in the bound arena (needs arena_bytes >= n_slots' * S);
+ * otherwise records move to new_arena, which becomes the bound arena.  Synchronises stream.
+ * MOE_ESTATE inside prefill; MOE_ENOTSUP in FUSED mode.
+ */
+MOE_API moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_n_slots, void* new_arena, size_t new_arena_bytes,
+                                       moe_stream_t stream);
+
+/*
+ * Number of misses to fill; the rest run on the CPU ([FT-KR] "측정된 대역폭이 분할을 결정합니다";
+ * [FT-CN] 04 Design, mechanism 2 equations): q* = m * B_P / B_H rounded half-up, at least one
+ * fill when m >= 1 and a slot is evictable, at most min(m, evictable); B_H <= B_P fills every
+ * miss (the pure on-demand limit).  OFFLOAD: min(m, evictable).  CPU and FUSED: 0.
+ * Negative m or evictable, or an unknown mode: returns -1.  Pure host function.
+ */
+MOE_API int32_t qstar_split(int32_t m, uint64_t bw_pcie, uint64_t bw_host, int32_t mode, int32_t evictable);
+
+/*
+ * Measure B_P (pinned host -> device copies of whole records) and B_H (the CPU branch over whole
+ * records at batch 1) on this machine at the record size, as the pages profile both on the
+ * deployed machine ([FT-KR] "실험 환경" and usage: ft bench bw).  Needs a bound pool and arena
+ * with at least one slot.  Outputs bytes/s; does not change the context's bandwidths.
+ */
+MOE_API moe_status moe_bench_bw(moe_ctx* ctx, uint64_t* bw_pcie, uint64_t* bw_host);
+
+/* Copy the residency tables to host memory (any pointer may be NULL):
+ * slot_of [L*E], key_of [n_slots], stamp [n_slots]; *counter = the recency counter. */
+MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, uint64_t* stamp,
+                                      uint64_t* counter, int32_t* n_slots);
+
+/* Accumulated statistics (synchronises the context's streams to read kernel timings). */
+MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);
+MOE_API moe_status moe_reset_stats(moe_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROUTED_MOE_H */

@@ -1,0 +1,95 @@
+// Device helpers shared by the HIP kernels of the routed-MoE library (gfx950,
+// wavefront 64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.hpp"
+
+namespace rmoe {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int AFMT>
+__device__ __forceinline__ float load_act(const void* x, size_t i) {
+  if constexpr (AFMT == MOE_AFMT_BF16) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[i]);
+  } else {
+    return reinterpret_cast<const float*>(x)[i];
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Two e2m1 codes (byte `sel` of w, low nibble first) -> two fp32 values, exact.
+template <int SEL>
+__device__ __forceinline__ void fp4x2_to_f32(uint32_t w, float& a, float& b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  a = v[0];
+  b = v[1];
+}
+
+// 32 e2m1 codes in 16 bytes -> 32 fp32 values (element i = nibble i, low nibble first).
+__device__ __forceinline__ void fp4x32_to_f32(const uint4& q, float* v) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fp4x2_to_f32<0>(w[i], v[8 * i + 0], v[8 * i + 1]);
+    fp4x2_to_f32<1>(w[i], v[8 * i + 2], v[8 * i + 3]);
+    fp4x2_to_f32<2>(w[i], v[8 * i + 4], v[8 * i + 5]);
+    fp4x2_to_f32<3>(w[i], v[8 * i + 6], v[8 * i + 7]);
+  }
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads); returns the
+// thread's exclusive prefix and writes the total to *total.
+__device__ int block_excl_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_tmp[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = (lane < (kLookupThreads / 64)) ? s_tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int y = __shfl_up(w, off);
+      if (lane >= off) w += y;
+    }
+    if (lane < (kLookupThreads / 64)) s_tmp[32 + lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  int base = (wave > 0) ? s_tmp[32 + wave - 1] : 0;
+  *total = s_tmp[32 + (kLookupThreads / 64) - 1];
+  __syncthreads();
+  return base + x - v;
+}
+
+}  // namespace rmoe

@@ -1,0 +1,240 @@
+// Internal declarations of the routed-MoE library: context state, kernel
+// launchers and device helpers.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <condition_variable>
+#include <cstdint>
+#include <functional>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/routed_moe.h"
+
+namespace rmoe {
+
+// ---------------------------------------------------------------- limits
+constexpr int kMaxExperts = 1024;       // E (lookup kernel keeps per-expert tables in LDS)
+constexpr int kMaxCachedSlots = 4096;   // slots of a cached (non-FUSED) context
+constexpr int kLookupThreads = 1024;
+constexpr int kSlotsPerThread = kMaxCachedSlots / kLookupThreads;
+constexpr int kDecodeMaxTH = 16384;     // decode: T * H fp32 activations staged in 64 KiB of LDS
+constexpr int kDecodeMaxTok = 8;        // decode: tokens routed to one expert within a call
+
+// lookup counters (device int32 array)
+enum {
+  C_NU = 0, C_HIT = 1, C_FILL = 2, C_CPU = 3, C_EVICT = 4, C_NGRP = 5, C_M = 6, C_EV = 7,
+  C_NPAIR_GPU = 8, C_ERR = 9, C_COUNT = 16
+};
+
+enum LookupMode { LK_FUSED = 0, LK_OFFLOAD = 1, LK_CPU = 2, LK_HYBRID = 3, LK_BUFFER = 4 };
+
+struct LookupArgs {
+  const int32_t* topk_idx;   // [T,k] experts (or nullptr when cand is used)
+  const int32_t* cand;       // candidate key list (on-demand prefill rounds) or nullptr
+  int32_t n_cand;
+  int32_t T, k, E, layer;
+  int32_t mode;              // LookupMode
+  int32_t n_slots;
+  int32_t buffer_base;       // LK_BUFFER: slot of expert 0 of this layer
+  uint64_t bw_pcie, bw_host;
+  // cache tables
+  int32_t* slot_of;          // [L*E]
+  int32_t* key_of;           // [cap]
+  uint64_t* stamp;           // [cap]
+  const uint8_t* reserved;   // [cap]
+  uint64_t* counter;         // [1]
+  // outputs
+  int32_t* slot_idx;         // [T,k]
+  moe_trace_rec* trace;      // [<=E] or nullptr (caller's)
+  int32_t* counts_out;       // [4] or nullptr (caller's)
+  int32_t* u_key; int32_t* u_kind; int32_t* u_slot; int32_t* u_evict;  // [E]
+  int32_t* fill_key; int32_t* fill_slot; int32_t* cpu_key;              // [E]
+  int32_t* grp_slot;         // [E]
+  int32_t* pair_grp;         // [T*k]
+  int32_t* cnt;              // [C_COUNT]
+};
+
+struct DecodeArgs {
+  const void* x;             // [T,H] afmt
+  const float* w;            // [T,k]
+  const uint8_t* arena;
+  int64_t rec_bytes;
+  int32_t T, k, H, I;
+  const int32_t* grp_slot;   // [G]
+  const int32_t* pair_grp;   // [T*k]
+  const int32_t* cnt;        // device counters (C_NGRP)
+  float* h;                  // [T*k, I] scratch
+  float* d;                  // [T*k, H] scratch (per-pair expert outputs)
+  int32_t* rowblock_done;    // [H / rows per block] zero-initialised counters
+  float* y;                  // [T,H]
+};
+
+struct PrefillArgs {
+  const void* x;             // [T,H] afmt
+  const float* w;            // [T,k]
+  const uint8_t* arena;
+  int64_t rec_bytes;
+  int32_t T, k, H, I, E;
+  const int32_t* grp_slot;   // [G]
+  const int32_t* perm;       // [P] sorted position -> pair
+  const int32_t* inv;        // [P] pair -> sorted position or -1
+  const int32_t* offsets;    // [G+1]
+  const int32_t* tile_base;  // [G+1] cumulative m-tiles
+  const int32_t* cnt;        // C_NGRP, C_NPAIR_GPU
+  void* act;                 // [P, I] bf16/f16 (sorted order)
+  float* ypair;              // [P, H] fp32 (sorted order)
+  float* y;                  // [T, H]
+  const float* y_cpu;        // [T, H] or nullptr
+  const int32_t* pair_gpu;   // [T*k]: >= 0 for pairs evaluated on the GPU; nullptr = every pair
+};
+
+// ---------------------------------------------------------------- launchers
+void launch_route_logits(const void* x, int afmt, const float* wr, const float* bias, float* logits, int T, int E,
+                         int H, hipStream_t s);
+void launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w, hipStream_t s);
+void launch_lookup(const LookupArgs& a, hipStream_t s);
+void launch_evict_range(int32_t* slot_of, int32_t* key_of, uint64_t* stamp, uint8_t* reserved, int lo, int hi,
+                        uint8_t reserve_value, hipStream_t s);
+void launch_admit_buffer(int32_t* slot_of, int32_t* key_of, uint64_t* stamp, uint64_t* counter, int layer, int E,
+                         int base, hipStream_t s);
+void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s);
+void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s);
+int decode_phase2_rowblocks(int H);
+void launch_add_inplace(float* y, const float* src, int64_t n, hipStream_t s);
+void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
+                    int32_t* inv, int32_t* offsets, int32_t* tile_base, int bm, hipStream_t s);
+void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp, int32_t* grp_slot, int32_t* cnt,
+                              int32_t* scratch_flags, int n_slot_range, hipStream_t s);
+int prefill_bm();
+void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s);
+void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s);
+void launch_prefill_combine(const PrefillArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- CPU branch
+struct CpuPool {
+  explicit CpuPool(int threads);
+  ~CpuPool();
+  // Run fn(i) for i in [0, n) on the pool (caller participates); returns when all are done.
+  void run(int n, const std::function<void(int)>& fn);
+  int size() const { return nthreads_; }
+
+ private:
+  void worker(int id);
+  int nthreads_;
+  std::vector<std::thread> threads_;
+  std::mutex mu_;
+  std::condition_variable cv_;
+  std::atomic<uint64_t> gen_{0};    // bumped once per run(): wakes the workers
+  // One word per generation: (generation << 44) | (task count << 22) | next task index.
+  // A claim succeeds only while next < count of the word it read, so a worker that is
+  // late for one generation can never claim a task index that generation does not have.
+  std::atomic<uint64_t> claim_{0};
+  std::atomic<int> done_{0};
+  std::atomic<const std::function<void(int)>*> fn_{nullptr};
+  std::atomic<bool> stop_{false};
+};
+
+struct CpuFfnJob {
+  int wfmt;
+  int H, I, T, k;
+  int64_t rec_bytes;
+  const float* x;                   // [T,H] fp32 (host)
+  const float* w;                   // [T,k] gates (host)
+  const int32_t* slot_idx;          // [T,k] (host): CPU pairs are < 0
+  std::vector<const uint8_t*> rec;  // record address of CPU list entry c
+  float* h;                         // [T*k, I] scratch (host)
+  float* y;                         // [T,H] out (host), CPU partial sum
+};
+void cpu_ffn(CpuPool& pool, const CpuFfnJob& job);
+
+}  // namespace rmoe
+
+// ---------------------------------------------------------------- context
+struct moe_ctx {
+  moe_config cfg{};
+  int device = 0;
+  int64_t S = 0;                 // record bytes
+  std::string err;
+
+  // host pool
+  uint8_t* pool = nullptr;
+  int64_t pool_records = 0;
+  bool pool_owned = false, pool_pinned = false;
+
+  // bound device memory
+  const float* router_w = nullptr;
+  uint8_t* arena = nullptr;
+  size_t arena_bytes = 0;
+  int32_t n_slots = 0;
+  bool bound = false;
+
+  // residency tables (device)
+  int32_t* slot_of = nullptr;    // [L*E]
+  int32_t* key_of = nullptr;     // [kMaxCachedSlots]
+  uint64_t* stamp = nullptr;     // [kMaxCachedSlots]
+  uint8_t* reserved = nullptr;   // [kMaxCachedSlots]
+  uint64_t* counter = nullptr;   // [1]
+
+  // per-step work lists (device).  cnt, fill_key, fill_slot, cpu_key, u_key and u_kind
+  // are consecutive pieces of one block (step_dev) so the host reads them with one copy.
+  int32_t* step_dev = nullptr;   // [C_COUNT + 5E]
+  int32_t *cnt = nullptr, *fill_key = nullptr, *fill_slot = nullptr, *cpu_key = nullptr;
+  int32_t *u_key = nullptr, *u_kind = nullptr;
+  int32_t *u_slot = nullptr, *u_evict = nullptr, *grp_slot = nullptr;
+  int32_t* pair_grp = nullptr;   // [Pmax]
+  int32_t* slot_scratch = nullptr;  // [Pmax] slot ids of steps whose caller passes none
+
+  // scratch (device)
+  float* logits = nullptr;       // [max_tokens*E]
+  float* h = nullptr;            // [decode pairs * I]
+  float* dpair = nullptr;        // [decode pairs * H]
+  int32_t* rowblock_done = nullptr;
+  float* y_cpu_dev = nullptr;    // [max_tokens*H]
+  // prefill scratch (device, sized for max_tokens)
+  int32_t *perm = nullptr, *inv = nullptr, *offsets = nullptr, *tile_base = nullptr, *hist = nullptr;
+  int32_t* cand = nullptr;       // [E]
+  void* act = nullptr;
+  float* ypair = nullptr;
+  int32_t* flags = nullptr;
+
+  // pinned host staging; h_cnt .. h_u_kind mirror step_dev
+  int32_t* step_host = nullptr;
+  int32_t* h_cnt = nullptr;      // [C_COUNT]
+  int32_t* h_fill_key = nullptr;
+  int32_t* h_fill_slot = nullptr;
+  int32_t* h_cpu_key = nullptr;
+  int32_t* h_u_key = nullptr;
+  int32_t* h_u_kind = nullptr;
+  int32_t* h_slot_idx = nullptr; // [Pmax]
+  float* h_w = nullptr;          // [Pmax]
+  void* h_x = nullptr;           // [max_tokens*H] in afmt
+  float* h_xf = nullptr;         // [max_tokens*H] fp32
+  float* h_y = nullptr;          // [max_tokens*H] fp32 (pinned, CPU partial)
+  float* h_hbuf = nullptr;       // [Pmax*I] fp32 (CPU intermediate)
+
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_sync = nullptr, ev_fill = nullptr, ev_ycpu = nullptr;
+  hipEvent_t ev_layer_copied[2] = {nullptr, nullptr};
+  hipEvent_t ev_layer_done[2] = {nullptr, nullptr};
+
+  // state machine
+  int last_lookup_layer = -1;
+  int last_lookup_T = 0;
+  bool in_prefill = false;
+  bool prefill_buffers = false;
+  int buffer_layer[2] = {-1, -1};
+  int next_prefill_layer = 0;
+
+  // stats and profiling
+  moe_stats stats{};
+  struct Timed { hipEvent_t a, b; int kind; };
+  std::vector<Timed> pending_timed;
+  std::vector<hipEvent_t> event_pool;
+
+  rmoe::CpuPool* cpu = nullptr;
+};

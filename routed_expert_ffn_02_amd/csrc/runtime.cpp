@@ -1,0 +1,1075 @@
+// Host runtime and C ABI of the routed-MoE library.
+//
+// Owns the residency tables, work lists, pinned staging, the copy stream and the
+// CPU worker pool; sequences the per-layer hot path:
+//   decode   route -> lookup (one device kernel) -> [read the step's fill / CPU
+//            lists from host-mapped staging] -> CPU branch started first ->
+//            fills on the copy stream -> GEMV phases on the compute stream ->
+//            exact merge y = y_GPU + y_CPU
+//            (FreeToken summary, "측정된 대역폭이 분할을 결정합니다");
+//   prefill  two full-layer buffers from the shared slot pool; the copy stream
+//            loads layer l+2 into the buffer layer l frees while later layers
+//            compute (FreeToken summary, "전층 이중 버퍼링");
+//   resize   rebuild the cache for a new slot budget at a safe point without
+//            touching the host pool (FreeToken summary, "탄력적 메모리 관리").
+#include <hip/hip_runtime.h>
+#include <sched.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+
+using namespace rmoe;
+
+namespace {
+
+moe_status fail(moe_ctx* c, moe_status st, const std::string& msg) {
+  if (c) c->err = msg;
+  return st;
+}
+
+#define HIPCHK(expr)                                                                           \
+  do {                                                                                         \
+    hipError_t e_ = (expr);                                                                    \
+    if (e_ != hipSuccess) return fail(ctx, MOE_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+#define CHECK_ARG(cond, msg) \
+  do {                       \
+    if (!(cond)) return fail(ctx, MOE_EINVAL, msg); \
+  } while (0)
+
+int64_t record_bytes(const moe_config& c) {
+  const int64_t n = (int64_t)c.hidden * c.inter;
+  switch (c.wfmt) {
+    case MOE_WFMT_F32: return 3 * n * 4;
+    case MOE_WFMT_BF16: return 3 * n * 2;
+    case MOE_WFMT_FP4: return 3 * (n / 2) + 3 * (n / 32) * 2;
+  }
+  return -1;
+}
+
+int64_t weight_row_bytes(const moe_config& c, int cols) {
+  switch (c.wfmt) {
+    case MOE_WFMT_F32: return (int64_t)cols * 4;
+    case MOE_WFMT_BF16: return (int64_t)cols * 2;
+    default: return (int64_t)cols / 2 + (int64_t)cols / 32 * 2;
+  }
+}
+
+int act_bytes(const moe_config& c) { return c.afmt == MOE_AFMT_BF16 ? 2 : 4; }
+
+template <typename T>
+hipError_t dev_alloc(T** p, size_t n) {
+  return hipMalloc(reinterpret_cast<void**>(p), std::max<size_t>(n, 1) * sizeof(T));
+}
+
+const uint8_t* pool_record(const moe_ctx* c, int64_t key) {
+  const int64_t b = (c->pool_records > 0) ? key % c->pool_records : key;
+  return c->pool + b * c->S;
+}
+
+// Enqueue copies of keys [k0, k0+n) into consecutive arena slots starting at dst_slot,
+// merging runs that are contiguous in the pool.
+hipError_t copy_keys(moe_ctx* c, int64_t k0, int64_t n, int64_t dst_slot, hipStream_t s) {
+  int64_t i = 0;
+  while (i < n) {
+    const uint8_t* src = pool_record(c, k0 + i);
+    int64_t run = 1;
+    while (i + run < n && pool_record(c, k0 + i + run) == src + run * c->S) ++run;
+    hipError_t e = hipMemcpyAsync(c->arena + (dst_slot + i) * c->S, src, run * c->S, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return e;
+    c->stats.fill_bytes += run * c->S;
+    i += run;
+  }
+  return hipSuccess;
+}
+
+hipEvent_t take_event(moe_ctx* c) {
+  if (!c->event_pool.empty()) {
+    hipEvent_t e = c->event_pool.back();
+    c->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+enum TimedKind { TK_P1 = 0, TK_P2 = 1, TK_G1 = 2, TK_G2 = 3, TK_COPY = 4 };
+
+struct TimedScope {
+  moe_ctx* c;
+  hipStream_t s;
+  int kind;
+  hipEvent_t a = nullptr;
+  TimedScope(moe_ctx* c_, hipStream_t s_, int kind_) : c(c_), s(s_), kind(kind_) {
+    if (c->cfg.flags & MOE_FLAG_PROFILE) {
+      a = take_event(c);
+      if (a) hipEventRecord(a, s);
+    }
+  }
+  ~TimedScope() {
+    if (a) {
+      hipEvent_t b = take_event(c);
+      if (b) {
+        hipEventRecord(b, s);
+        c->pending_timed.push_back({a, b, kind});
+      }
+    }
+  }
+};
+
+void drain_timed(moe_ctx* c) {
+  for (auto& t : c->pending_timed) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.b) == hipSuccess && hipEventElapsedTime(&ms, t.a, t.b) == hipSuccess) {
+      switch (t.kind) {
+        case TK_P1: c->stats.phase1_ms += ms; break;
+        case TK_P2: c->stats.phase2_ms += ms; break;
+        case TK_G1: c->stats.gemm1_ms += ms; break;
+        case TK_G2: c->stats.gemm2_ms += ms; break;
+        case TK_COPY: c->stats.copy_ms += ms; break;
+      }
+    }
+    c->event_pool.push_back(t.a);
+    c->event_pool.push_back(t.b);
+  }
+  c->pending_timed.clear();
+}
+
+rmoe::CpuPool& cpu_pool(moe_ctx* c) {
+  if (!c->cpu) {
+    int n = c->cfg.cpu_threads;
+    if (n <= 0) {
+      cpu_set_t set;
+      CPU_ZERO(&set);
+      n = (sched_getaffinity(0, sizeof(set), &set) == 0) ? CPU_COUNT(&set) : 1;
+    }
+    c->cpu = new rmoe::CpuPool(n);
+  }
+  return *c->cpu;
+}
+
+void fill_lookup_args(moe_ctx* c, LookupArgs& a, int layer, const int32_t* idx, int T, int mode) {
+  std::memset(&a, 0, sizeof(a));
+  a.topk_idx = idx;
+  a.T = T;
+  a.k = c->cfg.top_k;
+  a.E = c->cfg.n_experts;
+  a.layer = layer;
+  a.mode = mode;
+  a.n_slots = c->n_slots;
+  a.bw_pcie = c->cfg.bw_pcie;
+  a.bw_host = c->cfg.bw_host;
+  a.slot_of = c->slot_of;
+  a.key_of = c->key_of;
+  a.stamp = c->stamp;
+  a.reserved = c->reserved;
+  a.counter = c->counter;
+  a.u_key = c->u_key;
+  a.u_kind = c->u_kind;
+  a.u_slot = c->u_slot;
+  a.u_evict = c->u_evict;
+  a.fill_key = c->fill_key;
+  a.fill_slot = c->fill_slot;
+  a.cpu_key = c->cpu_key;
+  a.grp_slot = c->grp_slot;
+  a.pair_grp = c->pair_grp;
+  a.cnt = c->cnt;
+}
+
+int lookup_mode_of(int mode) {
+  switch (mode) {
+    case MOE_MODE_FUSED: return LK_FUSED;
+    case MOE_MODE_OFFLOAD: return LK_OFFLOAD;
+    case MOE_MODE_CPU: return LK_CPU;
+    default: return LK_HYBRID;
+  }
+}
+
+// Copy the step's counts and work lists (one contiguous block) to pinned host memory,
+// with the CPU branch's inputs when `inputs` is set, and wait: the one device -> host
+// decision point of a cached step.
+moe_status read_step(moe_ctx* ctx, hipStream_t s, bool inputs, const void* x, const float* w, const int32_t* slot_idx,
+                     int T) {
+  const int E = ctx->cfg.n_experts;
+  HIPCHK(hipMemcpyAsync(ctx->step_host, ctx->step_dev, (size_t)(C_COUNT + 5 * E) * sizeof(int32_t),
+                        hipMemcpyDeviceToHost, s));
+  if (inputs) {
+    const int P = T * ctx->cfg.top_k;
+    HIPCHK(hipEventSynchronize(ctx->ev_ycpu));  // the previous H2D from the host staging has finished
+    HIPCHK(hipMemcpyAsync(ctx->h_x, x, (size_t)T * ctx->cfg.hidden * act_bytes(ctx->cfg), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(ctx->h_w, w, (size_t)P * sizeof(float), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipMemcpyAsync(ctx->h_slot_idx, slot_idx, (size_t)P * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  }
+  HIPCHK(hipEventRecord(ctx->ev_sync, s));
+  HIPCHK(hipEventSynchronize(ctx->ev_sync));
+  if (ctx->h_cnt[C_ERR]) return fail(ctx, MOE_EINVAL, "expert id out of range in topk_idx");
+  ctx->stats.lookups += 1;
+  ctx->stats.hits += ctx->h_cnt[C_HIT];
+  ctx->stats.fills += ctx->h_cnt[C_FILL];
+  ctx->stats.cpu_experts += ctx->h_cnt[C_CPU];
+  ctx->stats.evictions += ctx->h_cnt[C_EVICT];
+  return MOE_OK;
+}
+
+// Fills of the current step: pinned pool -> victim slots on the copy stream; the
+// compute stream waits for them.  The compute stream is idle up to the lookup here
+// (read_step synchronised it), so no kernel still reads a victim slot.
+moe_status issue_fills(moe_ctx* ctx, hipStream_t s) {
+  const int nf = ctx->h_cnt[C_FILL];
+  if (nf <= 0) return MOE_OK;
+  if (!ctx->pool_pinned) return fail(ctx, MOE_ENOPIN, "fills need a page-locked host pool");
+  TimedScope ts(ctx, ctx->copy_stream, TK_COPY);
+  for (int i = 0; i < nf; ++i) {
+    const int key = ctx->h_fill_key[i], slot = ctx->h_fill_slot[i];
+    HIPCHK(hipMemcpyAsync(ctx->arena + (int64_t)slot * ctx->S, pool_record(ctx, key), ctx->S, hipMemcpyHostToDevice,
+                          ctx->copy_stream));
+    ctx->stats.fill_bytes += ctx->S;
+  }
+  HIPCHK(hipEventRecord(ctx->ev_fill, ctx->copy_stream));
+  HIPCHK(hipStreamWaitEvent(s, ctx->ev_fill, 0));
+  return MOE_OK;
+}
+
+// CPU branch over the step's CPU list.  x, w and slot ids are already in pinned
+// staging (read_step with inputs); the GPU work of the step is enqueued before this
+// runs, so both branches proceed together.  Ends with the H2D copy of the partial sum.
+moe_status run_cpu_branch(moe_ctx* ctx, int T, hipStream_t s, float** y_cpu_dev_out) {
+  *y_cpu_dev_out = nullptr;
+  const int ncpu = ctx->h_cnt[C_CPU];
+  if (ncpu <= 0) return MOE_OK;
+  const int H = ctx->cfg.hidden;
+  if (ctx->cfg.afmt == MOE_AFMT_BF16) {
+    const uint16_t* xb = static_cast<const uint16_t*>(ctx->h_x);
+    for (int64_t i = 0; i < (int64_t)T * H; ++i) {
+      uint32_t u = (uint32_t)xb[i] << 16;
+      std::memcpy(&ctx->h_xf[i], &u, 4);
+    }
+  } else {
+    std::memcpy(ctx->h_xf, ctx->h_x, (size_t)T * H * sizeof(float));
+  }
+  CpuFfnJob job;
+  job.wfmt = ctx->cfg.wfmt;
+  job.H = H;
+  job.I = ctx->cfg.inter;
+  job.T = T;
+  job.k = ctx->cfg.top_k;
+  job.rec_bytes = ctx->S;
+  job.x = ctx->h_xf;
+  job.w = ctx->h_w;
+  job.slot_idx = ctx->h_slot_idx;
+  for (int c = 0; c < ncpu; ++c) job.rec.push_back(pool_record(ctx, ctx->h_cpu_key[c]));
+  job.h = ctx->h_hbuf;
+  job.y = ctx->h_y;
+  std::memset(ctx->h_y, 0, (size_t)T * H * sizeof(float));
+  const auto t0 = std::chrono::steady_clock::now();
+  cpu_ffn(cpu_pool(ctx), job);
+  ctx->stats.cpu_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  HIPCHK(hipMemcpyAsync(ctx->y_cpu_dev, ctx->h_y, (size_t)T * H * sizeof(float), hipMemcpyHostToDevice, s));
+  HIPCHK(hipEventRecord(ctx->ev_ycpu, s));
+  *y_cpu_dev_out = ctx->y_cpu_dev;
+  return MOE_OK;
+}
+
+// A step may send experts to the CPU: CPU and HYBRID modes, or too few slots.
+bool may_use_cpu(const moe_ctx* c, int P) {
+  return c->cfg.mode == MOE_MODE_CPU || c->cfg.mode == MOE_MODE_HYBRID || c->n_slots < 2 * P;
+}
+
+bool valid_mode(int m) { return m >= MOE_MODE_FUSED && m <= MOE_MODE_HYBRID; }
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+MOE_API int64_t moe_record_bytes(const moe_config* cfg) {
+  if (!cfg || cfg->hidden <= 0 || cfg->inter <= 0) return -1;
+  return record_bytes(*cfg);
+}
+
+MOE_API int32_t qstar_split(int32_t m, uint64_t bw_pcie, uint64_t bw_host, int32_t mode, int32_t evictable) {
+  if (m < 0 || evictable < 0 || !valid_mode(mode)) return -1;
+  if (mode == MOE_MODE_FUSED || mode == MOE_MODE_CPU) return 0;
+  const int32_t cap = std::min(m, evictable);
+  if (mode == MOE_MODE_OFFLOAD) return cap;
+  if (m == 0 || evictable == 0) return 0;
+  if (bw_host <= bw_pcie) return cap;
+  // round-half-up of m * B_P / B_H in exact integer arithmetic
+  const unsigned __int128 num = (unsigned __int128)2 * (unsigned __int128)m * bw_pcie + bw_host;
+  const unsigned __int128 q = num / ((unsigned __int128)2 * bw_host);
+  const int64_t qi = std::max<int64_t>(1, (int64_t)std::min<unsigned __int128>(q, (unsigned __int128)INT32_MAX));
+  return (int32_t)std::min<int64_t>(cap, qi);
+}
+
+MOE_API const char* moe_last_error(const moe_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
+
+MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
+  moe_ctx* ctx = nullptr;
+  if (!cfg || !out) return MOE_EINVAL;
+  *out = nullptr;
+  const moe_config& c = *cfg;
+  if (c.n_layers < 1 || c.n_experts < 1 || c.n_experts > kMaxExperts || c.top_k < 1 || c.top_k > c.n_experts ||
+      c.hidden < 64 || c.hidden % 64 || c.inter < 64 || c.inter % 64 || c.max_tokens < 1 ||
+      (int64_t)c.n_layers * c.n_experts > (1 << 24) || c.wfmt < MOE_WFMT_F32 || c.wfmt > MOE_WFMT_FP4 ||
+      c.afmt < MOE_AFMT_F32 || c.afmt > MOE_AFMT_BF16 || !valid_mode(c.mode) ||
+      (int64_t)c.max_tokens * c.top_k > (1 << 22))
+    return MOE_EINVAL;
+  ctx = new moe_ctx();
+  ctx->cfg = c;
+  ctx->S = record_bytes(c);
+  ctx->stats = moe_stats{};
+  HIPCHK(hipGetDevice(&ctx->device));
+  const int L = c.n_layers, E = c.n_experts, H = c.hidden, I = c.inter, k = c.top_k;
+  const int64_t Pmax = (int64_t)c.max_tokens * k;
+  const int64_t Pdec = (int64_t)std::min(c.max_tokens, kDecodeMaxTok) * k;
+  auto cleanup_fail = [&](moe_status st) {
+    moe_destroy(ctx);
+    return st;
+  };
+  if (dev_alloc(&ctx->slot_of, (size_t)L * E) || dev_alloc(&ctx->key_of, kMaxCachedSlots) ||
+      dev_alloc(&ctx->stamp, kMaxCachedSlots) || dev_alloc(&ctx->reserved, kMaxCachedSlots) ||
+      dev_alloc(&ctx->counter, 1) || dev_alloc(&ctx->step_dev, C_COUNT + 5 * E) ||
+      dev_alloc(&ctx->u_slot, E) || dev_alloc(&ctx->u_evict, E) ||
+      dev_alloc(&ctx->grp_slot, std::max<int64_t>(E, Pmax)) || dev_alloc(&ctx->slot_scratch, Pmax) ||
+      dev_alloc(&ctx->pair_grp, Pmax) ||
+      dev_alloc(&ctx->logits, (size_t)c.max_tokens * E) || dev_alloc(&ctx->h, (size_t)Pdec * I) ||
+      dev_alloc(&ctx->dpair, (size_t)Pdec * H) || dev_alloc(&ctx->rowblock_done, decode_phase2_rowblocks(H)) ||
+      dev_alloc(&ctx->y_cpu_dev, (size_t)c.max_tokens * H) || dev_alloc(&ctx->perm, Pmax) ||
+      dev_alloc(&ctx->inv, Pmax) || dev_alloc(&ctx->offsets, std::max<int64_t>(E, Pmax) + 1) ||
+      dev_alloc(&ctx->tile_base, std::max<int64_t>(E, Pmax) + 1) ||
+      dev_alloc(&ctx->hist, (size_t)((Pmax + 255) / 256) * kMaxExperts) || dev_alloc(&ctx->cand, E) ||
+      dev_alloc(reinterpret_cast<uint8_t**>(&ctx->act), (size_t)Pmax * I * 4) ||
+      dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)))
+    return cleanup_fail(MOE_ENOMEM);
+  ctx->cnt = ctx->step_dev;
+  ctx->fill_key = ctx->cnt + C_COUNT;
+  ctx->fill_slot = ctx->fill_key + E;
+  ctx->cpu_key = ctx->fill_slot + E;
+  ctx->u_key = ctx->cpu_key + E;
+  ctx->u_kind = ctx->u_key + E;
+  if (hipMemset(ctx->slot_of, 0xff, (size_t)L * E * 4) || hipMemset(ctx->key_of, 0xff, kMaxCachedSlots * 4) ||
+      hipMemset(ctx->stamp, 0, kMaxCachedSlots * 8) || hipMemset(ctx->reserved, 0, kMaxCachedSlots) ||
+      hipMemset(ctx->counter, 0, 8) || hipMemset(ctx->rowblock_done, 0, decode_phase2_rowblocks(H) * 4) ||
+      hipMemset(ctx->step_dev, 0, (C_COUNT + 5 * E) * 4))
+    return cleanup_fail(MOE_EHIP);
+  // pinned host staging
+  if (hipHostMalloc(reinterpret_cast<void**>(&ctx->step_host), (C_COUNT + 5 * E) * 4, 0) ||
+      hipHostMalloc(reinterpret_cast<void**>(&ctx->h_slot_idx), Pmax * 4, 0) ||
+      hipHostMalloc(reinterpret_cast<void**>(&ctx->h_w), Pmax * 4, 0) ||
+      hipHostMalloc(&ctx->h_x, (size_t)c.max_tokens * H * 4, 0) ||
+      hipHostMalloc(reinterpret_cast<void**>(&ctx->h_xf), (size_t)c.max_tokens * H * 4, 0) ||
+      hipHostMalloc(reinterpret_cast<void**>(&ctx->h_y), (size_t)c.max_tokens * H * 4, 0) ||
+      hipHostMalloc(reinterpret_cast<void**>(&ctx->h_hbuf), (size_t)Pmax * I * 4, 0))
+    return cleanup_fail(MOE_ENOMEM);
+  ctx->h_cnt = ctx->step_host;
+  ctx->h_fill_key = ctx->h_cnt + C_COUNT;
+  ctx->h_fill_slot = ctx->h_fill_key + E;
+  ctx->h_cpu_key = ctx->h_fill_slot + E;
+  ctx->h_u_key = ctx->h_cpu_key + E;
+  ctx->h_u_kind = ctx->h_u_key + E;
+  std::memset(ctx->h_cnt, 0, C_COUNT * 4);
+  if (hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking) ||
+      hipEventCreateWithFlags(&ctx->ev_sync, hipEventDisableTiming) ||
+      hipEventCreateWithFlags(&ctx->ev_fill, hipEventDisableTiming) ||
+      hipEventCreateWithFlags(&ctx->ev_ycpu, hipEventDisableTiming) ||
+      hipEventCreateWithFlags(&ctx->ev_layer_copied[0], hipEventDisableTiming) ||
+      hipEventCreateWithFlags(&ctx->ev_layer_copied[1], hipEventDisableTiming) ||
+      hipEventCreateWithFlags(&ctx->ev_layer_done[0], hipEventDisableTiming) ||
+      hipEventCreateWithFlags(&ctx->ev_layer_done[1], hipEventDisableTiming))
+    return cleanup_fail(MOE_EHIP);
+  if (hipDeviceSynchronize() != hipSuccess) return cleanup_fail(MOE_EHIP);
+  *out = ctx;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_destroy(moe_ctx* ctx) {
+  if (!ctx) return MOE_EINVAL;
+  if (ctx->copy_stream) hipStreamSynchronize(ctx->copy_stream);
+  hipDeviceSynchronize();
+  delete ctx->cpu;
+  ctx->cpu = nullptr;
+  for (auto& t : ctx->pending_timed) {
+    hipEventDestroy(t.a);
+    hipEventDestroy(t.b);
+  }
+  for (auto e : ctx->event_pool) hipEventDestroy(e);
+  void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
+                 ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->rowblock_done, ctx->y_cpu_dev,
+                 ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
+                 ctx->flags};
+  for (void* p : dev)
+    if (p) hipFree(p);
+  void* host[] = {ctx->step_host, ctx->h_slot_idx, ctx->h_w, ctx->h_x, ctx->h_xf, ctx->h_y, ctx->h_hbuf};
+  for (void* p : host)
+    if (p) hipHostFree(p);
+  if (ctx->pool_owned && ctx->pool) hipHostFree(ctx->pool);
+  hipEvent_t evs[] = {ctx->ev_sync, ctx->ev_fill, ctx->ev_ycpu, ctx->ev_layer_copied[0], ctx->ev_layer_copied[1],
+                      ctx->ev_layer_done[0], ctx->ev_layer_done[1]};
+  for (auto e : evs)
+    if (e) hipEventDestroy(e);
+  if (ctx->copy_stream) hipStreamDestroy(ctx->copy_stream);
+  delete ctx;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_pool_alloc(moe_ctx* ctx, int64_t n_records, void** host_pool) {
+  if (!ctx || !host_pool) return MOE_EINVAL;
+  const int64_t nkeys = (int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts;
+  CHECK_ARG(n_records >= 1 && n_records <= nkeys, "n_records must be in [1, L*E]");
+  CHECK_ARG(!ctx->pool, "a pool is already set");
+  void* p = nullptr;
+  HIPCHK(hipHostMalloc(&p, (size_t)n_records * ctx->S, 0));
+  ctx->pool = static_cast<uint8_t*>(p);
+  ctx->pool_records = n_records;
+  ctx->pool_owned = true;
+  ctx->pool_pinned = true;
+  *host_pool = p;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_pool_register(moe_ctx* ctx, void* host_pool, int64_t n_records, int32_t pinned) {
+  if (!ctx) return MOE_EINVAL;
+  const int64_t nkeys = (int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts;
+  CHECK_ARG(host_pool && n_records >= 1 && n_records <= nkeys, "bad pool");
+  CHECK_ARG(!ctx->pool, "a pool is already set");
+  ctx->pool = static_cast<uint8_t*>(host_pool);
+  ctx->pool_records = n_records;
+  ctx->pool_owned = false;
+  ctx->pool_pinned = pinned != 0;
+  if (!ctx->pool_pinned && ctx->cfg.mode != MOE_MODE_CPU)
+    return fail(ctx, MOE_ENOPIN, "pageable pool: only MOE_MODE_CPU can run (every expert on the host)");
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_bind(moe_ctx* ctx, const float* router_w, void* arena, size_t arena_bytes, int32_t n_slots) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(router_w, "router weights required");
+  CHECK_ARG(!ctx->in_prefill, "bind inside prefill");
+  const int64_t nkeys = (int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts;
+  if (ctx->cfg.mode == MOE_MODE_FUSED) {
+    CHECK_ARG(n_slots >= nkeys, "FUSED mode needs n_slots >= L*E");
+  } else {
+    CHECK_ARG(n_slots >= 0 && n_slots <= kMaxCachedSlots, "n_slots must be in [0, 4096]");
+  }
+  CHECK_ARG(n_slots == 0 || (arena && arena_bytes >= (size_t)n_slots * ctx->S), "arena too small");
+  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(hipMemset(ctx->slot_of, 0xff, (size_t)nkeys * 4));
+  HIPCHK(hipMemset(ctx->key_of, 0xff, kMaxCachedSlots * 4));
+  HIPCHK(hipMemset(ctx->stamp, 0, kMaxCachedSlots * 8));
+  HIPCHK(hipMemset(ctx->reserved, 0, kMaxCachedSlots));
+  HIPCHK(hipMemset(ctx->counter, 0, 8));
+  HIPCHK(hipDeviceSynchronize());
+  ctx->router_w = router_w;
+  ctx->arena = static_cast<uint8_t*>(arena);
+  ctx->arena_bytes = arena_bytes;
+  ctx->n_slots = n_slots;
+  ctx->bound = true;
+  ctx->last_lookup_layer = -1;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_fused_load(moe_ctx* ctx, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(ctx->bound && ctx->pool, "bind and pool first");
+  CHECK_ARG(ctx->cfg.mode == MOE_MODE_FUSED, "FUSED mode only");
+  const int64_t nkeys = (int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts;
+  HIPCHK(copy_keys(ctx, 0, nkeys, 0, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_set_bandwidths(moe_ctx* ctx, uint64_t bw_pcie, uint64_t bw_host) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(bw_pcie > 0 && bw_host > 0 && bw_pcie < (1ull << 53) && bw_host < (1ull << 53), "bandwidths out of range");
+  ctx->cfg.bw_pcie = bw_pcie;
+  ctx->cfg.bw_host = bw_host;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_set_mode(moe_ctx* ctx, int32_t mode) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(valid_mode(mode), "bad mode");
+  CHECK_ARG((mode == MOE_MODE_FUSED) == (ctx->cfg.mode == MOE_MODE_FUSED), "FUSED <-> cached needs a new context");
+  CHECK_ARG(ctx->pool_pinned || mode == MOE_MODE_CPU, "pageable pool: only MOE_MODE_CPU");
+  ctx->cfg.mode = mode;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
+                             float* logits_out, int32_t* topk_idx, float* topk_w, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(ctx->router_w, "bind router weights first");
+  CHECK_ARG(layer >= 0 && layer < ctx->cfg.n_layers, "layer out of range");
+  CHECK_ARG(T >= 1 && T <= ctx->cfg.max_tokens, "T out of range");
+  CHECK_ARG(x && topk_idx && topk_w, "null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = ctx->cfg.n_experts, H = ctx->cfg.hidden;
+  float* z = logits_out ? logits_out : ctx->logits;
+  launch_route_logits(x, ctx->cfg.afmt, ctx->router_w + (int64_t)layer * E * H, logit_bias, z, T, E, H, s);
+  launch_topk(z, T, E, ctx->cfg.top_k, ctx->cfg.renorm, topk_idx, topk_w, s);
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_topk(moe_ctx* ctx, const float* logits, int32_t T, int32_t* topk_idx, float* topk_w,
+                            moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(T >= 1 && logits && topk_idx && topk_w, "bad arguments");
+  launch_topk(logits, T, ctx->cfg.n_experts, ctx->cfg.top_k, ctx->cfg.renorm, topk_idx, topk_w,
+              static_cast<hipStream_t>(stream));
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* topk_idx, int32_t T,
+                                       int32_t* slot_idx, moe_trace_rec* trace, int32_t* counts, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(ctx->bound, "bind first");
+  CHECK_ARG(!ctx->in_prefill, "decode lookup inside prefill");
+  CHECK_ARG(layer >= 0 && layer < ctx->cfg.n_layers, "layer out of range");
+  CHECK_ARG(T >= 1 && T <= ctx->cfg.max_tokens, "T out of range");
+  CHECK_ARG(topk_idx && slot_idx, "null pointer");
+  LookupArgs a;
+  fill_lookup_args(ctx, a, layer, topk_idx, T, lookup_mode_of(ctx->cfg.mode));
+  a.slot_idx = slot_idx;
+  a.trace = trace;
+  a.counts_out = counts;
+  launch_lookup(a, static_cast<hipStream_t>(stream));
+  HIPCHK(hipGetLastError());
+  ctx->last_lookup_layer = layer;
+  ctx->last_lookup_T = T;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
+                                  const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(x && topk_idx && topk_w && slot_idx && y, "null pointer");
+  CHECK_ARG(T >= 1 && T <= kDecodeMaxTok && (int64_t)T * ctx->cfg.hidden <= kDecodeMaxTH,
+            "decode needs T <= 8 and T*H <= 16384 (use moe_ffn_prefill)");
+  if (ctx->last_lookup_layer != layer || ctx->last_lookup_T != T)
+    return fail(ctx, MOE_ESTATE, "moe_ffn_decode must follow expert_cache_lookup of the same layer and T");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int k = ctx->cfg.top_k, E = ctx->cfg.n_experts, H = ctx->cfg.hidden, I = ctx->cfg.inter;
+  const int P = T * k;
+  const bool fused = ctx->cfg.mode == MOE_MODE_FUSED;
+  const bool profile = (ctx->cfg.flags & MOE_FLAG_PROFILE) != 0;
+  float* y_cpu = nullptr;
+  const bool inputs = !fused && may_use_cpu(ctx, P);
+  if (!fused || profile) {
+    moe_status st = read_step(ctx, s, inputs, x, topk_w, slot_idx, T);
+    if (st != MOE_OK) return st;
+  }
+  const bool has_cpu = !fused && ctx->h_cnt[C_CPU] > 0;
+  if (has_cpu && !inputs) {  // unexpected CPU work (e.g. every slot protected): fetch its inputs
+    moe_status st = read_step(ctx, s, true, x, topk_w, slot_idx, T);
+    if (st != MOE_OK) return st;
+  }
+  DecodeArgs d;
+  d.x = x;
+  d.w = topk_w;
+  d.arena = ctx->arena;
+  d.rec_bytes = ctx->S;
+  d.T = T;
+  d.k = k;
+  d.H = H;
+  d.I = I;
+  d.grp_slot = ctx->grp_slot;
+  d.pair_grp = ctx->pair_grp;
+  d.cnt = ctx->cnt;
+  d.h = ctx->h;
+  d.d = ctx->dpair;
+  d.rowblock_done = ctx->rowblock_done;
+  d.y = y;
+  const int max_groups = std::min(P, E);
+  if (!fused) {
+    moe_status st = issue_fills(ctx, s);
+    if (st != MOE_OK) return st;
+  }
+  {
+    TimedScope t1(ctx, s, TK_P1);
+    launch_decode_phase1(ctx->cfg.wfmt, ctx->cfg.afmt, d, max_groups, s);
+  }
+  {
+    TimedScope t2(ctx, s, TK_P2);
+    launch_decode_phase2(ctx->cfg.wfmt, d, max_groups, s);
+  }
+  if (has_cpu) {
+    // the GPU path is enqueued; the CPU branch runs now, concurrently, then merges exactly
+    moe_status st = run_cpu_branch(ctx, T, s, &y_cpu);
+    if (st != MOE_OK) return st;
+    launch_add_inplace(y, y_cpu, (int64_t)T * H, s);
+  }
+  HIPCHK(hipGetLastError());
+  if (profile) {
+    const int ngrp = ctx->h_cnt[C_NGRP];
+    const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
+    ctx->stats.phase1_launches += 1;
+    ctx->stats.phase2_launches += 1;
+    // algorithmic bytes: the GPU experts' gate+up rows, x once, h out / down rows, h in, y out
+    ctx->stats.phase1_bytes += (uint64_t)ngrp * 2 * I * wrow_h + (uint64_t)T * H * act_bytes(ctx->cfg) +
+                               (uint64_t)ctx->h_cnt[C_NPAIR_GPU] * I * 4;
+    ctx->stats.phase2_bytes += (uint64_t)ngrp * H * wrow_i + (uint64_t)ctx->h_cnt[C_NPAIR_GPU] * I * 4 +
+                               (uint64_t)T * H * 4;
+  }
+  ctx->stats.decode_calls += 1;
+  ctx->last_lookup_layer = -1;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- prefill
+namespace {
+
+moe_status prefill_gpu_part(moe_ctx* ctx, const void* x, int T, const float* w, float* y, const int32_t* pair_gpu,
+                            const float* y_cpu, bool do_combine, hipStream_t s) {
+  const int k = ctx->cfg.top_k, E = ctx->cfg.n_experts, H = ctx->cfg.hidden, I = ctx->cfg.inter;
+  const int P = T * k;
+  const int bm = prefill_bm();
+  launch_permute(ctx->pair_grp, ctx->cnt, P, E, ctx->hist, ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, bm, s);
+  PrefillArgs a;
+  a.x = x;
+  a.w = w;
+  a.arena = ctx->arena;
+  a.rec_bytes = ctx->S;
+  a.T = T;
+  a.k = k;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.grp_slot = ctx->grp_slot;
+  a.perm = ctx->perm;
+  a.inv = ctx->inv;
+  a.offsets = ctx->offsets;
+  a.tile_base = ctx->tile_base;
+  a.cnt = ctx->cnt;
+  a.act = ctx->act;
+  a.ypair = ctx->ypair;
+  a.y = y;
+  a.y_cpu = y_cpu;
+  a.pair_gpu = pair_gpu;
+  const int max_tiles_m = (P + bm - 1) / bm + std::min(E, P);
+  {
+    TimedScope t(ctx, s, TK_G1);
+    launch_prefill_gemm1(ctx->cfg.wfmt, ctx->cfg.afmt, a, max_tiles_m, s);
+  }
+  {
+    TimedScope t(ctx, s, TK_G2);
+    launch_prefill_gemm2(ctx->cfg.wfmt, a, max_tiles_m, s);
+  }
+  if (ctx->cfg.flags & MOE_FLAG_PROFILE) {
+    ctx->stats.gemm1_launches += 1;
+    ctx->stats.gemm2_launches += 1;
+  }
+  if (do_combine) launch_prefill_combine(a, s);
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+// Write the caller's trace (device) from host records.
+moe_status put_trace(moe_ctx* ctx, moe_trace_rec* trace, const std::vector<moe_trace_rec>& recs, hipStream_t s) {
+  if (!trace || recs.empty()) return MOE_OK;
+  HIPCHK(hipMemcpyAsync(trace, recs.data(), recs.size() * sizeof(moe_trace_rec), hipMemcpyHostToDevice, s));
+  HIPCHK(hipStreamSynchronize(s));
+  return MOE_OK;
+}
+
+moe_status put_counts(moe_ctx* ctx, int32_t* counts, const int32_t v[4], hipStream_t s) {
+  if (!counts) return MOE_OK;
+  HIPCHK(hipMemcpyAsync(counts, v, 4 * sizeof(int32_t), hipMemcpyHostToDevice, s));
+  HIPCHK(hipStreamSynchronize(s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_prefill_begin(moe_ctx* ctx, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(ctx->bound, "bind first");
+  if (ctx->in_prefill) return fail(ctx, MOE_ESTATE, "prefill already begun");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = ctx->cfg.n_experts, L = ctx->cfg.n_layers;
+  ctx->in_prefill = true;
+  ctx->prefill_buffers = false;
+  ctx->buffer_layer[0] = ctx->buffer_layer[1] = -1;
+  ctx->next_prefill_layer = 0;
+  const int mode = ctx->cfg.mode;
+  if ((mode == MOE_MODE_OFFLOAD || mode == MOE_MODE_HYBRID) && ctx->n_slots >= 2 * E) {
+    if (!ctx->pool_pinned) return fail(ctx, MOE_ENOPIN, "prefill buffers need a page-locked pool");
+    HIPCHK(hipStreamSynchronize(s));
+    launch_evict_range(ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, 0, 2 * E, 1, s);
+    HIPCHK(hipGetLastError());
+    HIPCHK(hipStreamSynchronize(s));
+    ctx->prefill_buffers = true;
+    for (int l = 0; l < std::min(2, L); ++l) {
+      TimedScope ts(ctx, ctx->copy_stream, TK_COPY);
+      HIPCHK(copy_keys(ctx, (int64_t)l * E, E, (int64_t)(l % 2) * E, ctx->copy_stream));
+      HIPCHK(hipEventRecord(ctx->ev_layer_copied[l % 2], ctx->copy_stream));
+      ctx->stats.copy_bytes += (uint64_t)E * ctx->S;
+    }
+  }
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_ffn_prefill(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
+                                   const float* topk_w, float* y, moe_trace_rec* trace, int32_t* counts,
+                                   moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  if (!ctx->in_prefill) return fail(ctx, MOE_ESTATE, "moe_prefill_begin first");
+  CHECK_ARG(layer >= 0 && layer < ctx->cfg.n_layers, "layer out of range");
+  CHECK_ARG(T >= 1 && T <= ctx->cfg.max_tokens, "T out of range");
+  CHECK_ARG(x && topk_idx && topk_w && y, "null pointer");
+  if (ctx->cfg.wfmt != MOE_WFMT_F32 && ctx->cfg.hidden % 128)
+    return fail(ctx, MOE_ENOTSUP, "MFMA prefill needs hidden % 128 == 0");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int k = ctx->cfg.top_k, E = ctx->cfg.n_experts, L = ctx->cfg.n_layers, P = T * k;
+  const int mode = ctx->cfg.mode;
+  ctx->stats.prefill_calls += 1;
+  if (ctx->cfg.flags & MOE_FLAG_PROFILE) ctx->stats.gemm_flops += 2.0 * P * 3.0 * ctx->cfg.hidden * ctx->cfg.inter;
+
+  if (ctx->prefill_buffers) {
+    if (layer != ctx->next_prefill_layer)
+      return fail(ctx, MOE_ESTATE, "buffered prefill runs layers 0..L-1 in ascending order");
+    const int b = layer % 2;
+    HIPCHK(hipStreamWaitEvent(s, ctx->ev_layer_copied[b], 0));
+    LookupArgs a;
+    fill_lookup_args(ctx, a, layer, topk_idx, T, LK_BUFFER);
+    a.buffer_base = b * E;
+    a.slot_idx = ctx->slot_scratch;
+    a.trace = trace;
+    a.counts_out = counts;
+    launch_lookup(a, s);
+    moe_status st = prefill_gpu_part(ctx, x, T, topk_w, y, nullptr, nullptr, true, s);
+    if (st != MOE_OK) return st;
+    HIPCHK(hipEventRecord(ctx->ev_layer_done[b], s));
+    ctx->buffer_layer[b] = layer;
+    if (layer + 2 < L) {
+      HIPCHK(hipStreamWaitEvent(ctx->copy_stream, ctx->ev_layer_done[b], 0));
+      TimedScope ts(ctx, ctx->copy_stream, TK_COPY);
+      HIPCHK(copy_keys(ctx, (int64_t)(layer + 2) * E, E, (int64_t)b * E, ctx->copy_stream));
+      HIPCHK(hipEventRecord(ctx->ev_layer_copied[b], ctx->copy_stream));
+      ctx->stats.copy_bytes += (uint64_t)E * ctx->S;
+    }
+    ctx->next_prefill_layer = layer + 1;
+    return MOE_OK;
+  }
+
+  if (mode == MOE_MODE_FUSED || mode == MOE_MODE_CPU) {
+    LookupArgs a;
+    fill_lookup_args(ctx, a, layer, topk_idx, T, lookup_mode_of(mode));
+    a.slot_idx = ctx->slot_scratch;
+    a.trace = trace;
+    a.counts_out = counts;
+    launch_lookup(a, s);
+    HIPCHK(hipGetLastError());
+    float* y_cpu = nullptr;
+    if (mode == MOE_MODE_CPU) {
+      moe_status st = read_step(ctx, s, true, x, topk_w, ctx->slot_scratch, T);
+      if (st != MOE_OK) return st;
+      // GPU part for the hits first, then the CPU branch; the combine adds both
+      st = prefill_gpu_part(ctx, x, T, topk_w, y, ctx->pair_grp, nullptr, false, s);
+      if (st != MOE_OK) return st;
+      st = run_cpu_branch(ctx, T, s, &y_cpu);
+      if (st != MOE_OK) return st;
+      PrefillArgs c{};
+      c.w = topk_w;
+      c.T = T;
+      c.k = k;
+      c.H = ctx->cfg.hidden;
+      c.ypair = ctx->ypair;
+      c.y = y;
+      c.y_cpu = y_cpu;
+      c.pair_gpu = ctx->pair_grp;
+      launch_prefill_combine(c, s);
+      HIPCHK(hipGetLastError());
+      return MOE_OK;
+    }
+    return prefill_gpu_part(ctx, x, T, topk_w, y, ctx->pair_grp, y_cpu, true, s);
+  }
+
+  // On-demand prefill: offload lookups in rounds; a round's leftover misses wait for the next.
+  if (ctx->n_slots == 0) return fail(ctx, MOE_ENOTSUP, "on-demand prefill needs at least one slot");
+  if (!ctx->pool_pinned) return fail(ctx, MOE_ENOPIN, "fills need a page-locked host pool");
+  std::vector<moe_trace_rec> final_recs;
+  std::vector<int> pending;
+  int32_t tot[4] = {0, 0, 0, 0};
+  bool first = true;
+  int guard = 0;
+  while (first || !pending.empty()) {
+    if (++guard > 4 * E + 4) return fail(ctx, MOE_ESTATE, "on-demand prefill did not converge");
+    LookupArgs a;
+    fill_lookup_args(ctx, a, layer, topk_idx, T, LK_OFFLOAD);
+    a.slot_idx = ctx->slot_scratch;
+    if (!first) {
+      HIPCHK(hipMemcpyAsync(ctx->cand, pending.data(), pending.size() * 4, hipMemcpyHostToDevice, s));
+      a.cand = ctx->cand;
+      a.n_cand = (int)pending.size();
+    }
+    launch_lookup(a, s);
+    HIPCHK(hipGetLastError());
+    moe_status st = read_step(ctx, s, false, nullptr, nullptr, nullptr, T);
+    if (st != MOE_OK) return st;
+    const int nU = ctx->h_cnt[C_NU];
+    std::vector<int32_t> u_slot(nU), u_evict(nU);
+    HIPCHK(hipMemcpy(u_slot.data(), ctx->u_slot, nU * 4, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(u_evict.data(), ctx->u_evict, nU * 4, hipMemcpyDeviceToHost));
+    pending.clear();
+    for (int u = 0; u < nU; ++u) {
+      const int kind = ctx->h_u_kind[u];
+      if (kind == MOE_KIND_CPU) {
+        pending.push_back(ctx->h_u_key[u]);
+      } else {
+        final_recs.push_back(moe_trace_rec{ctx->h_u_key[u], kind, u_slot[u], u_evict[u]});
+      }
+    }
+    tot[0] += ctx->h_cnt[C_HIT];
+    tot[1] += ctx->h_cnt[C_FILL];
+    tot[3] += ctx->h_cnt[C_EVICT];
+    st = issue_fills(ctx, s);
+    if (st != MOE_OK) return st;
+    st = prefill_gpu_part(ctx, x, T, topk_w, y, nullptr, nullptr, false, s);
+    if (st != MOE_OK) return st;
+    if (!pending.empty()) HIPCHK(hipStreamSynchronize(s));  // the next round may evict this round's slots
+    first = false;
+  }
+  // records in U order of the first appearance over (token, rank) pairs
+  {
+    std::vector<int32_t> idx((size_t)P);
+    HIPCHK(hipMemcpy(idx.data(), topk_idx, (size_t)P * 4, hipMemcpyDeviceToHost));
+    std::vector<int> order;
+    std::vector<char> seen(E, 0);
+    for (int p = 0; p < P; ++p)
+      if (idx[p] >= 0 && idx[p] < E && !seen[idx[p]]) {
+        seen[idx[p]] = 1;
+        order.push_back(layer * E + idx[p]);
+      }
+    std::vector<moe_trace_rec> sorted;
+    for (int key : order)
+      for (auto& r : final_recs)
+        if (r.key == key) {
+          sorted.push_back(r);
+          break;
+        }
+    moe_status st = put_trace(ctx, trace, sorted, s);
+    if (st != MOE_OK) return st;
+  }
+  moe_status st = put_counts(ctx, counts, tot, s);
+  if (st != MOE_OK) return st;
+  PrefillArgs a{};
+  a.w = topk_w;
+  a.T = T;
+  a.k = k;
+  a.H = ctx->cfg.hidden;
+  a.ypair = ctx->ypair;
+  a.y = y;
+  launch_prefill_combine(a, s);
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_prefill_end(moe_ctx* ctx, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  if (!ctx->in_prefill) return fail(ctx, MOE_ESTATE, "no prefill in progress");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIPCHK(hipStreamSynchronize(ctx->copy_stream));
+  HIPCHK(hipStreamSynchronize(s));
+  const int E = ctx->cfg.n_experts;
+  if (ctx->prefill_buffers) {
+    std::vector<std::pair<int, int>> held;
+    for (int b = 0; b < 2; ++b)
+      if (ctx->buffer_layer[b] >= 0) held.push_back({ctx->buffer_layer[b], b});
+    std::sort(held.begin(), held.end());
+    for (auto& hb : held)
+      launch_admit_buffer(ctx->slot_of, ctx->key_of, ctx->stamp, ctx->counter, hb.first, E, hb.second * E, s);
+    launch_evict_range(ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, 0, 2 * E, 0, s);
+    HIPCHK(hipGetLastError());
+    HIPCHK(hipStreamSynchronize(s));
+  }
+  ctx->in_prefill = false;
+  ctx->prefill_buffers = false;
+  ctx->buffer_layer[0] = ctx->buffer_layer[1] = -1;
+  ctx->last_lookup_layer = -1;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_permute(moe_ctx* ctx, const int32_t* slot_idx, int32_t T, int32_t* perm, int32_t* offsets,
+                               int32_t* group_slot, int32_t* n_groups, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(T >= 1 && T <= ctx->cfg.max_tokens, "T out of range");
+  CHECK_ARG(slot_idx && perm && offsets && group_slot && n_groups, "null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int P = T * ctx->cfg.top_k;
+  const int nrange = (int)std::max<int64_t>((int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts, kMaxCachedSlots);
+  // groups are indexed by distinct slot; up to min(P, nrange) of them
+  launch_groups_from_slots(slot_idx, P, ctx->pair_grp, group_slot, ctx->cnt, ctx->flags, nrange, s);
+  const int gmax = std::min(P, kMaxExperts);
+  HIPCHK(hipMemcpyAsync(ctx->h_cnt, ctx->cnt, C_COUNT * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  if (ctx->h_cnt[C_ERR]) return fail(ctx, MOE_EINVAL, "slot id out of range");
+  if (ctx->h_cnt[C_NGRP] > gmax) return fail(ctx, MOE_ENOTSUP, "more than 1024 distinct slots");
+  launch_permute(ctx->pair_grp, ctx->cnt, P, gmax, ctx->hist, perm, ctx->inv, offsets, ctx->tile_base, prefill_bm(), s);
+  HIPCHK(hipMemcpyAsync(n_groups, ctx->cnt + C_NGRP, 4, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipGetLastError());
+  return MOE_OK;
+}
+
+MOE_API moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_n_slots, void* new_arena, size_t new_arena_bytes,
+                                       moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  if (ctx->in_prefill) return fail(ctx, MOE_ESTATE, "resize inside prefill");
+  if (ctx->cfg.mode == MOE_MODE_FUSED) return fail(ctx, MOE_ENOTSUP, "FUSED mode has no cache to resize");
+  CHECK_ARG(ctx->bound, "bind first");
+  CHECK_ARG(new_n_slots >= 0 && new_n_slots <= kMaxCachedSlots, "n_slots must be in [0, 4096]");
+  uint8_t* dst = new_arena ? static_cast<uint8_t*>(new_arena) : ctx->arena;
+  const size_t dst_bytes = new_arena ? new_arena_bytes : ctx->arena_bytes;
+  CHECK_ARG(new_n_slots == 0 || (dst && dst_bytes >= (size_t)new_n_slots * ctx->S), "arena too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIPCHK(hipStreamSynchronize(s));
+  HIPCHK(hipStreamSynchronize(ctx->copy_stream));
+  const int N = ctx->n_slots;
+  const int64_t nkeys = (int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts;
+  std::vector<int32_t> key_of(std::max(N, 1));
+  std::vector<uint64_t> stamp(std::max(N, 1));
+  if (N > 0) {
+    HIPCHK(hipMemcpy(key_of.data(), ctx->key_of, N * 4, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(stamp.data(), ctx->stamp, N * 8, hipMemcpyDeviceToHost));
+  }
+  std::vector<int> occupied;
+  for (int sl = 0; sl < N; ++sl)
+    if (key_of[sl] >= 0) occupied.push_back(sl);
+  std::vector<std::pair<int, int>> moves;  // (old slot, new slot)
+  if (new_n_slots < N) {
+    std::vector<int> by_recency = occupied;
+    std::sort(by_recency.begin(), by_recency.end(), [&](int a, int b) {
+      return stamp[a] != stamp[b] ? stamp[a] > stamp[b] : a < b;
+    });
+    if ((int)by_recency.size() > new_n_slots) by_recency.resize(new_n_slots);
+    std::sort(by_recency.begin(), by_recency.end());
+    for (int i = 0; i < (int)by_recency.size(); ++i) moves.push_back({by_recency[i], i});
+  } else {
+    for (int sl : occupied) moves.push_back({sl, sl});
+  }
+  // move records: ascending old slots; a destination never precedes a source still unread
+  for (auto& mv : moves) {
+    if (mv.first == mv.second && dst == ctx->arena) continue;
+    HIPCHK(hipMemcpyAsync(dst + (int64_t)mv.second * ctx->S, ctx->arena + (int64_t)mv.first * ctx->S, ctx->S,
+                          hipMemcpyDeviceToDevice, s));
+  }
+  std::vector<int32_t> new_key(std::max(new_n_slots, 1), -1), slot_of(nkeys, -1);
+  std::vector<uint64_t> new_stamp(std::max(new_n_slots, 1), 0);
+  for (auto& mv : moves) {
+    new_key[mv.second] = key_of[mv.first];
+    new_stamp[mv.second] = stamp[mv.first];
+    slot_of[key_of[mv.first]] = mv.second;
+  }
+  HIPCHK(hipMemcpyAsync(ctx->slot_of, slot_of.data(), nkeys * 4, hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemsetAsync(ctx->key_of, 0xff, kMaxCachedSlots * 4, s));
+  HIPCHK(hipMemsetAsync(ctx->stamp, 0, kMaxCachedSlots * 8, s));
+  HIPCHK(hipMemsetAsync(ctx->reserved, 0, kMaxCachedSlots, s));
+  if (new_n_slots > 0) {
+    HIPCHK(hipMemcpyAsync(ctx->key_of, new_key.data(), new_n_slots * 4, hipMemcpyHostToDevice, s));
+    HIPCHK(hipMemcpyAsync(ctx->stamp, new_stamp.data(), new_n_slots * 8, hipMemcpyHostToDevice, s));
+  }
+  HIPCHK(hipStreamSynchronize(s));
+  ctx->arena = dst;
+  ctx->arena_bytes = dst_bytes;
+  ctx->n_slots = new_n_slots;
+  ctx->last_lookup_layer = -1;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_bench_bw(moe_ctx* ctx, uint64_t* bw_pcie, uint64_t* bw_host) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(ctx->pool && bw_pcie && bw_host, "pool and outputs required");
+  const int64_t S = ctx->S;
+  const int nrec = (int)std::min<int64_t>(ctx->pool_records, 32);
+  // B_P: pinned pool -> device, whole records
+  uint8_t* scratch = nullptr;
+  HIPCHK(hipMalloc(&scratch, (size_t)S * 2));
+  hipEvent_t e0, e1;
+  HIPCHK(hipEventCreate(&e0));
+  HIPCHK(hipEventCreate(&e1));
+  double best_p = 0.0;
+  if (ctx->pool_pinned) {
+    for (int rep = 0; rep < 3; ++rep) {
+      HIPCHK(hipEventRecord(e0, ctx->copy_stream));
+      for (int i = 0; i < 4 * nrec; ++i)
+        HIPCHK(hipMemcpyAsync(scratch + (i & 1) * S, ctx->pool + (int64_t)(i % nrec) * S, S, hipMemcpyHostToDevice,
+                              ctx->copy_stream));
+      HIPCHK(hipEventRecord(e1, ctx->copy_stream));
+      HIPCHK(hipEventSynchronize(e1));
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+      if (rep > 0) best_p = std::max(best_p, (double)S * 4 * nrec / (ms * 1e-3));
+    }
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  hipFree(scratch);
+  // B_H: the CPU branch at batch 1 over distinct records
+  const int H = ctx->cfg.hidden, I = ctx->cfg.inter, k = ctx->cfg.top_k;
+  const int ncpu = std::min(nrec, k);
+  std::vector<float> x(H, 0.01f), w(k, 1.0f / k), y(H), h((size_t)k * I);
+  std::vector<int32_t> sidx(k);
+  for (int j = 0; j < k; ++j) sidx[j] = (j < ncpu) ? -1 - j : 0;
+  double best_h = 0.0;
+  for (int rep = 0; rep < 4; ++rep) {
+    CpuFfnJob job;
+    job.wfmt = ctx->cfg.wfmt;
+    job.H = H;
+    job.I = I;
+    job.T = 1;
+    job.k = k;
+    job.rec_bytes = S;
+    job.x = x.data();
+    job.w = w.data();
+    job.slot_idx = sidx.data();
+    for (int c = 0; c < ncpu; ++c) job.rec.push_back(ctx->pool + (int64_t)((rep * ncpu + c) % nrec) * S);
+    job.h = h.data();
+    job.y = y.data();
+    const auto t0 = std::chrono::steady_clock::now();
+    cpu_ffn(cpu_pool(ctx), job);
+    const double sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    if (rep > 0) best_h = std::max(best_h, (double)S * ncpu / sec);
+  }
+  *bw_pcie = (uint64_t)best_p;
+  *bw_host = (uint64_t)best_h;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, uint64_t* stamp,
+                                      uint64_t* counter, int32_t* n_slots) {
+  if (!ctx) return MOE_EINVAL;
+  HIPCHK(hipDeviceSynchronize());
+  const int64_t nkeys = (int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts;
+  const int N = ctx->n_slots;
+  const int Ncap = std::min(N, kMaxCachedSlots);
+  if (slot_of) HIPCHK(hipMemcpy(slot_of, ctx->slot_of, nkeys * 4, hipMemcpyDeviceToHost));
+  if (key_of && Ncap > 0) HIPCHK(hipMemcpy(key_of, ctx->key_of, Ncap * 4, hipMemcpyDeviceToHost));
+  if (stamp && Ncap > 0) HIPCHK(hipMemcpy(stamp, ctx->stamp, Ncap * 8, hipMemcpyDeviceToHost));
+  if (counter) HIPCHK(hipMemcpy(counter, ctx->counter, 8, hipMemcpyDeviceToHost));
+  if (n_slots) *n_slots = N;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
+  if (!ctx || !out) return MOE_EINVAL;
+  drain_timed(ctx);
+  *out = ctx->stats;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_reset_stats(moe_ctx* ctx) {
+  if (!ctx) return MOE_EINVAL;
+  drain_timed(ctx);
+  ctx->stats = moe_stats{};
+  return MOE_OK;
+}
+
+}  // extern "C"

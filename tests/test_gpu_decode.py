@@ -1,0 +1,95 @@
+"""GPU parity: the decode path (lookup -> fills / CPU branch -> GEMV phases -> combine)
+against the oracle's all-resident output and cache traces, per mode and format."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from moe_harness import Harness, row_rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+BF16 = W.A3B_DECODE.with_(name="dec_bf16", n_layers=2, n_experts=16, top_k=4, hidden=256, inter=128)
+FP4 = W.DSV4.with_(name="dec_fp4", n_layers=2, n_experts=16, top_k=3, hidden=256, inter=128)
+FMT = {"fp32": W.TINY, "bf16": BF16, "fp4": FP4}
+
+
+def _gates(wl, step, layer, T):
+    u = wl.uniforms(1000 + step * 64 + layer, T * wl.top_k).reshape(T, wl.top_k) + 0.05
+    return (u / u.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def _expected(wl, layer, x, idx, w):
+    x64 = oracle.formats.activations_f64(x)
+    outs = oracle.moe_layer_dense(x64, idx, lambda e: oracle.expert_weights_f64(wl, layer * wl.n_experts + e))
+    return oracle.moe_combine(outs, w)
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4"])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_matches_oracle(fmt, mode, T):
+    import routed_expert_ffn_02_amd as R
+    wl = FMT[fmt]
+    if wl.top_k * T > wl.n_experts * 2:
+        pytest.skip("shape")
+    n_slots = max(2, wl.n_keys // 3)
+    bw = (25_000_000_000, 100_000_000_000)
+    h = Harness(wl, mode, n_slots=n_slots, bw=bw)
+    ref = oracle.ExpertCache(wl.n_layers, wl.n_experts, n_slots)
+    routes = {l: wl.synthetic_routing(10, l, T) for l in range(wl.n_layers)}
+    for step in range(10):
+        for layer in range(wl.n_layers):
+            idx = routes[layer][step]
+            x = wl.decode_activations(step, layer, T)
+            w = _gates(wl, step, layer, T)
+            y, slot, trace, cnt = h.decode(layer, x, idx, w)
+            assert row_rel_err(y, _expected(wl, layer, x, idx, w)) <= tol_for(wl), (step, layer)
+            if mode != R.MOE_MODE_FUSED:
+                r = ref.lookup(layer, idx, mode, *bw)
+                assert trace == r.trace and np.array_equal(slot, r.slot_idx), (step, layer)
+    st = R.moe_get_stats(h.ctx)
+    if mode in (R.MOE_MODE_CPU, R.MOE_MODE_HYBRID):
+        assert st["cpu_experts"] > 0
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4"])
+def test_full_residency_bit_identical_to_fused(fmt):
+    """Once every expert is resident, the cached path equals the all-resident path bit for bit."""
+    import routed_expert_ffn_02_amd as R
+    wl = FMT[fmt]
+    fused = Harness(wl, R.MOE_MODE_FUSED)
+    cached = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=wl.n_keys)
+    for layer in range(wl.n_layers):   # warm: touch every expert
+        for e0 in range(0, wl.n_experts, wl.top_k):
+            idx = np.array([[(e0 + j) % wl.n_experts for j in range(wl.top_k)]])
+            x = wl.decode_activations(99, layer, 1)
+            cached.decode(layer, x, idx, _gates(wl, 99, layer, 1))
+    for step in range(6):
+        for layer in range(wl.n_layers):
+            idx = wl.synthetic_routing(6, layer, 2)[step]
+            x = wl.decode_activations(step, layer, 2)
+            w = _gates(wl, step, layer, 2)
+            ya, _, _, _ = fused.decode(layer, x, idx, w)
+            yb, _, trace, cnt = cached.decode(layer, x, idx, w)
+            assert cnt[1] == 0 and cnt[2] == 0          # all hits
+            assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), (step, layer)
+
+
+def test_decode_requires_lookup_first():
+    import routed_expert_ffn_02_amd as R
+    import torch
+    h = Harness(BF16, R.MOE_MODE_OFFLOAD, n_slots=8)
+    x = torch.zeros((1, BF16.hidden), dtype=torch.int16, device="cuda")
+    idx = torch.zeros((1, BF16.top_k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((1, BF16.top_k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((1, BF16.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(R.MoeError) as e:
+        R.moe_ffn_decode(h.ctx, 0, x, 1, idx, w, idx, y)
+    assert e.value.status == R.MOE_ESTATE
+    bad = torch.full((1, BF16.top_k), BF16.n_experts + 3, dtype=torch.int32, device="cuda")
+    slot = torch.empty_like(bad)
+    R.expert_cache_lookup(h.ctx, 0, bad, 1, slot)
+    with pytest.raises(R.MoeError) as e:
+        R.moe_ffn_decode(h.ctx, 0, x, 1, bad, w, slot, y)
+    assert e.value.status == R.MOE_EINVAL

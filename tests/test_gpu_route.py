@@ -1,0 +1,63 @@
+"""GPU parity: router logits, top-k and gates (moe_route, moe_topk) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from moe_harness import Harness, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = W.A3B_DECODE.with_(name="small_bf16", n_layers=2, n_experts=64, top_k=4, hidden=256, inter=128,
+                                n_slots=24)
+
+
+def test_topk_bitexact_on_identical_logits():
+    """Decisions taken on the same fp32 logits: indices bit-exact, ties to the lower index."""
+    import routed_expert_ffn_02_amd as R
+    for E, k in ((8, 2), (256, 8), (256, 6), (1024, 16)):
+        wl = W.TINY.with_(n_experts=E, top_k=k)
+        h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=1)
+        rng = np.random.default_rng(E + k)
+        T = 37
+        z = (rng.integers(-6, 7, size=(T, E)) / 8.0).astype(np.float32)   # many exact ties
+        z[0] = 0.0
+        z[1, ::2] = -0.0
+        zt = torch.from_numpy(z).cuda()
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        R.moe_topk(h.ctx, zt, T, idx, w)
+        torch.cuda.synchronize()
+        ref_idx, ref_w = oracle.route(z, k, 0)
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), (E, k)
+        np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-9)
+
+
+@pytest.mark.parametrize("wl,T", [(W.TINY, 1), (W.TINY, 16), (SMALL_BF16, 1), (SMALL_BF16, 4), (SMALL_BF16, 96),
+                                  (W.A3B_DECODE.with_(n_layers=2), 1), (W.A3B_DECODE.with_(n_layers=2), 300)])
+def test_route_matches_oracle(wl, T):
+    import routed_expert_ffn_02_amd as R
+    h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=1, max_tokens=max(T, 8))
+    orc = oracle.OracleMoE(wl)
+    for layer in range(min(2, wl.n_layers)):
+        x = wl.prefill_activations(layer, T) if T > 8 else wl.decode_activations(7, layer, T)
+        bias = np.tile(wl.zipf_bias(layer), (T, 1))
+        z, idx, w = h.route(layer, x, bias)
+        rz, ridx, rw = orc.route(layer, x, bias)
+        scale = np.abs(rz).max()
+        assert np.abs(z - rz).max() <= 1e-5 * scale
+        # identical decisions wherever the oracle's order has a margin above the logit error
+        ambiguous = 0
+        for t in range(T):
+            srt = np.sort(rz[t].astype(np.float64))[::-1][: wl.top_k + 1]
+            margin = np.min(np.abs(np.diff(srt))) if len(srt) > 1 else np.inf
+            if margin > 4e-6 * scale:
+                assert np.array_equal(idx[t], ridx[t]), (layer, t)
+                np.testing.assert_allclose(w[t], rw[t], rtol=1e-5)
+            else:
+                ambiguous += 1
+                # any valid choice: every selected logit within the error bound of the k-th largest
+                kth = srt[wl.top_k - 1]
+                assert np.all(rz[t][idx[t]] >= kth - 4e-6 * scale)
+        assert ambiguous <= max(1, T // 50)
