@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE layer over a bounded shared expert cache (one MI355X).
+
+A step is one decode token through every MoE layer: router softmax/top-k, cache
+lookup with LRU update, fills of misses from the pinned host pool, the SwiGLU
+expert GEMVs and the rank-order combine.  Default workload: the 35B-A3B shape
+(40 layers, 256 experts, top-8, hidden 2048, expert intermediate 512, bf16
+weights, a 64,424,509,440-byte pinned host pool), batch 1, a 1280-slot cache
+(12.5% of the pool), cold start, misses filled over PCIe (offload mode).
+Routing has temporal locality: a per-layer Zipf(1.1) popularity bias plus a
+bonus for the previous token's experts at the same layer.
+
+After the timed decode, a prefill leg streams a 4096-token prompt through all
+layers with full-layer double buffering (reported beside the headline value).
+
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="a3b", choices=["a3b", "dsv4"])
+    ap.add_argument("--mode", default="offload", choices=["offload", "hybrid", "fused"])
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--alias-records", type=int, default=0,
+                    help="back keys by key %% R records (smaller host pool; same transfer sizes)")
+    return ap.parse_args()
+
+
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of this build",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import routed_expert_ffn_02_amd as R
+    import workloads as W
+
+    wl = W.A3B_DECODE if args.config == "a3b" else W.DSV4
+    if args.alias_records:
+        wl = wl.with_(alias_records=args.alias_records)
+    mode = {"offload": R.MOE_MODE_OFFLOAD, "hybrid": R.MOE_MODE_HYBRID, "fused": R.MOE_MODE_FUSED}[args.mode]
+    L, E, k, H = wl.n_layers, wl.n_experts, wl.top_k, wl.hidden
+    T = wl.tokens
+    total_steps = args.warmup + args.steps
+    dev = torch.device("cuda:0")
+
+    # ---------------------------------------------------------------- set-up (untimed)
+    t0 = time.time()
+    prompt = W.A3B_PREFILL.prefill_tokens if args.config == "a3b" else wl.prefill_tokens
+    max_tokens = 8 if args.no_prefill else max(8, prompt)
+    cfg = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, max_tokens, mode, wl.renorm,
+                        flags=R.MOE_FLAG_PROFILE)
+    ctx = R.moe_create(cfg)
+    S = R.moe_record_bytes(cfg)
+    pool = R.moe_pool_alloc(ctx, wl.pool_records)
+    wl.fill_pool(pool, 0, wl.pool_records, threads=min(16, len(os.sched_getaffinity(0))))
+    log(f"pool: {wl.pool_records} records x {S} B = {wl.pool_records * S / 1e9:.1f} GB in {time.time() - t0:.1f}s")
+    router = torch.from_numpy(np.stack([wl.router_weight(l) for l in range(L)])).to(dev)
+    n_slots = L * E if mode == R.MOE_MODE_FUSED else wl.n_slots
+    arena = torch.empty(n_slots * S, dtype=torch.uint8, device=dev)
+    R.moe_bind(ctx, router, arena, arena.numel(), n_slots)
+    if mode == R.MOE_MODE_FUSED:
+        R.moe_fused_load(ctx)
+    bw_p, bw_h = R.moe_bench_bw(ctx)
+    R.moe_set_bandwidths(ctx, max(bw_p, 1), max(bw_h, 1))
+    log(f"B_P = {bw_p / 1e9:.1f} GB/s, B_H = {bw_h / 1e9:.1f} GB/s")
+
+    # activations for every (step, layer), resident in HBM before timing
+    X = np.empty((total_steps, L, T, H), np.uint16)
+    for s in range(total_steps):
+        for l in range(L):
+            X[s, l] = wl.decode_activations(s, l, T)
+    Xd = torch.from_numpy(X.view(np.int16)).to(dev)
+    zipf = torch.from_numpy(np.stack([wl.zipf_bias(l) for l in range(L)])).to(dev)        # [L, E]
+    bias = torch.empty((L, T, E), dtype=torch.float32, device=dev)
+    bonus = torch.full((T, k), float(wl.prev_bonus), dtype=torch.float32, device=dev)
+    idx = torch.zeros((L, T, k), dtype=torch.int32, device=dev)
+    idx64 = torch.zeros((T, k), dtype=torch.int64, device=dev)
+    wts = torch.zeros((L, T, k), dtype=torch.float32, device=dev)
+    slot = torch.zeros((L, T, k), dtype=torch.int32, device=dev)
+    y = torch.zeros((L, T, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    log(f"set-up {time.time() - t0:.1f}s")
+
+    def step(s):
+        for l in range(L):
+            b = bias[l]
+            b.copy_(zipf[l].expand(T, E))
+            if s > 0 and wl.prev_bonus:
+                idx64.copy_(idx[l])
+                b.scatter_add_(1, idx64, bonus)
+            x = Xd[s, l]
+            R.moe_route(ctx, l, x, T, b, None, idx[l], wts[l], stream)
+            R.expert_cache_lookup(ctx, l, idx[l], T, slot[l], None, None, stream)
+            R.moe_ffn_decode(ctx, l, x, T, idx[l], wts[l], slot[l], y[l], stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    R.moe_reset_stats(ctx)
+    t1 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        step(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t1
+    st = R.moe_get_stats(ctx)
+    tok_s = args.steps * T / elapsed
+    lookups = max(1, st["lookups"])
+    distinct = st["hits"] + st["fills"] + st["cpu_experts"]
+    miss_rate = (st["fills"] + st["cpu_experts"]) / max(1, distinct)
+    p1_avg_ms = st["phase1_ms"] / max(1, st["phase1_launches"])
+    p2_avg_ms = st["phase2_ms"] / max(1, st["phase2_launches"])
+    p1_bytes = st["phase1_bytes"] / max(1, st["phase1_launches"])
+    p2_bytes = st["phase2_bytes"] / max(1, st["phase2_launches"])
+    p1_gbs = p1_bytes / (p1_avg_ms * 1e-3) / 1e9 if p1_avg_ms > 0 else 0.0
+    p2_gbs = p2_bytes / (p2_avg_ms * 1e-3) / 1e9 if p2_avg_ms > 0 else 0.0
+    log(f"decode: {tok_s:.1f} tok/s, miss rate {miss_rate:.3f}, phase1 {p1_avg_ms * 1e3:.1f} us "
+        f"{p1_gbs:.0f} GB/s, phase2 {p2_avg_ms * 1e3:.1f} us {p2_gbs:.0f} GB/s")
+    decode_detail = {
+        "miss_rate": round(miss_rate, 4), "fills": st["fills"], "cpu_experts": st["cpu_experts"],
+        "fill_GBps_wall": round(st["fill_bytes"] / elapsed / 1e9, 2),
+        "copy_engine_ms": round(st["copy_ms"], 2),
+        "phase1_avg_us": round(p1_avg_ms * 1e3, 2), "phase1_GBps": round(p1_gbs, 1),
+        "phase2_avg_us": round(p2_avg_ms * 1e3, 2), "phase2_GBps": round(p2_gbs, 1),
+        "bw_pcie_GBps": round(bw_p / 1e9, 2), "bw_host_GBps": round(bw_h / 1e9, 2), "lookups": lookups,
+    }
+
+    # ---------------------------------------------------------------- prefill leg
+    prefill = None
+    if not args.no_prefill and mode != R.MOE_MODE_FUSED:
+        Tp = cfg.max_tokens
+        R.moe_reset_stats(ctx)
+        xs = [torch.from_numpy(wl.prefill_activations(l, Tp).view(np.int16)).to(dev) for l in range(L)]
+        pb = torch.from_numpy(np.stack([wl.zipf_bias(l) for l in range(L)])).to(dev)
+        pidx = torch.empty((Tp, k), dtype=torch.int32, device=dev)
+        pw = torch.empty((Tp, k), dtype=torch.float32, device=dev)
+        py = torch.empty((Tp, H), dtype=torch.float32, device=dev)
+        pbias = torch.empty((Tp, E), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        R.moe_prefill_begin(ctx, stream)
+        for l in range(L):
+            pbias.copy_(pb[l].expand(Tp, E))
+            R.moe_route(ctx, l, xs[l], Tp, pbias, None, pidx, pw, stream)
+            R.moe_ffn_prefill(ctx, l, xs[l], Tp, pidx, pw, py, None, None, stream)
+        R.moe_prefill_end(ctx, stream)
+        torch.cuda.synchronize()
+        pel = time.perf_counter() - t2
+        ps = R.moe_get_stats(ctx)
+        gemm_ms = ps["gemm1_ms"] + ps["gemm2_ms"]
+        tflops = ps["gemm_flops"] / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
+        prefill = {
+            "tokens": Tp, "tokens_per_s": round(Tp / pel, 1), "wall_s": round(pel, 3),
+            "copy_GBps": round(ps["copy_bytes"] / (ps["copy_ms"] * 1e-3) / 1e9, 2) if ps["copy_ms"] > 0 else None,
+            "copy_bytes": ps["copy_bytes"], "gemm_ms_per_layer": round(gemm_ms / L, 3),
+            "gemm_TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "overlap": round(max(0.0, (ps["copy_ms"] + gemm_ms - pel * 1e3) / max(1e-9, min(ps["copy_ms"], gemm_ms))), 3),
+        }
+        log(f"prefill: {prefill}")
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        cpu_baseline = oracle_baseline(wl, args.cpu_baseline_seconds)
+        log(f"cpu baseline: {cpu_baseline}")
+
+    out = {
+        "metric": "routed-MoE decode tokens/s + prefill tokens/s; achieved HBM GB/s vs peak",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.wfmt == W.WFMT_BF16 else "fp4(e2m1)+bf16 scale",
+        "data": "synthetic (seeded; random-init weights of the stated shape)",
+        "config": {"workload": f"{wl.name}: L={L} E={E} k={k} H={H} I={wl.inter}, batch {T}, "
+                               f"{n_slots}-slot shared cache, {args.mode}, cold start",
+                   "pool_records": wl.pool_records, "record_bytes": S},
+        "roofline": {"bound": "hbm", "kernel": "dec_phase1 (gate/up GEMV + SwiGLU)",
+                     "achieved": round(p1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(p1_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(p1_bytes), "avg_launch_us": round(p1_avg_ms * 1e3, 3)},
+        "cpu_baseline": cpu_baseline,
+        "decode": decode_detail,
+        "prefill": prefill,
+    }
+    print(json.dumps(out), flush=True)
+    R.moe_destroy(ctx)
+
+
+def oracle_baseline(wl, seconds):
+    """The oracle (as it stands) timed on the host cores over the first decode steps of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    orc = oracle.OracleMoE(wl, mode=oracle.MODE_OFFLOAD, weight_cache=False)
+    T = wl.tokens
+    prev = {}
+    t0 = time.perf_counter()
+    steps = 0
+    while steps < 2 or time.perf_counter() - t0 < seconds:
+        for l in range(wl.n_layers):
+            x = wl.decode_activations(steps, l, T)
+            b = orc.decode_bias(l, prev.get(l), T)
+            r = orc.decode_layer(l, x, b)
+            prev[l] = r["idx"]
+        steps += 1
+    el = time.perf_counter() - t0
+    return {"value": round(steps * T / el, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {steps} decode steps of {wl.name} (all {wl.n_layers} layers, fp64 NumPy)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -2,6 +2,7 @@
 // wavefront 64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -9,6 +10,16 @@
 #include "internal.hpp"
 
 namespace rmoe {
+
+// Launch with dispatch-timestamped events when timing is requested.
+template <typename... KArgs, typename... Args>
+inline void launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s, Timing tm,
+                         Args... args) {
+  if (tm.start && tm.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, tm.start, tm.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

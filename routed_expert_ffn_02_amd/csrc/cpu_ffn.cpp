@@ -68,7 +68,11 @@ static inline bool claim(std::atomic<uint64_t>& word, int* out) {
 }
 
 void CpuPool::worker(int) {
-  uint64_t seen = gen_.load();
+  // Start from the constructor's generation (0), not from whatever gen_ holds when
+  // this thread first runs: a run() or the destructor may already have bumped it,
+  // and a worker that took that value as "seen" would wait for a change that never
+  // comes (the destructor's join would then block forever).
+  uint64_t seen = 0;
   for (;;) {
     uint64_t g;
     int spins = 0;

@@ -5,13 +5,14 @@
 // host/GPU bandwidth comparison).  So the kernels are built around streaming
 // each resident record exactly once with 16-byte lane loads:
 //
-//  phase 1  grid (I / 4, groups): each wavefront reads gate row i and up row i
-//           of one expert and forms h = silu(W_g x) * (W_u x) for every token
-//           routed to that expert; activations are staged once per block in LDS.
-//  phase 2  grid (H / 16, groups): each wavefront reads 4 rows of W_down of one
-//           expert and writes per-pair outputs d[pair][row]; the last block to
-//           finish a row range (atomic arrival count) combines
-//           y[t] = sum_j w[t,j] d[(t,j)] over the GPU pairs in rank order.
+//  phase 1  grid (I / rows per block, groups): each wavefront reads a few gate
+//           and up rows of one expert and forms h = silu(W_g x) * (W_u x) for
+//           every token routed to that expert; activations are staged in LDS
+//           while the weight loads are already in flight.
+//  phase 2  grid (H / 32, groups): each wavefront reads 8 rows of W_down of one
+//           expert and writes per-pair outputs d[pair][row].
+//  combine  y[t] = sum_j w[t,j] d[(t,j)] over the GPU pairs in rank order
+//           (plus the CPU branch's partial sum when there is one).
 // The per-pair values never depend on which slot an expert sits in, and the
 // combine order is fixed, so a fully resident cache reproduces the all-resident
 // (FUSED) result bit for bit (the Luce Spark post reports the same property
@@ -24,8 +25,7 @@
 
 namespace rmoe {
 
-constexpr int kP1Waves = 4;          // rows (gate/up pairs) per phase-1 block
-constexpr int kP2RowsPerWave = 4;
+constexpr int kP2RowsPerWave = 8;
 constexpr int kP2Rows = 4 * kP2RowsPerWave;  // rows per phase-2 block
 
 int decode_phase2_rowblocks(int H) { return (H + kP2Rows - 1) / kP2Rows; }
@@ -45,6 +45,27 @@ __device__ __forceinline__ int group_pairs(const DecodeArgs& a, int g, int* s_pa
   return min(*s_n, kDecodeMaxTok);
 }
 
+// Stage the activation rows of the group's tokens into LDS as fp32 with one
+// 16-byte global load per thread per 8 (bf16) or 4 (fp32) elements.
+template <int AFMT>
+__device__ __forceinline__ void stage_rows(const void* x, const int* s_pair, int k, int n, int H, float* s_x) {
+  constexpr int EV = (AFMT == MOE_AFMT_BF16) ? 8 : 4;
+  const int per_row = H / EV;
+  for (int i = threadIdx.x; i < n * per_row; i += blockDim.x) {
+    const int r = i / per_row, c = i % per_row;
+    const int t = s_pair[r] / k;
+    const uint4 q = reinterpret_cast<const uint4*>(x)[((size_t)t * H) / EV + c];
+    float* dst = s_x + r * H + c * EV;
+    if constexpr (AFMT == MOE_AFMT_BF16) {
+      *reinterpret_cast<float4*>(dst) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                                                    __uint_as_float(q.z), __uint_as_float(q.w));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row dot products against LDS activations.  Each lane covers elements
 // [16*c/bpe, ...) of the row for c = lane, lane+64, ...
@@ -54,9 +75,11 @@ struct RowDot;
 template <>
 struct RowDot<MOE_WFMT_F32> {
   static constexpr int kElems = 4;  // per 16-byte chunk
-  static __device__ __forceinline__ void chunk(const uint8_t* row, int c, const float* scales_row, float* v) {
-    float4 q = reinterpret_cast<const float4*>(row)[c];
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  static __device__ __forceinline__ void unpack(const uint4& q, float* v) {
+    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y); v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+  }
+  static __device__ __forceinline__ void chunk(const uint8_t* row, int c, const float*, float* v) {
+    unpack(reinterpret_cast<const uint4*>(row)[c], v);
   }
   static __device__ __forceinline__ float scale(const uint8_t*, int) { return 1.f; }
 };
@@ -64,10 +87,12 @@ struct RowDot<MOE_WFMT_F32> {
 template <>
 struct RowDot<MOE_WFMT_BF16> {
   static constexpr int kElems = 8;
-  static __device__ __forceinline__ void chunk(const uint8_t* row, int c, const float*, float* v) {
-    uint4 q = reinterpret_cast<const uint4*>(row)[c];
+  static __device__ __forceinline__ void unpack(const uint4& q, float* v) {
     v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
     v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+  }
+  static __device__ __forceinline__ void chunk(const uint8_t* row, int c, const float*, float* v) {
+    unpack(reinterpret_cast<const uint4*>(row)[c], v);
   }
   static __device__ __forceinline__ float scale(const uint8_t*, int) { return 1.f; }
 };
@@ -75,9 +100,9 @@ struct RowDot<MOE_WFMT_BF16> {
 template <>
 struct RowDot<MOE_WFMT_FP4> {
   static constexpr int kElems = 32;
+  static __device__ __forceinline__ void unpack(const uint4& q, float* v) { fp4x32_to_f32(q, v); }
   static __device__ __forceinline__ void chunk(const uint8_t* row, int c, const float*, float* v) {
-    uint4 q = reinterpret_cast<const uint4*>(row)[c];
-    fp4x32_to_f32(q, v);
+    unpack(reinterpret_cast<const uint4*>(row)[c], v);
   }
   // scale row pointer holds bf16 scales, one per 32-element block (= one per chunk)
   static __device__ __forceinline__ float scale(const uint8_t* srow, int c) {
@@ -117,195 +142,260 @@ __device__ __forceinline__ const uint8_t* scale_row(const uint8_t* rec, int t, i
 }
 
 // ---------------------------------------------------------------------------
-template <int WFMT, int AFMT>
+// Phase 1.  Each wavefront owns RW consecutive (gate, up) row pairs of one
+// expert.  CPL > 0: every lane's 16-byte weight chunks (CPL per row) are loaded
+// into registers before the block stages the activations, so the HBM stream
+// starts at once and the staging latency hides under it.  CPL == 0: generic
+// shapes, chunks loaded inside the loop.
+template <int WFMT, int AFMT, int CPL, int RW>
 __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
   const int g = blockIdx.y;
   if (g >= a.cnt[C_NGRP]) return;
   __shared__ int s_pair[kDecodeMaxTok];
   __shared__ int s_n;
   extern __shared__ float s_x[];  // [n][H]
-  const int n = group_pairs(a, g, s_pair, &s_n);
   const int H = a.H, I = a.I;
-  for (int i = threadIdx.x; i < n * H; i += blockDim.x) {
-    const int t = s_pair[i / H] / a.k;
-    s_x[i] = load_act<AFMT>(a.x, (size_t)t * H + (i % H));
-  }
-  __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kP1Waves + wave;
-  if (row >= I) return;
+  const int row0 = (blockIdx.x * 4 + wave) * RW;
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
-  const uint8_t* grow = tensor_row<WFMT>(rec, 0, row, H, I);
-  const uint8_t* urow = tensor_row<WFMT>(rec, 1, row, H, I);
-  const uint8_t* gsrow = scale_row<WFMT>(rec, 0, row, H, I);
-  const uint8_t* usrow = scale_row<WFMT>(rec, 1, row, H, I);
   using RD = RowDot<WFMT>;
   constexpr int EPC = RD::kElems;
-  const int chunks = H / EPC;
-  float accg[kDecodeMaxTok], accu[kDecodeMaxTok];
+  constexpr int NQ = (CPL > 0) ? CPL : 1;
+  uint4 qg[RW][NQ], qu[RW][NQ];
+  float sg[RW][NQ], su[RW][NQ];
+  if constexpr (CPL > 0) {
 #pragma unroll
-  for (int t = 0; t < kDecodeMaxTok; ++t) { accg[t] = 0.f; accu[t] = 0.f; }
-#pragma unroll 4
-  for (int c = lane; c < chunks; c += 64) {
-    float vg[EPC], vu[EPC];
-    RD::chunk(grow, c, nullptr, vg);
-    RD::chunk(urow, c, nullptr, vu);
-    const float sg = RD::scale(gsrow, c), su = RD::scale(usrow, c);
+    for (int r = 0; r < RW; ++r) {
+      const int row = min(row0 + r, I - 1);
+      const uint4* gp = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 0, row, H, I));
+      const uint4* up = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 1, row, H, I));
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxTok; ++t) {
-      if (t < n) {
-        const float* xs = &s_x[t * H + c * EPC];
-        float pg = 0.f, pu = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPC; i += 4) {
-          const float4 x4 = *reinterpret_cast<const float4*>(xs + i);
-          pg += vg[i] * x4.x + vg[i + 1] * x4.y + vg[i + 2] * x4.z + vg[i + 3] * x4.w;
-          pu += vu[i] * x4.x + vu[i + 1] * x4.y + vu[i + 2] * x4.z + vu[i + 3] * x4.w;
-        }
-        accg[t] += sg * pg;
-        accu[t] += su * pu;
+      for (int c = 0; c < CPL; ++c) {
+        qg[r][c] = gp[lane + 64 * c];
+        qu[r][c] = up[lane + 64 * c];
+        sg[r][c] = RD::scale(scale_row<WFMT>(rec, 0, row, H, I), lane + 64 * c);
+        su[r][c] = RD::scale(scale_row<WFMT>(rec, 1, row, H, I), lane + 64 * c);
       }
     }
   }
+  const int n = group_pairs(a, g, s_pair, &s_n);
+  stage_rows<AFMT>(a.x, s_pair, a.k, n, H, s_x);
+  __syncthreads();
 #pragma unroll
-  for (int t = 0; t < kDecodeMaxTok; ++t) {
-    if (t < n) {
-      const float gs = wave_sum(accg[t]);
-      const float us = wave_sum(accu[t]);
-      if (lane == 0) a.h[(int64_t)s_pair[t] * I + row] = silu(gs) * us;
+  for (int r = 0; r < RW; ++r) {
+    const int row = row0 + r;
+    if (row >= I) break;
+    float accg[kDecodeMaxTok], accu[kDecodeMaxTok];
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTok; ++t) { accg[t] = 0.f; accu[t] = 0.f; }
+    const int nchunks = (CPL > 0) ? CPL : (H / EPC + 63 - lane) / 64;
+    for (int ci = 0; ci < nchunks; ++ci) {
+      const int c = lane + 64 * ci;
+      float vg[EPC], vu[EPC], scg, scu;
+      if constexpr (CPL > 0) {
+        RowDot<WFMT>::unpack(qg[r][ci], vg);
+        RowDot<WFMT>::unpack(qu[r][ci], vu);
+        scg = sg[r][ci];
+        scu = su[r][ci];
+      } else {
+        RowDot<WFMT>::chunk(tensor_row<WFMT>(rec, 0, row, H, I), c, nullptr, vg);
+        RowDot<WFMT>::chunk(tensor_row<WFMT>(rec, 1, row, H, I), c, nullptr, vu);
+        scg = RD::scale(scale_row<WFMT>(rec, 0, row, H, I), c);
+        scu = RD::scale(scale_row<WFMT>(rec, 1, row, H, I), c);
+      }
+#pragma unroll
+      for (int t = 0; t < kDecodeMaxTok; ++t) {
+        if (t < n) {
+          const float* xs = &s_x[t * H + c * EPC];
+          float pg = 0.f, pu = 0.f;
+#pragma unroll
+          for (int i = 0; i < EPC; i += 4) {
+            const float4 x4 = *reinterpret_cast<const float4*>(xs + i);
+            pg += vg[i] * x4.x + vg[i + 1] * x4.y + vg[i + 2] * x4.z + vg[i + 3] * x4.w;
+            pu += vu[i] * x4.x + vu[i + 1] * x4.y + vu[i + 2] * x4.z + vu[i + 3] * x4.w;
+          }
+          accg[t] += scg * pg;
+          accu[t] += scu * pu;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTok; ++t) {
+      if (t < n) {
+        const float gs = wave_sum(accg[t]);
+        const float us = wave_sum(accu[t]);
+        if (lane == 0) a.h[(int64_t)s_pair[t] * I + row] = silu(gs) * us;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-template <int WFMT, int MAXT>
+// Phase 2.  Each wavefront owns R2 consecutive rows of W_down of one expert and
+// writes the per-pair outputs d[pair][row]; chunks are loaded before the h slices.
+template <int WFMT, int MAXT, int CPL>
 __global__ __launch_bounds__(256) void dec_phase2(DecodeArgs a) {
+  constexpr int R2 = kP2RowsPerWave;
   const int g = blockIdx.y;
+  if (g >= a.cnt[C_NGRP]) return;
   const int H = a.H, I = a.I;
   __shared__ int s_pair[kDecodeMaxTok];
   __shared__ int s_n;
-  __shared__ int s_last;
-  const int ngrp = a.cnt[C_NGRP];
-  if (g < ngrp) {
-    const int n = min(group_pairs(a, g, s_pair, &s_n), MAXT);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint8_t* rec = a.arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
-    using RD = RowDot<WFMT>;
-    constexpr int EPC = RD::kElems;
-    const int chunks = I / EPC;
-    const int r0 = blockIdx.x * kP2Rows + wave * kP2RowsPerWave;
-    float acc[kP2RowsPerWave][MAXT];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
+  using RD = RowDot<WFMT>;
+  constexpr int EPC = RD::kElems;
+  constexpr int NQ = (CPL > 0) ? CPL : 1;
+  const int r0 = blockIdx.x * kP2Rows + wave * R2;
+  uint4 q[R2][NQ];
+  float sc[R2][NQ];
+  if constexpr (CPL > 0) {
 #pragma unroll
-    for (int r = 0; r < kP2RowsPerWave; ++r)
+    for (int r = 0; r < R2; ++r) {
+      const int row = min(r0 + r, H - 1);
+      const uint4* dp = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 2, row, H, I));
 #pragma unroll
-      for (int t = 0; t < MAXT; ++t) acc[r][t] = 0.f;
-    for (int c = lane; c < chunks; c += 64) {
-      // this lane's slice of h for every token of the group
-      float hv[MAXT][EPC];
+      for (int c = 0; c < CPL; ++c) {
+        q[r][c] = dp[lane + 64 * c];
+        sc[r][c] = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), lane + 64 * c);
+      }
+    }
+  }
+  const int n = min(group_pairs(a, g, s_pair, &s_n), MAXT);
+  float acc[R2][MAXT];
+#pragma unroll
+  for (int r = 0; r < R2; ++r)
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) acc[r][t] = 0.f;
+  const int nchunks = (CPL > 0) ? CPL : (I / EPC + 63 - lane) / 64;
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int c = lane + 64 * ci;
+    float hv[MAXT][EPC];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      if (t < n) {
+        const float4* hp = reinterpret_cast<const float4*>(a.h + (int64_t)s_pair[t] * I + c * EPC);
+#pragma unroll
+        for (int i = 0; i < EPC / 4; ++i) {
+          const float4 v = hp[i];
+          hv[t][4 * i] = v.x; hv[t][4 * i + 1] = v.y; hv[t][4 * i + 2] = v.z; hv[t][4 * i + 3] = v.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R2; ++r) {
+      const int row = r0 + r;
+      float v[EPC], s;
+      if constexpr (CPL > 0) {
+        RowDot<WFMT>::unpack(q[r][ci], v);
+        s = sc[r][ci];
+      } else {
+        if (row >= H) continue;
+        RowDot<WFMT>::chunk(tensor_row<WFMT>(rec, 2, row, H, I), c, nullptr, v);
+        s = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), c);
+      }
 #pragma unroll
       for (int t = 0; t < MAXT; ++t) {
         if (t < n) {
-          const float4* hp = reinterpret_cast<const float4*>(a.h + (int64_t)s_pair[t] * I + c * EPC);
+          float p = 0.f;
 #pragma unroll
-          for (int i = 0; i < EPC / 4; ++i) {
-            float4 q = hp[i];
-            hv[t][4 * i] = q.x; hv[t][4 * i + 1] = q.y; hv[t][4 * i + 2] = q.z; hv[t][4 * i + 3] = q.w;
-          }
+          for (int i = 0; i < EPC; ++i) p += v[i] * hv[t][i];
+          acc[r][t] += s * p;
         }
       }
+    }
+  }
 #pragma unroll
-      for (int r = 0; r < kP2RowsPerWave; ++r) {
+  for (int r = 0; r < R2; ++r) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      if (t < n) {
+        const float sum = wave_sum(acc[r][t]);
         const int row = r0 + r;
-        if (row < H) {
-          float v[EPC];
-          RD::chunk(tensor_row<WFMT>(rec, 2, row, H, I), c, nullptr, v);
-          const float sc = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), c);
-#pragma unroll
-          for (int t = 0; t < MAXT; ++t) {
-            if (t < n) {
-              float p = 0.f;
-#pragma unroll
-              for (int i = 0; i < EPC; ++i) p += v[i] * hv[t][i];
-              acc[r][t] += sc * p;
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kP2RowsPerWave; ++r) {
-#pragma unroll
-      for (int t = 0; t < MAXT; ++t) {
-        if (t < n) {
-          const float s = wave_sum(acc[r][t]);
-          const int row = r0 + r;
-          if (lane == 0 && row < H) a.d[(int64_t)s_pair[t] * H + row] = s;
-        }
+        if (lane == 0 && row < H) a.d[(int64_t)s_pair[t] * H + row] = sum;
       }
     }
   }
-  // arrival count for this row range; the last block combines in rank order
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&a.rowblock_done[blockIdx.x], 1);
-    s_last = (prev == (int)gridDim.y - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int P = a.T * a.k;
-  for (int i = threadIdx.x; i < a.T * kP2Rows; i += blockDim.x) {
-    const int t = i / kP2Rows, row = blockIdx.x * kP2Rows + (i % kP2Rows);
-    if (row >= H) continue;
-    float y = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      const int p = t * a.k + j;
-      if (p < P && a.pair_grp[p] >= 0) y += a.w[p] * __builtin_nontemporal_load(&a.d[(int64_t)p * H + row]);
-    }
-    a.y[(int64_t)t * H + row] = y;
-  }
-  if (threadIdx.x == 0) a.rowblock_done[blockIdx.x] = 0;
 }
 
-void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s) {
-  dim3 grid((a.I + kP1Waves - 1) / kP1Waves, max_groups);
+// Combine: y[t, r] = sum_{j: GPU pair, rank order} w[t,j] d[(t,j), r]  (+ y_cpu[t, r]).
+__global__ void dec_combine(DecodeArgs a, const float* y_cpu) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.T * a.H) return;
+  const int t = i / a.H, row = i % a.H;
+  float y = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    const int p = t * a.k + j;
+    if (a.pair_grp[p] >= 0) y += a.w[p] * a.d[(int64_t)p * a.H + row];
+  }
+  if (y_cpu) y += y_cpu[i];
+  a.y[i] = y;
+}
+
+// Chunks per lane of a row of `cols` elements, when it is a whole number of
+// wavefront-wide 16-byte loads (1, 2, 4, 8); 0 selects the generic loop.
+static int lane_chunks(int wfmt, int cols) {
+  const int epc = wfmt == MOE_WFMT_F32 ? 4 : wfmt == MOE_WFMT_BF16 ? 8 : 32;
+  if (cols % (64 * epc)) return 0;
+  const int c = cols / (64 * epc);
+  return (c == 1 || c == 2 || c == 4 || c == 8) ? c : 0;
+}
+
+template <int W, int A, int CPL>
+static void p1_launch(const DecodeArgs& a, int max_groups, size_t lds, hipStream_t s, Timing tm) {
+  // about 16 in-flight 16-byte chunks per lane; wide FP4 rows unpack to many registers
+  constexpr int RW = (W == MOE_WFMT_FP4 && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : (CPL == 1 ? 8 : 1));
+  dim3 grid((a.I + 4 * RW - 1) / (4 * RW), max_groups);
+  launch_timed(dec_phase1<W, A, CPL, RW>, grid, dim3(256), (uint32_t)lds, s, tm, a);
+}
+
+template <int W, int A>
+static void p1_dispatch(const DecodeArgs& a, int max_groups, size_t lds, hipStream_t s, Timing tm) {
+  switch (lane_chunks(W, a.H)) {
+    case 1: p1_launch<W, A, 1>(a, max_groups, lds, s, tm); break;
+    case 2: p1_launch<W, A, 2>(a, max_groups, lds, s, tm); break;
+    case 4: p1_launch<W, A, 4>(a, max_groups, lds, s, tm); break;
+    case 8: p1_launch<W, A, 8>(a, max_groups, lds, s, tm); break;
+    default: p1_launch<W, A, 0>(a, max_groups, lds, s, tm); break;
+  }
+}
+
+void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
   const size_t lds = (size_t)min(a.T, kDecodeMaxTok) * a.H * sizeof(float);
-#define P1(W, A) hipLaunchKernelGGL((dec_phase1<W, A>), grid, dim3(256), lds, s, a)
   if (afmt == MOE_AFMT_BF16) {
-    if (wfmt == MOE_WFMT_BF16) P1(MOE_WFMT_BF16, MOE_AFMT_BF16);
-    else if (wfmt == MOE_WFMT_FP4) P1(MOE_WFMT_FP4, MOE_AFMT_BF16);
-    else P1(MOE_WFMT_F32, MOE_AFMT_BF16);
+    if (wfmt == MOE_WFMT_BF16) p1_dispatch<MOE_WFMT_BF16, MOE_AFMT_BF16>(a, max_groups, lds, s, tm);
+    else if (wfmt == MOE_WFMT_FP4) p1_dispatch<MOE_WFMT_FP4, MOE_AFMT_BF16>(a, max_groups, lds, s, tm);
+    else p1_dispatch<MOE_WFMT_F32, MOE_AFMT_BF16>(a, max_groups, lds, s, tm);
   } else {
-    if (wfmt == MOE_WFMT_BF16) P1(MOE_WFMT_BF16, MOE_AFMT_F32);
-    else if (wfmt == MOE_WFMT_FP4) P1(MOE_WFMT_FP4, MOE_AFMT_F32);
-    else P1(MOE_WFMT_F32, MOE_AFMT_F32);
+    if (wfmt == MOE_WFMT_BF16) p1_dispatch<MOE_WFMT_BF16, MOE_AFMT_F32>(a, max_groups, lds, s, tm);
+    else if (wfmt == MOE_WFMT_FP4) p1_dispatch<MOE_WFMT_FP4, MOE_AFMT_F32>(a, max_groups, lds, s, tm);
+    else p1_dispatch<MOE_WFMT_F32, MOE_AFMT_F32>(a, max_groups, lds, s, tm);
   }
-#undef P1
 }
 
-void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s) {
+template <int W, int M>
+static void p2_dispatch(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
   dim3 grid(decode_phase2_rowblocks(a.H), max_groups);
-#define P2(W, M) hipLaunchKernelGGL((dec_phase2<W, M>), grid, dim3(256), 0, s, a)
-  const int maxt = a.T;  // tokens routed to one expert <= T
-  if (wfmt == MOE_WFMT_BF16) {
-    if (maxt <= 1) P2(MOE_WFMT_BF16, 1); else if (maxt <= 4) P2(MOE_WFMT_BF16, 4); else P2(MOE_WFMT_BF16, 8);
-  } else if (wfmt == MOE_WFMT_FP4) {
-    if (maxt <= 1) P2(MOE_WFMT_FP4, 1); else if (maxt <= 4) P2(MOE_WFMT_FP4, 4); else P2(MOE_WFMT_FP4, 8);
-  } else {
-    if (maxt <= 1) P2(MOE_WFMT_F32, 1); else if (maxt <= 4) P2(MOE_WFMT_F32, 4); else P2(MOE_WFMT_F32, 8);
-  }
-#undef P2
+  if (lane_chunks(W, a.I) == 1) launch_timed(dec_phase2<W, M, 1>, grid, dim3(256), 0, s, tm, a);
+  else launch_timed(dec_phase2<W, M, 0>, grid, dim3(256), 0, s, tm, a);
 }
 
-__global__ void add_inplace_kernel(float* y, const float* src, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) y[i] += src[i];
+template <int W>
+static void p2_tokens(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
+  if (a.T <= 1) p2_dispatch<W, 1>(a, max_groups, s, tm);
+  else if (a.T <= 4) p2_dispatch<W, 4>(a, max_groups, s, tm);
+  else p2_dispatch<W, 8>(a, max_groups, s, tm);
 }
 
-void launch_add_inplace(float* y, const float* src, int64_t n, hipStream_t s) {
-  if (n <= 0) return;
-  hipLaunchKernelGGL(add_inplace_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, src, n);
+void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
+  if (wfmt == MOE_WFMT_BF16) p2_tokens<MOE_WFMT_BF16>(a, max_groups, s, tm);
+  else if (wfmt == MOE_WFMT_FP4) p2_tokens<MOE_WFMT_FP4>(a, max_groups, s, tm);
+  else p2_tokens<MOE_WFMT_F32>(a, max_groups, s, tm);
+}
+
+void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s) {
+  const int n = a.T * a.H;
+  hipLaunchKernelGGL(dec_combine, dim3((n + 255) / 256), dim3(256), 0, s, a, y_cpu);
 }
 
 }  // namespace rmoe

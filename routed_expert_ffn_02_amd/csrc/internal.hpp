@@ -70,7 +70,6 @@ struct DecodeArgs {
   const int32_t* cnt;        // device counters (C_NGRP)
   float* h;                  // [T*k, I] scratch
   float* d;                  // [T*k, H] scratch (per-pair expert outputs)
-  int32_t* rowblock_done;    // [H / rows per block] zero-initialised counters
   float* y;                  // [T,H]
 };
 
@@ -102,17 +101,22 @@ void launch_evict_range(int32_t* slot_of, int32_t* key_of, uint64_t* stamp, uint
                         uint8_t reserve_value, hipStream_t s);
 void launch_admit_buffer(int32_t* slot_of, int32_t* key_of, uint64_t* stamp, uint64_t* counter, int layer, int E,
                          int base, hipStream_t s);
-void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s);
-void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s);
+// Launchers of timed kernels take optional start / stop events that the dispatch
+// itself timestamps (hipExtLaunchKernelGGL): the elapsed time is the kernel's own.
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
+void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 int decode_phase2_rowblocks(int H);
-void launch_add_inplace(float* y, const float* src, int64_t n, hipStream_t s);
+void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s);
 void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
                     int32_t* inv, int32_t* offsets, int32_t* tile_base, int bm, hipStream_t s);
 void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp, int32_t* grp_slot, int32_t* cnt,
                               int32_t* scratch_flags, int n_slot_range, hipStream_t s);
 int prefill_bm();
-void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s);
-void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s);
+void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
+void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
 void launch_prefill_combine(const PrefillArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- CPU branch
@@ -193,7 +197,6 @@ struct moe_ctx {
   float* logits = nullptr;       // [max_tokens*E]
   float* h = nullptr;            // [decode pairs * I]
   float* dpair = nullptr;        // [decode pairs * H]
-  int32_t* rowblock_done = nullptr;
   float* y_cpu_dev = nullptr;    // [max_tokens*H]
   // prefill scratch (device, sized for max_tokens)
   int32_t *perm = nullptr, *inv = nullptr, *offsets = nullptr, *tile_base = nullptr, *hist = nullptr;

@@ -533,16 +533,16 @@ static int padded_grid(int tiles_m, int nt) {
   return ((n + 7) / 8) * 8;
 }
 
-void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s) {
+void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
   if (wfmt == MOE_WFMT_F32) {
     const int64_t n = (int64_t)a.T * a.k * a.I;
     const dim3 grid((unsigned)((n + 255) / 256));
-    if (afmt == MOE_AFMT_BF16) hipLaunchKernelGGL(gemm1_f32_kernel<MOE_AFMT_BF16>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(gemm1_f32_kernel<MOE_AFMT_F32>, grid, dim3(256), 0, s, a);
+    if (afmt == MOE_AFMT_BF16) launch_timed(gemm1_f32_kernel<MOE_AFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+    else launch_timed(gemm1_f32_kernel<MOE_AFMT_F32>, grid, dim3(256), 0, s, tm, a);
     return;
   }
   const dim3 grid(padded_grid(max_tiles_m, a.I / 64));
-#define G1(W, A) hipLaunchKernelGGL((gemm1_kernel<W, A>), grid, dim3(256), 0, s, a)
+#define G1(W, A) launch_timed(gemm1_kernel<W, A>, grid, dim3(256), 0, s, tm, a)
   if (wfmt == MOE_WFMT_BF16) {
     if (afmt == MOE_AFMT_BF16) G1(MOE_WFMT_BF16, MOE_AFMT_BF16); else G1(MOE_WFMT_BF16, MOE_AFMT_F32);
   } else {
@@ -551,15 +551,15 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
 #undef G1
 }
 
-void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s) {
+void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
   if (wfmt == MOE_WFMT_F32) {
     const int64_t n = (int64_t)a.T * a.k * a.H;
-    hipLaunchKernelGGL(gemm2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    launch_timed(gemm2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tm, a);
     return;
   }
   const dim3 grid(padded_grid(max_tiles_m, a.H / 128));
-  if (wfmt == MOE_WFMT_BF16) hipLaunchKernelGGL(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(gemm2_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, a);
+  if (wfmt == MOE_WFMT_BF16) launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  else launch_timed(gemm2_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
 }
 
 // ---------------------------------------------------------------------------

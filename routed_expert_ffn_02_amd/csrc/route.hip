@@ -18,7 +18,18 @@ __global__ __launch_bounds__(256) void route_gemv(const void* __restrict__ x, co
                                                    const float* __restrict__ bias, float* __restrict__ logits,
                                                    int T, int E, int H) {
   extern __shared__ float s_x[];  // [T][H]
-  for (int i = threadIdx.x; i < T * H; i += blockDim.x) s_x[i] = load_act<AFMT>(x, i);
+  constexpr int EV = (AFMT == MOE_AFMT_BF16) ? 8 : 4;
+  for (int i = threadIdx.x; i < T * H / EV; i += blockDim.x) {
+    const uint4 q = reinterpret_cast<const uint4*>(x)[i];
+    float* dst = s_x + i * EV;
+    if constexpr (AFMT == MOE_AFMT_BF16) {
+      *reinterpret_cast<float4*>(dst) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                                                    __uint_as_float(q.z), __uint_as_float(q.w));
+    }
+  }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * kRouteWaves + wave;

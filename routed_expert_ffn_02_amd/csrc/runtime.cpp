@@ -103,24 +103,27 @@ hipEvent_t take_event(moe_ctx* c) {
 
 enum TimedKind { TK_P1 = 0, TK_P2 = 1, TK_G1 = 2, TK_G2 = 3, TK_COPY = 4 };
 
+// Events for one timed launch (none unless MOE_FLAG_PROFILE).  Kernels receive them
+// through hipExtLaunchKernelGGL, so the interval is the kernel's own execution; copies
+// are bracketed by records on their stream.
 struct TimedScope {
   moe_ctx* c;
   hipStream_t s;
   int kind;
-  hipEvent_t a = nullptr;
-  TimedScope(moe_ctx* c_, hipStream_t s_, int kind_) : c(c_), s(s_), kind(kind_) {
+  bool record;
+  Timing tm;
+  TimedScope(moe_ctx* c_, hipStream_t s_, int kind_, bool record_around = false)
+      : c(c_), s(s_), kind(kind_), record(record_around) {
     if (c->cfg.flags & MOE_FLAG_PROFILE) {
-      a = take_event(c);
-      if (a) hipEventRecord(a, s);
+      tm.start = take_event(c);
+      tm.stop = take_event(c);
+      if (record && tm.start) hipEventRecord(tm.start, s);
     }
   }
   ~TimedScope() {
-    if (a) {
-      hipEvent_t b = take_event(c);
-      if (b) {
-        hipEventRecord(b, s);
-        c->pending_timed.push_back({a, b, kind});
-      }
+    if (tm.start && tm.stop) {
+      if (record) hipEventRecord(tm.stop, s);
+      c->pending_timed.push_back({tm.start, tm.stop, kind});
     }
   }
 };
@@ -226,7 +229,7 @@ moe_status issue_fills(moe_ctx* ctx, hipStream_t s) {
   const int nf = ctx->h_cnt[C_FILL];
   if (nf <= 0) return MOE_OK;
   if (!ctx->pool_pinned) return fail(ctx, MOE_ENOPIN, "fills need a page-locked host pool");
-  TimedScope ts(ctx, ctx->copy_stream, TK_COPY);
+  TimedScope ts(ctx, ctx->copy_stream, TK_COPY, true);
   for (int i = 0; i < nf; ++i) {
     const int key = ctx->h_fill_key[i], slot = ctx->h_fill_slot[i];
     HIPCHK(hipMemcpyAsync(ctx->arena + (int64_t)slot * ctx->S, pool_record(ctx, key), ctx->S, hipMemcpyHostToDevice,
@@ -341,7 +344,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->grp_slot, std::max<int64_t>(E, Pmax)) || dev_alloc(&ctx->slot_scratch, Pmax) ||
       dev_alloc(&ctx->pair_grp, Pmax) ||
       dev_alloc(&ctx->logits, (size_t)c.max_tokens * E) || dev_alloc(&ctx->h, (size_t)Pdec * I) ||
-      dev_alloc(&ctx->dpair, (size_t)Pdec * H) || dev_alloc(&ctx->rowblock_done, decode_phase2_rowblocks(H)) ||
+      dev_alloc(&ctx->dpair, (size_t)Pdec * H) ||
       dev_alloc(&ctx->y_cpu_dev, (size_t)c.max_tokens * H) || dev_alloc(&ctx->perm, Pmax) ||
       dev_alloc(&ctx->inv, Pmax) || dev_alloc(&ctx->offsets, std::max<int64_t>(E, Pmax) + 1) ||
       dev_alloc(&ctx->tile_base, std::max<int64_t>(E, Pmax) + 1) ||
@@ -357,7 +360,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ctx->u_kind = ctx->u_key + E;
   if (hipMemset(ctx->slot_of, 0xff, (size_t)L * E * 4) || hipMemset(ctx->key_of, 0xff, kMaxCachedSlots * 4) ||
       hipMemset(ctx->stamp, 0, kMaxCachedSlots * 8) || hipMemset(ctx->reserved, 0, kMaxCachedSlots) ||
-      hipMemset(ctx->counter, 0, 8) || hipMemset(ctx->rowblock_done, 0, decode_phase2_rowblocks(H) * 4) ||
+      hipMemset(ctx->counter, 0, 8) ||
       hipMemset(ctx->step_dev, 0, (C_COUNT + 5 * E) * 4))
     return cleanup_fail(MOE_EHIP);
   // pinned host staging
@@ -402,7 +405,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   }
   for (auto e : ctx->event_pool) hipEventDestroy(e);
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
-                 ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->rowblock_done, ctx->y_cpu_dev,
+                 ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
                  ctx->flags};
   for (void* p : dev)
@@ -586,7 +589,6 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   d.cnt = ctx->cnt;
   d.h = ctx->h;
   d.d = ctx->dpair;
-  d.rowblock_done = ctx->rowblock_done;
   d.y = y;
   const int max_groups = std::min(P, E);
   if (!fused) {
@@ -595,18 +597,18 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   }
   {
     TimedScope t1(ctx, s, TK_P1);
-    launch_decode_phase1(ctx->cfg.wfmt, ctx->cfg.afmt, d, max_groups, s);
+    launch_decode_phase1(ctx->cfg.wfmt, ctx->cfg.afmt, d, max_groups, s, t1.tm);
   }
   {
     TimedScope t2(ctx, s, TK_P2);
-    launch_decode_phase2(ctx->cfg.wfmt, d, max_groups, s);
+    launch_decode_phase2(ctx->cfg.wfmt, d, max_groups, s, t2.tm);
   }
   if (has_cpu) {
     // the GPU path is enqueued; the CPU branch runs now, concurrently, then merges exactly
     moe_status st = run_cpu_branch(ctx, T, s, &y_cpu);
     if (st != MOE_OK) return st;
-    launch_add_inplace(y, y_cpu, (int64_t)T * H, s);
   }
+  launch_decode_combine(d, y_cpu, s);
   HIPCHK(hipGetLastError());
   if (profile) {
     const int ngrp = ctx->h_cnt[C_NGRP];
@@ -657,11 +659,11 @@ moe_status prefill_gpu_part(moe_ctx* ctx, const void* x, int T, const float* w, 
   const int max_tiles_m = (P + bm - 1) / bm + std::min(E, P);
   {
     TimedScope t(ctx, s, TK_G1);
-    launch_prefill_gemm1(ctx->cfg.wfmt, ctx->cfg.afmt, a, max_tiles_m, s);
+    launch_prefill_gemm1(ctx->cfg.wfmt, ctx->cfg.afmt, a, max_tiles_m, s, t.tm);
   }
   {
     TimedScope t(ctx, s, TK_G2);
-    launch_prefill_gemm2(ctx->cfg.wfmt, a, max_tiles_m, s);
+    launch_prefill_gemm2(ctx->cfg.wfmt, a, max_tiles_m, s, t.tm);
   }
   if (ctx->cfg.flags & MOE_FLAG_PROFILE) {
     ctx->stats.gemm1_launches += 1;
@@ -708,7 +710,7 @@ MOE_API moe_status moe_prefill_begin(moe_ctx* ctx, moe_stream_t stream) {
     HIPCHK(hipStreamSynchronize(s));
     ctx->prefill_buffers = true;
     for (int l = 0; l < std::min(2, L); ++l) {
-      TimedScope ts(ctx, ctx->copy_stream, TK_COPY);
+      TimedScope ts(ctx, ctx->copy_stream, TK_COPY, true);
       HIPCHK(copy_keys(ctx, (int64_t)l * E, E, (int64_t)(l % 2) * E, ctx->copy_stream));
       HIPCHK(hipEventRecord(ctx->ev_layer_copied[l % 2], ctx->copy_stream));
       ctx->stats.copy_bytes += (uint64_t)E * ctx->S;
@@ -751,7 +753,7 @@ MOE_API moe_status moe_ffn_prefill(moe_ctx* ctx, int32_t layer, const void* x, i
     ctx->buffer_layer[b] = layer;
     if (layer + 2 < L) {
       HIPCHK(hipStreamWaitEvent(ctx->copy_stream, ctx->ev_layer_done[b], 0));
-      TimedScope ts(ctx, ctx->copy_stream, TK_COPY);
+      TimedScope ts(ctx, ctx->copy_stream, TK_COPY, true);
       HIPCHK(copy_keys(ctx, (int64_t)(layer + 2) * E, E, (int64_t)b * E, ctx->copy_stream));
       HIPCHK(hipEventRecord(ctx->ev_layer_copied[b], ctx->copy_stream));
       ctx->stats.copy_bytes += (uint64_t)E * ctx->S;

@@ -65,6 +65,16 @@ def test_alias_maps_to_backing_record():
 def test_zipf_bias_shape():
     w = W.A3B_DECODE
     b = w.zipf_bias(0)
-    p = np.exp(b.astype(np.float64))
-    assert abs(p.sum() - 1.0) < 1e-5          # alpha = 1: exp(bias) is the Zipf pmf
+    p = np.exp(b.astype(np.float64) / w.zipf_alpha)
+    assert abs(p.sum() - 1.0) < 1e-5          # exp(bias / alpha) is the Zipf(1.1) pmf over ranks
+    ranks = w.popularity_perm(0) + 1.0
+    np.testing.assert_allclose(p, ranks ** -1.1 / np.sum(np.arange(1, 257) ** -1.1), rtol=1e-5)
     assert sorted(w.popularity_perm(0).tolist()) == list(range(256))
+
+
+def test_locality_constants_match_calibration():
+    """The frozen routing constants are the ones the committed calibration chose."""
+    cal = json.load(open(os.path.join(os.path.dirname(W.__file__), "calibration.json")))
+    assert cal["chosen"]["zipf_alpha"] == W.ZIPF_ALPHA and cal["chosen"]["prev_bonus"] == W.PREV_BONUS
+    assert cal["chosen"]["prefill_coverage"] >= 0.95
+    assert W.A3B_DECODE.zipf_alpha == W.ZIPF_ALPHA and W.DSV4.prev_bonus == W.PREV_BONUS

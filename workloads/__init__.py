@@ -276,15 +276,22 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 TINY = Workload(name="tiny_fp32", seed=1, n_layers=1, n_experts=8, top_k=2, hidden=64, inter=128,
                 wfmt=WFMT_F32, afmt=AFMT_F32, tokens=1, steps=16, n_slots=4, prefill_tokens=16)
 
+# Routing locality constants, frozen from workloads/calibration.json (written by
+# `python -m workloads.calibrate`, which runs only the oracle): Zipf weight 0.5 keeps a
+# 4096-token prompt routed to every expert; a 0.25 previous-token bonus puts the
+# steady-state LRU miss rate at 1280 slots nearest the pages' 39%.
+ZIPF_ALPHA = 0.5
+PREV_BONUS = 0.25
+
 A3B_DECODE = Workload(name="a3b_decode_bf16", seed=2, n_layers=40, n_experts=256, top_k=8, hidden=2048,
                       inter=512, wfmt=WFMT_BF16, afmt=AFMT_BF16, tokens=1, steps=512, n_slots=1280,
-                      zipf_alpha=1.0, prev_bonus=2.0)
+                      zipf_alpha=ZIPF_ALPHA, prev_bonus=PREV_BONUS)
 
 A3B_PREFILL = A3B_DECODE.with_(name="a3b_prefill_bf16", seed=2, prefill_tokens=4096, prev_bonus=0.0)
 
 DSV4 = Workload(name="dsv4_fp4", seed=4, n_layers=43, n_experts=256, top_k=6, hidden=4096, inter=2048,
                 wfmt=WFMT_FP4, afmt=AFMT_BF16, tokens=1, steps=512, n_slots=1695,
-                zipf_alpha=1.0, prev_bonus=2.0, prefill_tokens=2048)
+                zipf_alpha=ZIPF_ALPHA, prev_bonus=PREV_BONUS, prefill_tokens=2048)
 
 A3B_ELASTIC = A3B_DECODE.with_(name="a3b_elastic_hybrid", seed=5, tokens=4, steps=1024,
                                resize_schedule=((341, 640), (682, 960)))
