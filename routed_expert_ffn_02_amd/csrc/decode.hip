@@ -141,13 +141,127 @@ __device__ __forceinline__ const uint8_t* scale_row(const uint8_t* rec, int t, i
   return rec + 3 * (n / 2) + (int64_t)t * (n / 32) * 2 + (int64_t)r * (cols / 32) * 2;
 }
 
+// Pairs of group g, found by one wavefront with a ballot (no block barrier, so no
+// fence waits on the weight loads already in flight).  P <= 64 on the fast path.
+__device__ __forceinline__ uint64_t group_mask(const DecodeArgs& a, int g) {
+  const int lane = threadIdx.x & 63;
+  const int P = a.T * a.k;
+  const bool mine = lane < P && a.pair_grp[lane] == g;
+  return __ballot(mine);
+}
+
+// Activation chunk of token t for lane chunk c: EPC consecutive elements as fp32.
+template <int AFMT, int EPC>
+__device__ __forceinline__ void load_x_chunk(const void* x, int H, int t, int c, float* v) {
+  if constexpr (AFMT == MOE_AFMT_BF16 && EPC == 4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + (size_t)t * H + (size_t)c * 4);
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+  } else if constexpr (AFMT == MOE_AFMT_BF16) {
+    static_assert(EPC % 8 == 0, "bf16 activation chunks are whole 16-byte loads");
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + (size_t)t * H + (size_t)c * EPC);
+#pragma unroll
+    for (int i = 0; i < EPC / 8; ++i) {
+      const uint4 q = p[i];
+      v[8 * i + 0] = bf16_lo(q.x); v[8 * i + 1] = bf16_hi(q.x); v[8 * i + 2] = bf16_lo(q.y); v[8 * i + 3] = bf16_hi(q.y);
+      v[8 * i + 4] = bf16_lo(q.z); v[8 * i + 5] = bf16_hi(q.z); v[8 * i + 6] = bf16_lo(q.w); v[8 * i + 7] = bf16_hi(q.w);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + (size_t)t * H + (size_t)c * EPC);
+#pragma unroll
+    for (int i = 0; i < EPC / 4; ++i) {
+      const float4 q = p[i];
+      v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Phase 1.  Each wavefront owns RW consecutive (gate, up) row pairs of one
-// expert.  CPL > 0: every lane's 16-byte weight chunks (CPL per row) are loaded
-// into registers before the block stages the activations, so the HBM stream
-// starts at once and the staging latency hides under it.  CPL == 0: generic
-// shapes, chunks loaded inside the loop.
-template <int WFMT, int AFMT, int CPL, int RW>
+// Phase 1, fast path (H a whole number of wavefront-wide chunks, P <= 64): each
+// wavefront owns RW consecutive (gate, up) row pairs of one expert; its weight
+// chunks and the matching activation chunks are all requested before any is used.
+template <int WFMT, int AFMT, int CPL, int RW, int MAXT>
+__global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
+  const int g = blockIdx.y;
+  // both loads issue together (grp_slot has E >= gridDim.y entries, so the read is in
+  // bounds even for a group beyond the count, whose value is then unused)
+  const int slot = a.grp_slot[g];
+  if (g >= a.cnt[C_NGRP]) return;
+  const int H = a.H, I = a.I;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * 4 + wave) * RW;
+  if (row0 >= I) return;
+  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  using RD = RowDot<WFMT>;
+  constexpr int EPC = RD::kElems;
+  uint4 qg[RW][CPL], qu[RW][CPL];
+  float sg[RW][CPL], su[RW][CPL];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = min(row0 + r, I - 1);
+    const uint4* gp = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 0, row, H, I));
+    const uint4* up = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 1, row, H, I));
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      qg[r][c] = gp[lane + 64 * c];
+      qu[r][c] = up[lane + 64 * c];
+      sg[r][c] = RD::scale(scale_row<WFMT>(rec, 0, row, H, I), lane + 64 * c);
+      su[r][c] = RD::scale(scale_row<WFMT>(rec, 1, row, H, I), lane + 64 * c);
+    }
+  }
+  // the group's pairs (tokens) and their activation chunks
+  uint64_t m = group_mask(a, g);
+  int pair[MAXT];
+  int n = 0;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    pair[t] = m ? __builtin_ctzll(m) : 0;
+    n += (m != 0);
+    m &= m - 1;
+  }
+  float xv[MAXT][CPL][EPC];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+    if (t < n)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) load_x_chunk<AFMT, EPC>(a.x, H, pair[t] / a.k, lane + 64 * c, xv[t][c]);
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = row0 + r;
+    float accg[MAXT], accu[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) { accg[t] = 0.f; accu[t] = 0.f; }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float vg[EPC], vu[EPC];
+      RD::unpack(qg[r][c], vg);
+      RD::unpack(qu[r][c], vu);
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t < n) {
+          float pg = 0.f, pu = 0.f;
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) {
+            pg += vg[i] * xv[t][c][i];
+            pu += vu[i] * xv[t][c][i];
+          }
+          accg[t] += sg[r][c] * pg;
+          accu[t] += su[r][c] * pu;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      if (t < n) {
+        const float gs = wave_sum(accg[t]);
+        const float us = wave_sum(accu[t]);
+        if (lane == 0 && row < I) a.h[(int64_t)pair[t] * I + row] = silu(gs) * us;
+      }
+    }
+  }
+}
+
+// Phase 1, generic shapes: one row pair per wavefront, activations staged in LDS.
+template <int WFMT, int AFMT>
 __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
   const int g = blockIdx.y;
   if (g >= a.cnt[C_NGRP]) return;
@@ -156,84 +270,114 @@ __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
   extern __shared__ float s_x[];  // [n][H]
   const int H = a.H, I = a.I;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row0 = (blockIdx.x * 4 + wave) * RW;
+  const int row = blockIdx.x * 4 + wave;
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
   using RD = RowDot<WFMT>;
   constexpr int EPC = RD::kElems;
-  constexpr int NQ = (CPL > 0) ? CPL : 1;
-  uint4 qg[RW][NQ], qu[RW][NQ];
-  float sg[RW][NQ], su[RW][NQ];
-  if constexpr (CPL > 0) {
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const int row = min(row0 + r, I - 1);
-      const uint4* gp = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 0, row, H, I));
-      const uint4* up = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 1, row, H, I));
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        qg[r][c] = gp[lane + 64 * c];
-        qu[r][c] = up[lane + 64 * c];
-        sg[r][c] = RD::scale(scale_row<WFMT>(rec, 0, row, H, I), lane + 64 * c);
-        su[r][c] = RD::scale(scale_row<WFMT>(rec, 1, row, H, I), lane + 64 * c);
-      }
-    }
-  }
   const int n = group_pairs(a, g, s_pair, &s_n);
   stage_rows<AFMT>(a.x, s_pair, a.k, n, H, s_x);
   __syncthreads();
+  if (row >= I) return;
+  float accg[kDecodeMaxTok], accu[kDecodeMaxTok];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int row = row0 + r;
-    if (row >= I) break;
-    float accg[kDecodeMaxTok], accu[kDecodeMaxTok];
-#pragma unroll
-    for (int t = 0; t < kDecodeMaxTok; ++t) { accg[t] = 0.f; accu[t] = 0.f; }
-    const int nchunks = (CPL > 0) ? CPL : (H / EPC + 63 - lane) / 64;
-    for (int ci = 0; ci < nchunks; ++ci) {
-      const int c = lane + 64 * ci;
-      float vg[EPC], vu[EPC], scg, scu;
-      if constexpr (CPL > 0) {
-        RowDot<WFMT>::unpack(qg[r][ci], vg);
-        RowDot<WFMT>::unpack(qu[r][ci], vu);
-        scg = sg[r][ci];
-        scu = su[r][ci];
-      } else {
-        RowDot<WFMT>::chunk(tensor_row<WFMT>(rec, 0, row, H, I), c, nullptr, vg);
-        RowDot<WFMT>::chunk(tensor_row<WFMT>(rec, 1, row, H, I), c, nullptr, vu);
-        scg = RD::scale(scale_row<WFMT>(rec, 0, row, H, I), c);
-        scu = RD::scale(scale_row<WFMT>(rec, 1, row, H, I), c);
-      }
-#pragma unroll
-      for (int t = 0; t < kDecodeMaxTok; ++t) {
-        if (t < n) {
-          const float* xs = &s_x[t * H + c * EPC];
-          float pg = 0.f, pu = 0.f;
-#pragma unroll
-          for (int i = 0; i < EPC; i += 4) {
-            const float4 x4 = *reinterpret_cast<const float4*>(xs + i);
-            pg += vg[i] * x4.x + vg[i + 1] * x4.y + vg[i + 2] * x4.z + vg[i + 3] * x4.w;
-            pu += vu[i] * x4.x + vu[i + 1] * x4.y + vu[i + 2] * x4.z + vu[i + 3] * x4.w;
-          }
-          accg[t] += scg * pg;
-          accu[t] += scu * pu;
-        }
-      }
-    }
+  for (int t = 0; t < kDecodeMaxTok; ++t) { accg[t] = 0.f; accu[t] = 0.f; }
+  for (int c = lane; c < H / EPC; c += 64) {
+    float vg[EPC], vu[EPC];
+    RD::chunk(tensor_row<WFMT>(rec, 0, row, H, I), c, nullptr, vg);
+    RD::chunk(tensor_row<WFMT>(rec, 1, row, H, I), c, nullptr, vu);
+    const float scg = RD::scale(scale_row<WFMT>(rec, 0, row, H, I), c);
+    const float scu = RD::scale(scale_row<WFMT>(rec, 1, row, H, I), c);
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTok; ++t) {
       if (t < n) {
-        const float gs = wave_sum(accg[t]);
-        const float us = wave_sum(accu[t]);
-        if (lane == 0) a.h[(int64_t)s_pair[t] * I + row] = silu(gs) * us;
+        const float* xs = &s_x[t * H + c * EPC];
+        float pg = 0.f, pu = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPC; i += 4) {
+          const float4 x4 = *reinterpret_cast<const float4*>(xs + i);
+          pg += vg[i] * x4.x + vg[i + 1] * x4.y + vg[i + 2] * x4.z + vg[i + 3] * x4.w;
+          pu += vu[i] * x4.x + vu[i + 1] * x4.y + vu[i + 2] * x4.z + vu[i + 3] * x4.w;
+        }
+        accg[t] += scg * pg;
+        accu[t] += scu * pu;
       }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTok; ++t) {
+    if (t < n) {
+      const float gs = wave_sum(accg[t]);
+      const float us = wave_sum(accu[t]);
+      if (lane == 0) a.h[(int64_t)s_pair[t] * I + row] = silu(gs) * us;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2.  Each wavefront owns R2 consecutive rows of W_down of one expert and
-// writes the per-pair outputs d[pair][row]; chunks are loaded before the h slices.
-template <int WFMT, int MAXT, int CPL>
+// Phase 2, fast path (I = 64 chunks per row, P <= 64): each wavefront owns R2 rows
+// of W_down of one expert; weight chunks and h slices requested up front.
+template <int WFMT, int MAXT>
+__global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
+  constexpr int R2 = kP2RowsPerWave;
+  const int g = blockIdx.y;
+  const int slot = a.grp_slot[g];  // issued with the count (see phase 1)
+  if (g >= a.cnt[C_NGRP]) return;
+  const int H = a.H, I = a.I;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = blockIdx.x * kP2Rows + wave * R2;
+  if (r0 >= H) return;
+  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  using RD = RowDot<WFMT>;
+  constexpr int EPC = RD::kElems;
+  uint4 q[R2];
+  float sc[R2];
+#pragma unroll
+  for (int r = 0; r < R2; ++r) {
+    const int row = min(r0 + r, H - 1);
+    q[r] = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 2, row, H, I))[lane];
+    sc[r] = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), lane);
+  }
+  uint64_t m = group_mask(a, g);
+  int pair[MAXT];
+  int n = 0;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    pair[t] = m ? __builtin_ctzll(m) : 0;
+    n += (m != 0);
+    m &= m - 1;
+  }
+  float hv[MAXT][EPC];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t < n) {
+      const float4* hp = reinterpret_cast<const float4*>(a.h + (int64_t)pair[t] * I + lane * EPC);
+#pragma unroll
+      for (int i = 0; i < EPC / 4; ++i) {
+        const float4 v = hp[i];
+        hv[t][4 * i] = v.x; hv[t][4 * i + 1] = v.y; hv[t][4 * i + 2] = v.z; hv[t][4 * i + 3] = v.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R2; ++r) {
+    float v[EPC];
+    RD::unpack(q[r], v);
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      if (t < n) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) p += v[i] * hv[t][i];
+        const float sum = wave_sum(sc[r] * p);
+        const int row = r0 + r;
+        if (lane == 0 && row < H) a.d[(int64_t)pair[t] * H + row] = sum;
+      }
+    }
+  }
+}
+
+// Phase 2, generic shapes.
+template <int WFMT, int MAXT>
 __global__ __launch_bounds__(256) void dec_phase2(DecodeArgs a) {
   constexpr int R2 = kP2RowsPerWave;
   const int g = blockIdx.y;
@@ -245,31 +389,14 @@ __global__ __launch_bounds__(256) void dec_phase2(DecodeArgs a) {
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
   using RD = RowDot<WFMT>;
   constexpr int EPC = RD::kElems;
-  constexpr int NQ = (CPL > 0) ? CPL : 1;
   const int r0 = blockIdx.x * kP2Rows + wave * R2;
-  uint4 q[R2][NQ];
-  float sc[R2][NQ];
-  if constexpr (CPL > 0) {
-#pragma unroll
-    for (int r = 0; r < R2; ++r) {
-      const int row = min(r0 + r, H - 1);
-      const uint4* dp = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 2, row, H, I));
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        q[r][c] = dp[lane + 64 * c];
-        sc[r][c] = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), lane + 64 * c);
-      }
-    }
-  }
   const int n = min(group_pairs(a, g, s_pair, &s_n), MAXT);
   float acc[R2][MAXT];
 #pragma unroll
   for (int r = 0; r < R2; ++r)
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) acc[r][t] = 0.f;
-  const int nchunks = (CPL > 0) ? CPL : (I / EPC + 63 - lane) / 64;
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int c = lane + 64 * ci;
+  for (int c = lane; c < I / EPC; c += 64) {
     float hv[MAXT][EPC];
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
@@ -285,15 +412,10 @@ __global__ __launch_bounds__(256) void dec_phase2(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < R2; ++r) {
       const int row = r0 + r;
-      float v[EPC], s;
-      if constexpr (CPL > 0) {
-        RowDot<WFMT>::unpack(q[r][ci], v);
-        s = sc[r][ci];
-      } else {
-        if (row >= H) continue;
-        RowDot<WFMT>::chunk(tensor_row<WFMT>(rec, 2, row, H, I), c, nullptr, v);
-        s = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), c);
-      }
+      if (row >= H) continue;
+      float v[EPC];
+      RD::chunk(tensor_row<WFMT>(rec, 2, row, H, I), c, nullptr, v);
+      const float s = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), c);
 #pragma unroll
       for (int t = 0; t < MAXT; ++t) {
         if (t < n) {
@@ -333,7 +455,7 @@ __global__ void dec_combine(DecodeArgs a, const float* y_cpu) {
 }
 
 // Chunks per lane of a row of `cols` elements, when it is a whole number of
-// wavefront-wide 16-byte loads (1, 2, 4, 8); 0 selects the generic loop.
+// wavefront-wide 16-byte loads (1, 2, 4, 8); 0 selects the generic kernels.
 static int lane_chunks(int wfmt, int cols) {
   const int epc = wfmt == MOE_WFMT_F32 ? 4 : wfmt == MOE_WFMT_BF16 ? 8 : 32;
   if (cols % (64 * epc)) return 0;
@@ -341,22 +463,36 @@ static int lane_chunks(int wfmt, int cols) {
   return (c == 1 || c == 2 || c == 4 || c == 8) ? c : 0;
 }
 
-template <int W, int A, int CPL>
-static void p1_launch(const DecodeArgs& a, int max_groups, size_t lds, hipStream_t s, Timing tm) {
-  // about 16 in-flight 16-byte chunks per lane; wide FP4 rows unpack to many registers
-  constexpr int RW = (W == MOE_WFMT_FP4 && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : (CPL == 1 ? 8 : 1));
+template <int W, int A, int CPL, int MAXT>
+static void p1_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
+  // about 16 in-flight 16-byte weight chunks per lane; wide FP4 rows unpack to many registers
+  constexpr int RW = (W == MOE_WFMT_FP4 && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : 8);
   dim3 grid((a.I + 4 * RW - 1) / (4 * RW), max_groups);
-  launch_timed(dec_phase1<W, A, CPL, RW>, grid, dim3(256), (uint32_t)lds, s, tm, a);
+  launch_timed(dec_phase1_fast<W, A, CPL, RW, MAXT>, grid, dim3(256), 0, s, tm, a);
+}
+
+template <int W, int A, int MAXT>
+static bool p1_try_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
+  switch (lane_chunks(W, a.H)) {
+    case 1: p1_fast<W, A, 1, MAXT>(a, max_groups, s, tm); return true;
+    case 2: p1_fast<W, A, 2, MAXT>(a, max_groups, s, tm); return true;
+    case 4: p1_fast<W, A, 4, MAXT>(a, max_groups, s, tm); return true;
+    default: return false;
+  }
 }
 
 template <int W, int A>
 static void p1_dispatch(const DecodeArgs& a, int max_groups, size_t lds, hipStream_t s, Timing tm) {
-  switch (lane_chunks(W, a.H)) {
-    case 1: p1_launch<W, A, 1>(a, max_groups, lds, s, tm); break;
-    case 2: p1_launch<W, A, 2>(a, max_groups, lds, s, tm); break;
-    case 4: p1_launch<W, A, 4>(a, max_groups, lds, s, tm); break;
-    case 8: p1_launch<W, A, 8>(a, max_groups, lds, s, tm); break;
-    default: p1_launch<W, A, 0>(a, max_groups, lds, s, tm); break;
+  const bool small = a.T * a.k <= 64;
+  bool done = false;
+  if (small && a.T <= 1) {
+    done = p1_try_fast<W, A, 1>(a, max_groups, s, tm);
+  } else if constexpr (W != MOE_WFMT_FP4) {  // FP4 rows with 4 tokens exceed the register file
+    if (small && a.T <= 4) done = p1_try_fast<W, A, 4>(a, max_groups, s, tm);
+  }
+  if (!done) {
+    dim3 grid((a.I + 3) / 4, max_groups);
+    launch_timed(dec_phase1<W, A>, grid, dim3(256), (uint32_t)lds, s, tm, a);
   }
 }
 
@@ -376,8 +512,8 @@ void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_group
 template <int W, int M>
 static void p2_dispatch(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
   dim3 grid(decode_phase2_rowblocks(a.H), max_groups);
-  if (lane_chunks(W, a.I) == 1) launch_timed(dec_phase2<W, M, 1>, grid, dim3(256), 0, s, tm, a);
-  else launch_timed(dec_phase2<W, M, 0>, grid, dim3(256), 0, s, tm, a);
+  if (lane_chunks(W, a.I) == 1 && a.T * a.k <= 64) launch_timed(dec_phase2_fast<W, M>, grid, dim3(256), 0, s, tm, a);
+  else launch_timed(dec_phase2<W, M>, grid, dim3(256), 0, s, tm, a);
 }
 
 template <int W>

@@ -27,6 +27,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Native 16-byte vector for register stages: HIP's uint4 is a union-backed struct
+// whose copies lower to memcpy and keep the stage out of registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 64;   // sorted pair rows per tile
 constexpr int BK = 64;   // reduction step (elements)
@@ -211,10 +214,10 @@ __device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int NT, TileIn
 
 // 8 activation values (bf16 or f32 source) -> 16 bytes of bf16 or f16 for the MFMA A operand.
 template <int AFMT, bool TO_F16>
-__device__ __forceinline__ uint4 load_x8(const void* x, int64_t off) {
+__device__ __forceinline__ u32x4 load_x8(const void* x, int64_t off) {
   float v[8];
   if constexpr (AFMT == MOE_AFMT_BF16) {
-    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
     if constexpr (!TO_F16) return q;
     v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
     v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
@@ -237,11 +240,11 @@ __device__ __forceinline__ uint4 load_x8(const void* x, int64_t off) {
     }
     w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return u32x4{w[0], w[1], w[2], w[3]};
 }
 
 // 32 e2m1 codes (16 bytes) times one bf16 scale -> 32 f16 (64 bytes), exact in range.
-__device__ __forceinline__ void fp4x32_to_f16(const uint4& q, uint16_t scale_bits, uint4* out) {
+__device__ __forceinline__ void fp4x32_to_f16(const u32x4& q, uint16_t scale_bits, u32x4* out) {
   const _Float16 sh = (_Float16)bf16_to_f32(scale_bits);
   const f16x2 s2 = {sh, sh};
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -258,11 +261,11 @@ __device__ __forceinline__ void fp4x32_to_f16(const uint4& q, uint16_t scale_bit
     o[4 * i + 3] = __builtin_bit_cast(uint32_t, v3);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  for (int i = 0; i < 4; ++i) out[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
 }
 
 template <bool F16>
-__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   if constexpr (F16) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
                                                   0);
@@ -270,6 +273,83 @@ __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                    0, 0);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Tile loaders.  Register stages are plain unrolled arrays (no captures), so they
+// stay in VGPRs and the next k-step's loads overlap the current step's MFMAs.
+
+// A: 64 rows x 64 k of activations (2 16-byte chunks per thread), rows gathered
+// through the permutation (GEMM1) or contiguous sorted rows (GEMM2).
+struct AStage {
+  u32x4 v[2];
+};
+// B (bf16): 128 weight rows x 64 k (4 chunks per thread); (fp4): 128 rows x 32 bytes of
+// codes (1 chunk per thread) and that chunk's bf16 block scale.
+template <int WFMT>
+struct BStage {
+  u32x4 v[WFMT == MOE_WFMT_BF16 ? 4 : 1];
+  uint16_t sc;
+};
+
+template <int WFMT>
+__device__ __forceinline__ void load_b(BStage<WFMT>& st, const uint8_t* const* rowp, const uint16_t* const* scp,
+                                       int k0, int tid) {
+  if constexpr (WFMT == MOE_WFMT_BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.v[j] = *reinterpret_cast<const u32x4*>(rowp[j] + (int64_t)k0 * 2 + (tid & 7) * 16);
+  } else {
+    st.v[0] = *reinterpret_cast<const u32x4*>(rowp[0] + k0 / 2 + (tid & 1) * 16);
+    st.sc = scp[0][k0 / 32 + (tid & 1)];
+  }
+}
+
+template <int WFMT>
+__device__ __forceinline__ void store_b(const BStage<WFMT>& st, uint16_t (*sB)[LDSW], int tid) {
+  if constexpr (WFMT == MOE_WFMT_BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + 256 * j;
+      *reinterpret_cast<u32x4*>(&sB[idx >> 3][(idx & 7) * 8]) = st.v[j];
+    }
+  } else {
+    u32x4 o[4];
+    fp4x32_to_f16(st.v[0], st.sc, o);
+    const int wr = tid >> 1, half = tid & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sB[wr][half * 32 + i * 8]) = o[i];
+  }
+}
+
+__device__ __forceinline__ void store_a(const AStage& st, uint16_t (*sA)[LDSW], int tid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = tid + 256 * j;
+    *reinterpret_cast<u32x4*>(&sA[idx >> 3][(idx & 7) * 8]) = st.v[j];
+  }
+}
+
+// Per-thread source rows of the B tile: bf16 threads own rows idx >> 3 for idx = tid + 256 j;
+// fp4 threads own row tid >> 1.  wrow(i) maps tile row i (0..127) to a tensor row.
+template <int WFMT, typename RowFn>
+__device__ __forceinline__ void b_rows(const uint8_t* rec, int H, int I, int t_base, RowFn wrow, int cols, int tid,
+                                       const uint8_t** rowp, const uint16_t** scp) {
+  const int64_t tb = tbytes<WFMT>(H, I);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * ((int64_t)H * I / 2));
+  if constexpr (WFMT == MOE_WFMT_BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int t, r;
+      wrow((tid + 256 * j) >> 3, t, r);
+      rowp[j] = rec + (int64_t)t * tb + (int64_t)r * cols * 2;
+    }
+  } else {
+    int t, r;
+    wrow(tid >> 1, t, r);
+    rowp[0] = rec + (int64_t)t * tb + (int64_t)r * (cols / 2);
+    scp[0] = scales + (int64_t)t * ((int64_t)H * I / 32) + (int64_t)r * (cols / 32);
+  }
+  (void)t_base;
 }
 
 // ---------------------------------------------------------------------------
@@ -290,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // A chunks: 2 per thread (row = idx / 8, 16-byte column chunk = idx % 8)
+  // A sources: 2 chunks per thread (row = idx / 8, 16-byte column chunk = idx % 8)
   int64_t a_src[2];
   bool a_ok[2];
 #pragma unroll
@@ -300,68 +380,40 @@ __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
     const int tok = a_ok[j] ? a.perm[ti.row0 + r] / a.k : 0;
     a_src[j] = (int64_t)tok * H + (idx & 7) * 8;
   }
-  uint4 ra[2], rb[4];
-  uint16_t rsc = 0;
-  auto load_tiles = [&](int k0) {
+  // B sources: tile rows 0..63 are gate rows n0.., 64..127 the up rows n0..
+  const uint8_t* rowp[WFMT == MOE_WFMT_BF16 ? 4 : 1];
+  const uint16_t* scp[1] = {nullptr};
+  b_rows<WFMT>(rec, H, I, 0, [&](int i, int& t, int& r) { t = i >> 6; r = n0 + (i & 63); }, H, tid, rowp, scp);
+
+  AStage ra;
+  BStage<WFMT> rb;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) ra[j] = a_ok[j] ? load_x8<AFMT, F16>(a.x, a_src[j] + k0) : make_uint4(0, 0, 0, 0);
-    if constexpr (WFMT == MOE_WFMT_BF16) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = tid + 256 * j, wr = idx >> 3, c = idx & 7;
-        const int t = wr >> 6, row = n0 + (wr & 63);
-        const uint8_t* src = rec + (int64_t)t * tbytes<WFMT>(H, I) + ((int64_t)row * H + k0 + c * 8) * 2;
-        rb[j] = *reinterpret_cast<const uint4*>(src);
-      }
-    } else {
-      const int wr = tid >> 1, half = tid & 1;
-      const int t = wr >> 6, row = n0 + (wr & 63);
-      const uint8_t* src = rec + (int64_t)t * tbytes<WFMT>(H, I) + (int64_t)row * (H / 2) + k0 / 2 + half * 16;
-      rb[0] = *reinterpret_cast<const uint4*>(src);
-      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + 3 * ((int64_t)H * I / 2)) +
-                           (int64_t)t * ((int64_t)H * I / 32) + (int64_t)row * (H / 32) + k0 / 32 + half;
-      rsc = *sc;
-    }
-  };
-  auto store_tiles = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = tid + 256 * j;
-      *reinterpret_cast<uint4*>(&sA[buf][idx >> 3][(idx & 7) * 8]) = ra[j];
-    }
-    if constexpr (WFMT == MOE_WFMT_BF16) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = tid + 256 * j;
-        *reinterpret_cast<uint4*>(&sB[buf][idx >> 3][(idx & 7) * 8]) = rb[j];
-      }
-    } else {
-      uint4 o[4];
-      fp4x32_to_f16(rb[0], rsc, o);
-      const int wr = tid >> 1, half = tid & 1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sB[buf][wr][half * 32 + i * 8]) = o[i];
-    }
-  };
+  for (int j = 0; j < 2; ++j) ra.v[j] = a_ok[j] ? load_x8<AFMT, F16>(a.x, a_src[j]) : u32x4{0, 0, 0, 0};
+  load_b<WFMT>(rb, rowp, scp, 0, tid);
 
   f32x16 accg, accu;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { accg[i] = 0.f; accu[i] = 0.f; }
   const int nk = H / BK;
-  load_tiles(0);
+  const int arow = wm * 32 + (lane & 31);
+  const int bg = wn * 32 + (lane & 31), bu = 64 + wn * 32 + (lane & 31);
+  const int koff = (lane >> 5) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    store_tiles(buf);
+    store_a(ra, sA[buf], tid);
+    store_b<WFMT>(rb, sB[buf], tid);
     __syncthreads();
-    if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-    const int arow = wm * 32 + (lane & 31);
-    const int bg = wn * 32 + (lane & 31), bu = 64 + wn * 32 + (lane & 31);
-    const int koff = (lane >> 5) * 8;
+    if (kt + 1 < nk) {
+      const int k0 = (kt + 1) * BK;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ra.v[j] = a_ok[j] ? load_x8<AFMT, F16>(a.x, a_src[j] + k0) : u32x4{0, 0, 0, 0};
+      load_b<WFMT>(rb, rowp, scp, k0, tid);
+    }
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      const uint4 av = *reinterpret_cast<const uint4*>(&sA[buf][arow][kk + koff]);
-      const uint4 gv = *reinterpret_cast<const uint4*>(&sB[buf][bg][kk + koff]);
-      const uint4 uv = *reinterpret_cast<const uint4*>(&sB[buf][bu][kk + koff]);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(&sA[buf][arow][kk + koff]);
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(&sB[buf][bg][kk + koff]);
+      const u32x4 uv = *reinterpret_cast<const u32x4*>(&sB[buf][bu][kk + koff]);
       accg = mfma32<F16>(av, gv, accg);
       accu = mfma32<F16>(av, uv, accu);
     }
@@ -373,7 +425,8 @@ __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
   for (int i = 0; i < 16; ++i) {
     const int r = wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
     if (r < ti.rows) {
-      const float v = silu(accg[i]) * accu[i];
+      const float g = accg[i];
+      const float v = g * __frcp_rn(1.0f + __expf(-g)) * accu[i];
       uint16_t bits;
       if constexpr (F16) bits = __builtin_bit_cast(uint16_t, (_Float16)v);
       else bits = f32_to_bf16_rne(v);
@@ -398,70 +451,48 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
   const int wm = wave & 1, wn = wave >> 1;
   const uint16_t* act = reinterpret_cast<const uint16_t*>(a.act);
 
-  uint4 ra[2], rb[4];
-  uint16_t rsc = 0;
-  auto load_tiles = [&](int k0) {
+  const uint16_t* a_src[2];
+  bool a_ok[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = tid + 256 * j, r = idx >> 3;
-      ra[j] = (r < ti.rows) ? *reinterpret_cast<const uint4*>(act + (int64_t)(ti.row0 + r) * I + k0 + (idx & 7) * 8)
-                            : make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (WFMT == MOE_WFMT_BF16) {
+  for (int j = 0; j < 2; ++j) {
+    const int idx = tid + 256 * j, r = idx >> 3;
+    a_ok[j] = r < ti.rows;
+    a_src[j] = act + (int64_t)(ti.row0 + (a_ok[j] ? r : 0)) * I + (idx & 7) * 8;
+  }
+  const uint8_t* rowp[WFMT == MOE_WFMT_BF16 ? 4 : 1];
+  const uint16_t* scp[1] = {nullptr};
+  b_rows<WFMT>(rec, H, I, 0, [&](int i, int& t, int& r) { t = 2; r = n0 + i; }, I, tid, rowp, scp);
+
+  AStage ra;
+  BStage<WFMT> rb;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = tid + 256 * j, wr = idx >> 3, c = idx & 7;
-        const uint8_t* src = rec + 2 * tbytes<WFMT>(H, I) + ((int64_t)(n0 + wr) * I + k0 + c * 8) * 2;
-        rb[j] = *reinterpret_cast<const uint4*>(src);
-      }
-    } else {
-      const int wr = tid >> 1, half = tid & 1;
-      const uint8_t* src = rec + 2 * tbytes<WFMT>(H, I) + (int64_t)(n0 + wr) * (I / 2) + k0 / 2 + half * 16;
-      rb[0] = *reinterpret_cast<const uint4*>(src);
-      const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + 3 * ((int64_t)H * I / 2)) +
-                           2 * ((int64_t)H * I / 32) + (int64_t)(n0 + wr) * (I / 32) + k0 / 32 + half;
-      rsc = *sc;
-    }
-  };
-  auto store_tiles = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = tid + 256 * j;
-      *reinterpret_cast<uint4*>(&sA[buf][idx >> 3][(idx & 7) * 8]) = ra[j];
-    }
-    if constexpr (WFMT == MOE_WFMT_BF16) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = tid + 256 * j;
-        *reinterpret_cast<uint4*>(&sB[buf][idx >> 3][(idx & 7) * 8]) = rb[j];
-      }
-    } else {
-      uint4 o[4];
-      fp4x32_to_f16(rb[0], rsc, o);
-      const int wr = tid >> 1, half = tid & 1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sB[buf][wr][half * 32 + i * 8]) = o[i];
-    }
-  };
+  for (int j = 0; j < 2; ++j) ra.v[j] = a_ok[j] ? *reinterpret_cast<const u32x4*>(a_src[j]) : u32x4{0, 0, 0, 0};
+  load_b<WFMT>(rb, rowp, scp, 0, tid);
 
   f32x16 acc0, acc1;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
   const int nk = I / BK;
-  load_tiles(0);
+  const int arow = wm * 32 + (lane & 31);
+  const int b0 = wn * 64 + (lane & 31), b1 = b0 + 32;
+  const int koff = (lane >> 5) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    store_tiles(buf);
+    store_a(ra, sA[buf], tid);
+    store_b<WFMT>(rb, sB[buf], tid);
     __syncthreads();
-    if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-    const int arow = wm * 32 + (lane & 31);
-    const int b0 = wn * 64 + (lane & 31), b1 = b0 + 32;
-    const int koff = (lane >> 5) * 8;
+    if (kt + 1 < nk) {
+      const int k0 = (kt + 1) * BK;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        ra.v[j] = a_ok[j] ? *reinterpret_cast<const u32x4*>(a_src[j] + k0) : u32x4{0, 0, 0, 0};
+      load_b<WFMT>(rb, rowp, scp, k0, tid);
+    }
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      const uint4 av = *reinterpret_cast<const uint4*>(&sA[buf][arow][kk + koff]);
-      const uint4 w0 = *reinterpret_cast<const uint4*>(&sB[buf][b0][kk + koff]);
-      const uint4 w1 = *reinterpret_cast<const uint4*>(&sB[buf][b1][kk + koff]);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(&sA[buf][arow][kk + koff]);
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(&sB[buf][b0][kk + koff]);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(&sB[buf][b1][kk + koff]);
       acc0 = mfma32<F16>(av, w0, acc0);
       acc1 = mfma32<F16>(av, w1, acc1);
     }

@@ -93,3 +93,32 @@ def test_decode_requires_lookup_first():
     with pytest.raises(R.MoeError) as e:
         R.moe_ffn_decode(h.ctx, 0, x, 1, bad, w, slot, y)
     assert e.value.status == R.MOE_EINVAL
+
+
+REAL_ROWS = {
+    "a3b_bf16": W.A3B_DECODE.with_(name="a3b_rows", n_layers=2, n_experts=16, n_slots=12),
+    "dsv4_fp4": W.DSV4.with_(name="dsv4_rows", n_layers=2, n_experts=8, n_slots=6),
+    "wide_bf16": W.A3B_DECODE.with_(name="wide_rows", n_layers=1, n_experts=8, top_k=4, hidden=4096, inter=512,
+                                    n_slots=6),
+}
+
+
+@pytest.mark.parametrize("name", list(REAL_ROWS))
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("mode", [1, 3])
+def test_decode_real_row_widths(name, T, mode):
+    """The register-resident GEMV variants used at the A3B and DSV4 row widths."""
+    wl = REAL_ROWS[name]
+    bw = (25_000_000_000, 100_000_000_000)
+    h = Harness(wl, mode, bw=bw)
+    ref = oracle.ExpertCache(wl.n_layers, wl.n_experts, wl.n_slots)
+    routes = {l: wl.synthetic_routing(4, l, T) for l in range(wl.n_layers)}
+    for step in range(4):
+        for layer in range(wl.n_layers):
+            idx = routes[layer][step]
+            x = wl.decode_activations(step, layer, T)
+            w = _gates(wl, step, layer, T)
+            y, slot, trace, cnt = h.decode(layer, x, idx, w)
+            r = ref.lookup(layer, idx, mode, *bw)
+            assert trace == r.trace
+            assert row_rel_err(y, _expected(wl, layer, x, idx, w)) <= tol_for(wl), (step, layer)
