@@ -127,10 +127,13 @@ class Ctx:
     def __init__(self, handle: int, cfg: moe_config):
         self.handle = handle
         self.cfg = cfg
+        # held here so that a context collected at interpreter exit, after the
+        # module globals are cleared, can still be destroyed
+        self._destroy = lib.moe_destroy
 
     def __del__(self):
         if getattr(self, "handle", None):
-            lib.moe_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
 

@@ -61,6 +61,7 @@ struct LookupArgs {
 
 struct DecodeArgs {
   const void* x;             // [T,H] afmt
+  const void* xa;            // [T,H] 16-bit MFMA operands (x itself, or its converted copy)
   const float* w;            // [T,k]
   const uint8_t* arena;
   int64_t rec_bytes;
@@ -75,6 +76,7 @@ struct DecodeArgs {
 
 struct PrefillArgs {
   const void* x;             // [T,H] afmt
+  const void* xa;            // [T,H] 16-bit MFMA operands (x itself, or its converted copy)
   const float* w;            // [T,k]
   const uint8_t* arena;
   int64_t rec_bytes;
@@ -115,6 +117,8 @@ void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_ma
 void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp, int32_t* grp_slot, int32_t* cnt,
                               int32_t* scratch_flags, int n_slot_range, hipStream_t s);
 int prefill_bm();
+bool prefill_needs_act_operands(int wfmt, int afmt);
+void launch_act_operands(int wfmt, int afmt, const void* x, void* xo, int64_t n, hipStream_t s);
 void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
 void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
 void launch_prefill_combine(const PrefillArgs& a, hipStream_t s);
@@ -202,6 +206,7 @@ struct moe_ctx {
   int32_t *perm = nullptr, *inv = nullptr, *offsets = nullptr, *tile_base = nullptr, *hist = nullptr;
   int32_t* cand = nullptr;       // [E]
   void* act = nullptr;
+  void* xo = nullptr;        // [max_tokens, H] 16-bit MFMA operands of the prefill activations
   float* ypair = nullptr;
   int32_t* flags = nullptr;
 

@@ -176,15 +176,6 @@ void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp,
 }
 
 // ---------------------------------------------------------------------------
-// Record addressing (same layout as the decode kernels).
-template <int WFMT>
-__device__ __forceinline__ int64_t tbytes(int H, int I) {
-  const int64_t n = (int64_t)H * I;
-  if constexpr (WFMT == MOE_WFMT_F32) return n * 4;
-  else if constexpr (WFMT == MOE_WFMT_BF16) return n * 2;
-  else return n / 2;
-}
-
 // Tile decode shared by both GEMMs: returns false when the block has no tile.
 struct TileInfo {
   int g, row0, rows, nt;
@@ -212,58 +203,6 @@ __device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int NT, TileIn
   return true;
 }
 
-// 8 activation values (bf16 or f32 source) -> 16 bytes of bf16 or f16 for the MFMA A operand.
-template <int AFMT, bool TO_F16>
-__device__ __forceinline__ u32x4 load_x8(const void* x, int64_t off) {
-  float v[8];
-  if constexpr (AFMT == MOE_AFMT_BF16) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
-    if constexpr (!TO_F16) return q;
-    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
-    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint16_t lo, hi;
-    if constexpr (TO_F16) {
-      _Float16 l = (_Float16)v[2 * i], h = (_Float16)v[2 * i + 1];
-      lo = __builtin_bit_cast(uint16_t, l);
-      hi = __builtin_bit_cast(uint16_t, h);
-    } else {
-      lo = f32_to_bf16_rne(v[2 * i]);
-      hi = f32_to_bf16_rne(v[2 * i + 1]);
-    }
-    w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// 32 e2m1 codes (16 bytes) times one bf16 scale -> 32 f16 (64 bytes), exact in range.
-__device__ __forceinline__ void fp4x32_to_f16(const u32x4& q, uint16_t scale_bits, u32x4* out) {
-  const _Float16 sh = (_Float16)bf16_to_f32(scale_bits);
-  const f16x2 s2 = {sh, sh};
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  uint32_t o[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0) * s2;
-    f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1) * s2;
-    f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2) * s2;
-    f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3) * s2;
-    o[4 * i + 0] = __builtin_bit_cast(uint32_t, v0);
-    o[4 * i + 1] = __builtin_bit_cast(uint32_t, v1);
-    o[4 * i + 2] = __builtin_bit_cast(uint32_t, v2);
-    o[4 * i + 3] = __builtin_bit_cast(uint32_t, v3);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
-}
-
 template <bool F16>
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   if constexpr (F16) {
@@ -276,237 +215,417 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 }
 
 // ---------------------------------------------------------------------------
-// Tile loaders.  Register stages are plain unrolled arrays (no captures), so they
-// stay in VGPRs and the next k-step's loads overlap the current step's MFMAs.
+// Grouped GEMM structure (both GEMMs).  Block = 4 wavefronts, 64 sorted rows
+// (2 MFMA row fragments) x 4 * 64 weight rows; every wavefront owns 2 weight-row
+// fragments of 32 and computes the 2 x 2 fragment product.
+//   * B (weights) never touches LDS: each wavefront loads its own weight rows
+//     straight into MFMA operand registers (FP4: dequantised there), so every
+//     weight byte is read and converted exactly once.
+//   * A (activation rows, shared by the 4 wavefronts) goes global -> registers
+//     -> LDS, one 64-row x 64-k tile per k-step.
+//   * Within a k-step of 64, lane half h (lane >> 5) covers k in [32h, 32h + 32)
+//     and MFMA j takes its 8-element slice [32h + 8j, 32h + 8j + 8) from A and B
+//     alike: a lane's weight loads are one contiguous 32-element run of a row
+//     (for FP4, one 16-byte block of codes with its single scale).
+//   * Register stages are indexed by compile-time constants (the k loop is
+//     unrolled by the pipeline depth D): D k-steps of loads are in flight while
+//     the current step's MFMAs run.
 
-// A: 64 rows x 64 k of activations (2 16-byte chunks per thread), rows gathered
-// through the permutation (GEMM1) or contiguous sorted rows (GEMM2).
+// A: 64 rows x 64 k; thread owns chunks idx = tid + 256 j (row idx / 8, 8-element
+// column chunk idx % 8).  f32 sources take two 16-byte loads per chunk.
+template <int AFMT>
 struct AStage {
-  u32x4 v[2];
-};
-// B (bf16): 128 weight rows x 64 k (4 chunks per thread); (fp4): 128 rows x 32 bytes of
-// codes (1 chunk per thread) and that chunk's bf16 block scale.
-template <int WFMT>
-struct BStage {
-  u32x4 v[WFMT == MOE_WFMT_BF16 ? 4 : 1];
-  uint16_t sc;
+  u32x4 v[AFMT == MOE_AFMT_F32 ? 4 : 2];
 };
 
-template <int WFMT>
-__device__ __forceinline__ void load_b(BStage<WFMT>& st, const uint8_t* const* rowp, const uint16_t* const* scp,
-                                       int k0, int tid) {
-  if constexpr (WFMT == MOE_WFMT_BF16) {
+template <int AFMT>
+__device__ __forceinline__ void load_a(AStage<AFMT>& st, const void* base, const int64_t* src, int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.v[j] = *reinterpret_cast<const u32x4*>(rowp[j] + (int64_t)k0 * 2 + (tid & 7) * 16);
-  } else {
-    st.v[0] = *reinterpret_cast<const u32x4*>(rowp[0] + k0 / 2 + (tid & 1) * 16);
-    st.sc = scp[0][k0 / 32 + (tid & 1)];
-  }
-}
-
-template <int WFMT>
-__device__ __forceinline__ void store_b(const BStage<WFMT>& st, uint16_t (*sB)[LDSW], int tid) {
-  if constexpr (WFMT == MOE_WFMT_BF16) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + 256 * j;
-      *reinterpret_cast<u32x4*>(&sB[idx >> 3][(idx & 7) * 8]) = st.v[j];
+  for (int j = 0; j < 2; ++j) {
+    if constexpr (AFMT == MOE_AFMT_F32) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(base) + src[j] + k0);
+      st.v[2 * j] = p[0];
+      st.v[2 * j + 1] = p[1];
+    } else {
+      st.v[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + src[j] + k0);
     }
-  } else {
-    u32x4 o[4];
-    fp4x32_to_f16(st.v[0], st.sc, o);
-    const int wr = tid >> 1, half = tid & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sB[wr][half * 32 + i * 8]) = o[i];
   }
 }
 
-__device__ __forceinline__ void store_a(const AStage& st, uint16_t (*sA)[LDSW], int tid) {
+// Chunk j of the stage -> 8 MFMA operand values (bf16, or f16 when TO_F16).
+template <int AFMT, bool TO_F16>
+__device__ __forceinline__ u32x4 cvt_a8(const AStage<AFMT>& st, int j) {
+  if constexpr (AFMT == MOE_AFMT_BF16 && !TO_F16) {
+    return st.v[j];
+  } else {
+    float v[8];
+    if constexpr (AFMT == MOE_AFMT_BF16) {
+      const u32x4 q = st.v[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(q[i]); v[2 * i + 1] = bf16_hi(q[i]); }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = __uint_as_float(st.v[2 * j][i]);
+        v[4 + i] = __uint_as_float(st.v[2 * j + 1][i]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t lo, hi;
+      if constexpr (TO_F16) {
+        lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
+        hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+      } else {
+        lo = f32_to_bf16_rne(v[2 * i]);
+        hi = f32_to_bf16_rne(v[2 * i + 1]);
+      }
+      o[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    return o;
+  }
+}
+
+template <int AFMT, bool TO_F16>
+__device__ __forceinline__ void store_a(const AStage<AFMT>& st, uint16_t (*sA)[LDSW], int tid) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int idx = tid + 256 * j;
-    *reinterpret_cast<u32x4*>(&sA[idx >> 3][(idx & 7) * 8]) = st.v[j];
+    *reinterpret_cast<u32x4*>(&sA[idx >> 3][(idx & 7) * 8]) = cvt_a8<AFMT, TO_F16>(st, j);
   }
 }
 
-// Per-thread source rows of the B tile: bf16 threads own rows idx >> 3 for idx = tid + 256 j;
-// fp4 threads own row tid >> 1.  wrow(i) maps tile row i (0..127) to a tensor row.
-template <int WFMT, typename RowFn>
-__device__ __forceinline__ void b_rows(const uint8_t* rec, int H, int I, int t_base, RowFn wrow, int cols, int tid,
-                                       const uint8_t** rowp, const uint16_t** scp) {
-  const int64_t tb = tbytes<WFMT>(H, I);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * ((int64_t)H * I / 2));
+// B: this lane's 32-element run of one weight row for one k-step.
+//   FP4: 16 bytes at row offset (k0 + 32 h) / 2 -- the MFMA slice j of the step is
+//        the lane's codes 8 j .. 8 j + 7, i.e. k = 32 h + 8 j + [0, 8).
+//   bf16: four 16-byte chunks 2 j + h (j = 0..3) of the step's 128-byte row segment,
+//        so lanes r and r + 32 read adjacent chunks of row r in every load; MFMA
+//        slice j of the step covers k = 16 j + 8 h + [0, 8).
+// The activation fragments use the same k order (a_koff below).
+template <int WFMT>
+struct BRun;
+template <>
+struct BRun<MOE_WFMT_BF16> {
+  u32x4 v[4];
+};
+template <>
+struct BRun<MOE_WFMT_FP4> {
+  u32x4 v;  // 32 e2m1 codes, element 2i in the low nibble of byte i
+};
+
+template <int WFMT>
+__device__ __forceinline__ int a_koff(int h, int j) {
+  return WFMT == MOE_WFMT_FP4 ? 32 * h + 8 * j : 16 * j + 8 * h;
+}
+
+// Row source of a B run: this lane's row base (FP4: and its scale row).
+struct BRow {
+  const uint8_t* p;
+  const uint16_t* sc;
+};
+
+template <int WFMT>
+__device__ __forceinline__ BRow b_row(const uint8_t* rec, int H, int I, int tensor, int row, int cols) {
+  const int64_t n = (int64_t)H * I;
+  if constexpr (WFMT == MOE_WFMT_BF16) {
+    return {rec + tensor * n * 2 + (int64_t)row * cols * 2, nullptr};
+  } else {
+    const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2));
+    return {rec + tensor * (n / 2) + (int64_t)row * (cols / 2), scales + tensor * (n / 32) + (int64_t)row * (cols / 32)};
+  }
+}
+
+// Loads of k-step kt (h = lane half).
+template <int WFMT>
+__device__ __forceinline__ void load_b(BRun<WFMT>& r, const BRow& src, int kt, int h) {
+  if constexpr (WFMT == MOE_WFMT_BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(src.p + (int64_t)kt * (BK * 2)) + h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.v[j] = p[2 * j];
+  } else {
+    r.v = *reinterpret_cast<const u32x4*>(src.p + kt * (BK / 2) + 16 * h);
+  }
+}
+
+// FP4 block scales of a row for the k-step pair (kt, kt + 1), kt even: scales
+// [2 kt, 2 kt + 4) in one 8-byte load (aligned: a row holds cols / 32 scales and
+// cols % 128 == 0).  Word e holds k-step kt + e; its low half belongs to lane half 0.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 load_scales(const BRow& src, int kt) {
+  return *reinterpret_cast<const u32x2*>(src.sc + 2 * kt);
+}
+
+// MFMA operand j (8 values) of a run: bf16 as stored, FP4 expanded to f16 and scaled.
+template <int WFMT>
+struct BOps {
+  u32x4 op[4];
+};
+
+template <int WFMT>
+__device__ __forceinline__ void b_operands(BOps<WFMT>& o, const BRun<WFMT>& r, uint32_t scale_bits) {
   if constexpr (WFMT == MOE_WFMT_BF16) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int t, r;
-      wrow((tid + 256 * j) >> 3, t, r);
-      rowp[j] = rec + (int64_t)t * tb + (int64_t)r * cols * 2;
-    }
+    for (int j = 0; j < 4; ++j) o.op[j] = r.v[j];
   } else {
-    int t, r;
-    wrow(tid >> 1, t, r);
-    rowp[0] = rec + (int64_t)t * tb + (int64_t)r * (cols / 2);
-    scp[0] = scales + (int64_t)t * ((int64_t)H * I / 32) + (int64_t)r * (cols / 32);
+    const _Float16 sh = (_Float16)bf16_to_f32((uint16_t)scale_bits);
+    const f16x2 s2 = {sh, sh};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = r.v[j];
+      const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+      const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+      const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+      const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+      o.op[j] = u32x4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                      __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
+    }
   }
-  (void)t_base;
 }
 
+// One k-step: 4 MFMA slices j x (2 row fragments) x (2 weight fragments).
+template <int WFMT, bool F16>
+__device__ __forceinline__ void mfma_step(const uint16_t (*sA)[LDSW], const BOps<WFMT>& b0, const BOps<WFMT>& b1,
+                                          int lane, f32x16 (&acc)[2][2]) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sA[r][a_koff<WFMT>(h, j)]);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sA[32 + r][a_koff<WFMT>(h, j)]);
+    acc[0][0] = mfma32<F16>(a0, b0.op[j], acc[0][0]);
+    acc[0][1] = mfma32<F16>(a0, b1.op[j], acc[0][1]);
+    acc[1][0] = mfma32<F16>(a1, b0.op[j], acc[1][0]);
+    acc[1][1] = mfma32<F16>(a1, b1.op[j], acc[1][1]);
+  }
+}
+
+// Register stage of one k-step: A chunks and the two B runs.
+template <int WFMT>
+struct Stage {
+  AStage<MOE_AFMT_BF16> a;
+  BRun<WFMT> b0, b1;
+};
+
+template <int WFMT>
+__device__ __forceinline__ void issue(Stage<WFMT>& st, const uint16_t* abase, const int64_t* a_src, const BRow& br0,
+                                      const BRow& br1, int kt, int h) {
+  load_a<MOE_AFMT_BF16>(st.a, abase, a_src, kt * BK);
+  load_b<WFMT>(st.b0, br0, kt, h);
+  load_b<WFMT>(st.b1, br1, kt, h);
+}
+
+// Prepare a k-step for the MFMAs: its A tile into LDS buffer sAb, its B operands
+// into registers (s0, s1: the FP4 scale of each run for this k-step).
+template <int WFMT>
+__device__ __forceinline__ void prepare(const Stage<WFMT>& st, uint16_t (*sAb)[LDSW], int tid, uint32_t s0,
+                                        uint32_t s1, BOps<WFMT>& o0, BOps<WFMT>& o1) {
+  store_a<MOE_AFMT_BF16, false>(st.a, sAb, tid);
+  b_operands<WFMT>(o0, st.b0, s0);
+  b_operands<WFMT>(o1, st.b1, s1);
+}
+
+// Software-pipelined k loop over nk k-steps (nk even), two k-steps per iteration.
+// Register stages X (even k-steps) and Y (odd) are each refilled two k-steps
+// ahead; LDS buffers 0 / 1 hold the A tiles of even / odd k-steps; operand sets
+// oX / oY alternate likewise, so nothing is copied at the loop edge.  While the
+// MFMAs of k-step s run, the wavefront stores k-step s + 1's A tile and
+// dequantises its B operands; one barrier per k-step publishes the A tile.
+// Buffer b is rewritten one k-step after it was last read, behind the barrier
+// that ended that k-step.  Refills past the end re-read the last k-step (in
+// bounds, unused), so the body has no branches and every wait covers exactly one
+// stage.  FP4 scales of the pair (s, s + 1) travel with stage X.
+template <int WFMT, bool F16>
+__device__ __forceinline__ void kloop(int nk, const uint16_t* abase, const int64_t* a_src, const BRow& br0,
+                                      const BRow& br1, uint16_t (*sA)[BM][LDSW], int tid, f32x16 (&acc)[2][2]) {
+  constexpr bool FP4 = (WFMT == MOE_WFMT_FP4);
+  const int lane = tid & 63, h = lane >> 5, hs = 16 * h;
+  Stage<WFMT> X, Y;
+  BOps<WFMT> oX0, oX1, oY0, oY1;
+  u32x2 scX0{}, scX1{};
+  issue<WFMT>(X, abase, a_src, br0, br1, 0, h);
+  if constexpr (FP4) { scX0 = load_scales(br0, 0); scX1 = load_scales(br1, 0); }
+  __builtin_amdgcn_sched_barrier(0);
+  issue<WFMT>(Y, abase, a_src, br0, br1, 1, h);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t sY0 = FP4 ? scX0[1] >> hs : 0, sY1 = FP4 ? scX1[1] >> hs : 0;
+  prepare<WFMT>(X, sA[0], tid, FP4 ? scX0[0] >> hs : 0, FP4 ? scX1[0] >> hs : 0, oX0, oX1);
+  {
+    const int kn = min(2, nk - 1);
+    issue<WFMT>(X, abase, a_src, br0, br1, kn, h);
+    if constexpr (FP4) { scX0 = load_scales(br0, kn & ~1); scX1 = load_scales(br1, kn & ~1); }
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    // even k-step kt: operands oX, A tile in buffer 0; prepare kt + 1 (stage Y)
+    prepare<WFMT>(Y, sA[1], tid, sY0, sY1, oY0, oY1);
+    issue<WFMT>(Y, abase, a_src, br0, br1, min(kt + 3, nk - 1), h);
+    mfma_step<WFMT, F16>(sA[0], oX0, oX1, lane, acc);
+    __syncthreads();
+    // odd k-step kt + 1: operands oY, A tile in buffer 1; prepare kt + 2 (stage X)
+    sY0 = FP4 ? scX0[1] >> hs : 0;
+    sY1 = FP4 ? scX1[1] >> hs : 0;
+    prepare<WFMT>(X, sA[0], tid, FP4 ? scX0[0] >> hs : 0, FP4 ? scX1[0] >> hs : 0, oX0, oX1);
+    {
+      const int kn = min(kt + 4, nk - 1);
+      issue<WFMT>(X, abase, a_src, br0, br1, kn, h);
+      if constexpr (FP4) { scX0 = load_scales(br0, kn & ~1); scX1 = load_scales(br1, kn & ~1); }
+    }
+    mfma_step<WFMT, F16>(sA[1], oY0, oY1, lane, acc);
+    __syncthreads();
+  }
+}
+
+
+// Row of output element i (0..15) of a 32x32 MFMA fragment for this lane.
+__device__ __forceinline__ int frag_row(int lane, int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
 // ---------------------------------------------------------------------------
-// GEMM1: act[sorted row, n0..n0+63] = silu(X W_gate^T) * (X W_up^T) for one group.
-// Block: 256 threads = 4 wavefronts in a 2 (rows) x 2 (act columns) grid of
-// 32x32 output blocks; each wavefront owns the gate and the up accumulators of
-// the same 32x32 block.
-template <int WFMT, int AFMT>
+// GEMM1: act[sorted row, n0..n0+127] = silu(X W_gate^T) * (X W_up^T) for one group.
+// Wavefront w owns act columns n0 + 32 w .. + 31: its two weight fragments are the
+// gate and the up rows of those columns, so SwiGLU runs on its own accumulators.
+template <int WFMT>
 __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
   constexpr bool F16 = (WFMT == MOE_WFMT_FP4);
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDSW];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][128][LDSW];
   TileInfo ti;
-  if (!decode_tile(a, a.I / 64, ti)) return;
+  if (!decode_tile(a, a.I / 128, ti)) return;
   const int H = a.H, I = a.I;
-  const int n0 = ti.nt * 64;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int col0 = ti.nt * 128 + wave * 32;
+  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
 
-  // A sources: 2 chunks per thread (row = idx / 8, 16-byte column chunk = idx % 8)
+  // A sources: token rows gathered through the permutation.  Rows past the group
+  // end read the group's first token; their outputs are never stored.
   int64_t a_src[2];
-  bool a_ok[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int idx = tid + 256 * j, r = idx >> 3;
-    a_ok[j] = r < ti.rows;
-    const int tok = a_ok[j] ? a.perm[ti.row0 + r] / a.k : 0;
+    const int tok = a.perm[ti.row0 + (r < ti.rows ? r : 0)] / a.k;
     a_src[j] = (int64_t)tok * H + (idx & 7) * 8;
   }
-  // B sources: tile rows 0..63 are gate rows n0.., 64..127 the up rows n0..
-  const uint8_t* rowp[WFMT == MOE_WFMT_BF16 ? 4 : 1];
-  const uint16_t* scp[1] = {nullptr};
-  b_rows<WFMT>(rec, H, I, 0, [&](int i, int& t, int& r) { t = i >> 6; r = n0 + (i & 63); }, H, tid, rowp, scp);
+  const BRow bg = b_row<WFMT>(rec, H, I, 0, col0 + (lane & 31), H);
+  const BRow bu = b_row<WFMT>(rec, H, I, 1, col0 + (lane & 31), H);
 
-  AStage ra;
-  BStage<WFMT> rb;
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) ra.v[j] = a_ok[j] ? load_x8<AFMT, F16>(a.x, a_src[j]) : u32x4{0, 0, 0, 0};
-  load_b<WFMT>(rb, rowp, scp, 0, tid);
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+  kloop<WFMT, F16>(H / BK, reinterpret_cast<const uint16_t*>(a.xa), a_src, bg, bu, sA, tid, acc);
 
-  f32x16 accg, accu;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) { accg[i] = 0.f; accu[i] = 0.f; }
-  const int nk = H / BK;
-  const int arow = wm * 32 + (lane & 31);
-  const int bg = wn * 32 + (lane & 31), bu = 64 + wn * 32 + (lane & 31);
-  const int koff = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    store_a(ra, sA[buf], tid);
-    store_b<WFMT>(rb, sB[buf], tid);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      const int k0 = (kt + 1) * BK;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) ra.v[j] = a_ok[j] ? load_x8<AFMT, F16>(a.x, a_src[j] + k0) : u32x4{0, 0, 0, 0};
-      load_b<WFMT>(rb, rowp, scp, k0, tid);
-    }
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      const u32x4 av = *reinterpret_cast<const u32x4*>(&sA[buf][arow][kk + koff]);
-      const u32x4 gv = *reinterpret_cast<const u32x4*>(&sB[buf][bg][kk + koff]);
-      const u32x4 uv = *reinterpret_cast<const u32x4*>(&sB[buf][bu][kk + koff]);
-      accg = mfma32<F16>(av, gv, accg);
-      accu = mfma32<F16>(av, uv, accu);
-    }
-  }
   // epilogue: SwiGLU in registers, store act (sorted order) as bf16 / f16
   uint16_t* act = reinterpret_cast<uint16_t*>(a.act);
-  const int col = n0 + wn * 32 + (lane & 31);
+  const int col = col0 + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    if (r < ti.rows) {
-      const float g = accg[i];
-      const float v = g * __frcp_rn(1.0f + __expf(-g)) * accu[i];
-      uint16_t bits;
-      if constexpr (F16) bits = __builtin_bit_cast(uint16_t, (_Float16)v);
-      else bits = f32_to_bf16_rne(v);
-      act[(int64_t)(ti.row0 + r) * I + col] = bits;
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      if (r < ti.rows) {
+        const float g = acc[m][0][i];
+        const float v = g * __frcp_rn(1.0f + __expf(-g)) * acc[m][1][i];
+        uint16_t bits;
+        if constexpr (F16) bits = __builtin_bit_cast(uint16_t, (_Float16)v);
+        else bits = f32_to_bf16_rne(v);
+        act[(int64_t)(ti.row0 + r) * I + col] = bits;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// GEMM2: ypair[pair, n0..n0+127] = act[sorted rows] W_down^T for one group.
+// GEMM2: ypair[pair, n0..n0+255] = act[sorted rows] W_down^T for one group.
+// Wavefront w owns output columns n0 + 64 w .. + 63 (two weight fragments).
 template <int WFMT>
 __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
   constexpr bool F16 = (WFMT == MOE_WFMT_FP4);
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDSW];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][128][LDSW];
   TileInfo ti;
-  if (!decode_tile(a, a.H / 128, ti)) return;
+  if (!decode_tile(a, a.H / 256, ti)) return;
   const int H = a.H, I = a.I;
-  const int n0 = ti.nt * 128;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const uint16_t* act = reinterpret_cast<const uint16_t*>(a.act);
+  const int c0 = ti.nt * 256 + wave * 64;
+  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
 
-  const uint16_t* a_src[2];
-  bool a_ok[2];
+  // A sources: sorted act rows (already in the MFMA operand type).
+  int64_t a_src[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int idx = tid + 256 * j, r = idx >> 3;
-    a_ok[j] = r < ti.rows;
-    a_src[j] = act + (int64_t)(ti.row0 + (a_ok[j] ? r : 0)) * I + (idx & 7) * 8;
+    a_src[j] = (int64_t)(ti.row0 + (r < ti.rows ? r : 0)) * I + (idx & 7) * 8;
   }
-  const uint8_t* rowp[WFMT == MOE_WFMT_BF16 ? 4 : 1];
-  const uint16_t* scp[1] = {nullptr};
-  b_rows<WFMT>(rec, H, I, 0, [&](int i, int& t, int& r) { t = 2; r = n0 + i; }, I, tid, rowp, scp);
+  const BRow b0 = b_row<WFMT>(rec, H, I, 2, c0 + (lane & 31), I);
+  const BRow b1 = b_row<WFMT>(rec, H, I, 2, c0 + 32 + (lane & 31), I);
 
-  AStage ra;
-  BStage<WFMT> rb;
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) ra.v[j] = a_ok[j] ? *reinterpret_cast<const u32x4*>(a_src[j]) : u32x4{0, 0, 0, 0};
-  load_b<WFMT>(rb, rowp, scp, 0, tid);
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+  kloop<WFMT, F16>(I / BK, reinterpret_cast<const uint16_t*>(a.act), a_src, b0, b1, sA, tid, acc);
 
-  f32x16 acc0, acc1;
+  // pair index of each of the lane's 32 output rows, fetched together (rows past
+  // the group end read a valid entry and are not stored)
+  int pr[2][16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
-  const int nk = I / BK;
-  const int arow = wm * 32 + (lane & 31);
-  const int b0 = wn * 64 + (lane & 31), b1 = b0 + 32;
-  const int koff = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    store_a(ra, sA[buf], tid);
-    store_b<WFMT>(rb, sB[buf], tid);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      const int k0 = (kt + 1) * BK;
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        ra.v[j] = a_ok[j] ? *reinterpret_cast<const u32x4*>(a_src[j] + k0) : u32x4{0, 0, 0, 0};
-      load_b<WFMT>(rb, rowp, scp, k0, tid);
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      pr[m][i] = a.perm[ti.row0 + (r < ti.rows ? r : 0)];
     }
+  const int col = c0 + (lane & 31);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      const u32x4 av = *reinterpret_cast<const u32x4*>(&sA[buf][arow][kk + koff]);
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(&sB[buf][b0][kk + koff]);
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(&sB[buf][b1][kk + koff]);
-      acc0 = mfma32<F16>(av, w0, acc0);
-      acc1 = mfma32<F16>(av, w1, acc1);
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      if (r < ti.rows) {
+        float* dst = a.ypair + (int64_t)pr[m][i] * H;
+        dst[col] = acc[m][0][i];
+        dst[col + 32] = acc[m][1][i];
+      }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Activations -> 16-bit MFMA operands, once per call (FP4 weights take f16, bf16
+// weights bf16).  Same rounding as an in-GEMM conversion (round to nearest even).
+template <int AFMT, bool TO_F16>
+__global__ __launch_bounds__(256) void act_operands_kernel(const void* __restrict__ x, uint16_t* __restrict__ xo,
+                                                            int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  AStage<AFMT> st;
+  const int64_t src[2] = {8 * i, 0};
+  if constexpr (AFMT == MOE_AFMT_F32) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(x) + src[0]);
+    st.v[0] = p[0];
+    st.v[1] = p[1];
+  } else {
+    st.v[0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + src[0]);
   }
-  const int c0 = n0 + wn * 64 + (lane & 31);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    if (r < ti.rows) {
-      const int p = a.perm[ti.row0 + r];
-      float* dst = a.ypair + (int64_t)p * H;
-      dst[c0] = acc0[i];
-      dst[c0 + 32] = acc1[i];
-    }
+  *reinterpret_cast<u32x4*>(xo + 8 * i) = cvt_a8<AFMT, TO_F16>(st, 0);
+}
+
+bool prefill_needs_act_operands(int wfmt, int afmt) {
+  return wfmt == MOE_WFMT_FP4 || (wfmt == MOE_WFMT_BF16 && afmt == MOE_AFMT_F32);
+}
+
+void launch_act_operands(int wfmt, int afmt, const void* x, void* xo, int64_t n, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  const dim3 grid((unsigned)((n8 + 255) / 256));
+  uint16_t* o = reinterpret_cast<uint16_t*>(xo);
+  if (wfmt == MOE_WFMT_FP4) {
+    if (afmt == MOE_AFMT_BF16) hipLaunchKernelGGL((act_operands_kernel<MOE_AFMT_BF16, true>), grid, dim3(256), 0, s, x, o, n8);
+    else hipLaunchKernelGGL((act_operands_kernel<MOE_AFMT_F32, true>), grid, dim3(256), 0, s, x, o, n8);
+  } else {
+    hipLaunchKernelGGL((act_operands_kernel<MOE_AFMT_F32, false>), grid, dim3(256), 0, s, x, o, n8);
   }
 }
 
@@ -572,14 +691,9 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
     else launch_timed(gemm1_f32_kernel<MOE_AFMT_F32>, grid, dim3(256), 0, s, tm, a);
     return;
   }
-  const dim3 grid(padded_grid(max_tiles_m, a.I / 64));
-#define G1(W, A) launch_timed(gemm1_kernel<W, A>, grid, dim3(256), 0, s, tm, a)
-  if (wfmt == MOE_WFMT_BF16) {
-    if (afmt == MOE_AFMT_BF16) G1(MOE_WFMT_BF16, MOE_AFMT_BF16); else G1(MOE_WFMT_BF16, MOE_AFMT_F32);
-  } else {
-    if (afmt == MOE_AFMT_BF16) G1(MOE_WFMT_FP4, MOE_AFMT_BF16); else G1(MOE_WFMT_FP4, MOE_AFMT_F32);
-  }
-#undef G1
+  const dim3 grid(padded_grid(max_tiles_m, a.I / 128));
+  if (wfmt == MOE_WFMT_BF16) launch_timed(gemm1_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  else launch_timed(gemm1_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
 }
 
 void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
@@ -588,7 +702,7 @@ void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipSt
     launch_timed(gemm2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tm, a);
     return;
   }
-  const dim3 grid(padded_grid(max_tiles_m, a.H / 128));
+  const dim3 grid(padded_grid(max_tiles_m, a.H / 256));
   if (wfmt == MOE_WFMT_BF16) launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm2_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
 }

@@ -352,6 +352,9 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->act), (size_t)Pmax * I * 4) ||
       dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)))
     return cleanup_fail(MOE_ENOMEM);
+  if (prefill_needs_act_operands(c.wfmt, c.afmt) &&
+      dev_alloc(reinterpret_cast<uint8_t**>(&ctx->xo), (size_t)c.max_tokens * H * 2))
+    return cleanup_fail(MOE_ENOMEM);
   ctx->cnt = ctx->step_dev;
   ctx->fill_key = ctx->cnt + C_COUNT;
   ctx->fill_slot = ctx->fill_key + E;
@@ -407,7 +410,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
                  ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
-                 ctx->flags};
+                 ctx->flags, ctx->xo};
   for (void* p : dev)
     if (p) hipFree(p);
   void* host[] = {ctx->step_host, ctx->h_slot_idx, ctx->h_w, ctx->h_x, ctx->h_xf, ctx->h_y, ctx->h_hbuf};
@@ -637,6 +640,11 @@ moe_status prefill_gpu_part(moe_ctx* ctx, const void* x, int T, const float* w, 
   launch_permute(ctx->pair_grp, ctx->cnt, P, E, ctx->hist, ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, bm, s);
   PrefillArgs a;
   a.x = x;
+  a.xa = x;
+  if (prefill_needs_act_operands(ctx->cfg.wfmt, ctx->cfg.afmt)) {
+    launch_act_operands(ctx->cfg.wfmt, ctx->cfg.afmt, x, ctx->xo, (int64_t)T * H, s);
+    a.xa = ctx->xo;
+  }
   a.w = w;
   a.arena = ctx->arena;
   a.rec_bytes = ctx->S;
@@ -727,8 +735,8 @@ MOE_API moe_status moe_ffn_prefill(moe_ctx* ctx, int32_t layer, const void* x, i
   CHECK_ARG(layer >= 0 && layer < ctx->cfg.n_layers, "layer out of range");
   CHECK_ARG(T >= 1 && T <= ctx->cfg.max_tokens, "T out of range");
   CHECK_ARG(x && topk_idx && topk_w && y, "null pointer");
-  if (ctx->cfg.wfmt != MOE_WFMT_F32 && ctx->cfg.hidden % 128)
-    return fail(ctx, MOE_ENOTSUP, "MFMA prefill needs hidden % 128 == 0");
+  if (ctx->cfg.wfmt != MOE_WFMT_F32 && (ctx->cfg.hidden % 256 || ctx->cfg.inter % 128))
+    return fail(ctx, MOE_ENOTSUP, "MFMA prefill needs hidden % 256 == 0 and inter % 128 == 0");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int k = ctx->cfg.top_k, E = ctx->cfg.n_experts, L = ctx->cfg.n_layers, P = T * k;
   const int mode = ctx->cfg.mode;
