@@ -37,10 +37,6 @@ constexpr int LDSW = BK + 8;  // padded LDS row (elements)
 
 int prefill_bm() { return BM; }
 
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int per = nblocks >> 3;
-  return (bid & 7) * per + (bid >> 3);
-}
 
 // ---------------------------------------------------------------------------
 // Permutation: counting sort of GPU pairs by group (groups are ordered by slot).
@@ -184,8 +180,16 @@ struct TileInfo {
 __device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int NT, TileInfo& ti) {
   const int ngrp = a.cnt[C_NGRP];
   if (ngrp <= 0) return false;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  // The grid is sized for the most tiles a call can have; the real count is only
+  // known here.  Blocks go to the 8 XCDs round-robin (block b to XCD b % 8), so
+  // spread the real tiles evenly: XCD x takes the contiguous range
+  // [x * per, (x + 1) * per), which keeps one group's tiles (and their shared
+  // activation rows) in one XCD's L2.  Blocks beyond the real work exit at once.
   const int total = a.tile_base[ngrp] * NT;
+  const int per = (total + 7) >> 3;
+  const int i = blockIdx.x >> 3;
+  if (i >= per) return false;
+  const int bid = (blockIdx.x & 7) * per + i;
   if (bid >= total) return false;
   int lo = 0, hi = ngrp - 1;
   while (lo < hi) {
