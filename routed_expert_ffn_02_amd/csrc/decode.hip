@@ -175,6 +175,48 @@ __device__ __forceinline__ void load_x_chunk(const void* x, int H, int t, int c,
   }
 }
 
+// Raw (unconverted) activation chunk: the loads are issued early and the values are
+// converted only where they are used, so nothing waits on them before the weight
+// loads have been issued.  Native vectors keep the registers out of memory.
+typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2n __attribute__((ext_vector_type(2)));
+
+template <int AFMT, int EPC>
+struct XRaw {
+  static constexpr bool kHalf = (AFMT == MOE_AFMT_BF16 && EPC == 4);  // one 8-byte load
+  static constexpr int kN = (AFMT == MOE_AFMT_BF16) ? (kHalf ? 1 : EPC / 8) : EPC / 4;
+  u32x4n q[kN];
+  u32x2n h;
+  __device__ __forceinline__ void load(const void* x, int H, int t, int c) {
+    if constexpr (kHalf) {
+      h = *reinterpret_cast<const u32x2n*>(reinterpret_cast<const uint16_t*>(x) + (size_t)t * H + (size_t)c * 4);
+    } else if constexpr (AFMT == MOE_AFMT_BF16) {
+      const u32x4n* p = reinterpret_cast<const u32x4n*>(reinterpret_cast<const uint16_t*>(x) + (size_t)t * H + (size_t)c * EPC);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) q[i] = p[i];
+    } else {
+      const u32x4n* p = reinterpret_cast<const u32x4n*>(reinterpret_cast<const float*>(x) + (size_t)t * H + (size_t)c * EPC);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) q[i] = p[i];
+    }
+  }
+  __device__ __forceinline__ void to_f32(float* v) const {
+    if constexpr (kHalf) {
+      v[0] = bf16_lo(h[0]); v[1] = bf16_hi(h[0]); v[2] = bf16_lo(h[1]); v[3] = bf16_hi(h[1]);
+    } else if constexpr (AFMT == MOE_AFMT_BF16) {
+#pragma unroll
+      for (int i = 0; i < kN; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { v[8 * i + 2 * j] = bf16_lo(q[i][j]); v[8 * i + 2 * j + 1] = bf16_hi(q[i][j]); }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kN; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = __uint_as_float(q[i][j]);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Phase 1, fast path (H a whole number of wavefront-wide chunks, P <= 64): each
 // wavefront owns RW consecutive (gate, up) row pairs of one expert; its weight
@@ -185,14 +227,26 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
   // both loads issue together (grp_slot has E >= gridDim.y entries, so the read is in
   // bounds even for a group beyond the count, whose value is then unused)
   const int slot = a.grp_slot[g];
-  if (g >= a.cnt[C_NGRP]) return;
   const int H = a.H, I = a.I;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  using RD = RowDot<WFMT>;
+  constexpr int EPC = RD::kElems;
+  // Loads return in issue order, so whatever a row's dot product needs besides its
+  // weights is requested before the weights.  With one token (MAXT == 1) that is
+  // token 0's activation chunks, whose address needs no other load; the group's
+  // single pair (needed only for the store) comes with the slot.
+  float xv[MAXT][CPL][EPC];
+  XRaw<AFMT, EPC> xr[CPL];
+  int pair0 = 0;
+  if constexpr (MAXT == 1) {
+    pair0 = a.grp_pair0[g];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) xr[c].load(a.x, H, 0, lane + 64 * c);
+  }
+  if (g >= a.cnt[C_NGRP]) return;
   const int row0 = (blockIdx.x * 4 + wave) * RW;
   if (row0 >= I) return;
   const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
-  using RD = RowDot<WFMT>;
-  constexpr int EPC = RD::kElems;
   uint4 qg[RW][CPL], qu[RW][CPL];
   float sg[RW][CPL], su[RW][CPL];
 #pragma unroll
@@ -209,21 +263,29 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
     }
   }
   // the group's pairs (tokens) and their activation chunks
-  uint64_t m = group_mask(a, g);
   int pair[MAXT];
   int n = 0;
+  if constexpr (MAXT == 1) {
+    // every load is in flight; only now consume the first ones (the activations)
+    __builtin_amdgcn_sched_barrier(0);
+    pair[0] = pair0;
+    n = 1;
 #pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    pair[t] = m ? __builtin_ctzll(m) : 0;
-    n += (m != 0);
-    m &= m - 1;
+    for (int c = 0; c < CPL; ++c) xr[c].to_f32(xv[0][c]);
+  } else {
+    uint64_t m = group_mask(a, g);
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      pair[t] = m ? __builtin_ctzll(m) : 0;
+      n += (m != 0);
+      m &= m - 1;
+    }
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      if (t < n)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) load_x_chunk<AFMT, EPC>(a.x, H, pair[t] / a.k, lane + 64 * c, xv[t][c]);
   }
-  float xv[MAXT][CPL][EPC];
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t)
-    if (t < n)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) load_x_chunk<AFMT, EPC>(a.x, H, pair[t] / a.k, lane + 64 * c, xv[t][c]);
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int row = row0 + r;
@@ -321,6 +383,7 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
   constexpr int R2 = kP2RowsPerWave;
   const int g = blockIdx.y;
   const int slot = a.grp_slot[g];  // issued with the count (see phase 1)
+  const int pair0 = (MAXT == 1) ? a.grp_pair0[g] : 0;
   if (g >= a.cnt[C_NGRP]) return;
   const int H = a.H, I = a.I;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -329,32 +392,53 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
   const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
   using RD = RowDot<WFMT>;
   constexpr int EPC = RD::kElems;
-  uint4 q[R2];
-  float sc[R2];
+  // one token: the group's activated row is requested before the weights (loads
+  // return in issue order)
+  float hv[MAXT][EPC];
+  if constexpr (MAXT == 1) {
+    const float4* hp = reinterpret_cast<const float4*>(a.h + (int64_t)pair0 * I + lane * EPC);
 #pragma unroll
-  for (int r = 0; r < R2; ++r) {
-    const int row = min(r0 + r, H - 1);
-    q[r] = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 2, row, H, I))[lane];
-    sc[r] = RD::scale(scale_row<WFMT>(rec, 2, row, H, I), lane);
+    for (int i = 0; i < EPC / 4; ++i) {
+      const float4 v = hp[i];
+      hv[0][4 * i] = v.x; hv[0][4 * i + 1] = v.y; hv[0][4 * i + 2] = v.z; hv[0][4 * i + 3] = v.w;
+    }
   }
-  uint64_t m = group_mask(a, g);
+  uint4 q[R2];
+  // the (small) block scales first, kept as raw bits until used: row r then waits
+  // only for its own weights
+  uint16_t scr[R2];
+  if constexpr (WFMT == MOE_WFMT_FP4) {
+#pragma unroll
+    for (int r = 0; r < R2; ++r)
+      scr[r] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < R2; ++r)
+    q[r] = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
+  if constexpr (MAXT == 1) __builtin_amdgcn_sched_barrier(0);  // every load in flight before any use
   int pair[MAXT];
   int n = 0;
+  if constexpr (MAXT == 1) {
+    pair[0] = pair0;
+    n = 1;
+  } else {
+    uint64_t m = group_mask(a, g);
 #pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    pair[t] = m ? __builtin_ctzll(m) : 0;
-    n += (m != 0);
-    m &= m - 1;
-  }
-  float hv[MAXT][EPC];
+    for (int t = 0; t < MAXT; ++t) {
+      pair[t] = m ? __builtin_ctzll(m) : 0;
+      n += (m != 0);
+      m &= m - 1;
+    }
 #pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    if (t < n) {
-      const float4* hp = reinterpret_cast<const float4*>(a.h + (int64_t)pair[t] * I + lane * EPC);
+    for (int t = 0; t < MAXT; ++t) {
+      if (t < n) {
+        const float4* hp = reinterpret_cast<const float4*>(a.h + (int64_t)pair[t] * I + lane * EPC);
 #pragma unroll
-      for (int i = 0; i < EPC / 4; ++i) {
-        const float4 v = hp[i];
-        hv[t][4 * i] = v.x; hv[t][4 * i + 1] = v.y; hv[t][4 * i + 2] = v.z; hv[t][4 * i + 3] = v.w;
+        for (int i = 0; i < EPC / 4; ++i) {
+          const float4 v = hp[i];
+          hv[t][4 * i] = v.x; hv[t][4 * i + 1] = v.y; hv[t][4 * i + 2] = v.z; hv[t][4 * i + 3] = v.w;
+        }
       }
     }
   }
@@ -368,7 +452,8 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
         float p = 0.f;
 #pragma unroll
         for (int i = 0; i < EPC; ++i) p += v[i] * hv[t][i];
-        const float sum = wave_sum(sc[r] * p);
+        const float scale = (WFMT == MOE_WFMT_FP4) ? bf16_to_f32(scr[r]) : 1.f;
+        const float sum = wave_sum(scale * p);
         const int row = r0 + r;
         if (lane == 0 && row < H) a.d[(int64_t)pair[t] * H + row] = sum;
       }

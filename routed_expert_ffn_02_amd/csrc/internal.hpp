@@ -55,18 +55,19 @@ struct LookupArgs {
   int32_t* u_key; int32_t* u_kind; int32_t* u_slot; int32_t* u_evict;  // [E]
   int32_t* fill_key; int32_t* fill_slot; int32_t* cpu_key;              // [E]
   int32_t* grp_slot;         // [E]
+  int32_t* grp_pair0;        // [E] first pair of each group (-1 in candidate mode)
   int32_t* pair_grp;         // [T*k]
   int32_t* cnt;              // [C_COUNT]
 };
 
 struct DecodeArgs {
   const void* x;             // [T,H] afmt
-  const void* xa;            // [T,H] 16-bit MFMA operands (x itself, or its converted copy)
   const float* w;            // [T,k]
   const uint8_t* arena;
   int64_t rec_bytes;
   int32_t T, k, H, I;
   const int32_t* grp_slot;   // [G]
+  const int32_t* grp_pair0;  // [G] first pair routed to group g (the only one when T == 1)
   const int32_t* pair_grp;   // [T*k]
   const int32_t* cnt;        // device counters (C_NGRP)
   float* h;                  // [T*k, I] scratch
@@ -193,7 +194,7 @@ struct moe_ctx {
   int32_t* step_dev = nullptr;   // [C_COUNT + 5E]
   int32_t *cnt = nullptr, *fill_key = nullptr, *fill_slot = nullptr, *cpu_key = nullptr;
   int32_t *u_key = nullptr, *u_kind = nullptr;
-  int32_t *u_slot = nullptr, *u_evict = nullptr, *grp_slot = nullptr;
+  int32_t *u_slot = nullptr, *u_evict = nullptr, *grp_slot = nullptr, *grp_pair0 = nullptr;
   int32_t* pair_grp = nullptr;   // [Pmax]
   int32_t* slot_scratch = nullptr;  // [Pmax] slot ids of steps whose caller passes none
 

@@ -240,6 +240,7 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
     }
     s_uaux[tid] = g;  // group id (misses that became fills are GPU now; their miss rank is no longer needed)
     a.grp_slot[g] = my;
+    a.grp_pair0[g] = (a.cand == nullptr) ? s_first[s_ukey[tid] - kbase] : -1;
   }
   __syncthreads();
 

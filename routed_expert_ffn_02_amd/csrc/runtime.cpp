@@ -183,6 +183,7 @@ void fill_lookup_args(moe_ctx* c, LookupArgs& a, int layer, const int32_t* idx, 
   a.fill_slot = c->fill_slot;
   a.cpu_key = c->cpu_key;
   a.grp_slot = c->grp_slot;
+  a.grp_pair0 = c->grp_pair0;
   a.pair_grp = c->pair_grp;
   a.cnt = c->cnt;
 }
@@ -341,7 +342,8 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->stamp, kMaxCachedSlots) || dev_alloc(&ctx->reserved, kMaxCachedSlots) ||
       dev_alloc(&ctx->counter, 1) || dev_alloc(&ctx->step_dev, C_COUNT + 5 * E) ||
       dev_alloc(&ctx->u_slot, E) || dev_alloc(&ctx->u_evict, E) ||
-      dev_alloc(&ctx->grp_slot, std::max<int64_t>(E, Pmax)) || dev_alloc(&ctx->slot_scratch, Pmax) ||
+      dev_alloc(&ctx->grp_slot, std::max<int64_t>(E, Pmax)) || dev_alloc(&ctx->grp_pair0, std::max<int64_t>(E, Pmax)) ||
+      dev_alloc(&ctx->slot_scratch, Pmax) ||
       dev_alloc(&ctx->pair_grp, Pmax) ||
       dev_alloc(&ctx->logits, (size_t)c.max_tokens * E) || dev_alloc(&ctx->h, (size_t)Pdec * I) ||
       dev_alloc(&ctx->dpair, (size_t)Pdec * H) ||
@@ -408,7 +410,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   }
   for (auto e : ctx->event_pool) hipEventDestroy(e);
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
-                 ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
+                 ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
                  ctx->flags, ctx->xo};
   for (void* p : dev)
@@ -588,6 +590,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   d.H = H;
   d.I = I;
   d.grp_slot = ctx->grp_slot;
+  d.grp_pair0 = ctx->grp_pair0;
   d.pair_grp = ctx->pair_grp;
   d.cnt = ctx->cnt;
   d.h = ctx->h;
