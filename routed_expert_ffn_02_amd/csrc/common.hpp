@@ -40,10 +40,23 @@ __device__ __forceinline__ float load_act(const void* x, size_t i) {
   }
 }
 
+// Sum over the 64 lanes of a wavefront, returned to every lane.  Data-parallel
+// primitives (DPP) move values between lanes inside the VALU: quad permutes and the
+// (half-)row mirrors sum each 16-lane row, then the row broadcasts of lanes 15 and
+// 31 carry the partial sums up to lane 63, which is read out as a uniform value.
+// No LDS round trips, unlike lane shuffles.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_move<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]: pairs
+  v += dpp_move<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]: quads
+  v += dpp_move<0x141, 0xf>(v);  // row_half_mirror: 8 lanes
+  v += dpp_move<0x140, 0xf>(v);  // row_mirror: 16 lanes
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -175,6 +175,20 @@ __device__ __forceinline__ void load_x_chunk(const void* x, int H, int t, int c,
   }
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 32 e2m1 codes (16 bytes) -> 16 f16 pairs, exact (element 2i in the low nibble).
+__device__ __forceinline__ void fp4x32_to_f16x2(const uint4& q, f16x2* o) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0);
+    o[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1);
+    o[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2);
+    o[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3);
+  }
+}
+
 // Raw (unconverted) activation chunk: the loads are issued early and the values are
 // converted only where they are used, so nothing waits on them before the weight
 // loads have been issued.  Native vectors keep the registers out of memory.
@@ -286,6 +300,18 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) load_x_chunk<AFMT, EPC>(a.x, H, pair[t] / a.k, lane + 64 * c, xv[t][c]);
   }
+  // FP4: activations as f16 pairs, once per chunk (exact for bf16 inputs in the f16
+  // range; larger magnitudes saturate like the prefill GEMM's f16 operands)
+  f16x2 xh[MAXT][CPL][WFMT == MOE_WFMT_FP4 ? 16 : 1];
+  if constexpr (WFMT == MOE_WFMT_FP4) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      if (t < n)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xh[t][c][i] = f16x2{(_Float16)xv[t][c][2 * i], (_Float16)xv[t][c][2 * i + 1]};
+  }
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int row = row0 + r;
@@ -294,20 +320,41 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
     for (int t = 0; t < MAXT; ++t) { accg[t] = 0.f; accu[t] = 0.f; }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      float vg[EPC], vu[EPC];
-      RD::unpack(qg[r][c], vg);
-      RD::unpack(qu[r][c], vu);
+      if constexpr (WFMT == MOE_WFMT_FP4) {
+        // codes expand to f16 pairs (exact) and meet the activations in packed dot
+        // products with fp32 accumulation: half the VALU work of fp32 FMAs
+        f16x2 hg[16], hu[16];
+        fp4x32_to_f16x2(qg[r][c], hg);
+        fp4x32_to_f16x2(qu[r][c], hu);
 #pragma unroll
-      for (int t = 0; t < MAXT; ++t) {
-        if (t < n) {
-          float pg = 0.f, pu = 0.f;
+        for (int t = 0; t < MAXT; ++t) {
+          if (t < n) {
+            float pg = 0.f, pu = 0.f;
 #pragma unroll
-          for (int i = 0; i < EPC; ++i) {
-            pg += vg[i] * xv[t][c][i];
-            pu += vu[i] * xv[t][c][i];
+            for (int i = 0; i < 16; ++i) {
+              pg = __builtin_amdgcn_fdot2(hg[i], xh[t][c][i], pg, false);
+              pu = __builtin_amdgcn_fdot2(hu[i], xh[t][c][i], pu, false);
+            }
+            accg[t] += sg[r][c] * pg;
+            accu[t] += su[r][c] * pu;
           }
-          accg[t] += sg[r][c] * pg;
-          accu[t] += su[r][c] * pu;
+        }
+      } else {
+        float vg[EPC], vu[EPC];
+        RD::unpack(qg[r][c], vg);
+        RD::unpack(qu[r][c], vu);
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+          if (t < n) {
+            float pg = 0.f, pu = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPC; ++i) {
+              pg += vg[i] * xv[t][c][i];
+              pu += vu[i] * xv[t][c][i];
+            }
+            accg[t] += sg[r][c] * pg;
+            accu[t] += su[r][c] * pu;
+          }
         }
       }
     }
