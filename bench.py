@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--alias-records", type=int, default=0,
                     help="back keys by key %% R records (smaller host pool; same transfer sizes)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -50,12 +52,60 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# sources the decode phase-1 kernel is built from; a traffic figure counts only if
+# it was measured on exactly these
+PHASE1_SOURCES = ("routed_expert_ffn_02_amd/csrc/decode.hip", "routed_expert_ffn_02_amd/csrc/common.hpp")
+
+
+def phase1_source_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    for rel in PHASE1_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config):
+    """HBM bytes per dec_phase1 launch from the committed counter summary for this config
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when that summary is
+    missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"dec_phase1_{config}_traffic.md")
+    try:
+        with open(path) as f:
+            fields = dict(line.strip("- \n").split(": ", 1) for line in f if line.startswith("- ") and ": " in line)
+        if fields.get("source_sha1") != phase1_source_sha1():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    """A plain 512 MiB device copy, three times: reads and writes of known size for the
+    byte counters."""
+    import torch
+    n = 512 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of this build",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
     import routed_expert_ffn_02_amd as R
@@ -230,7 +280,7 @@ def main():
                    "pool_aliased": bool(wl.alias_records)},
         "roofline": {"bound": "hbm", "kernel": "dec_phase1 (gate/up GEMV + SwiGLU)",
                      "achieved": round(p1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(p1_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(p1_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(args.config),
                      "bytes_per_launch": int(p1_bytes), "avg_launch_us": round(p1_avg_ms * 1e3, 3)},
         "cpu_baseline": cpu_baseline,
         "decode": decode_detail,
