@@ -59,11 +59,17 @@ PHASE1_SOURCES = ("routed_expert_ffn_02_amd/csrc/decode.hip", "routed_expert_ffn
 
 
 def phase1_source_sha1():
+    """SHA-1 of the phase-1 sources with comments and whitespace removed (edits to
+    comments leave a measurement valid; any code change invalidates it)."""
     import hashlib
+    import re
     h = hashlib.sha1()
     for rel in PHASE1_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -300,8 +300,9 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) load_x_chunk<AFMT, EPC>(a.x, H, pair[t] / a.k, lane + 64 * c, xv[t][c]);
   }
-  // FP4: activations as f16 pairs, once per chunk (exact for bf16 inputs in the f16
-  // range; larger magnitudes saturate like the prefill GEMM's f16 operands)
+  // FP4: activations as f16 pairs, once per chunk (exact for bf16 inputs inside the
+  // f16 range; larger magnitudes overflow to infinity, as the prefill GEMM's f16
+  // operands do)
   f16x2 xh[MAXT][CPL][WFMT == MOE_WFMT_FP4 ? 16 : 1];
   if constexpr (WFMT == MOE_WFMT_FP4) {
 #pragma unroll
