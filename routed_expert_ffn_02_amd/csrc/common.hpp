@@ -59,10 +59,38 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Maximum over the 64 lanes (same DPP pattern as wave_sum; lanes a row broadcast does
+// not write read -inf, the identity).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move_or(float v, float ident) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, ident), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xf, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  const float ni = -INFINITY;
+  v = fmaxf(v, dpp_move_or<0xB1, 0xf>(v, ni));
+  v = fmaxf(v, dpp_move_or<0x4E, 0xf>(v, ni));
+  v = fmaxf(v, dpp_move_or<0x141, 0xf>(v, ni));
+  v = fmaxf(v, dpp_move_or<0x140, 0xf>(v, ni));
+  v = fmaxf(v, dpp_move_or<0x142, 0xa>(v, ni));
+  v = fmaxf(v, dpp_move_or<0x143, 0xc>(v, ni));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Minimum of an int over the 64 lanes (INT_MAX is the identity).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_move_i(int v, int ident) {
+  return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  const int id = 0x7fffffff;
+  v = min(v, dpp_move_i<0xB1, 0xf>(v, id));
+  v = min(v, dpp_move_i<0x4E, 0xf>(v, id));
+  v = min(v, dpp_move_i<0x141, 0xf>(v, id));
+  v = min(v, dpp_move_i<0x140, 0xf>(v, id));
+  v = min(v, dpp_move_i<0x142, 0xa>(v, id));
+  v = min(v, dpp_move_i<0x143, 0xc>(v, id));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

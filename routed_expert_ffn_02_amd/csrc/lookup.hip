@@ -60,10 +60,35 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
   __shared__ int s_tmp[64];
   __shared__ int s_sc[8];
 
+  __shared__ int s_slotrow[kMaxExperts];       // slot_of of this layer's keys at kernel start
+  __shared__ int s_keyof[kMaxCachedSlots];     // key_of at kernel start
+  __shared__ uint64_t s_c0;
+
   const int tid = threadIdx.x;
   const int E = a.E, k = a.k, P = a.T * a.k;
   const int kbase = a.layer * E;
   const bool cached = (a.mode == LK_OFFLOAD || a.mode == LK_CPU || a.mode == LK_HYBRID);
+
+  // Every piece of cache state this step reads is requested now, in parallel, instead of
+  // one dependent round trip per stage: this layer's slot_of row, and per slot the
+  // stamp, the reservation flag and the resident key (E <= kLookupThreads).
+  int slotrow_r = -1;
+  uint64_t st_r[kSlotsPerThread];
+  uint8_t rs_r[kSlotsPerThread];
+  int ko_r[kSlotsPerThread];
+  uint64_t c0_r = 0;
+  if (cached) {
+    if (tid < E) slotrow_r = a.slot_of[kbase + tid];
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int s = tid + j * kLookupThreads;
+      const bool in = s < a.n_slots;
+      st_r[j] = in ? a.stamp[s] : 0;
+      rs_r[j] = in ? a.reserved[s] : 1;
+      ko_r[j] = in ? a.key_of[s] : -1;
+    }
+    if (tid == 0) c0_r = *a.counter;
+  }
 
   // ---- 1. U in first-appearance order --------------------------------------
   for (int e = tid; e < E; e += kLookupThreads) {
@@ -71,6 +96,15 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
     s_upos[e] = -1;
   }
   for (int s = tid; s < kMaxCachedSlots; s += kLookupThreads) s_prot[s] = 0;
+  if (cached) {
+    if (tid < E) s_slotrow[tid] = slotrow_r;
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int s = tid + j * kLookupThreads;
+      if (s < a.n_slots) s_keyof[s] = ko_r[j];
+    }
+    if (tid == 0) s_c0 = c0_r;
+  }
   __syncthreads();
   if (tid == 0) s_sc[0] = 0;
   __syncthreads();
@@ -128,7 +162,7 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
       slot = a.buffer_base + (key - kbase);
       kind = MOE_KIND_BUF;
     } else {
-      slot = a.slot_of[key];
+      slot = s_slotrow[key - kbase];
       if (slot >= 0) {
         kind = MOE_KIND_HIT;
         s_prot[slot] = 1;
@@ -151,7 +185,11 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
   int q = 0, ev = 0;
   if (cached) {
     int cnt = 0;
-    for (int s = tid; s < a.n_slots; s += kLookupThreads) cnt += (!s_prot[s] && !a.reserved[s]);
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int s = tid + j * kLookupThreads;
+      cnt += (s < a.n_slots && !s_prot[s] && !rs_r[j]);
+    }
     ev = block_sum(cnt, s_tmp);
     // ---- 4. q: same rule as the host qstar_split ---------------------------
     if (a.mode == LK_OFFLOAD) {
@@ -178,8 +216,8 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
 #pragma unroll
     for (int j = 0; j < kSlotsPerThread; ++j) {
       int s = tid + j * kLookupThreads;
-      bool elig = (s < a.n_slots) && !s_prot[s] && !a.reserved[s];
-      keys[j] = elig ? ((a.stamp[s] << 16) | (uint64_t)s) : ~0ull;
+      bool elig = (s < a.n_slots) && !s_prot[s] && !rs_r[j];
+      keys[j] = elig ? ((st_r[j] << 16) | (uint64_t)s) : ~0ull;
     }
     uint64_t last = 0;
     bool first = true;
@@ -197,14 +235,14 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
   __syncthreads();
 
   // ---- 6. admit fills -----------------------------------------------------------
-  uint64_t c0 = cached ? *a.counter : 0;
+  uint64_t c0 = cached ? s_c0 : 0;
   int n_evict_local = 0;
   for (int r = tid; r < m; r += kLookupThreads) {
     const int u = s_miss_u[r];
     if (r < q) {
       const int slot = (int)(s_victim[r] & 0xffffull);
       const int key = s_ukey[u];
-      const int old = a.key_of[slot];
+      const int old = s_keyof[slot];
       if (old >= 0) {
         a.slot_of[old] = -1;
         ++n_evict_local;

@@ -161,12 +161,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       int e = lane + 64 * i;
       if (!taken[i] && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    // wave arg-max under the same order: the largest value, then the lowest index
+    // among the lanes holding it (-0 and +0 compare equal, as in `better`)
+    const float wv = wave_max(bv);
+    bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
+    bv = wv;
     // bi is the same on every lane; mark it taken
 #pragma unroll
     for (int i = 0; i < kTopkPerLane; ++i)
