@@ -63,7 +63,7 @@ class moe_stats(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m routed_expert_ffn_02_amd._build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python routed_expert_ffn_02_amd/_build.py` "
                           "(hipcc, gfx950).  There is no CPU fallback.")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, U64, VP = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p

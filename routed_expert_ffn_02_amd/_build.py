@@ -1,6 +1,6 @@
 """Build the routed-MoE C-ABI library for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m routed_expert_ffn_02_amd._build        # compile csrc/ -> libroutedmoe.so
+    python routed_expert_ffn_02_amd/_build.py        # compile csrc/ -> libroutedmoe.so
 """
 from __future__ import annotations
 

@@ -598,6 +598,237 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// FP4 grouped GEMMs with the codes staged in LDS.
+//
+// Fetching MFMA operands lane by lane makes each 1 KB weight load touch 32 rows, i.e.
+// 32 cache lines, and the address / L1 path (not the ALUs) then bounds the kernel.
+// Here each stage's codes are fetched four lanes per row (16 lines per 1 KB load),
+// written to LDS raw (4 bits a weight, a quarter of the bytes of f16), and read back
+// by each lane in MFMA layout, where it dequantises them.  A stage covers 128 k: the
+// activation tile (64 x 128, 16 KB) and the block's 256 weight rows x 64 B of codes
+// (16 KB).  Block scales travel in registers, 16 bytes per lane for two stages.
+// Register stages X (even stages) and Y (odd) are refilled two stages ahead; the
+// stage just computed frees its LDS buffer, which the next store reuses behind the
+// barrier that closed the previous stage (one barrier per stage).  Refills past the
+// end re-read the last stage (in bounds, unused).  Needs K % 256 == 0.
+constexpr int F4_KS = 128;                 // k per stage
+constexpr int F4_AW = F4_KS + 8;           // padded activation row (elements)
+constexpr int F4_BP = F4_KS / 2 + 16;      // padded code row (bytes): conflict-free 16-byte reads
+constexpr int F4_ROWS = 256;               // weight rows per block
+
+struct F4Stage {
+  u32x4 a[4];  // activation chunk i: tile row (tid >> 4) + 16 i, 8-element chunk tid & 15
+  u32x4 b[4];  // code chunk j: block row (tid >> 2) + 64 j, 16-byte chunk tid & 3
+};
+
+struct F4Src {
+  const uint16_t* a[4];  // activation row starts (+ chunk offset)
+  const uint8_t* b[4];   // code row starts (+ chunk offset)
+};
+
+__device__ __forceinline__ void f4_issue(F4Stage& st, const F4Src& src, int stage) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(src.a[i] + stage * F4_KS);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st.b[j] = *reinterpret_cast<const u32x4*>(src.b[j] + stage * (F4_KS / 2));
+}
+
+__device__ __forceinline__ void f4_store(const F4Stage& st, uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sA[(tid >> 4) + 16 * i][(tid & 15) * 8]) = st.a[i];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 2) + 64 * j][(tid & 3) * 16]) = st.b[j];
+}
+
+// Scales of one run row for stages 2p, 2p + 1: blocks [8p, 8p + 8); word 2s + u holds
+// sub-step u of stage s of the pair, its low half belongs to lane half 0.
+__device__ __forceinline__ u32x4 f4_scales(const uint16_t* srow, int pair) {
+  return *reinterpret_cast<const u32x4*>(srow + 8 * pair);
+}
+
+// One stage: two 64-k sub-steps; lane half h covers k in [32h, 32h + 32) of a sub-step
+// (one scale block) and MFMA j its slice [32h + 8j, + 8), in A and B alike.
+__device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const uint8_t (*sB)[F4_BP], int rb0, int rb1,
+                                           uint32_t s0u0, uint32_t s0u1, uint32_t s1u0, uint32_t s1u1, int lane,
+                                           f32x16 (&acc)[2][2]) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    BOps<MOE_WFMT_FP4> o0, o1;
+    const BRun<MOE_WFMT_FP4> c0{*reinterpret_cast<const u32x4*>(&sB[rb0 + r][u * 32 + 16 * h])};
+    const BRun<MOE_WFMT_FP4> c1{*reinterpret_cast<const u32x4*>(&sB[rb1 + r][u * 32 + 16 * h])};
+    b_operands<MOE_WFMT_FP4>(o0, c0, u ? s0u1 : s0u0);
+    b_operands<MOE_WFMT_FP4>(o1, c1, u ? s1u1 : s1u0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = u * 64 + 32 * h + 8 * j;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sA[r][k]);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sA[32 + r][k]);
+      acc[0][0] = mfma32<true>(a0, o0.op[j], acc[0][0]);
+      acc[0][1] = mfma32<true>(a0, o1.op[j], acc[0][1]);
+      acc[1][0] = mfma32<true>(a1, o0.op[j], acc[1][0]);
+      acc[1][1] = mfma32<true>(a1, o1.op[j], acc[1][1]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t half_of(uint32_t w, int h) { return w >> (16 * h); }
+
+// The k loop over nk = K / 128 stages (even).  rb0 / rb1: the wavefront's two 32-row
+// weight fragments in the block's LDS rows; sc0 / sc1: their scale rows.
+__device__ __forceinline__ void f4_kloop(int nk, const F4Src& src, const uint16_t* sc0, const uint16_t* sc1,
+                                         uint16_t (*sA)[64][F4_AW], uint8_t (*sB)[F4_ROWS][F4_BP], int rb0, int rb1,
+                                         int tid, f32x16 (&acc)[2][2]) {
+  const int lane = tid & 63, h = lane >> 5;
+  F4Stage X, Y;
+  f4_issue(X, src, 0);
+  u32x4 q0 = f4_scales(sc0, 0), q1 = f4_scales(sc1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  f4_issue(Y, src, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  f4_store(X, sA[0], sB[0], tid);
+  // this pair's scales, taken out before the registers are refilled
+  uint32_t a00 = half_of(q0[0], h), a01 = half_of(q0[1], h), a10 = half_of(q1[0], h), a11 = half_of(q1[1], h);
+  uint32_t b00 = half_of(q0[2], h), b01 = half_of(q0[3], h), b10 = half_of(q1[2], h), b11 = half_of(q1[3], h);
+  __syncthreads();
+  f4_issue(X, src, min(2, nk - 1));
+  q0 = f4_scales(sc0, min(1, nk / 2 - 1));
+  q1 = f4_scales(sc1, min(1, nk / 2 - 1));
+  for (int s = 0; s < nk; s += 2) {
+    // even stage s: buffer 0, scales a..
+    f4_compute(sA[0], sB[0], rb0, rb1, a00, a01, a10, a11, lane, acc);
+    f4_store(Y, sA[1], sB[1], tid);
+    __syncthreads();
+    f4_issue(Y, src, min(s + 3, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // odd stage s + 1: buffer 1, scales b..
+    f4_compute(sA[1], sB[1], rb0, rb1, b00, b01, b10, b11, lane, acc);
+    f4_store(X, sA[0], sB[0], tid);
+    a00 = half_of(q0[0], h); a01 = half_of(q0[1], h); a10 = half_of(q1[0], h); a11 = half_of(q1[1], h);
+    b00 = half_of(q0[2], h); b01 = half_of(q0[3], h); b10 = half_of(q1[2], h); b11 = half_of(q1[3], h);
+    __syncthreads();
+    f4_issue(X, src, min(s + 4, nk - 1));
+    q0 = f4_scales(sc0, min(s / 2 + 2, nk / 2 - 1));
+    q1 = f4_scales(sc1, min(s / 2 + 2, nk / 2 - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// GEMM1 (FP4): act columns n0 .. n0 + 127; block rows 0..127 gate rows n0.., 128..255 up.
+__global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][64][F4_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][F4_ROWS][F4_BP];
+  TileInfo ti;
+  if (!decode_tile(a, a.I / 128, ti)) return;
+  const int H = a.H, I = a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = ti.nt * 128;
+  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const int64_t n = (int64_t)H * I;
+  const uint8_t* gate = rec;
+  const uint8_t* up = rec + n / 2;
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2));
+
+  F4Src src;
+  const uint16_t* xa = reinterpret_cast<const uint16_t*>(a.xa);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    const int tok = a.perm[ti.row0 + (row < ti.rows ? row : 0)] / a.k;
+    src.a[i] = xa + (int64_t)tok * H + (tid & 15) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = (tid >> 2) + 64 * j;
+    const uint8_t* t = R < 128 ? gate + (int64_t)(n0 + R) * (H / 2) : up + (int64_t)(n0 + R - 128) * (H / 2);
+    src.b[j] = t + (tid & 3) * 16;
+  }
+  const int col = n0 + wave * 32 + (lane & 31);
+  const uint16_t* sc_g = scales + (int64_t)col * (H / 32);
+  const uint16_t* sc_u = scales + n / 32 + (int64_t)col * (H / 32);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
+  f4_kloop(H / F4_KS, src, sc_g, sc_u, sA, sB, wave * 32, 128 + wave * 32, tid, acc);
+
+  uint16_t* act = reinterpret_cast<uint16_t*>(a.act);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      if (r < ti.rows) {
+        const float g = acc[m][0][i];
+        const float v = g * __frcp_rn(1.0f + __expf(-g)) * acc[m][1][i];
+        act[(int64_t)(ti.row0 + r) * I + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+      }
+    }
+  }
+}
+
+// GEMM2 (FP4): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64 of them.
+__global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][64][F4_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][F4_ROWS][F4_BP];
+  TileInfo ti;
+  if (!decode_tile(a, a.H / 256, ti)) return;
+  const int H = a.H, I = a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = ti.nt * 256;
+  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const int64_t n = (int64_t)H * I;
+  const uint8_t* down = rec + n;  // after gate and up codes (n / 2 bytes each)
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2)) + 2 * (n / 32);
+
+  F4Src src;
+  const uint16_t* act = reinterpret_cast<const uint16_t*>(a.act);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    src.a[i] = act + (int64_t)(ti.row0 + (row < ti.rows ? row : 0)) * I + (tid & 15) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) src.b[j] = down + (int64_t)(n0 + (tid >> 2) + 64 * j) * (I / 2) + (tid & 3) * 16;
+  const int c0 = n0 + wave * 64 + (lane & 31);
+  const uint16_t* sc0 = scales + (int64_t)c0 * (I / 32);
+  const uint16_t* sc1 = scales + (int64_t)(c0 + 32) * (I / 32);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
+  f4_kloop(I / F4_KS, src, sc0, sc1, sA, sB, wave * 64, wave * 64 + 32, tid, acc);
+
+  int pr[2][16];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      pr[m][i] = a.perm[ti.row0 + (r < ti.rows ? r : 0)];
+    }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      if (r < ti.rows) {
+        float* dst = a.ypair + (int64_t)pr[m][i] * H;
+        dst[c0] = acc[m][0][i];
+        dst[c0 + 32] = acc[m][1][i];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Activations -> 16-bit MFMA operands, once per call (FP4 weights take f16, bf16
 // weights bf16).  Same rounding as an in-GEMM conversion (round to nearest even).
 template <int AFMT, bool TO_F16>
@@ -682,6 +913,9 @@ __global__ void gemm2_f32_kernel(PrefillArgs a) {
   a.ypair[(int64_t)a.perm[row] * a.H + col] = s;
 }
 
+// The LDS-staged FP4 kernels take two 128-k stages per 16-byte scale load.
+static bool fp4_staged(const PrefillArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0; }
+
 static int padded_grid(int tiles_m, int nt) {
   int n = tiles_m * nt;
   return ((n + 7) / 8) * 8;
@@ -697,6 +931,7 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
   }
   const dim3 grid(padded_grid(max_tiles_m, a.I / 128));
   if (wfmt == MOE_WFMT_BF16) launch_timed(gemm1_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  else if (fp4_staged(a)) launch_timed(gemm1_fp4_kernel, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm1_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
 }
 
@@ -708,6 +943,7 @@ void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipSt
   }
   const dim3 grid(padded_grid(max_tiles_m, a.H / 256));
   if (wfmt == MOE_WFMT_BF16) launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  else if (fp4_staged(a)) launch_timed(gemm2_fp4_kernel, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm2_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
 }
 
