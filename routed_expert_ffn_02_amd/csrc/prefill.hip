@@ -602,63 +602,83 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
 //
 // Fetching MFMA operands lane by lane makes each 1 KB weight load touch 32 rows, i.e.
 // 32 cache lines, and the address / L1 path (not the ALUs) then bounds the kernel.
-// Here each stage's codes are fetched four lanes per row (16 lines per 1 KB load),
-// written to LDS raw (4 bits a weight, a quarter of the bytes of f16), and read back
-// by each lane in MFMA layout, where it dequantises them.  A stage covers 128 k: the
-// activation tile (64 x 128, 16 KB) and the block's 256 weight rows x 64 B of codes
-// (16 KB).  Block scales travel in registers, 16 bytes per lane for two stages.
-// Register stages X (even stages) and Y (odd) are refilled two stages ahead; the
-// stage just computed frees its LDS buffer, which the next store reuses behind the
-// barrier that closed the previous stage (one barrier per stage).  Refills past the
-// end re-read the last stage (in bounds, unused).  Needs K % 256 == 0.
-constexpr int F4_KS = 128;                 // k per stage
+// Here the codes are fetched eight lanes per row, so every load covers whole 128-byte
+// lines (a line fetched in two halves at different times reaches HBM twice), written
+// to LDS raw (4 bits a weight, a quarter of the bytes of f16), and read back by each
+// lane in MFMA layout, where it dequantises them.  A chunk covers 256 k: the
+// activation tile (64 x 256, 32 KB) and the block's 256 weight rows x 128 B of codes
+// (32 KB), single-buffered in LDS (69 KB, two blocks per CU).  The next chunk waits in
+// registers while the current one is multiplied; block scales travel in registers,
+// 16 bytes per lane per chunk.  Refills past the end re-read the last chunk (in
+// bounds, unused).  Needs K % 256 == 0.
+constexpr int F4_KS = 256;                 // k per chunk
 constexpr int F4_AW = F4_KS + 8;           // padded activation row (elements)
 constexpr int F4_BP = F4_KS / 2 + 16;      // padded code row (bytes): conflict-free 16-byte reads
 constexpr int F4_ROWS = 256;               // weight rows per block
 
-struct F4Stage {
-  u32x4 a[4];  // activation chunk i: tile row (tid >> 4) + 16 i, 8-element chunk tid & 15
-  u32x4 b[4];  // code chunk j: block row (tid >> 2) + 64 j, 16-byte chunk tid & 3
+struct F4Chunk {
+  u32x4 a[8];  // activation piece i: tile row (tid >> 5) + 8 i, 8 elements at (tid & 31) * 8
+  u32x4 b[8];  // code piece j: block row (tid >> 3) + 32 j, 16 bytes at (tid & 7) * 16
 };
 
+// Per-thread parts are 32-bit byte offsets from wave-uniform bases, so the loads take
+// a scalar base and one VGPR offset each.
 struct F4Src {
-  const uint16_t* a[4];  // activation row starts (+ chunk offset)
-  const uint8_t* b[4];   // code row starts (+ chunk offset)
+  const uint8_t* a;    // activation base (uniform)
+  uint32_t aoff[8];    // byte offset of activation piece i at k = 0
+  const uint8_t* b;    // expert record (uniform)
+  uint32_t boff[2];    // byte offset of code piece 0 (rows < 128) and piece 4 (rows >= 128) at k = 0
+  int64_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
 };
 
-__device__ __forceinline__ void f4_issue(F4Stage& st, const F4Src& src, int stage) {
+__device__ __forceinline__ void f4_issue(F4Chunk& st, const F4Src& src, int c) {
+  const uint8_t* ab = src.a + c * (2 * F4_KS);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(src.a[i] + stage * F4_KS);
+  for (int i = 0; i < 8; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(ab + src.aoff[i]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) st.b[j] = *reinterpret_cast<const u32x4*>(src.b[j] + stage * (F4_KS / 2));
+  for (int j = 0; j < 8; ++j) {
+    const uint8_t* bb = src.b + (j & 3) * src.bstep + c * (F4_KS / 2);
+    st.b[j] = *reinterpret_cast<const u32x4*>(bb + src.boff[j >> 2]);
+  }
 }
 
-__device__ __forceinline__ void f4_store(const F4Stage& st, uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int tid) {
+__device__ __forceinline__ void f4_store(const F4Chunk& st, uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sA[(tid >> 4) + 16 * i][(tid & 15) * 8]) = st.a[i];
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sA[(tid >> 5) + 8 * i][(tid & 31) * 8]) = st.a[i];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 2) + 64 * j][(tid & 3) * 16]) = st.b[j];
+  for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 3) + 32 * j][(tid & 7) * 16]) = st.b[j];
 }
 
-// Scales of one run row for stages 2p, 2p + 1: blocks [8p, 8p + 8); word 2s + u holds
-// sub-step u of stage s of the pair, its low half belongs to lane half 0.
-__device__ __forceinline__ u32x4 f4_scales(const uint16_t* srow, int pair) {
-  return *reinterpret_cast<const u32x4*>(srow + 8 * pair);
+// Scales of one weight row for chunk c: blocks [8c, 8c + 8); word w covers k in
+// [64w, 64w + 64) of the chunk, its low half the lanes of half 0, its high half half 1.
+__device__ __forceinline__ u32x4 f4_scales(const uint8_t* rec, uint32_t soff, int c) {
+  return *reinterpret_cast<const u32x4*>(rec + 16 * c + soff);
 }
 
-// One stage: two 64-k sub-steps; lane half h covers k in [32h, 32h + 32) of a sub-step
-// (one scale block) and MFMA j its slice [32h + 8j, + 8), in A and B alike.
+struct F4Scales {
+  uint32_t w0[4], w1[4];  // this lane's scale words for fragments rb0 and rb1
+};
+
+__device__ __forceinline__ void f4_take(F4Scales& s, const u32x4& q0, const u32x4& q1, int h) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    s.w0[w] = q0[w] >> (16 * h);
+    s.w1[w] = q1[w] >> (16 * h);
+  }
+}
+
+// One chunk: four 64-k sub-steps; lane half h covers k in [32h, 32h + 32) of a
+// sub-step (one scale block) and MFMA j its slice [32h + 8j, + 8), in A and B alike.
 __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const uint8_t (*sB)[F4_BP], int rb0, int rb1,
-                                           uint32_t s0u0, uint32_t s0u1, uint32_t s1u0, uint32_t s1u1, int lane,
-                                           f32x16 (&acc)[2][2]) {
+                                           const F4Scales& sc, int lane, f32x16 (&acc)[2][2]) {
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < 4; ++u) {
     BOps<MOE_WFMT_FP4> o0, o1;
     const BRun<MOE_WFMT_FP4> c0{*reinterpret_cast<const u32x4*>(&sB[rb0 + r][u * 32 + 16 * h])};
     const BRun<MOE_WFMT_FP4> c1{*reinterpret_cast<const u32x4*>(&sB[rb1 + r][u * 32 + 16 * h])};
-    b_operands<MOE_WFMT_FP4>(o0, c0, u ? s0u1 : s0u0);
-    b_operands<MOE_WFMT_FP4>(o1, c1, u ? s1u1 : s1u0);
+    b_operands<MOE_WFMT_FP4>(o0, c0, sc.w0[u]);
+    b_operands<MOE_WFMT_FP4>(o1, c1, sc.w1[u]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = u * 64 + 32 * h + 8 * j;
@@ -672,52 +692,41 @@ __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const ui
   }
 }
 
-__device__ __forceinline__ uint32_t half_of(uint32_t w, int h) { return w >> (16 * h); }
-
-// The k loop over nk = K / 128 stages (even).  rb0 / rb1: the wavefront's two 32-row
-// weight fragments in the block's LDS rows; sc0 / sc1: their scale rows.
-__device__ __forceinline__ void f4_kloop(int nk, const F4Src& src, const uint16_t* sc0, const uint16_t* sc1,
-                                         uint16_t (*sA)[64][F4_AW], uint8_t (*sB)[F4_ROWS][F4_BP], int rb0, int rb1,
-                                         int tid, f32x16 (&acc)[2][2]) {
+// The k loop over nc = K / 256 chunks.  rb0 / rb1: the wavefront's two 32-row weight
+// fragments in the block's LDS rows; sc0 / sc1: byte offsets of their scale rows.
+__device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0, uint32_t sc1,
+                                         uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int rb0, int rb1, int tid,
+                                         f32x16 (&acc)[2][2]) {
   const int lane = tid & 63, h = lane >> 5;
-  F4Stage X, Y;
-  f4_issue(X, src, 0);
-  u32x4 q0 = f4_scales(sc0, 0), q1 = f4_scales(sc1, 0);
+  F4Chunk N;
+  F4Scales sc;
+  f4_issue(N, src, 0);
+  u32x4 q0 = f4_scales(src.b, sc0, 0), q1 = f4_scales(src.b, sc1, 0);
   __builtin_amdgcn_sched_barrier(0);
-  f4_issue(Y, src, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  f4_store(X, sA[0], sB[0], tid);
-  // this pair's scales, taken out before the registers are refilled
-  uint32_t a00 = half_of(q0[0], h), a01 = half_of(q0[1], h), a10 = half_of(q1[0], h), a11 = half_of(q1[1], h);
-  uint32_t b00 = half_of(q0[2], h), b01 = half_of(q0[3], h), b10 = half_of(q1[2], h), b11 = half_of(q1[3], h);
+  f4_store(N, sA, sB, tid);
+  f4_take(sc, q0, q1, h);
   __syncthreads();
-  f4_issue(X, src, min(2, nk - 1));
-  q0 = f4_scales(sc0, min(1, nk / 2 - 1));
-  q1 = f4_scales(sc1, min(1, nk / 2 - 1));
-  for (int s = 0; s < nk; s += 2) {
-    // even stage s: buffer 0, scales a..
-    f4_compute(sA[0], sB[0], rb0, rb1, a00, a01, a10, a11, lane, acc);
-    f4_store(Y, sA[1], sB[1], tid);
+  f4_issue(N, src, min(1, nc - 1));
+  q0 = f4_scales(src.b, sc0, min(1, nc - 1));
+  q1 = f4_scales(src.b, sc1, min(1, nc - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c = 0; c < nc; ++c) {
+    f4_compute(sA, sB, rb0, rb1, sc, lane, acc);
+    __syncthreads();  // every wavefront is done with chunk c
+    f4_store(N, sA, sB, tid);
+    f4_take(sc, q0, q1, h);
     __syncthreads();
-    f4_issue(Y, src, min(s + 3, nk - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    // odd stage s + 1: buffer 1, scales b..
-    f4_compute(sA[1], sB[1], rb0, rb1, b00, b01, b10, b11, lane, acc);
-    f4_store(X, sA[0], sB[0], tid);
-    a00 = half_of(q0[0], h); a01 = half_of(q0[1], h); a10 = half_of(q1[0], h); a11 = half_of(q1[1], h);
-    b00 = half_of(q0[2], h); b01 = half_of(q0[3], h); b10 = half_of(q1[2], h); b11 = half_of(q1[3], h);
-    __syncthreads();
-    f4_issue(X, src, min(s + 4, nk - 1));
-    q0 = f4_scales(sc0, min(s / 2 + 2, nk / 2 - 1));
-    q1 = f4_scales(sc1, min(s / 2 + 2, nk / 2 - 1));
+    f4_issue(N, src, min(c + 2, nc - 1));
+    q0 = f4_scales(src.b, sc0, min(c + 2, nc - 1));
+    q1 = f4_scales(src.b, sc1, min(c + 2, nc - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // GEMM1 (FP4): act columns n0 .. n0 + 127; block rows 0..127 gate rows n0.., 128..255 up.
 __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][64][F4_AW];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][F4_ROWS][F4_BP];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
   if (!decode_tile(a, a.I / 128, ti)) return;
   const int H = a.H, I = a.I;
@@ -725,27 +734,24 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   const int n0 = ti.nt * 128;
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int64_t n = (int64_t)H * I;
-  const uint8_t* gate = rec;
-  const uint8_t* up = rec + n / 2;
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2));
+  // record: gate codes, up codes, down codes (n / 2 bytes each), then bf16 scales
 
   F4Src src;
-  const uint16_t* xa = reinterpret_cast<const uint16_t*>(a.xa);
+  src.a = reinterpret_cast<const uint8_t*>(a.xa);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    const int tok = a.perm[ti.row0 + (row < ti.rows ? row : 0)] / a.k;
-    src.a[i] = xa + (int64_t)tok * H + (tid & 15) * 8;
+  for (int i = 0; i < 8; ++i) {
+    const int row = (tid >> 5) + 8 * i;
+    const uint32_t tok = (uint32_t)(a.perm[ti.row0 + (row < ti.rows ? row : 0)] / a.k);
+    src.aoff[i] = 2u * (tok * (uint32_t)H + (uint32_t)(tid & 31) * 8u);
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int R = (tid >> 2) + 64 * j;
-    const uint8_t* t = R < 128 ? gate + (int64_t)(n0 + R) * (H / 2) : up + (int64_t)(n0 + R - 128) * (H / 2);
-    src.b[j] = t + (tid & 3) * 16;
-  }
+  // block rows 0..127: gate rows n0.., 128..255: up rows n0..
+  src.b = rec;
+  src.boff[0] = (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(H / 2) + (uint32_t)(tid & 7) * 16u;
+  src.boff[1] = src.boff[0] + (uint32_t)(n / 2);
+  src.bstep = (int64_t)32 * (H / 2);
   const int col = n0 + wave * 32 + (lane & 31);
-  const uint16_t* sc_g = scales + (int64_t)col * (H / 32);
-  const uint16_t* sc_u = scales + n / 32 + (int64_t)col * (H / 32);
+  const uint32_t sc_g = (uint32_t)(3 * (n / 2)) + 2u * (uint32_t)col * (uint32_t)(H / 32);
+  const uint32_t sc_u = sc_g + (uint32_t)(2 * (n / 32));
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -773,8 +779,8 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
 
 // GEMM2 (FP4): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64 of them.
 __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][64][F4_AW];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][F4_ROWS][F4_BP];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
   if (!decode_tile(a, a.H / 256, ti)) return;
   const int H = a.H, I = a.I;
@@ -782,21 +788,23 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
   const int n0 = ti.nt * 256;
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int64_t n = (int64_t)H * I;
-  const uint8_t* down = rec + n;  // after gate and up codes (n / 2 bytes each)
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2)) + 2 * (n / 32);
+  // record: gate codes, up codes, down codes (n / 2 bytes each), then bf16 scales
+  // (gate, up, down: n / 32 each)
 
   F4Src src;
-  const uint16_t* act = reinterpret_cast<const uint16_t*>(a.act);
+  src.a = reinterpret_cast<const uint8_t*>(a.act);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    src.a[i] = act + (int64_t)(ti.row0 + (row < ti.rows ? row : 0)) * I + (tid & 15) * 8;
+  for (int i = 0; i < 8; ++i) {
+    const int row = (tid >> 5) + 8 * i;
+    src.aoff[i] = 2u * ((uint32_t)(ti.row0 + (row < ti.rows ? row : 0)) * (uint32_t)I + (uint32_t)(tid & 31) * 8u);
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) src.b[j] = down + (int64_t)(n0 + (tid >> 2) + 64 * j) * (I / 2) + (tid & 3) * 16;
+  src.b = rec;
+  src.boff[0] = (uint32_t)n + (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(I / 2) + (uint32_t)(tid & 7) * 16u;
+  src.boff[1] = src.boff[0] + 128u * (uint32_t)(I / 2);
+  src.bstep = (int64_t)32 * (I / 2);
   const int c0 = n0 + wave * 64 + (lane & 31);
-  const uint16_t* sc0 = scales + (int64_t)c0 * (I / 32);
-  const uint16_t* sc1 = scales + (int64_t)(c0 + 32) * (I / 32);
+  const uint32_t sc0 = (uint32_t)(3 * (n / 2) + 2 * 2 * (n / 32)) + 2u * (uint32_t)c0 * (uint32_t)(I / 32);
+  const uint32_t sc1 = sc0 + 2u * 32u * (uint32_t)(I / 32);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -914,7 +922,12 @@ __global__ void gemm2_f32_kernel(PrefillArgs a) {
 }
 
 // The LDS-staged FP4 kernels take two 128-k stages per 16-byte scale load.
-static bool fp4_staged(const PrefillArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0; }
+// The LDS-staged FP4 kernels take 256-k chunks and hold byte offsets (activations,
+// record) in 32 bits.
+static bool fp4_staged(const PrefillArgs& a) {
+  return a.H % 256 == 0 && a.I % 256 == 0 && (int64_t)a.T * a.H < (1ll << 31) &&
+         (int64_t)a.T * a.k * a.I < (1ll << 31) && a.rec_bytes < (1ll << 32);
+}
 
 static int padded_grid(int tiles_m, int nt) {
   int n = tiles_m * nt;
