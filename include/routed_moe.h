@@ -78,6 +78,9 @@ typedef enum { MOE_MODE_FUSED = 0, MOE_MODE_OFFLOAD = 1, MOE_MODE_CPU = 2, MOE_M
 typedef enum { MOE_KIND_HIT = 0, MOE_KIND_FILL = 1, MOE_KIND_CPU = 2, MOE_KIND_BUF = 3 } moe_kind;
 
 #define MOE_FLAG_PROFILE 1 /* time the FFN kernels with HIP events (moe_get_stats) */
+/* OFFLOAD decode steps copy their fills with a kernel that reads the page-locked pool through
+ * its device mapping, so moe_ffn_decode never waits for the device (see moe_ffn_decode). */
+#define MOE_FLAG_DEVICE_FILLS 2
 
 typedef struct {
   int32_t n_layers, n_experts, top_k, hidden, inter; /* L, E, k, H, I */
@@ -222,6 +225,12 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
  * as given to / returned by the lookup; y: device fp32 [T,H].  Needs T * H <= 16384 (decode
  * batches); use moe_ffn_prefill for longer inputs.  Synchronises the stream when the step has
  * fills or CPU work (the fill list is read on the host), then enqueues the GPU work.
+ * With MOE_FLAG_DEVICE_FILLS, an OFFLOAD step that cannot send work to the CPU (n_slots >=
+ * 2*T*k) instead enqueues a copy kernel that executes the lookup's fill list from the mapped
+ * pool ([FT-KR] "CUDA Graph와 공존하는 LRU 캐시": cache control and transfer stay on the
+ * device): nothing is read on the host, the call only enqueues work, and an out-of-range id
+ * in topk_idx (the step then computes y = 0) is reported by the next moe_sync.  Needs a pool
+ * from moe_pool_alloc or a registered page-locked pool with a device mapping (MOE_ENOPIN).
  */
 MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);
@@ -288,6 +297,12 @@ MOE_API moe_status moe_bench_bw(moe_ctx* ctx, uint64_t* bw_pcie, uint64_t* bw_ho
  * slot_of [L*E], key_of [n_slots], stamp [n_slots]; *counter = the recency counter. */
 MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, uint64_t* stamp,
                                       uint64_t* counter, int32_t* n_slots);
+
+/*
+ * Wait for `stream` and report what device-fill steps could not report when they were
+ * enqueued: MOE_EINVAL if a step since the last moe_sync saw an expert id out of range.
+ */
+MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream);
 
 /* Accumulated statistics (synchronises the context's streams to read kernel timings). */
 MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);

@@ -22,6 +22,7 @@ MOE_AFMT_F32, MOE_AFMT_BF16 = 0, 1
 MOE_MODE_FUSED, MOE_MODE_OFFLOAD, MOE_MODE_CPU, MOE_MODE_HYBRID = 0, 1, 2, 3
 MOE_KIND_HIT, MOE_KIND_FILL, MOE_KIND_CPU, MOE_KIND_BUF = 0, 1, 2, 3
 MOE_FLAG_PROFILE = 1
+MOE_FLAG_DEVICE_FILLS = 2
 
 _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ESTATE",
            -5: "MOE_ENOPIN", -6: "MOE_ENOTSUP"}
@@ -92,6 +93,7 @@ def _load():
         "moe_cache_snapshot": (I32, [P, VP, VP, VP, ctypes.POINTER(U64), ctypes.POINTER(I32)]),
         "moe_get_stats": (I32, [P, ctypes.POINTER(moe_stats)]),
         "moe_reset_stats": (I32, [P]),
+        "moe_sync": (I32, [P, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -274,3 +276,7 @@ def moe_get_stats(ctx: Ctx) -> dict:
 
 def moe_reset_stats(ctx: Ctx) -> None:
     _check(ctx, lib.moe_reset_stats(ctx.handle), "moe_reset_stats")
+
+
+def moe_sync(ctx: Ctx, stream=None) -> None:
+    _check(ctx, lib.moe_sync(ctx.handle, _stream(stream)), "moe_sync")

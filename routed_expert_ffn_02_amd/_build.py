@@ -16,7 +16,7 @@ BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libroutedmoe.so")
 ARCH = os.environ.get("RMOE_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["route.hip", "lookup.hip", "decode.hip", "prefill.hip"]
+HIP_SOURCES = ["route.hip", "lookup.hip", "decode.hip", "prefill.hip", "fill.hip"]
 CPP_SOURCES = ["runtime.cpp", "cpu_ffn.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code (the host pass warns that it

@@ -1,0 +1,80 @@
+// Device-driven fills: the step's fill list, written by the cache-control kernel,
+// is executed by a copy kernel that reads the page-locked host pool through its
+// device mapping (over PCIe) and writes the victim slots of the arena.  The step
+// then needs no device -> host read and no host-issued copy, so the whole decode
+// step stays on one stream (FreeToken summary, "CUDA Graph와 공존하는 LRU 캐시":
+// the cache control and the fused transfer live inside the captured step).
+//
+// Measured on MI355X: a few dozen workgroups reading pinned host memory reach the
+// same 53-57 GB/s as the DMA engines for 6-14 MB records, so one launch of
+// (blocks per record) x (most fills a step can have) workgroups moves a step's
+// fills at link speed and leaves the other CUs idle for the GEMV that follows.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace rmoe {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kFillUnroll = 4;  // 16-byte loads in flight per thread before the stores
+
+__global__ __launch_bounds__(256) void fill_pull_kernel(FillArgs a) {
+  const int f = blockIdx.y;
+  const int err = a.cnt[C_ERR];
+  const int nfill = a.cnt[C_FILL];
+  if (a.dstats && f == 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+    // the step's counts, accumulated on the device (no host read)
+    if (err) {
+      a.dstats[D_ERR] += 1;
+    } else {
+      a.dstats[D_LOOKUP] += 1;
+      a.dstats[D_HIT] += (uint64_t)a.cnt[C_HIT];
+      a.dstats[D_FILL] += (uint64_t)nfill;
+      a.dstats[D_CPU] += (uint64_t)a.cnt[C_CPU];
+      a.dstats[D_EVICT] += (uint64_t)a.cnt[C_EVICT];
+    }
+  }
+  if (err || f >= nfill) return;
+  const int64_t key = a.fill_key[f];
+  const int64_t rec = a.pool_records > 0 ? key % a.pool_records : key;
+  const uint8_t* src = a.pool + rec * a.rec_bytes;
+  uint8_t* dst = a.arena + (int64_t)a.fill_slot[f] * a.rec_bytes;
+  // block x copies 16-byte units [lo, hi) of the record
+  const int64_t n16 = a.rec_bytes >> 4;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = min(n16, lo + per);
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  for (int64_t base = lo; base < hi; base += 256 * kFillUnroll) {
+    u32x4 v[kFillUnroll];
+#pragma unroll
+    for (int u = 0; u < kFillUnroll; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      if (i < hi) v[u] = s[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kFillUnroll; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      if (i < hi) d[i] = v[u];
+    }
+  }
+  // a record whose size is not a multiple of 16 bytes: the last block copies the tail
+  if (blockIdx.x == gridDim.x - 1)
+    for (int64_t b = (n16 << 4) + threadIdx.x; b < a.rec_bytes; b += 256) dst[b] = src[b];
+}
+
+}  // namespace
+
+int fill_blocks_per_record(int64_t rec_bytes) {
+  // about 256 KiB per workgroup
+  return (int)std::max<int64_t>(1, std::min<int64_t>(1024, (rec_bytes + (256 << 10) - 1) >> 18));
+}
+
+void launch_fill_pull(const FillArgs& a, int max_fills, hipStream_t s) {
+  dim3 grid(fill_blocks_per_record(a.rec_bytes), std::max(1, max_fills));
+  hipLaunchKernelGGL(fill_pull_kernel, grid, dim3(256), 0, s, a);
+}
+
+}  // namespace rmoe

@@ -31,6 +31,9 @@ enum {
   C_NPAIR_GPU = 8, C_ERR = 9, C_COUNT = 16
 };
 
+// device-side step statistics of device-fill steps (uint64 array)
+enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_COUNT = 8 };
+
 enum LookupMode { LK_FUSED = 0, LK_OFFLOAD = 1, LK_CPU = 2, LK_HYBRID = 3, LK_BUFFER = 4 };
 
 struct LookupArgs {
@@ -75,6 +78,17 @@ struct DecodeArgs {
   float* y;                  // [T,H]
 };
 
+struct FillArgs {
+  const int32_t* cnt;        // [C_COUNT]: C_FILL, C_ERR (and the step counts for dstats)
+  const int32_t* fill_key;   // [E]
+  const int32_t* fill_slot;  // [E]
+  const uint8_t* pool;       // device address of the page-locked host pool
+  int64_t pool_records;      // the pool holds records key % pool_records
+  uint8_t* arena;
+  int64_t rec_bytes;
+  uint64_t* dstats;          // [D_COUNT] accumulated step counts, or nullptr
+};
+
 struct PrefillArgs {
   const void* x;             // [T,H] afmt
   const void* xa;            // [T,H] 16-bit MFMA operands (x itself, or its converted copy)
@@ -113,6 +127,8 @@ void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_group
 void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 int decode_phase2_rowblocks(int H);
 void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s);
+int fill_blocks_per_record(int64_t rec_bytes);
+void launch_fill_pull(const FillArgs& a, int max_fills, hipStream_t s);
 void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
                     int32_t* inv, int32_t* offsets, int32_t* tile_base, int bm, hipStream_t s);
 void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp, int32_t* grp_slot, int32_t* cnt,
@@ -172,6 +188,7 @@ struct moe_ctx {
 
   // host pool
   uint8_t* pool = nullptr;
+  const uint8_t* pool_dev = nullptr;  // its device mapping (page-locked pools), for device fills
   int64_t pool_records = 0;
   bool pool_owned = false, pool_pinned = false;
 
@@ -210,6 +227,7 @@ struct moe_ctx {
   void* xo = nullptr;        // [max_tokens, H] 16-bit MFMA operands of the prefill activations
   float* ypair = nullptr;
   int32_t* flags = nullptr;
+  uint64_t* dstats = nullptr;    // [D_COUNT] counts of device-fill steps
 
   // pinned host staging; h_cnt .. h_u_kind mirror step_dev
   int32_t* step_host = nullptr;

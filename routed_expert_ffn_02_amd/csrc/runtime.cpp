@@ -352,7 +352,8 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->tile_base, std::max<int64_t>(E, Pmax) + 1) ||
       dev_alloc(&ctx->hist, (size_t)((Pmax + 255) / 256) * kMaxExperts) || dev_alloc(&ctx->cand, E) ||
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->act), (size_t)Pmax * I * 4) ||
-      dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)))
+      dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)) ||
+      dev_alloc(&ctx->dstats, D_COUNT))
     return cleanup_fail(MOE_ENOMEM);
   if (prefill_needs_act_operands(c.wfmt, c.afmt) &&
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->xo), (size_t)c.max_tokens * H * 2))
@@ -365,7 +366,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ctx->u_kind = ctx->u_key + E;
   if (hipMemset(ctx->slot_of, 0xff, (size_t)L * E * 4) || hipMemset(ctx->key_of, 0xff, kMaxCachedSlots * 4) ||
       hipMemset(ctx->stamp, 0, kMaxCachedSlots * 8) || hipMemset(ctx->reserved, 0, kMaxCachedSlots) ||
-      hipMemset(ctx->counter, 0, 8) ||
+      hipMemset(ctx->counter, 0, 8) || hipMemset(ctx->dstats, 0, D_COUNT * 8) ||
       hipMemset(ctx->step_dev, 0, (C_COUNT + 5 * E) * 4))
     return cleanup_fail(MOE_EHIP);
   // pinned host staging
@@ -412,7 +413,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
                  ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
-                 ctx->flags, ctx->xo};
+                 ctx->flags, ctx->xo, ctx->dstats};
   for (void* p : dev)
     if (p) hipFree(p);
   void* host[] = {ctx->step_host, ctx->h_slot_idx, ctx->h_w, ctx->h_x, ctx->h_xf, ctx->h_y, ctx->h_hbuf};
@@ -435,6 +436,12 @@ MOE_API moe_status moe_pool_alloc(moe_ctx* ctx, int64_t n_records, void** host_p
   CHECK_ARG(!ctx->pool, "a pool is already set");
   void* p = nullptr;
   HIPCHK(hipHostMalloc(&p, (size_t)n_records * ctx->S, 0));
+  void* pd = nullptr;
+  if (hipHostGetDevicePointer(&pd, p, 0) != hipSuccess) {
+    hipHostFree(p);
+    return fail(ctx, MOE_EHIP, "page-locked pool without a device mapping");
+  }
+  ctx->pool_dev = static_cast<const uint8_t*>(pd);
   ctx->pool = static_cast<uint8_t*>(p);
   ctx->pool_records = n_records;
   ctx->pool_owned = true;
@@ -454,6 +461,11 @@ MOE_API moe_status moe_pool_register(moe_ctx* ctx, void* host_pool, int64_t n_re
   ctx->pool_pinned = pinned != 0;
   if (!ctx->pool_pinned && ctx->cfg.mode != MOE_MODE_CPU)
     return fail(ctx, MOE_ENOPIN, "pageable pool: only MOE_MODE_CPU can run (every expert on the host)");
+  if (ctx->pool_pinned) {  // a device mapping enables device fills; without one they are refused
+    void* pd = nullptr;
+    if (hipHostGetDevicePointer(&pd, host_pool, 0) == hipSuccess) ctx->pool_dev = static_cast<const uint8_t*>(pd);
+    else (void)hipGetLastError();
+  }
   return MOE_OK;
 }
 
@@ -571,11 +583,14 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   const bool profile = (ctx->cfg.flags & MOE_FLAG_PROFILE) != 0;
   float* y_cpu = nullptr;
   const bool inputs = !fused && may_use_cpu(ctx, P);
-  if (!fused || profile) {
+  // device fills: no host read of the step unless profiling asks for its counts
+  const bool devfill = (ctx->cfg.flags & MOE_FLAG_DEVICE_FILLS) && ctx->cfg.mode == MOE_MODE_OFFLOAD && !inputs;
+  if (devfill && !ctx->pool_dev) return fail(ctx, MOE_ENOPIN, "device fills need a mapped page-locked pool");
+  if ((!fused && !devfill) || profile) {
     moe_status st = read_step(ctx, s, inputs, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
   }
-  const bool has_cpu = !fused && ctx->h_cnt[C_CPU] > 0;
+  const bool has_cpu = !fused && !devfill && ctx->h_cnt[C_CPU] > 0;
   if (has_cpu && !inputs) {  // unexpected CPU work (e.g. every slot protected): fetch its inputs
     moe_status st = read_step(ctx, s, true, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
@@ -597,7 +612,19 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   d.d = ctx->dpair;
   d.y = y;
   const int max_groups = std::min(P, E);
-  if (!fused) {
+  if (devfill) {
+    FillArgs f;
+    f.cnt = ctx->cnt;
+    f.fill_key = ctx->fill_key;
+    f.fill_slot = ctx->fill_slot;
+    f.pool = ctx->pool_dev;
+    f.pool_records = ctx->pool_records;
+    f.arena = ctx->arena;
+    f.rec_bytes = ctx->S;
+    f.dstats = profile ? nullptr : ctx->dstats;  // profiled steps were counted by read_step
+    launch_fill_pull(f, max_groups, s);
+    if (profile) ctx->stats.fill_bytes += (uint64_t)ctx->h_cnt[C_FILL] * ctx->S;
+  } else if (!fused) {
     moe_status st = issue_fills(ctx, s);
     if (st != MOE_OK) return st;
   }
@@ -1071,10 +1098,33 @@ MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* k
   return MOE_OK;
 }
 
+MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  HIPCHK(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  uint64_t err = 0;
+  HIPCHK(hipMemcpy(&err, ctx->dstats + D_ERR, 8, hipMemcpyDeviceToHost));
+  if (err) {
+    const uint64_t zero = 0;
+    HIPCHK(hipMemcpy(ctx->dstats + D_ERR, &zero, 8, hipMemcpyHostToDevice));
+    return fail(ctx, MOE_EINVAL, "expert id out of range in topk_idx (device-fill step)");
+  }
+  return MOE_OK;
+}
+
 MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
   if (!ctx || !out) return MOE_EINVAL;
   drain_timed(ctx);
   *out = ctx->stats;
+  // counts of device-fill steps live on the device
+  HIPCHK(hipDeviceSynchronize());
+  uint64_t d[D_COUNT];
+  HIPCHK(hipMemcpy(d, ctx->dstats, sizeof d, hipMemcpyDeviceToHost));
+  out->lookups += d[D_LOOKUP];
+  out->hits += d[D_HIT];
+  out->fills += d[D_FILL];
+  out->cpu_experts += d[D_CPU];
+  out->evictions += d[D_EVICT];
+  out->fill_bytes += d[D_FILL] * (uint64_t)ctx->S;
   return MOE_OK;
 }
 
@@ -1082,6 +1132,13 @@ MOE_API moe_status moe_reset_stats(moe_ctx* ctx) {
   if (!ctx) return MOE_EINVAL;
   drain_timed(ctx);
   ctx->stats = moe_stats{};
+  HIPCHK(hipDeviceSynchronize());
+  uint64_t d[D_COUNT];
+  HIPCHK(hipMemcpy(d, ctx->dstats, sizeof d, hipMemcpyDeviceToHost));
+  const uint64_t err = d[D_ERR];  // a pending error stays pending for moe_sync
+  for (auto& v : d) v = 0;
+  d[D_ERR] = err;
+  HIPCHK(hipMemcpy(ctx->dstats, d, sizeof d, hipMemcpyHostToDevice));
   return MOE_OK;
 }
 

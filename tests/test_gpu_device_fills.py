@@ -1,0 +1,109 @@
+"""GPU parity: OFFLOAD decode with device-driven fills (the copy kernel executes the
+lookup's fill list from the mapped pinned pool; no host read of the step).  Outputs,
+slot ids and traces must equal the host-issued path and the oracle exactly as there."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from moe_harness import Harness, row_rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+BF16 = W.A3B_DECODE.with_(name="dfill_bf16", n_layers=2, n_experts=16, top_k=4, hidden=256, inter=128)
+FP4 = W.DSV4.with_(name="dfill_fp4", n_layers=2, n_experts=16, top_k=3, hidden=256, inter=128)
+# an aliased pool: several keys share one backing record
+ALIAS = W.DSV4.with_(name="dfill_alias", n_layers=3, n_experts=8, top_k=2, hidden=256, inter=128, alias_records=5)
+TINY = W.TINY
+FMT = {"fp32": TINY, "bf16": BF16, "fp4": FP4, "fp4_alias": ALIAS}
+
+
+def _gates(wl, step, layer, T):
+    u = wl.uniforms(2000 + step * 64 + layer, T * wl.top_k).reshape(T, wl.top_k) + 0.05
+    return (u / u.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def _expected(wl, layer, x, idx, w):
+    x64 = oracle.formats.activations_f64(x)
+    outs = oracle.moe_layer_dense(x64, idx, lambda e: oracle.expert_weights_f64(wl, layer * wl.n_experts + e))
+    return oracle.moe_combine(outs, w)
+
+
+@pytest.mark.parametrize("fmt", list(FMT))
+@pytest.mark.parametrize("T", [1, 2])
+def test_device_fills_match_oracle(fmt, T):
+    import routed_expert_ffn_02_amd as R
+    wl = FMT[fmt]
+    n_slots = 2 * T * wl.top_k  # smallest cache that keeps every miss on the GPU
+    h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots, flags=R.MOE_FLAG_DEVICE_FILLS)
+    ref = oracle.ExpertCache(wl.n_layers, wl.n_experts, n_slots)
+    routes = {l: wl.synthetic_routing(12, l, T) for l in range(wl.n_layers)}
+    fills = hits = 0
+    for step in range(12):
+        for layer in range(wl.n_layers):
+            idx = routes[layer][step]
+            x = wl.decode_activations(step, layer, T)
+            w = _gates(wl, step, layer, T)
+            y, slot, trace, cnt = h.decode(layer, x, idx, w)
+            r = ref.lookup(layer, idx, R.MOE_MODE_OFFLOAD)
+            assert trace == r.trace and np.array_equal(slot, r.slot_idx), (step, layer)
+            assert row_rel_err(y, _expected(wl, layer, x, idx, w)) <= tol_for(wl), (step, layer)
+            fills += sum(1 for t in r.trace if t[1] == R.MOE_KIND_FILL)
+            hits += sum(1 for t in r.trace if t[1] == R.MOE_KIND_HIT)
+    R.moe_sync(h.ctx)
+    st = R.moe_get_stats(h.ctx)
+    assert fills > 0
+    assert st["fills"] == fills and st["hits"] == hits and st["lookups"] == 12 * wl.n_layers
+    assert st["fill_bytes"] == fills * h.S and st["cpu_experts"] == 0
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp4"])
+def test_device_fills_bit_identical_to_host_fills(fmt):
+    """Same steps through both fill paths: identical bytes in every output."""
+    import routed_expert_ffn_02_amd as R
+    wl = FMT[fmt]
+    n_slots = 2 * wl.top_k + 2
+    dev = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots, flags=R.MOE_FLAG_DEVICE_FILLS)
+    host = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots)
+    routes = {l: wl.synthetic_routing(10, l, 1) for l in range(wl.n_layers)}
+    for step in range(10):
+        for layer in range(wl.n_layers):
+            idx = routes[layer][step]
+            x = wl.decode_activations(step, layer, 1)
+            w = _gates(wl, step, layer, 1)
+            ya, sa, ta, _ = dev.decode(layer, x, idx, w)
+            yb, sb, tb, _ = host.decode(layer, x, idx, w)
+            assert ta == tb and np.array_equal(sa, sb)
+            assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), (step, layer)
+    # the occupied slots of both arenas hold the same records
+    _, key_dev, _, _ = dev.snapshot()
+    _, key_host, _, _ = host.snapshot()
+    assert np.array_equal(key_dev, key_host)
+    S = dev.S
+    for s_, key in enumerate(key_dev[:n_slots]):
+        if key >= 0:
+            assert bool((dev.arena[s_ * S:(s_ + 1) * S] == host.arena[s_ * S:(s_ + 1) * S]).all()), s_
+
+
+def test_device_fill_range_error_is_deferred_to_sync():
+    import routed_expert_ffn_02_amd as R
+    import torch
+    wl = BF16
+    h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=2 * wl.top_k, flags=R.MOE_FLAG_DEVICE_FILLS)
+    bad = torch.full((1, wl.top_k), wl.n_experts + 3, dtype=torch.int32, device="cuda")
+    w = torch.full((1, wl.top_k), 0.25, dtype=torch.float32, device="cuda")
+    x = torch.ones((1, wl.hidden), dtype=torch.int16, device="cuda")
+    slot = torch.empty_like(bad)
+    y = torch.full((1, wl.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    R.expert_cache_lookup(h.ctx, 0, bad, 1, slot, None, None)
+    R.moe_ffn_decode(h.ctx, 0, x, 1, bad, w, slot, y)  # enqueued; nothing read on the host
+    with pytest.raises(R.MoeError) as e:
+        R.moe_sync(h.ctx)
+    assert e.value.status == R.MOE_EINVAL
+    assert float(y.abs().max()) == 0.0  # the step computed nothing
+    R.moe_sync(h.ctx)  # reported once
+    # the cache is unchanged and the next valid step runs normally
+    idx = np.array([[0, 1, 2, 3]])
+    yy, _, trace, _ = h.decode(0, wl.decode_activations(0, 0, 1), idx, _gates(wl, 0, 0, 1))
+    assert [t[1] for t in trace] == [R.MOE_KIND_FILL] * 4
+    assert np.isfinite(yy).all()
