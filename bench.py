@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="a3b", choices=["a3b", "dsv4"])
     ap.add_argument("--mode", default="offload", choices=["offload", "hybrid", "fused"])
+    ap.add_argument("--host-fills", action="store_true",
+                    help="issue decode fills from the host (read the step's fill list, DMA copies) "
+                         "instead of the device copy kernel")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-hybrid", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,8 +137,8 @@ def main():
     t0 = time.time()
     prompt = W.A3B_PREFILL.prefill_tokens if args.config == "a3b" else wl.prefill_tokens
     max_tokens = 8 if args.no_prefill else max(8, prompt)
-    cfg = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, max_tokens, mode, wl.renorm,
-                        flags=R.MOE_FLAG_PROFILE)
+    flags = R.MOE_FLAG_PROFILE | (0 if args.host_fills else R.MOE_FLAG_DEVICE_FILLS)
+    cfg = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, max_tokens, mode, wl.renorm, flags=flags)
     ctx = R.moe_create(cfg)
     S = R.moe_record_bytes(cfg)
     pool = R.moe_pool_alloc(ctx, wl.pool_records)
@@ -204,6 +207,7 @@ def main():
     log(f"decode: {tok_s:.1f} tok/s, miss rate {miss_rate:.3f}, phase1 {p1_avg_ms * 1e3:.1f} us "
         f"{p1_gbs:.0f} GB/s, phase2 {p2_avg_ms * 1e3:.1f} us {p2_gbs:.0f} GB/s")
     decode_detail = {
+        "fill_path": "host DMA" if args.host_fills else "device copy kernel",
         "miss_rate": round(miss_rate, 4), "fills": st["fills"], "cpu_experts": st["cpu_experts"],
         "fill_GBps_wall": round(st["fill_bytes"] / elapsed / 1e9, 2),
         "copy_engine_ms": round(st["copy_ms"], 2),

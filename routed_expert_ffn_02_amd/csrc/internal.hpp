@@ -32,7 +32,7 @@ enum {
 };
 
 // device-side step statistics of device-fill steps (uint64 array)
-enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_COUNT = 8 };
+enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_P1_BYTES = 6, D_P2_BYTES = 7, D_COUNT = 8 };
 
 enum LookupMode { LK_FUSED = 0, LK_OFFLOAD = 1, LK_CPU = 2, LK_HYBRID = 3, LK_BUFFER = 4 };
 
@@ -87,6 +87,9 @@ struct FillArgs {
   uint8_t* arena;
   int64_t rec_bytes;
   uint64_t* dstats;          // [D_COUNT] accumulated step counts, or nullptr
+  // algorithmic bytes of the step's GEMV phases (zero unless profiling):
+  // phase 1 = groups * p1_grp + p1_fixed + gpu pairs * pair_bytes, phase 2 likewise
+  uint64_t p1_grp, p1_fixed, p2_grp, p2_fixed, pair_bytes;
 };
 
 struct PrefillArgs {

@@ -583,10 +583,10 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   const bool profile = (ctx->cfg.flags & MOE_FLAG_PROFILE) != 0;
   float* y_cpu = nullptr;
   const bool inputs = !fused && may_use_cpu(ctx, P);
-  // device fills: no host read of the step unless profiling asks for its counts
+  // device fills: no host read of the step (its counts and profiled bytes stay on the device)
   const bool devfill = (ctx->cfg.flags & MOE_FLAG_DEVICE_FILLS) && ctx->cfg.mode == MOE_MODE_OFFLOAD && !inputs;
   if (devfill && !ctx->pool_dev) return fail(ctx, MOE_ENOPIN, "device fills need a mapped page-locked pool");
-  if ((!fused && !devfill) || profile) {
+  if ((!fused && !devfill) || (fused && profile)) {
     moe_status st = read_step(ctx, s, inputs, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
   }
@@ -621,9 +621,14 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     f.pool_records = ctx->pool_records;
     f.arena = ctx->arena;
     f.rec_bytes = ctx->S;
-    f.dstats = profile ? nullptr : ctx->dstats;  // profiled steps were counted by read_step
+    f.dstats = ctx->dstats;
+    const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
+    f.p1_grp = profile ? (uint64_t)2 * I * wrow_h : 0;
+    f.p1_fixed = profile ? (uint64_t)T * H * act_bytes(ctx->cfg) : 0;
+    f.p2_grp = profile ? (uint64_t)H * wrow_i : 0;
+    f.p2_fixed = profile ? (uint64_t)T * H * 4 : 0;
+    f.pair_bytes = profile ? (uint64_t)I * 4 : 0;
     launch_fill_pull(f, max_groups, s);
-    if (profile) ctx->stats.fill_bytes += (uint64_t)ctx->h_cnt[C_FILL] * ctx->S;
   } else if (!fused) {
     moe_status st = issue_fills(ctx, s);
     if (st != MOE_OK) return st;
@@ -643,7 +648,10 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   }
   launch_decode_combine(d, y_cpu, s);
   HIPCHK(hipGetLastError());
-  if (profile) {
+  if (profile && devfill) {  // bytes are added on the device
+    ctx->stats.phase1_launches += 1;
+    ctx->stats.phase2_launches += 1;
+  } else if (profile) {
     const int ngrp = ctx->h_cnt[C_NGRP];
     const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
     ctx->stats.phase1_launches += 1;
@@ -1125,6 +1133,8 @@ MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
   out->cpu_experts += d[D_CPU];
   out->evictions += d[D_EVICT];
   out->fill_bytes += d[D_FILL] * (uint64_t)ctx->S;
+  out->phase1_bytes += d[D_P1_BYTES];
+  out->phase2_bytes += d[D_P2_BYTES];
   return MOE_OK;
 }
 

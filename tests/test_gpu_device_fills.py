@@ -63,8 +63,8 @@ def test_device_fills_bit_identical_to_host_fills(fmt):
     import routed_expert_ffn_02_amd as R
     wl = FMT[fmt]
     n_slots = 2 * wl.top_k + 2
-    dev = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots, flags=R.MOE_FLAG_DEVICE_FILLS)
-    host = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots)
+    dev = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots, flags=R.MOE_FLAG_DEVICE_FILLS | R.MOE_FLAG_PROFILE)
+    host = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots, flags=R.MOE_FLAG_PROFILE)
     routes = {l: wl.synthetic_routing(10, l, 1) for l in range(wl.n_layers)}
     for step in range(10):
         for layer in range(wl.n_layers):
@@ -75,6 +75,11 @@ def test_device_fills_bit_identical_to_host_fills(fmt):
             yb, sb, tb, _ = host.decode(layer, x, idx, w)
             assert ta == tb and np.array_equal(sa, sb)
             assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), (step, layer)
+    # the device-side step counts and profiled byte counts equal the host-read ones
+    sd, sh = R.moe_get_stats(dev.ctx), R.moe_get_stats(host.ctx)
+    for key in ("lookups", "hits", "fills", "cpu_experts", "evictions", "fill_bytes", "phase1_launches",
+                "phase2_launches", "phase1_bytes", "phase2_bytes"):
+        assert sd[key] == sh[key], key
     # the occupied slots of both arenas hold the same records
     _, key_dev, _, _ = dev.snapshot()
     _, key_host, _, _ = host.snapshot()
