@@ -231,6 +231,10 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
  * device): nothing is read on the host, the call only enqueues work, and an out-of-range id
  * in topk_idx (the step then computes y = 0) is reported by the next moe_sync.  Needs a pool
  * from moe_pool_alloc or a registered page-locked pool with a device mapping (MOE_ENOPIN).
+ * Such steps, and FUSED steps, enqueue device work only: route + lookup + decode of every layer
+ * may be captured into one HIP graph on `stream` and replayed ([FT-KR] "CUDA Graph와 공존하는
+ * LRU 캐시"); MOE_FLAG_PROFILE timing is skipped for captured launches, and a step that would
+ * read the host while the stream is capturing returns MOE_ESTATE.
  */
 MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);

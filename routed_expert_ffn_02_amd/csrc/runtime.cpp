@@ -103,6 +103,13 @@ hipEvent_t take_event(moe_ctx* c) {
 
 enum TimedKind { TK_P1 = 0, TK_P2 = 1, TK_G1 = 2, TK_G2 = 3, TK_COPY = 4 };
 
+// Work enqueued while `s` is being captured into a graph runs later, at each replay:
+// nothing may be read on the host then, and per-launch profiling is skipped.
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
 // Events for one timed launch (none unless MOE_FLAG_PROFILE).  Kernels receive them
 // through hipExtLaunchKernelGGL, so the interval is the kernel's own execution; copies
 // are bracketed by records on their stream.
@@ -114,7 +121,7 @@ struct TimedScope {
   Timing tm;
   TimedScope(moe_ctx* c_, hipStream_t s_, int kind_, bool record_around = false)
       : c(c_), s(s_), kind(kind_), record(record_around) {
-    if (c->cfg.flags & MOE_FLAG_PROFILE) {
+    if ((c->cfg.flags & MOE_FLAG_PROFILE) && !capturing(s)) {
       tm.start = take_event(c);
       tm.stop = take_event(c);
       if (record && tm.start) hipEventRecord(tm.start, s);
@@ -580,12 +587,16 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   const int k = ctx->cfg.top_k, E = ctx->cfg.n_experts, H = ctx->cfg.hidden, I = ctx->cfg.inter;
   const int P = T * k;
   const bool fused = ctx->cfg.mode == MOE_MODE_FUSED;
-  const bool profile = (ctx->cfg.flags & MOE_FLAG_PROFILE) != 0;
+  const bool captured = capturing(s);
+  const bool profile = (ctx->cfg.flags & MOE_FLAG_PROFILE) != 0 && !captured;
   float* y_cpu = nullptr;
   const bool inputs = !fused && may_use_cpu(ctx, P);
   // device fills: no host read of the step (its counts and profiled bytes stay on the device)
   const bool devfill = (ctx->cfg.flags & MOE_FLAG_DEVICE_FILLS) && ctx->cfg.mode == MOE_MODE_OFFLOAD && !inputs;
   if (devfill && !ctx->pool_dev) return fail(ctx, MOE_ENOPIN, "device fills need a mapped page-locked pool");
+  if (captured && !fused && !devfill)
+    return fail(ctx, MOE_ESTATE, "a captured decode step reads nothing on the host: use FUSED mode or OFFLOAD "
+                                 "with MOE_FLAG_DEVICE_FILLS and n_slots >= 2*T*k");
   if ((!fused && !devfill) || (fused && profile)) {
     moe_status st = read_step(ctx, s, inputs, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
