@@ -35,7 +35,8 @@ def test_topk_bitexact_on_identical_logits():
 
 
 @pytest.mark.parametrize("wl,T", [(W.TINY, 1), (W.TINY, 16), (SMALL_BF16, 1), (SMALL_BF16, 4), (SMALL_BF16, 96),
-                                  (W.A3B_DECODE.with_(n_layers=2), 1), (W.A3B_DECODE.with_(n_layers=2), 300)])
+                                  (W.A3B_DECODE.with_(n_layers=2), 1), (W.A3B_DECODE.with_(n_layers=2), 300),
+                                  (W.DSV4.with_(n_layers=2), 1), (W.DSV4.with_(n_layers=2), 70)])
 def test_route_matches_oracle(wl, T):
     import routed_expert_ffn_02_amd as R
     h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=1, max_tokens=max(T, 8))
