@@ -45,6 +45,266 @@ __device__ int block_sum(int v, int* s_tmp) {
   return total;
 }
 
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off);
+    v = (o < v) ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {  // set bits of mask below lane
+  return __popcll(mask & ((1ull << lane) - 1ull));
+}
+
+constexpr int kSmallP = 64;  // pairs a step may have for the one-wavefront path
+
+// Decode-sized steps (T*k <= 64, routed ids given): wavefront 0 holds one (token,
+// rank) pair per lane and does every per-key step (dedupe, classify, miss ranks,
+// admission, stamps, groups, outputs) with ballots and lane reads; the whole block
+// joins only for the per-slot scan (evictable count and each wavefront's smallest
+// (stamp, slot) candidates).  Three block barriers in all; the decisions and their
+// order are those of the general path below.
+__device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, unsigned char* s_prot,
+                             uint64_t (*s_cand)[kSmallP], int* s_evc, int* s_ufirst, int* s_sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, P = a.T * a.k;
+  const int kbase = a.layer * E;
+  const bool cached = (a.mode == LK_OFFLOAD || a.mode == LK_CPU || a.mode == LK_HYBRID);
+
+  // ---- 0. every piece of state requested at once (as in the general path)
+  int slotrow_r = -1;
+  uint64_t st_r[kSlotsPerThread];
+  uint8_t rs_r[kSlotsPerThread];
+  int ko_r[kSlotsPerThread];
+  uint64_t c0 = 0;
+  int e = -1;
+  if (wave == 0 && lane < P) e = a.topk_idx[lane];
+  if (cached) {
+    if (tid < E) slotrow_r = a.slot_of[kbase + tid];
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int sl = tid + j * kLookupThreads;
+      const bool in = sl < a.n_slots;
+      st_r[j] = in ? a.stamp[sl] : 0;
+      rs_r[j] = in ? a.reserved[sl] : 1;
+      ko_r[j] = in ? a.key_of[sl] : -1;
+    }
+    if (wave == 0) c0 = *a.counter;
+  }
+  reinterpret_cast<uint32_t*>(s_prot)[tid] = 0u;  // kMaxCachedSlots bytes = one word per thread
+  if (cached) {
+    if (tid < E) s_slotrow[tid] = slotrow_r;
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int sl = tid + j * kLookupThreads;
+      if (sl < a.n_slots) s_keyof[sl] = ko_r[j];
+    }
+  }
+  __syncthreads();  // #1
+
+  // ---- 1. wavefront 0: U, classification, miss ranks
+  const bool valid = lane < P;
+  int nU = 0, m = 0, upos_p = 0;       // pair lanes: U position of the pair's expert
+  int key = -1, slot = -1, kind = 9, p0 = 0;  // U lanes (lane < nU)
+  uint64_t missmask = 0;
+  if (wave == 0) {
+    const bool bad = valid && (e < 0 || e >= E);
+    if (__ballot(bad)) {
+      if (valid) a.pair_grp[lane] = -1;  // nothing runs for this step
+      if (lane == 0) {
+        a.cnt[C_ERR] = 1;
+        a.cnt[C_NGRP] = 0;
+        s_sc[0] = 1;
+      }
+    } else {
+      if (lane == 0) s_sc[0] = 0;
+      int first = lane;  // first pair routed to the same expert
+      for (int q = 0; q < P; ++q) {
+        const int eq = __shfl(e, q);
+        if (q < first && eq == e) first = q;
+      }
+      const uint64_t fmask = __ballot(valid && first == lane);
+      nU = __popcll(fmask);
+      if (valid && first == lane) s_ufirst[lanes_below(fmask, lane)] = lane;
+      upos_p = lanes_below(fmask, first);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): s_ufirst written before it is read
+      __builtin_amdgcn_wave_barrier();
+      if (lane < nU) {
+        p0 = s_ufirst[lane];
+      }
+      const int ue = __shfl(e, p0);
+      if (lane < nU) {
+        key = kbase + ue;
+        if (a.mode == LK_FUSED) {
+          slot = key;
+          kind = MOE_KIND_HIT;
+        } else if (a.mode == LK_BUFFER) {
+          slot = a.buffer_base + ue;
+          kind = MOE_KIND_BUF;
+        } else {
+          slot = s_slotrow[ue];
+          if (slot >= 0) {
+            kind = MOE_KIND_HIT;
+            s_prot[slot] = 1;
+          }
+        }
+      }
+      missmask = __ballot(lane < nU && kind == 9);
+      m = __popcll(missmask);
+      if (lane == 0) s_sc[1] = m;
+    }
+  }
+  __syncthreads();  // #2
+  if (s_sc[0]) return;  // range error: reported above
+  const int m_all = s_sc[1];
+
+  // ---- 2. every wavefront: evictable slots and its own smallest (stamp, slot) keys
+  if (cached) {
+    uint64_t keys[kSlotsPerThread];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int sl = tid + j * kLookupThreads;
+      const bool elig = (sl < a.n_slots) && !s_prot[sl] && !rs_r[j];
+      cnt += elig;
+      keys[j] = elig ? ((st_r[j] << 16) | (uint64_t)sl) : ~0ull;
+    }
+    // a wavefront's count: lanes hold 0..4
+    int wc = cnt;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wc += __shfl_xor(wc, off);
+    if (lane == 0) s_evc[wave] = wc;
+    if (a.mode != LK_CPU) {
+      uint64_t last = 0;
+      for (int r = 0; r < m_all; ++r) {
+        uint64_t best = ~0ull;
+#pragma unroll
+        for (int j = 0; j < kSlotsPerThread; ++j)
+          if ((r == 0 || keys[j] > last) && keys[j] < best) best = keys[j];
+        best = wave_min_u64(best);
+        if (lane == 0) s_cand[wave][r] = best;
+        last = best;
+      }
+    }
+  }
+  __syncthreads();  // #3
+  if (wave != 0) return;
+
+  // ---- 3. wavefront 0: q, victims, admission, stamps, groups, outputs
+  int ev = 0, q = 0;
+  if (cached) {
+    int w = lane < kWaves ? s_evc[lane] : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off);
+    ev = w;
+    if (a.mode == LK_OFFLOAD) {
+      q = min(m, ev);
+    } else if (a.mode == LK_HYBRID) {
+      if (m == 0 || ev == 0) {
+        q = 0;
+      } else if (a.bw_host <= a.bw_pcie) {
+        q = min(m, ev);
+      } else {
+        const uint64_t num = 2ull * (uint64_t)m * a.bw_pcie + a.bw_host;
+        const uint64_t qq = num / (2ull * a.bw_host);
+        const int qi = (int)max<uint64_t>(1ull, qq);
+        q = min(min(m, ev), qi);
+      }
+    }
+  }
+  const bool miss = (missmask >> lane) & 1ull;
+  const int mrank = miss ? lanes_below(missmask, lane) : -1;
+  // the q smallest of the union of every wavefront's m smallest (q <= m, so it holds them)
+  uint64_t victim = ~0ull;
+  if (q > 0) {
+    const int nc = kWaves * m;  // candidates s_cand[w][r], r < m
+    uint64_t last = 0;
+    for (int r = 0; r < q; ++r) {
+      uint64_t best = ~0ull;
+      for (int i = lane; i < nc; i += 64) {
+        const uint64_t c = s_cand[i / m][i % m];
+        if ((r == 0 || c > last) && c < best) best = c;
+      }
+      best = wave_min_u64(best);
+      if (mrank == r) victim = best;
+      last = best;
+    }
+  }
+  int evicted = -1;
+  if (miss) {
+    if (mrank < q) {
+      slot = (int)(victim & 0xffffull);
+      evicted = s_keyof[slot];
+      if (evicted >= 0) a.slot_of[evicted] = -1;
+      a.slot_of[key] = slot;
+      a.key_of[slot] = key;
+      kind = MOE_KIND_FILL;
+    } else {
+      kind = MOE_KIND_CPU;
+      slot = -1;
+    }
+  }
+  const int n_evict = __popcll(__ballot(miss && mrank < q && evicted >= 0));
+  const bool is_gpu = lane < nU && (kind == MOE_KIND_HIT || kind == MOE_KIND_FILL || kind == MOE_KIND_BUF);
+  const uint64_t gmask = __ballot(is_gpu);
+  const int nG = __popcll(gmask);
+  if (cached && is_gpu) a.stamp[slot] = c0 + (uint64_t)lanes_below(gmask, lane) + 1ull;
+  // group id: GPU entries ordered by slot
+  int g = 0;
+  for (int u = 0; u < nU; ++u) {
+    const int su = __shfl(slot, u);
+    if (((gmask >> u) & 1ull) && su < slot) ++g;
+  }
+  if (is_gpu) {
+    a.grp_slot[g] = slot;
+    a.grp_pair0[g] = p0;
+  }
+  if (lane < nU) {
+    a.u_key[lane] = key;
+    a.u_kind[lane] = kind;
+    a.u_slot[lane] = slot;
+    a.u_evict[lane] = evicted;
+    if (a.trace) a.trace[lane] = moe_trace_rec{key, kind, slot, evicted};
+    if (miss) {
+      if (mrank < q) {
+        a.fill_key[mrank] = key;
+        a.fill_slot[mrank] = slot;
+      } else {
+        a.cpu_key[mrank - q] = key;
+      }
+    }
+  }
+  // per pair: the data of its expert's U entry
+  const int pk = __shfl(kind, upos_p), ps = __shfl(slot, upos_p), pg = __shfl(g, upos_p);
+  const int pr = __shfl(mrank, upos_p);
+  if (valid) {
+    a.slot_idx[lane] = (pk == MOE_KIND_CPU) ? -1 - (pr - q) : ps;
+    a.pair_grp[lane] = (pk == MOE_KIND_CPU) ? -1 : pg;
+  }
+  const int gpu_pairs = __popcll(__ballot(valid && pk != MOE_KIND_CPU));
+  if (lane == 0) {
+    if (cached) *a.counter = c0 + (uint64_t)nG;
+    a.cnt[C_NU] = nU;
+    a.cnt[C_HIT] = nU - m;
+    a.cnt[C_FILL] = q;
+    a.cnt[C_CPU] = m - q;
+    a.cnt[C_EVICT] = n_evict;
+    a.cnt[C_NGRP] = nG;
+    a.cnt[C_M] = m;
+    a.cnt[C_EV] = ev;
+    a.cnt[C_NPAIR_GPU] = gpu_pairs;
+    a.cnt[C_ERR] = 0;
+    if (a.counts_out) {
+      a.counts_out[MOE_CNT_HIT] = nU - m;
+      a.counts_out[MOE_CNT_FILL] = q;
+      a.counts_out[MOE_CNT_CPU] = m - q;
+      a.counts_out[MOE_CNT_EVICT] = n_evict;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
   __shared__ int s_first[kMaxExperts];   // first pair index of expert e, or INT_MAX
   __shared__ int s_upos[kMaxExperts];    // position of expert e in U, or -1
@@ -54,7 +314,7 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
   __shared__ int s_uevict[kMaxExperts];
   __shared__ int s_uaux[kMaxExperts];    // miss rank (misses) ; group id (GPU entries)
   __shared__ int s_miss_u[kMaxExperts];  // U position of the r-th miss
-  __shared__ unsigned char s_prot[kMaxCachedSlots];
+  __shared__ __attribute__((aligned(4))) unsigned char s_prot[kMaxCachedSlots];
   __shared__ uint64_t s_victim[kMaxExperts];
   __shared__ uint64_t s_red[kWaves];
   __shared__ int s_tmp[64];
@@ -63,6 +323,14 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
   __shared__ int s_slotrow[kMaxExperts];       // slot_of of this layer's keys at kernel start
   __shared__ int s_keyof[kMaxCachedSlots];     // key_of at kernel start
   __shared__ uint64_t s_c0;
+
+  if (a.cand == nullptr && a.T * a.k <= kSmallP) {  // uniform
+    __shared__ uint64_t s_cand[kWaves][kSmallP];
+    __shared__ int s_evc[kWaves];
+    __shared__ int s_ufirst[kSmallP];
+    lookup_small(a, s_slotrow, s_keyof, s_prot, s_cand, s_evc, s_ufirst, s_sc);
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int E = a.E, k = a.k, P = a.T * a.k;

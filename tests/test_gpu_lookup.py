@@ -16,13 +16,15 @@ def _traces_equal(gpu, ref):
     return [tuple(r) for r in gpu] == [tuple(r) for r in ref]
 
 
+# T*k <= 64 takes the one-wavefront path of the kernel, larger steps the block-wide one
 @pytest.mark.parametrize("mode,n_slots,T", [
-    (1, 40, 1), (1, 7, 1), (1, 0, 1), (1, 200, 4), (1, 5, 4),
-    (3, 40, 1), (3, 13, 4), (2, 40, 1), (2, 9, 4)])
+    (1, 40, 1), (1, 7, 1), (1, 0, 1), (1, 200, 4), (1, 5, 4), (1, 3000, 4), (1, 70, 16),
+    (3, 40, 1), (3, 13, 4), (2, 40, 1), (2, 9, 4),
+    (1, 150, 20), (1, 30, 20), (3, 90, 20), (2, 40, 20)])
 def test_lookup_sequence_matches_oracle(mode, n_slots, T):
     import routed_expert_ffn_02_amd as R
     bw = (25_000_000_000, 100_000_000_000) if mode == R.MOE_MODE_HYBRID else (0, 0)
-    h = Harness(LK, mode, n_slots=n_slots, bw=bw)
+    h = Harness(LK, mode, n_slots=n_slots, bw=bw, max_tokens=max(8, T))
     ref = oracle.ExpertCache(LK.n_layers, LK.n_experts, n_slots)
     routes = {l: LK.synthetic_routing(50, l, T) for l in range(LK.n_layers)}
     for step in range(50):
