@@ -117,8 +117,6 @@ typedef struct {
   double copy_ms;                 /* prefill whole-layer copies (MOE_FLAG_PROFILE) */
   uint64_t copy_bytes;
   double cpu_ms;                  /* host CPU branch wall time */
-  uint64_t gemv_fused;            /* decode steps whose two GEMV phases ran as one kernel (their
-                                     time and bytes are counted under phase 1) */
 } moe_stats;
 
 /* ---- context ---------------------------------------------------------- */
@@ -306,8 +304,7 @@ MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* k
 
 /*
  * Wait for `stream` and report what device-fill steps could not report when they were
- * enqueued: MOE_EINVAL if a step since the last moe_sync saw an expert id out of range;
- * MOE_EHIP if a bounded wait inside the fused decode GEMV kernel ran out (never expected).
+ * enqueued: MOE_EINVAL if a step since the last moe_sync saw an expert id out of range.
  */
 MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream);
 

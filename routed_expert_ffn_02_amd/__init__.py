@@ -56,7 +56,7 @@ class moe_stats(ctypes.Structure):
         ("gemm1_ms", ctypes.c_double), ("gemm2_ms", ctypes.c_double),
         ("gemm1_launches", ctypes.c_uint64), ("gemm2_launches", ctypes.c_uint64),
         ("gemm_flops", ctypes.c_double), ("copy_ms", ctypes.c_double), ("copy_bytes", ctypes.c_uint64),
-        ("cpu_ms", ctypes.c_double), ("gemv_fused", ctypes.c_uint64)]
+        ("cpu_ms", ctypes.c_double)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -141,19 +141,6 @@ __device__ __forceinline__ const uint8_t* scale_row(const uint8_t* rec, int t, i
   return rec + 3 * (n / 2) + (int64_t)t * (n / 32) * 2 + (int64_t)r * (cols / 32) * 2;
 }
 
-// Wait until *count >= need, then an agent-scope acquire, so the producers' stores
-// that preceded their release are visible.  The polls themselves are relaxed (no cache
-// invalidation per poll).  Bounded: a spin that runs out is counted.
-constexpr int kSpinLimit = 1 << 20;
-
-__device__ __forceinline__ void wait_count(const int* count, int need, unsigned long long* spin_err) {
-  int it = 0;
-  while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need && ++it < kSpinLimit)
-    __builtin_amdgcn_s_sleep(2);
-  if (it >= kSpinLimit && (threadIdx.x & 63) == 0) atomicAdd(spin_err, 1ull);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
 // Pairs of group g, found by one wavefront with a ballot (no block barrier, so no
 // fence waits on the weight loads already in flight).  P <= 64 on the fast path.
 __device__ __forceinline__ uint64_t group_mask(const DecodeArgs& a, int g) {
@@ -249,7 +236,8 @@ struct XRaw {
 // wavefront owns RW consecutive (gate, up) row pairs of one expert; its weight
 // chunks and the matching activation chunks are all requested before any is used.
 template <int WFMT, int AFMT, int CPL, int RW, int MAXT>
-__device__ __forceinline__ void p1_fast_item(const DecodeArgs& a, int g, int bx) {
+__global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
+  const int g = blockIdx.y;
   // both loads issue together (grp_slot has E >= gridDim.y entries, so the read is in
   // bounds even for a group beyond the count, whose value is then unused)
   const int slot = a.grp_slot[g];
@@ -270,7 +258,7 @@ __device__ __forceinline__ void p1_fast_item(const DecodeArgs& a, int g, int bx)
     for (int c = 0; c < CPL; ++c) xr[c].load(a.x, H, 0, lane + 64 * c);
   }
   if (g >= a.cnt[C_NGRP]) return;
-  const int row0 = (bx * 4 + wave) * RW;
+  const int row0 = (blockIdx.x * 4 + wave) * RW;
   if (row0 >= I) return;
   const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
   uint4 qg[RW][CPL], qu[RW][CPL];
@@ -382,11 +370,6 @@ __device__ __forceinline__ void p1_fast_item(const DecodeArgs& a, int g, int bx)
   }
 }
 
-template <int WFMT, int AFMT, int CPL, int RW, int MAXT>
-__global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
-  p1_fast_item<WFMT, AFMT, CPL, RW, MAXT>(a, blockIdx.y, blockIdx.x);
-}
-
 // Phase 1, generic shapes: one row pair per wavefront, activations staged in LDS.
 template <int WFMT, int AFMT>
 __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
@@ -443,18 +426,16 @@ __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Phase 2, fast path (I = 64 chunks per row, P <= 64): each wavefront owns R2 rows
 // of W_down of one expert; weight chunks and h slices requested up front.
-// WAIT (the fused GEMV kernel): the group's activated row is produced by phase-1
-// items of the same launch, so the weights are requested first and the row only once
-// the group's phase-1 count is complete.
-template <int WFMT, int MAXT, bool WAIT>
-__device__ __forceinline__ void p2_fast_item(const DecodeArgs& a, int g, int bx, const FusedSync* fs) {
+template <int WFMT, int MAXT>
+__global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
   constexpr int R2 = kP2RowsPerWave;
+  const int g = blockIdx.y;
   const int slot = a.grp_slot[g];  // issued with the count (see phase 1)
   const int pair0 = (MAXT == 1) ? a.grp_pair0[g] : 0;
   if (g >= a.cnt[C_NGRP]) return;
   const int H = a.H, I = a.I;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = bx * kP2Rows + wave * R2;
+  const int r0 = blockIdx.x * kP2Rows + wave * R2;
   if (r0 >= H) return;
   const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
   using RD = RowDot<WFMT>;
@@ -462,15 +443,14 @@ __device__ __forceinline__ void p2_fast_item(const DecodeArgs& a, int g, int bx,
   // one token: the group's activated row is requested before the weights (loads
   // return in issue order)
   float hv[MAXT][EPC];
-  auto load_h0 = [&]() {
+  if constexpr (MAXT == 1) {
     const float4* hp = reinterpret_cast<const float4*>(a.h + (int64_t)pair0 * I + lane * EPC);
 #pragma unroll
     for (int i = 0; i < EPC / 4; ++i) {
       const float4 v = hp[i];
       hv[0][4 * i] = v.x; hv[0][4 * i + 1] = v.y; hv[0][4 * i + 2] = v.z; hv[0][4 * i + 3] = v.w;
     }
-  };
-  if constexpr (MAXT == 1 && !WAIT) load_h0();
+  }
   uint4 q[R2];
   // the (small) block scales first, kept as raw bits until used: row r then waits
   // only for its own weights
@@ -485,11 +465,6 @@ __device__ __forceinline__ void p2_fast_item(const DecodeArgs& a, int g, int bx,
   for (int r = 0; r < R2; ++r)
     q[r] = reinterpret_cast<const uint4*>(tensor_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
   if constexpr (MAXT == 1) __builtin_amdgcn_sched_barrier(0);  // every load in flight before any use
-  if constexpr (WAIT) {
-    static_assert(MAXT == 1, "the fused kernel serves one token");
-    wait_count(fs->ready + g, fs->b1, fs->spin_err);
-    load_h0();
-  }
   int pair[MAXT];
   int n = 0;
   if constexpr (MAXT == 1) {
@@ -530,49 +505,6 @@ __device__ __forceinline__ void p2_fast_item(const DecodeArgs& a, int g, int bx,
         const int row = r0 + r;
         if (lane == 0 && row < H) a.d[(int64_t)pair[t] * H + row] = sum;
       }
-    }
-  }
-}
-
-template <int WFMT, int MAXT>
-__global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
-  p2_fast_item<WFMT, MAXT, false>(a, blockIdx.y, blockIdx.x, nullptr);
-}
-
-// ---------------------------------------------------------------------------
-// Both GEMV phases in one launch (one token).  Workgroups take items from a ticket
-// counter: first every phase-1 item (group-major), then every phase-2 item.  A
-// phase-2 item streams its W_down rows at once and waits only for the count of its
-// group's finished phase-1 items, so the down projection's weights stream while the
-// gate/up phase finishes and neither phase has a separate ramp and tail.  No wait can
-// block progress: a phase-2 ticket is drawn only after every phase-1 ticket has gone
-// to a running workgroup, and phase-1 items never wait.  The wait is bounded all the
-// same (a spin that runs out is counted and the workgroup finishes).  The last
-// workgroup to finish returns the counters to zero for the next launch.
-template <int WFMT, int AFMT, int CPL, int RW>
-__global__ __launch_bounds__(256) void dec_fused(DecodeArgs a, FusedSync fs) {
-  __shared__ int s_t;
-  if (threadIdx.x == 0) s_t = atomicAdd(fs.ticket, 1);
-  __syncthreads();
-  const int t = s_t;
-  if (t < fs.n1) {
-    const int g = t / fs.b1;
-    p1_fast_item<WFMT, AFMT, CPL, RW, 1>(a, g, t - g * fs.b1);
-    __threadfence();  // this wavefront's rows of h are visible device-wide
-    __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(fs.ready + g, 1);
-  } else if (t < fs.n1 + fs.n2) {  // (always, unless the counters were left dirty)
-    const int t2 = t - fs.n1;
-    const int g = t2 / fs.b2;
-    p2_fast_item<WFMT, 1, true>(a, g, t2 - g * fs.b2, &fs);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(fs.done, 1);
-    if (prev == fs.n1 + fs.n2 - 1) {
-      for (int g = 0; g < fs.groups; ++g) fs.ready[g] = 0;
-      *fs.done = 0;
-      *fs.ticket = 0;
     }
   }
 }
@@ -728,41 +660,6 @@ void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStre
   if (wfmt == MOE_WFMT_BF16) p2_tokens<MOE_WFMT_BF16>(a, max_groups, s, tm);
   else if (wfmt == MOE_WFMT_FP4) p2_tokens<MOE_WFMT_FP4>(a, max_groups, s, tm);
   else p2_tokens<MOE_WFMT_F32>(a, max_groups, s, tm);
-}
-
-template <int W, int A, int CPL>
-static bool fused_go(const DecodeArgs& a, int max_groups, FusedSync fs, hipStream_t s, Timing tm) {
-  constexpr int RW = (W == MOE_WFMT_FP4 && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : 8);
-  fs.b1 = (a.I + 4 * RW - 1) / (4 * RW);
-  fs.b2 = decode_phase2_rowblocks(a.H);
-  fs.n1 = fs.b1 * max_groups;
-  fs.n2 = fs.b2 * max_groups;
-  fs.groups = max_groups;
-  launch_timed(dec_fused<W, A, CPL, RW>, dim3(fs.n1 + fs.n2), dim3(256), 0, s, tm, a, fs);
-  return true;
-}
-
-template <int W, int A>
-static bool fused_dispatch(const DecodeArgs& a, int max_groups, const FusedSync& fs, hipStream_t s, Timing tm) {
-  if (a.T != 1 || a.k > 64 || lane_chunks(W, a.I) != 1) return false;  // the fast phase-2 shape
-  switch (lane_chunks(W, a.H)) {
-    case 1: return fused_go<W, A, 1>(a, max_groups, fs, s, tm);
-    case 2: return fused_go<W, A, 2>(a, max_groups, fs, s, tm);
-    case 4: return fused_go<W, A, 4>(a, max_groups, fs, s, tm);
-    default: return false;
-  }
-}
-
-bool launch_decode_fused(int wfmt, int afmt, const DecodeArgs& a, int max_groups, const FusedSync& fs, hipStream_t s,
-                         Timing tm) {
-  if (afmt == MOE_AFMT_BF16) {
-    if (wfmt == MOE_WFMT_BF16) return fused_dispatch<MOE_WFMT_BF16, MOE_AFMT_BF16>(a, max_groups, fs, s, tm);
-    if (wfmt == MOE_WFMT_FP4) return fused_dispatch<MOE_WFMT_FP4, MOE_AFMT_BF16>(a, max_groups, fs, s, tm);
-    return fused_dispatch<MOE_WFMT_F32, MOE_AFMT_BF16>(a, max_groups, fs, s, tm);
-  }
-  if (wfmt == MOE_WFMT_BF16) return fused_dispatch<MOE_WFMT_BF16, MOE_AFMT_F32>(a, max_groups, fs, s, tm);
-  if (wfmt == MOE_WFMT_FP4) return fused_dispatch<MOE_WFMT_FP4, MOE_AFMT_F32>(a, max_groups, fs, s, tm);
-  return fused_dispatch<MOE_WFMT_F32, MOE_AFMT_F32>(a, max_groups, fs, s, tm);
 }
 
 void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s) {

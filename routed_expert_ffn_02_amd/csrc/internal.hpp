@@ -32,10 +32,7 @@ enum {
 };
 
 // device-side step statistics of device-fill steps (uint64 array)
-enum {
-  D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_P1_BYTES = 6, D_P2_BYTES = 7, D_SPIN = 8,
-  D_COUNT = 16
-};
+enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_P1_BYTES = 6, D_P2_BYTES = 7, D_COUNT = 8 };
 
 enum LookupMode { LK_FUSED = 0, LK_OFFLOAD = 1, LK_CPU = 2, LK_HYBRID = 3, LK_BUFFER = 4 };
 
@@ -79,16 +76,6 @@ struct DecodeArgs {
   float* h;                  // [T*k, I] scratch
   float* d;                  // [T*k, H] scratch (per-pair expert outputs)
   float* y;                  // [T,H]
-};
-
-// Work counters of the fused decode GEMV kernel (device int arrays, zero between
-// launches: the kernel's last workgroup resets them).
-struct FusedSync {
-  int* ticket;                    // [1] next item
-  int* done;                      // [1] finished items
-  int* ready;                     // [groups] finished phase-1 items per group
-  unsigned long long* spin_err;   // bounded waits that ran out (expected 0)
-  int n1, b1, n2, b2, groups;     // items: phase 1 = b1 per group, phase 2 = b2 per group
 };
 
 struct FillArgs {
@@ -143,10 +130,6 @@ void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_group
 void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 int decode_phase2_rowblocks(int H);
 void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s);
-// Both GEMV phases in one launch when the shape allows it (one token, fast-path row
-// widths); returns false otherwise (then launch_decode_phase1 / phase2).
-bool launch_decode_fused(int wfmt, int afmt, const DecodeArgs& a, int max_groups, const FusedSync& fs, hipStream_t s,
-                         Timing tm = {});
 int fill_blocks_per_record(int64_t rec_bytes);
 void launch_fill_pull(const FillArgs& a, int max_fills, hipStream_t s);
 void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
@@ -247,8 +230,7 @@ struct moe_ctx {
   void* xo = nullptr;        // [max_tokens, H] 16-bit MFMA operands of the prefill activations
   float* ypair = nullptr;
   int32_t* flags = nullptr;
-  uint64_t* dstats = nullptr;    // [D_COUNT] counts of device-fill steps; D_SPIN: fused-kernel waits that ran out
-  int32_t* fsync = nullptr;      // [2 + E] fused GEMV work counters (ticket, done, per-group ready)
+  uint64_t* dstats = nullptr;    // [D_COUNT] counts of device-fill steps
 
   // pinned host staging; h_cnt .. h_u_kind mirror step_dev
   int32_t* step_host = nullptr;

@@ -360,7 +360,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->hist, (size_t)((Pmax + 255) / 256) * kMaxExperts) || dev_alloc(&ctx->cand, E) ||
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->act), (size_t)Pmax * I * 4) ||
       dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)) ||
-      dev_alloc(&ctx->dstats, D_COUNT) || dev_alloc(&ctx->fsync, 2 + E))
+      dev_alloc(&ctx->dstats, D_COUNT))
     return cleanup_fail(MOE_ENOMEM);
   if (prefill_needs_act_operands(c.wfmt, c.afmt) &&
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->xo), (size_t)c.max_tokens * H * 2))
@@ -374,7 +374,6 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   if (hipMemset(ctx->slot_of, 0xff, (size_t)L * E * 4) || hipMemset(ctx->key_of, 0xff, kMaxCachedSlots * 4) ||
       hipMemset(ctx->stamp, 0, kMaxCachedSlots * 8) || hipMemset(ctx->reserved, 0, kMaxCachedSlots) ||
       hipMemset(ctx->counter, 0, 8) || hipMemset(ctx->dstats, 0, D_COUNT * 8) ||
-      hipMemset(ctx->fsync, 0, (2 + E) * 4) ||
       hipMemset(ctx->step_dev, 0, (C_COUNT + 5 * E) * 4))
     return cleanup_fail(MOE_EHIP);
   // pinned host staging
@@ -421,7 +420,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
                  ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
-                 ctx->flags, ctx->xo, ctx->dstats, ctx->fsync};
+                 ctx->flags, ctx->xo, ctx->dstats};
   for (void* p : dev)
     if (p) hipFree(p);
   void* host[] = {ctx->step_host, ctx->h_slot_idx, ctx->h_w, ctx->h_x, ctx->h_xf, ctx->h_y, ctx->h_hbuf};
@@ -645,18 +644,11 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     moe_status st = issue_fills(ctx, s);
     if (st != MOE_OK) return st;
   }
-  bool gemv_fused = false;
   {
     TimedScope t1(ctx, s, TK_P1);
-    FusedSync fs{};
-    fs.ticket = ctx->fsync;
-    fs.done = ctx->fsync + 1;
-    fs.ready = ctx->fsync + 2;
-    fs.spin_err = reinterpret_cast<unsigned long long*>(ctx->dstats + D_SPIN);
-    gemv_fused = launch_decode_fused(ctx->cfg.wfmt, ctx->cfg.afmt, d, max_groups, fs, s, t1.tm);
-    if (!gemv_fused) launch_decode_phase1(ctx->cfg.wfmt, ctx->cfg.afmt, d, max_groups, s, t1.tm);
+    launch_decode_phase1(ctx->cfg.wfmt, ctx->cfg.afmt, d, max_groups, s, t1.tm);
   }
-  if (!gemv_fused) {
+  {
     TimedScope t2(ctx, s, TK_P2);
     launch_decode_phase2(ctx->cfg.wfmt, d, max_groups, s, t2.tm);
   }
@@ -667,15 +659,14 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   }
   launch_decode_combine(d, y_cpu, s);
   HIPCHK(hipGetLastError());
-  if (gemv_fused) ctx->stats.gemv_fused += 1;
   if (profile && devfill) {  // bytes are added on the device
     ctx->stats.phase1_launches += 1;
-    ctx->stats.phase2_launches += gemv_fused ? 0 : 1;
+    ctx->stats.phase2_launches += 1;
   } else if (profile) {
     const int ngrp = ctx->h_cnt[C_NGRP];
     const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
     ctx->stats.phase1_launches += 1;
-    ctx->stats.phase2_launches += gemv_fused ? 0 : 1;
+    ctx->stats.phase2_launches += 1;
     // algorithmic bytes: the GPU experts' gate+up rows, x once, h out / down rows, h in, y out
     ctx->stats.phase1_bytes += (uint64_t)ngrp * 2 * I * wrow_h + (uint64_t)T * H * act_bytes(ctx->cfg) +
                                (uint64_t)ctx->h_cnt[C_NPAIR_GPU] * I * 4;
@@ -1129,14 +1120,12 @@ MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* k
 MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream) {
   if (!ctx) return MOE_EINVAL;
   HIPCHK(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  uint64_t d[D_COUNT];
-  HIPCHK(hipMemcpy(d, ctx->dstats, sizeof d, hipMemcpyDeviceToHost));
-  if (d[D_ERR] || d[D_SPIN]) {
+  uint64_t err = 0;
+  HIPCHK(hipMemcpy(&err, ctx->dstats + D_ERR, 8, hipMemcpyDeviceToHost));
+  if (err) {
     const uint64_t zero = 0;
     HIPCHK(hipMemcpy(ctx->dstats + D_ERR, &zero, 8, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(ctx->dstats + D_SPIN, &zero, 8, hipMemcpyHostToDevice));
-    if (d[D_ERR]) return fail(ctx, MOE_EINVAL, "expert id out of range in topk_idx (device-fill step)");
-    return fail(ctx, MOE_EHIP, "a bounded wait in the fused decode GEMV ran out");
+    return fail(ctx, MOE_EINVAL, "expert id out of range in topk_idx (device-fill step)");
   }
   return MOE_OK;
 }
@@ -1167,10 +1156,9 @@ MOE_API moe_status moe_reset_stats(moe_ctx* ctx) {
   HIPCHK(hipDeviceSynchronize());
   uint64_t d[D_COUNT];
   HIPCHK(hipMemcpy(d, ctx->dstats, sizeof d, hipMemcpyDeviceToHost));
-  const uint64_t err = d[D_ERR], spin = d[D_SPIN];  // pending errors stay pending for moe_sync
+  const uint64_t err = d[D_ERR];  // a pending error stays pending for moe_sync
   for (auto& v : d) v = 0;
   d[D_ERR] = err;
-  d[D_SPIN] = spin;
   HIPCHK(hipMemcpy(ctx->dstats, d, sizeof d, hipMemcpyHostToDevice));
   return MOE_OK;
 }

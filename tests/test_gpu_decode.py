@@ -107,9 +107,7 @@ REAL_ROWS = {
 @pytest.mark.parametrize("T", [1, 4])
 @pytest.mark.parametrize("mode", [1, 3])
 def test_decode_real_row_widths(name, T, mode):
-    """The register-resident GEMV variants used at the A3B and DSV4 row widths (one token:
-    the fused two-phase kernel)."""
-    import routed_expert_ffn_02_amd as R
+    """The register-resident GEMV variants used at the A3B and DSV4 row widths."""
     wl = REAL_ROWS[name]
     bw = (25_000_000_000, 100_000_000_000)
     h = Harness(wl, mode, bw=bw)
@@ -124,9 +122,3 @@ def test_decode_real_row_widths(name, T, mode):
             r = ref.lookup(layer, idx, mode, *bw)
             assert trace == r.trace
             assert row_rel_err(y, _expected(wl, layer, x, idx, w)) <= tol_for(wl), (step, layer)
-    R.moe_sync(h.ctx)  # no bounded wait of the fused GEMV ran out
-    st = R.moe_get_stats(h.ctx)
-    # one token at the A3B / DSV4 row widths: both GEMV phases run as one kernel (the
-    # 8-chunk rows of the wide shape take the generic phase-1 kernel)
-    fused = T == 1 and name != "wide_bf16"
-    assert (st["gemv_fused"] == st["decode_calls"] > 0) if fused else st["gemv_fused"] == 0

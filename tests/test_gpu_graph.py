@@ -12,8 +12,7 @@ pytestmark = pytest.mark.gpu
 
 BF16 = W.A3B_DECODE.with_(name="graph_bf16", n_layers=3, n_experts=16, top_k=4, hidden=256, inter=128)
 FP4 = W.DSV4.with_(name="graph_fp4", n_layers=3, n_experts=16, top_k=3, hidden=256, inter=128)
-# real row widths: one token runs both GEMV phases in one kernel whose work counters reset
-# themselves at the end of every launch, so replays must find them at zero
+# real row widths: the register-resident GEMV variants inside the graph
 ROWS = W.A3B_DECODE.with_(name="graph_rows", n_layers=2, n_experts=16)
 
 
@@ -90,8 +89,6 @@ def test_captured_step_replays_like_eager(wl, mode):
             assert np.array_equal(a.view(np.uint8), b_.view(np.uint8)), (step, name)
     R.moe_sync(graph.ctx)
     R.moe_sync(eager.ctx)
-    if wl is ROWS:
-        assert R.moe_get_stats(eager.ctx)["gemv_fused"] > 0
     sg, se = R.moe_get_stats(graph.ctx), R.moe_get_stats(eager.ctx)
     if mode != "fused":
         assert sg["fills"] == se["fills"] > 0 and sg["hits"] == se["hits"] and sg["lookups"] == se["lookups"]
