@@ -78,8 +78,9 @@ typedef enum { MOE_MODE_FUSED = 0, MOE_MODE_OFFLOAD = 1, MOE_MODE_CPU = 2, MOE_M
 typedef enum { MOE_KIND_HIT = 0, MOE_KIND_FILL = 1, MOE_KIND_CPU = 2, MOE_KIND_BUF = 3 } moe_kind;
 
 #define MOE_FLAG_PROFILE 1 /* time the FFN kernels with HIP events (moe_get_stats) */
-/* OFFLOAD decode steps copy their fills with a kernel that reads the page-locked pool through
- * its device mapping, so moe_ffn_decode never waits for the device (see moe_ffn_decode). */
+/* Cached decode steps copy their fills with a kernel that reads the page-locked pool through
+ * its device mapping and run their CPU branch as a host function on a side stream, so
+ * moe_ffn_decode never waits for the device (see moe_ffn_decode). */
 #define MOE_FLAG_DEVICE_FILLS 2
 
 typedef struct {
@@ -225,16 +226,20 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
  * as given to / returned by the lookup; y: device fp32 [T,H].  Needs T * H <= 16384 (decode
  * batches); use moe_ffn_prefill for longer inputs.  Synchronises the stream when the step has
  * fills or CPU work (the fill list is read on the host), then enqueues the GPU work.
- * With MOE_FLAG_DEVICE_FILLS, an OFFLOAD step that cannot send work to the CPU (n_slots >=
- * 2*T*k) instead enqueues a copy kernel that executes the lookup's fill list from the mapped
- * pool ([FT-KR] "CUDA Graph와 공존하는 LRU 캐시": cache control and transfer stay on the
- * device): nothing is read on the host, the call only enqueues work, and an out-of-range id
- * in topk_idx (the step then computes y = 0) is reported by the next moe_sync.  Needs a pool
- * from moe_pool_alloc or a registered page-locked pool with a device mapping (MOE_ENOPIN).
- * Such steps, and FUSED steps, enqueue device work only: route + lookup + decode of every layer
- * may be captured into one HIP graph on `stream` and replayed ([FT-KR] "CUDA Graph와 공존하는
- * LRU 캐시"); MOE_FLAG_PROFILE timing is skipped for captured launches, and a step that would
- * read the host while the stream is capturing returns MOE_ESTATE.
+ * With MOE_FLAG_DEVICE_FILLS a cached step that cannot send work to the CPU (OFFLOAD with
+ * n_slots >= 2*T*k) instead enqueues a copy kernel that executes the lookup's fill list from
+ * the mapped pool ([FT-KR] "CUDA Graph와 공존하는 LRU 캐시": cache control and transfer stay
+ * on the device); while `stream` is being captured, a step that may (CPU or HYBRID mode, or
+ * fewer slots) also forks the library's CPU stream: the step block and inputs are copied to
+ * pinned staging, a host function runs the CPU branch there, its partial sum is copied back,
+ * and the combine waits for it (eagerly such a step takes the host path above).  Nothing is
+ * read on the calling thread, the call only enqueues work, and an out-of-range id in
+ * topk_idx (the step then computes y = 0) is reported by the next moe_sync.  Needs a pool from moe_pool_alloc or a registered
+ * page-locked pool with a device mapping (MOE_ENOPIN).  Such steps, and FUSED steps, may be
+ * captured with route and lookup for every layer into one HIP graph on `stream` and replayed
+ * (the CPU branch becomes host nodes); MOE_FLAG_PROFILE timing is skipped for captured
+ * launches, and a step that would read the host while the stream is capturing returns
+ * MOE_ESTATE.
  */
 MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);

@@ -28,7 +28,7 @@ constexpr int kDecodeMaxTok = 8;        // decode: tokens routed to one expert w
 // lookup counters (device int32 array)
 enum {
   C_NU = 0, C_HIT = 1, C_FILL = 2, C_CPU = 3, C_EVICT = 4, C_NGRP = 5, C_M = 6, C_EV = 7,
-  C_NPAIR_GPU = 8, C_ERR = 9, C_COUNT = 16
+  C_NPAIR_GPU = 8, C_ERR = 9, C_T = 10, C_COUNT = 16
 };
 
 // device-side step statistics of device-fill steps (uint64 array)
@@ -248,6 +248,10 @@ struct moe_ctx {
   float* h_hbuf = nullptr;       // [Pmax*I] fp32 (CPU intermediate)
 
   hipStream_t copy_stream = nullptr;
+  // device-fill steps with CPU work: the branch runs as a host function on cpu_stream,
+  // forked from and joined to the caller's stream with events
+  hipStream_t cpu_stream = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t ev_sync = nullptr, ev_fill = nullptr, ev_ycpu = nullptr;
   hipEvent_t ev_layer_copied[2] = {nullptr, nullptr};
   hipEvent_t ev_layer_done[2] = {nullptr, nullptr};

@@ -116,6 +116,7 @@ __device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, 
       if (lane == 0) {
         a.cnt[C_ERR] = 1;
         a.cnt[C_NGRP] = 0;
+        a.cnt[C_T] = a.T;
         s_sc[0] = 1;
       }
     } else {
@@ -296,6 +297,7 @@ __device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, 
     a.cnt[C_EV] = ev;
     a.cnt[C_NPAIR_GPU] = gpu_pairs;
     a.cnt[C_ERR] = 0;
+    a.cnt[C_T] = a.T;
     if (a.counts_out) {
       a.counts_out[MOE_CNT_HIT] = nU - m;
       a.counts_out[MOE_CNT_FILL] = q;
@@ -389,6 +391,7 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
       if (tid == 0) {
         a.cnt[C_ERR] = 1;
         a.cnt[C_NGRP] = 0;
+        a.cnt[C_T] = a.T;
       }
       return;
     }
@@ -601,6 +604,7 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
     a.cnt[C_EV] = ev;
     a.cnt[C_NPAIR_GPU] = gpu_pairs;
     a.cnt[C_ERR] = 0;
+    a.cnt[C_T] = a.T;
     if (a.counts_out) {
       a.counts_out[MOE_CNT_HIT] = nU - m;
       a.counts_out[MOE_CNT_FILL] = q;

@@ -289,6 +289,63 @@ moe_status run_cpu_branch(moe_ctx* ctx, int T, hipStream_t s, float** y_cpu_dev_
   return MOE_OK;
 }
 
+// The CPU branch of a device-fill step, run by the HIP runtime as a host function on
+// cpu_stream once the step block and the inputs have landed in the pinned staging: it
+// reads the CPU list there and leaves the partial sum (zeros without CPU work) in h_y,
+// which the next node copies to the device.  It calls no HIP API.
+void cpu_branch_host_fn(void* user) {
+  moe_ctx* ctx = static_cast<moe_ctx*>(user);
+  const int T = ctx->h_cnt[C_T], H = ctx->cfg.hidden;
+  std::memset(ctx->h_y, 0, (size_t)T * H * sizeof(float));
+  const int ncpu = ctx->h_cnt[C_ERR] ? 0 : ctx->h_cnt[C_CPU];
+  if (ncpu <= 0) return;
+  if (ctx->cfg.afmt == MOE_AFMT_BF16) {
+    const uint16_t* xb = static_cast<const uint16_t*>(ctx->h_x);
+    for (int64_t i = 0; i < (int64_t)T * H; ++i) {
+      uint32_t u = (uint32_t)xb[i] << 16;
+      std::memcpy(&ctx->h_xf[i], &u, 4);
+    }
+  } else {
+    std::memcpy(ctx->h_xf, ctx->h_x, (size_t)T * H * sizeof(float));
+  }
+  CpuFfnJob job;
+  job.wfmt = ctx->cfg.wfmt;
+  job.H = H;
+  job.I = ctx->cfg.inter;
+  job.T = T;
+  job.k = ctx->cfg.top_k;
+  job.rec_bytes = ctx->S;
+  job.x = ctx->h_xf;
+  job.w = ctx->h_w;
+  job.slot_idx = ctx->h_slot_idx;
+  for (int c = 0; c < ncpu; ++c) job.rec.push_back(pool_record(ctx, ctx->h_cpu_key[c]));
+  job.h = ctx->h_hbuf;
+  job.y = ctx->h_y;
+  const auto t0 = std::chrono::steady_clock::now();
+  cpu_ffn(cpu_pool(ctx), job);
+  ctx->stats.cpu_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// Enqueue the CPU branch of a device-fill step on cpu_stream (forked from s after the
+// lookup): step block and inputs to the pinned staging, the host function, the
+// partial sum back to y_cpu_dev.  s must wait for ev_join before the combine.
+moe_status enqueue_cpu_branch(moe_ctx* ctx, const void* x, const float* w, const int32_t* slot_idx, int T,
+                              hipStream_t s) {
+  const int E = ctx->cfg.n_experts, H = ctx->cfg.hidden, P = T * ctx->cfg.top_k;
+  hipStream_t c = ctx->cpu_stream;
+  HIPCHK(hipEventRecord(ctx->ev_fork, s));
+  HIPCHK(hipStreamWaitEvent(c, ctx->ev_fork, 0));
+  HIPCHK(hipMemcpyAsync(ctx->step_host, ctx->step_dev, (size_t)(C_COUNT + 5 * E) * sizeof(int32_t),
+                        hipMemcpyDeviceToHost, c));
+  HIPCHK(hipMemcpyAsync(ctx->h_x, x, (size_t)T * H * act_bytes(ctx->cfg), hipMemcpyDeviceToHost, c));
+  HIPCHK(hipMemcpyAsync(ctx->h_w, w, (size_t)P * sizeof(float), hipMemcpyDeviceToHost, c));
+  HIPCHK(hipMemcpyAsync(ctx->h_slot_idx, slot_idx, (size_t)P * sizeof(int32_t), hipMemcpyDeviceToHost, c));
+  HIPCHK(hipLaunchHostFunc(c, cpu_branch_host_fn, ctx));
+  HIPCHK(hipMemcpyAsync(ctx->y_cpu_dev, ctx->h_y, (size_t)T * H * sizeof(float), hipMemcpyHostToDevice, c));
+  HIPCHK(hipEventRecord(ctx->ev_join, c));
+  return MOE_OK;
+}
+
 // A step may send experts to the CPU: CPU and HYBRID modes, or too few slots.
 bool may_use_cpu(const moe_ctx* c, int P) {
   return c->cfg.mode == MOE_MODE_CPU || c->cfg.mode == MOE_MODE_HYBRID || c->n_slots < 2 * P;
@@ -393,6 +450,9 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ctx->h_u_kind = ctx->h_u_key + E;
   std::memset(ctx->h_cnt, 0, C_COUNT * 4);
   if (hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking) ||
+      hipStreamCreateWithFlags(&ctx->cpu_stream, hipStreamNonBlocking) ||
+      hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming) ||
+      hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming) ||
       hipEventCreateWithFlags(&ctx->ev_sync, hipEventDisableTiming) ||
       hipEventCreateWithFlags(&ctx->ev_fill, hipEventDisableTiming) ||
       hipEventCreateWithFlags(&ctx->ev_ycpu, hipEventDisableTiming) ||
@@ -409,6 +469,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
 MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   if (!ctx) return MOE_EINVAL;
   if (ctx->copy_stream) hipStreamSynchronize(ctx->copy_stream);
+  if (ctx->cpu_stream) hipStreamSynchronize(ctx->cpu_stream);
   hipDeviceSynchronize();
   delete ctx->cpu;
   ctx->cpu = nullptr;
@@ -427,11 +488,13 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   for (void* p : host)
     if (p) hipHostFree(p);
   if (ctx->pool_owned && ctx->pool) hipHostFree(ctx->pool);
-  hipEvent_t evs[] = {ctx->ev_sync, ctx->ev_fill, ctx->ev_ycpu, ctx->ev_layer_copied[0], ctx->ev_layer_copied[1],
+  hipEvent_t evs[] = {ctx->ev_sync, ctx->ev_fill, ctx->ev_ycpu, ctx->ev_fork, ctx->ev_join, ctx->ev_layer_copied[0],
+                      ctx->ev_layer_copied[1],
                       ctx->ev_layer_done[0], ctx->ev_layer_done[1]};
   for (auto e : evs)
     if (e) hipEventDestroy(e);
   if (ctx->copy_stream) hipStreamDestroy(ctx->copy_stream);
+  if (ctx->cpu_stream) hipStreamDestroy(ctx->cpu_stream);
   delete ctx;
   return MOE_OK;
 }
@@ -591,12 +654,18 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   const bool profile = (ctx->cfg.flags & MOE_FLAG_PROFILE) != 0 && !captured;
   float* y_cpu = nullptr;
   const bool inputs = !fused && may_use_cpu(ctx, P);
-  // device fills: no host read of the step (its counts and profiled bytes stay on the device)
-  const bool devfill = (ctx->cfg.flags & MOE_FLAG_DEVICE_FILLS) && ctx->cfg.mode == MOE_MODE_OFFLOAD && !inputs;
+  // device fills: no host read of the step (its counts and profiled bytes stay on the
+  // device).  A step that may send work to the CPU does so only while the stream is being
+  // captured, running its branch as host nodes; eagerly it takes the host path (the
+  // calling thread reads the step, issues the fills and runs the branch itself, which
+  // measured faster than a host function competing with the enqueuing thread).
+  const bool devfill_flag = (ctx->cfg.flags & MOE_FLAG_DEVICE_FILLS) && !fused;
+  const bool async_cpu = devfill_flag && inputs && captured;
+  const bool devfill = devfill_flag && (!inputs || captured);
   if (devfill && !ctx->pool_dev) return fail(ctx, MOE_ENOPIN, "device fills need a mapped page-locked pool");
   if (captured && !fused && !devfill)
-    return fail(ctx, MOE_ESTATE, "a captured decode step reads nothing on the host: use FUSED mode or OFFLOAD "
-                                 "with MOE_FLAG_DEVICE_FILLS and n_slots >= 2*T*k");
+    return fail(ctx, MOE_ESTATE, "a captured decode step reads nothing on the host: use FUSED mode or a cached "
+                                 "mode with MOE_FLAG_DEVICE_FILLS");
   if ((!fused && !devfill) || (fused && profile)) {
     moe_status st = read_step(ctx, s, inputs, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
@@ -623,6 +692,11 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   d.d = ctx->dpair;
   d.y = y;
   const int max_groups = std::min(P, E);
+  if (async_cpu) {
+    moe_status st = enqueue_cpu_branch(ctx, x, topk_w, slot_idx, T, s);
+    if (st != MOE_OK) return st;
+    y_cpu = ctx->y_cpu_dev;
+  }
   if (devfill) {
     FillArgs f;
     f.cnt = ctx->cnt;
@@ -657,6 +731,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     moe_status st = run_cpu_branch(ctx, T, s, &y_cpu);
     if (st != MOE_OK) return st;
   }
+  if (async_cpu) HIPCHK(hipStreamWaitEvent(s, ctx->ev_join, 0));
   launch_decode_combine(d, y_cpu, s);
   HIPCHK(hipGetLastError());
   if (profile && devfill) {  // bytes are added on the device

@@ -57,6 +57,38 @@ def test_device_fills_match_oracle(fmt, T):
     assert st["fill_bytes"] == fills * h.S and st["cpu_experts"] == 0
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4"])
+@pytest.mark.parametrize("mode", [2, 3])
+def test_device_fill_steps_with_cpu_branch(fmt, mode):
+    """CPU and HYBRID modes with the device-fill flag, eagerly: such steps take the host
+    path; outputs, traces and counts as in the oracle (the captured form, with the CPU
+    branch as host nodes, is checked against this eager form in test_gpu_graph)."""
+    import routed_expert_ffn_02_amd as R
+    wl = FMT[fmt]
+    T = 2
+    bw = (25_000_000_000, 100_000_000_000)
+    n_slots = max(2, wl.n_keys // 3)
+    h = Harness(wl, mode, n_slots=n_slots, bw=bw, flags=R.MOE_FLAG_DEVICE_FILLS)
+    ref = oracle.ExpertCache(wl.n_layers, wl.n_experts, n_slots)
+    routes = {l: wl.synthetic_routing(8, l, T) for l in range(wl.n_layers)}
+    cpu = fills = 0
+    for step in range(8):
+        for layer in range(wl.n_layers):
+            idx = routes[layer][step]
+            x = wl.decode_activations(step, layer, T)
+            w = _gates(wl, step, layer, T)
+            y, slot, trace, cnt = h.decode(layer, x, idx, w)
+            r = ref.lookup(layer, idx, mode, *bw)
+            assert trace == r.trace and np.array_equal(slot, r.slot_idx), (step, layer)
+            assert row_rel_err(y, _expected(wl, layer, x, idx, w)) <= tol_for(wl), (step, layer)
+            cpu += sum(1 for t in r.trace if t[1] == R.MOE_KIND_CPU)
+            fills += sum(1 for t in r.trace if t[1] == R.MOE_KIND_FILL)
+    R.moe_sync(h.ctx)
+    st = R.moe_get_stats(h.ctx)
+    assert cpu > 0 and st["cpu_experts"] == cpu and st["fills"] == fills
+    assert st["cpu_ms"] > 0
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp4"])
 def test_device_fills_bit_identical_to_host_fills(fmt):
     """Same steps through both fill paths: identical bytes in every output."""

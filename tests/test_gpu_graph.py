@@ -52,20 +52,25 @@ def run_step(R, h, b, stream):
 
 
 @pytest.mark.parametrize("wl", [BF16, FP4, ROWS], ids=["bf16", "fp4", "rows"])
-@pytest.mark.parametrize("mode", ["offload_device_fills", "fused"])
+@pytest.mark.parametrize("mode", ["offload_device_fills", "hybrid_device_fills", "fused"])
 def test_captured_step_replays_like_eager(wl, mode):
     import routed_expert_ffn_02_amd as R
     import torch
     T = 1
+    bw = (0, 0)
     if mode == "fused":
         kw = dict(mode=R.MOE_MODE_FUSED)
         flags = 0
+    elif mode == "hybrid_device_fills":  # few slots: the CPU branch runs as host nodes
+        kw = dict(mode=R.MOE_MODE_HYBRID, n_slots=wl.top_k + 1)
+        flags = R.MOE_FLAG_DEVICE_FILLS
+        bw = (25_000_000_000, 100_000_000_000)
     else:
         kw = dict(mode=R.MOE_MODE_OFFLOAD, n_slots=2 * T * wl.top_k + 2)
         flags = R.MOE_FLAG_DEVICE_FILLS
-    eager = Harness(wl, kw["mode"], n_slots=kw.get("n_slots"), flags=flags)
+    eager = Harness(wl, kw["mode"], n_slots=kw.get("n_slots"), flags=flags, bw=bw)
     # profiling is requested on the captured context: captured launches must skip it
-    graph = Harness(wl, kw["mode"], n_slots=kw.get("n_slots"), flags=flags | R.MOE_FLAG_PROFILE)
+    graph = Harness(wl, kw["mode"], n_slots=kw.get("n_slots"), flags=flags | R.MOE_FLAG_PROFILE, bw=bw)
     be, bg = StepBuffers(wl, T), StepBuffers(wl, T)
     # step 0 eagerly on both
     be.load(wl, 0)
@@ -92,6 +97,9 @@ def test_captured_step_replays_like_eager(wl, mode):
     sg, se = R.moe_get_stats(graph.ctx), R.moe_get_stats(eager.ctx)
     if mode != "fused":
         assert sg["fills"] == se["fills"] > 0 and sg["hits"] == se["hits"] and sg["lookups"] == se["lookups"]
+        assert sg["cpu_experts"] == se["cpu_experts"]
+        if mode == "hybrid_device_fills":
+            assert se["cpu_experts"] > 0
     sa, ka, stamp_a, ca = graph.snapshot()
     sb, kb, stamp_b, cb = eager.snapshot()
     assert np.array_equal(sa, sb) and np.array_equal(ka, kb) and np.array_equal(stamp_a, stamp_b) and ca == cb
