@@ -194,6 +194,7 @@ __device__ __forceinline__ void fp4x32_to_f16x2(const uint4& q, f16x2* o) {
 // loads have been issued.  Native vectors keep the registers out of memory.
 typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2n __attribute__((ext_vector_type(2)));
+typedef float f32x4n __attribute__((ext_vector_type(4)));
 
 template <int AFMT, int EPC>
 struct XRaw {
@@ -370,6 +371,149 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 dot-product paths: bf16 activations against bf16 or FP4 weights.
+//
+// v_dot2_f32_bf16 multiplies two bf16 pairs exactly and accumulates in fp32, so the
+// weights meet the activations as they are stored: bf16 weight words directly, FP4
+// codes after the exact scaled convert to bf16 pairs (unit scale), activations as raw
+// bf16 words with no conversion.  Per 16-byte weight chunk that is 4 (bf16) or 32 (FP4)
+// VALU instructions, against 16 and 34 on the fp32 / f16 paths, which matters because
+// the arithmetic of a wavefront's last rows runs after its last bytes arrive.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot_bf16x2(uint32_t w, uint32_t x, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), c, false);
+}
+
+// Dot product of one 16-byte weight chunk with the matching activation words (bf16
+// pairs: 16 for the 32 elements of an FP4 chunk, 4 for the 8 of a bf16 chunk).
+template <int WFMT>
+__device__ __forceinline__ float chunk_dot_bf16(const u32x4n& q, const uint32_t* xw) {
+  float p = 0.f;
+  if constexpr (WFMT == MOE_WFMT_FP4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // byte j of word i holds elements 8i + 2j (low nibble) and 8i + 2j + 1
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 0)), xw[4 * i + 0], p);
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 1)), xw[4 * i + 1], p);
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 2)), xw[4 * i + 2], p);
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 3)), xw[4 * i + 3], p);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p = dot_bf16x2(q[i], xw[i], p);
+  }
+  return p;
+}
+
+// Activation words of token t for lane chunk c (XQ 16-byte loads: the chunk's 32 or 8
+// bf16 elements).
+template <int XQ>
+__device__ __forceinline__ void load_x_words(const void* x, int H, int t, int c, u32x4n* xq) {
+  const u32x4n* p = reinterpret_cast<const u32x4n*>(reinterpret_cast<const uint16_t*>(x) + (size_t)t * H) + (size_t)c * XQ;
+#pragma unroll
+  for (int i = 0; i < XQ; ++i) xq[i] = p[i];
+}
+
+// Phase 1, bf16 dot path (H a whole number of wavefront-wide chunks, P <= 64): each
+// wavefront owns RW consecutive (gate, up) row pairs of one expert; all its loads are
+// issued before any is used, activations first (loads return in issue order), and the
+// RW results of a token leave in one store from lanes 0..RW-1.
+template <int WFMT, int CPL, int RW, int MAXT>
+__global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
+  constexpr int XQ = (WFMT == MOE_WFMT_FP4) ? 4 : 1;
+  const int g = blockIdx.y;
+  // issued with the count (grp_slot has E >= gridDim.y entries, so the read is in bounds
+  // even for a group beyond the count, whose value is then unused)
+  const int slot = a.grp_slot[g];
+  const int H = a.H, I = a.I;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  u32x4n xq[MAXT][CPL][XQ];
+  int pair[MAXT];
+  int n = 0;
+  if constexpr (MAXT == 1) {
+    // one token: its activation chunks need no other load, so they go first; the
+    // group's single pair (needed only for the store) comes with the slot
+    pair[0] = a.grp_pair0[g];
+    n = 1;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) load_x_words<XQ>(a.x, H, 0, lane + 64 * c, xq[0][c]);
+  }
+  if (g >= a.cnt[C_NGRP]) return;
+  const int row0 = (blockIdx.x * 4 + wave) * RW;
+  if (row0 >= I) return;
+  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  u32x4n qg[RW][CPL], qu[RW][CPL];
+  uint16_t sg[RW][CPL], su[RW][CPL];  // FP4 block scales (raw bf16)
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = min(row0 + r, I - 1);
+    const u32x4n* gp = reinterpret_cast<const u32x4n*>(tensor_row<WFMT>(rec, 0, row, H, I));
+    const u32x4n* up = reinterpret_cast<const u32x4n*>(tensor_row<WFMT>(rec, 1, row, H, I));
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      qg[r][c] = gp[lane + 64 * c];
+      qu[r][c] = up[lane + 64 * c];
+      if constexpr (WFMT == MOE_WFMT_FP4) {
+        sg[r][c] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 0, row, H, I))[lane + 64 * c];
+        su[r][c] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 1, row, H, I))[lane + 64 * c];
+      }
+    }
+  }
+  if constexpr (MAXT > 1) {
+    uint64_t m = group_mask(a, g);
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      pair[t] = m ? __builtin_ctzll(m) : 0;
+      n += (m != 0);
+      m &= m - 1;
+    }
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      if (t < n)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) load_x_words<XQ>(a.x, H, pair[t] / a.k, lane + 64 * c, xq[t][c]);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before any use
+  float hv[RW][MAXT];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      hv[r][t] = 0.f;
+      if (t < n) {
+        float accg = 0.f, accu = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          uint32_t xw[4 * XQ];
+#pragma unroll
+          for (int i = 0; i < 4 * XQ; ++i) xw[i] = xq[t][c][i / 4][i % 4];
+          const float pg = chunk_dot_bf16<WFMT>(qg[r][c], xw);
+          const float pu = chunk_dot_bf16<WFMT>(qu[r][c], xw);
+          if constexpr (WFMT == MOE_WFMT_FP4) {
+            accg += bf16_to_f32(sg[r][c]) * pg;
+            accu += bf16_to_f32(su[r][c]) * pu;
+          } else {
+            accg += pg;
+            accu += pu;
+          }
+        }
+        hv[r][t] = silu(wave_sum(accg)) * wave_sum(accu);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t < n) {
+      float v = hv[0][t];
+#pragma unroll
+      for (int r = 1; r < RW; ++r) v = (lane == r) ? hv[r][t] : v;
+      if (lane < RW && row0 + lane < I) a.h[(int64_t)pair[t] * I + row0 + lane] = v;
+    }
+  }
+}
+
 // Phase 1, generic shapes: one row pair per wavefront, activations staged in LDS.
 template <int WFMT, int AFMT>
 __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
@@ -509,6 +653,96 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
   }
 }
 
+// Phase 2, bf16 dot path (I = 64 chunks per row, P <= 64, bf16 or FP4 weights): each
+// wavefront owns R2 rows of W_down of one expert.  The fp32 activated rows h are
+// rounded to bf16 once per wavefront (the 16-bit operand rounding the prefill GEMM
+// applies to the same values) and meet the weights in v_dot2_f32_bf16.
+template <int WFMT, int MAXT>
+__global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
+  constexpr int R2 = kP2RowsPerWave;
+  constexpr int EPC = (WFMT == MOE_WFMT_FP4) ? 32 : 8;
+  const int g = blockIdx.y;
+  const int slot = a.grp_slot[g];  // issued with the count (see phase 1)
+  const int pair0 = (MAXT == 1) ? a.grp_pair0[g] : 0;
+  if (g >= a.cnt[C_NGRP]) return;
+  const int H = a.H, I = a.I;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = blockIdx.x * kP2Rows + wave * R2;
+  if (r0 >= H) return;
+  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  // one token: the group's activated row is requested before the weights
+  f32x4n hq[MAXT][EPC / 4];
+  if constexpr (MAXT == 1) {
+    const f32x4n* hp = reinterpret_cast<const f32x4n*>(a.h + (int64_t)pair0 * I + lane * EPC);
+#pragma unroll
+    for (int i = 0; i < EPC / 4; ++i) hq[0][i] = hp[i];
+  }
+  uint16_t scr[R2];
+  if constexpr (WFMT == MOE_WFMT_FP4) {
+#pragma unroll
+    for (int r = 0; r < R2; ++r)
+      scr[r] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
+  }
+  u32x4n q[R2];
+#pragma unroll
+  for (int r = 0; r < R2; ++r)
+    q[r] = reinterpret_cast<const u32x4n*>(tensor_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
+  int pair[MAXT];
+  int n = 0;
+  if constexpr (MAXT == 1) {
+    pair[0] = pair0;
+    n = 1;
+  } else {
+    uint64_t m = group_mask(a, g);
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      pair[t] = m ? __builtin_ctzll(m) : 0;
+      n += (m != 0);
+      m &= m - 1;
+    }
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      if (t < n) {
+        const f32x4n* hp = reinterpret_cast<const f32x4n*>(a.h + (int64_t)pair[t] * I + lane * EPC);
+#pragma unroll
+        for (int i = 0; i < EPC / 4; ++i) hq[t][i] = hp[i];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before any use
+  uint32_t hw[MAXT][EPC / 2];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+    if (t < n)
+#pragma unroll
+      for (int i = 0; i < EPC / 2; ++i) {
+        const bf16x2 b = {(__bf16)hq[t][i / 2][2 * (i % 2)], (__bf16)hq[t][i / 2][2 * (i % 2) + 1]};
+        hw[t][i] = __builtin_bit_cast(uint32_t, b);
+      }
+  float out[R2][MAXT];
+#pragma unroll
+  for (int r = 0; r < R2; ++r) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      out[r][t] = 0.f;
+      if (t < n) {
+        float p = chunk_dot_bf16<WFMT>(q[r], hw[t]);
+        if constexpr (WFMT == MOE_WFMT_FP4) p *= bf16_to_f32(scr[r]);
+        out[r][t] = wave_sum(p);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t < n) {
+      float v = out[0][t];
+#pragma unroll
+      for (int r = 1; r < R2; ++r) v = (lane == r) ? out[r][t] : v;
+      if (lane < R2 && r0 + lane < H) a.d[(int64_t)pair[t] * H + r0 + lane] = v;
+    }
+  }
+}
+
 // Phase 2, generic shapes.
 template <int WFMT, int MAXT>
 __global__ __launch_bounds__(256) void dec_phase2(DecodeArgs a) {
@@ -598,10 +832,17 @@ static int lane_chunks(int wfmt, int cols) {
 
 template <int W, int A, int CPL, int MAXT>
 static void p1_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
-  // about 16 in-flight 16-byte weight chunks per lane; wide FP4 rows unpack to many registers
-  constexpr int RW = (W == MOE_WFMT_FP4 && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : 8);
-  dim3 grid((a.I + 4 * RW - 1) / (4 * RW), max_groups);
-  launch_timed(dec_phase1_fast<W, A, CPL, RW, MAXT>, grid, dim3(256), 0, s, tm, a);
+  if constexpr (A == MOE_AFMT_BF16 && W != MOE_WFMT_F32) {
+    // bf16 dot path: 8 KB of weights per wavefront (CPL * RW = 4 lane chunks per tensor)
+    constexpr int RW = 4 / CPL;
+    dim3 grid((a.I + 4 * RW - 1) / (4 * RW), max_groups);
+    launch_timed(dec_phase1_bf<W, CPL, RW, MAXT>, grid, dim3(256), 0, s, tm, a);
+  } else {
+    // about 16 in-flight 16-byte weight chunks per lane; wide FP4 rows unpack to many registers
+    constexpr int RW = (W == MOE_WFMT_FP4 && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : 8);
+    dim3 grid((a.I + 4 * RW - 1) / (4 * RW), max_groups);
+    launch_timed(dec_phase1_fast<W, A, CPL, RW, MAXT>, grid, dim3(256), 0, s, tm, a);
+  }
 }
 
 template <int W, int A, int MAXT>
@@ -609,7 +850,9 @@ static bool p1_try_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timi
   switch (lane_chunks(W, a.H)) {
     case 1: p1_fast<W, A, 1, MAXT>(a, max_groups, s, tm); return true;
     case 2: p1_fast<W, A, 2, MAXT>(a, max_groups, s, tm); return true;
-    case 4: p1_fast<W, A, 4, MAXT>(a, max_groups, s, tm); return true;
+    case 4:
+      if constexpr (W == MOE_WFMT_FP4 && MAXT > 1) return false;  // 8 KB of activations per token and lane
+      else { p1_fast<W, A, 4, MAXT>(a, max_groups, s, tm); return true; }
     default: return false;
   }
 }
@@ -620,7 +863,8 @@ static void p1_dispatch(const DecodeArgs& a, int max_groups, size_t lds, hipStre
   bool done = false;
   if (small && a.T <= 1) {
     done = p1_try_fast<W, A, 1>(a, max_groups, s, tm);
-  } else if constexpr (W != MOE_WFMT_FP4) {  // FP4 rows with 4 tokens exceed the register file
+  } else if constexpr (W != MOE_WFMT_FP4 || A == MOE_AFMT_BF16) {
+    // (FP4 rows with 4 fp32-activation tokens exceed the register file)
     if (small && a.T <= 4) done = p1_try_fast<W, A, 4>(a, max_groups, s, tm);
   }
   if (!done) {
@@ -645,8 +889,12 @@ void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_group
 template <int W, int M>
 static void p2_dispatch(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
   dim3 grid(decode_phase2_rowblocks(a.H), max_groups);
-  if (lane_chunks(W, a.I) == 1 && a.T * a.k <= 64) launch_timed(dec_phase2_fast<W, M>, grid, dim3(256), 0, s, tm, a);
-  else launch_timed(dec_phase2<W, M>, grid, dim3(256), 0, s, tm, a);
+  if (lane_chunks(W, a.I) == 1 && a.T * a.k <= 64) {
+    if constexpr (W != MOE_WFMT_F32 && M <= 4) launch_timed(dec_phase2_bf<W, M>, grid, dim3(256), 0, s, tm, a);
+    else launch_timed(dec_phase2_fast<W, M>, grid, dim3(256), 0, s, tm, a);
+  } else {
+    launch_timed(dec_phase2<W, M>, grid, dim3(256), 0, s, tm, a);
+  }
 }
 
 template <int W>
