@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--alias-records", type=int, default=0,
                     help="back keys by key %% R records (smaller host pool; same transfer sizes)")
+    ap.add_argument("--placement", action="store_true",
+                    help="only replay the decode routing trace against the placement policies (miss rate vs "
+                         "cache capacity) and print one JSON line of curves")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -115,6 +118,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.placement:
+        placement_curves(args)
         return
 
     import torch
@@ -337,6 +343,78 @@ def main():
     }
     print(json.dumps(out), flush=True)
     R.moe_destroy(ctx)
+
+
+def placement_curves(args):
+    """Decode-time expert miss rate against cache capacity for the placement policies
+    the pages compare (global LRU, prefill-time placement, routing-blind static split)
+    plus the calibrated pinned set with per-layer LRU rings, all replayed by the
+    library's host engine on one routing trace that the library's router produces on
+    the GPU: `--steps` decode tokens with the benchmark's Zipf and previous-token
+    locality bias from a cold start, and the prompt routing (Zipf bias only) as the
+    calibration trace.  Capacities are fractions of the whole expert pool."""
+    import torch
+    import routed_expert_ffn_02_amd as R
+    import workloads as W
+
+    wl = W.A3B_DECODE if args.config == "a3b" else W.DSV4
+    L, E, k, H = wl.n_layers, wl.n_experts, wl.top_k, wl.hidden
+    prompt = W.A3B_PREFILL.prefill_tokens if args.config == "a3b" else wl.prefill_tokens
+    dev = torch.device("cuda:0")
+    cfg = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, prompt, R.MOE_MODE_OFFLOAD)
+    ctx = R.moe_create(cfg)
+    router = torch.from_numpy(np.stack([wl.router_weight(l) for l in range(L)])).to(dev)
+    R.moe_bind(ctx, router, None, 0, 0)
+    zipf = torch.from_numpy(np.stack([wl.zipf_bias(l) for l in range(L)])).to(dev)
+    T, steps = wl.tokens, args.steps
+    idx = torch.zeros((steps, L, T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    bias = torch.empty((T, E), dtype=torch.float32, device=dev)
+    bonus = torch.full((T, k), float(wl.prev_bonus), dtype=torch.float32, device=dev)
+    t0 = time.time()
+    for s in range(steps):
+        xs = torch.from_numpy(np.stack([wl.decode_activations(s, l, T) for l in range(L)]).view(np.int16)).to(dev)
+        for l in range(L):
+            bias.copy_(zipf[l].expand(T, E))
+            if s > 0 and wl.prev_bonus:
+                bias.scatter_add_(1, idx[s - 1, l].long(), bonus)
+            R.moe_route(ctx, l, xs[l], T, bias, None, idx[s, l], w)
+    cal = torch.empty((prompt, L, k), dtype=torch.int32, device=dev)
+    pidx = torch.empty((prompt, k), dtype=torch.int32, device=dev)
+    pw = torch.empty((prompt, k), dtype=torch.float32, device=dev)
+    pbias = torch.empty((prompt, E), dtype=torch.float32, device=dev)
+    for l in range(L):
+        x = torch.from_numpy(wl.prefill_activations(l, prompt).view(np.int16)).to(dev)
+        pbias.copy_(zipf[l].expand(prompt, E))
+        R.moe_route(ctx, l, x, prompt, pbias, None, pidx, pw)
+        cal[:, l] = pidx
+    torch.cuda.synchronize()
+    decode = idx.reshape(steps, L, T * k).cpu().numpy()
+    calib = cal.cpu().numpy()
+    log(f"routing traces: {steps} decode steps, {prompt} prompt tokens in {time.time() - t0:.1f}s")
+    R.moe_destroy(ctx)
+
+    fracs = [0.02, 0.05, 0.08, 0.11, 0.125, 0.154, 0.2, 0.25, 0.3, 0.37, 0.5, 0.75, 1.0]
+    policies = [("lru", R.MOE_PLACE_LRU), ("prefill_update", R.MOE_PLACE_PREFILL),
+                ("static_split", R.MOE_PLACE_STATIC), ("pinned_ring", R.MOE_PLACE_PINNED_RING)]
+    curves = {name: [] for name, _ in policies}
+    t1 = time.perf_counter()
+    replays = 0
+    for f in fracs:
+        cap = int(round(f * L * E))
+        for name, pol in policies:
+            ring = min(k, cap // L) if pol == R.MOE_PLACE_PINNED_RING else 0
+            r = R.moe_placement_replay(L, E, pol, cap, decode, calib, ring_per_layer=ring)
+            curves[name].append(round(r["misses"] / max(1, r["keys"]), 4))
+            replays += 1
+    rel = time.perf_counter() - t1
+    out = {"placement_replay": f"{wl.name}: L={L} E={E} k={k}, batch {T}, {steps} decode steps from a cold cache, "
+                               f"{prompt}-token prompt as the calibration trace",
+           "capacity_frac_of_pool": fracs, "capacity_slots": [int(round(f * L * E)) for f in fracs],
+           "miss_rate": curves, "pinned_ring_slots_per_layer": k,
+           "replay_ms_per_policy": round(rel * 1e3 / replays, 2),
+           "reads_per_replay": int(decode.size)}
+    print(json.dumps(out), flush=True)
 
 
 def oracle_baseline(wl, seconds):

@@ -317,6 +317,52 @@ MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream);
 MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);
 MOE_API moe_status moe_reset_stats(moe_ctx* ctx);
 
+/* ------------------------------------------------------------------ placement replay */
+
+/* GPU placement policies compared on identical routing traces ([FT-KR] "무엇이 성능을 만들었나",
+ * expert-locality paragraph; [FT-CN] Figure 4b; the Luce Spark post, "calibrated placement" and
+ * "bounded async cache"). */
+typedef enum {
+  MOE_PLACE_LRU = 0,         /* the shared cache of this library, offload mode, cold start */
+  MOE_PLACE_PREFILL = 1,     /* the C keys the prompt routes most, fixed for the decode */
+  MOE_PLACE_STATIC = 2,      /* routing-blind: whole layers from the top, then experts 0.. below */
+  MOE_PLACE_PINNED_RING = 3  /* C - L*R keys pinned by prompt frequency + an R-slot LRU ring per layer */
+} moe_place_policy;
+
+typedef struct {
+  int32_t n_layers, n_experts; /* L, E */
+  int32_t pairs;               /* routed (token, rank) pairs per layer step of the decode trace (T*k) */
+  int32_t policy;              /* moe_place_policy */
+  int32_t capacity;            /* GPU expert slots C, 0 <= C <= L*E */
+  int32_t ring_per_layer;      /* PINNED_RING: R >= 0 with L*R <= C; ignored otherwise */
+} moe_replay_config;
+
+typedef struct {
+  uint64_t keys;    /* distinct routed keys summed over every (step, layer) */
+  uint64_t misses;  /* of those, keys not resident when their layer step began */
+  uint64_t reads;   /* routed pairs (steps * L * pairs) */
+} moe_replay_result;
+
+/*
+ * Replay a decode routing trace against one placement policy on the host (no GPU).  A layer
+ * step's pairs are deduplicated in first-appearance order (token-major, then rank); a key misses
+ * when it is not resident as the step begins.  LRU admits every miss exactly as
+ * expert_cache_lookup does in MOE_MODE_OFFLOAD (victims: least recently used slots holding no
+ * hit of the step; empty slots first, lowest slot first); PREFILL and STATIC never admit;
+ * PINNED_RING admits an unpinned miss into its layer's ring, evicting the least recently used
+ * entry that is not a hit of the step (none: not admitted).  Frequencies for PREFILL and
+ * PINNED_RING count every routed pair of the calibration trace, ties to the lower key.
+ *   decode     [steps][L][pairs] expert ids (host memory, caller-owned)
+ *   calib      [calib_tokens][L][calib_k] expert ids of the prompt (PREFILL, PINNED_RING; else
+ *              may be NULL)
+ *   miss_out   NULL, or [steps][L][pairs] bytes: 1 where the pair's key missed (every pair of a
+ *              missed key is marked), 0 otherwise
+ * MOE_EINVAL for shapes, ids or capacities out of range.  Pure host function.
+ */
+MOE_API moe_status moe_placement_replay(const moe_replay_config* cfg, const int32_t* decode, int32_t steps,
+                                        const int32_t* calib, int32_t calib_tokens, int32_t calib_k,
+                                        uint8_t* miss_out, moe_replay_result* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,8 @@ from .qstar import MODE_FUSED, MODE_OFFLOAD, MODE_CPU, MODE_HYBRID, qstar_split,
 from .cache import (ExpertCache, NaiveListCache, LookupResult, KIND_HIT, KIND_FILL, KIND_CPU, KIND_BUF)
 from .ffn import silu, expert_ffn, moe_combine, moe_layer_dense
 from .layer import OracleMoE
+from .placement import (POLICY_LRU, POLICY_PREFILL, POLICY_STATIC, POLICY_PINNED_RING, replay as placement_replay,
+                        routing_counts, top_keys, static_resident)
 
 __all__ = [
     "bf16_to_f64", "e2m1_decode", "dequant_fp4", "expert_weights_f64",
@@ -36,4 +38,6 @@ __all__ = [
     "MODE_FUSED", "MODE_OFFLOAD", "MODE_CPU", "MODE_HYBRID", "qstar_split", "qstar_real",
     "ExpertCache", "NaiveListCache", "LookupResult", "KIND_HIT", "KIND_FILL", "KIND_CPU", "KIND_BUF",
     "silu", "expert_ffn", "moe_combine", "moe_layer_dense", "OracleMoE",
+    "POLICY_LRU", "POLICY_PREFILL", "POLICY_STATIC", "POLICY_PINNED_RING", "placement_replay",
+    "routing_counts", "top_keys", "static_resident",
 ]

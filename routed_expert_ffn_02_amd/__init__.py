@@ -58,6 +58,18 @@ class moe_stats(ctypes.Structure):
         ("gemm_flops", ctypes.c_double), ("copy_ms", ctypes.c_double), ("copy_bytes", ctypes.c_uint64),
         ("cpu_ms", ctypes.c_double)]
 
+
+MOE_PLACE_LRU, MOE_PLACE_PREFILL, MOE_PLACE_STATIC, MOE_PLACE_PINNED_RING = 0, 1, 2, 3
+
+
+class moe_replay_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "n_experts", "pairs", "policy", "capacity",
+                                              "ring_per_layer")]
+
+
+class moe_replay_result(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("keys", "misses", "reads")]
+
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
@@ -94,6 +106,8 @@ def _load():
         "moe_get_stats": (I32, [P, ctypes.POINTER(moe_stats)]),
         "moe_reset_stats": (I32, [P]),
         "moe_sync": (I32, [P, VP]),
+        "moe_placement_replay": (I32, [ctypes.POINTER(moe_replay_config), VP, I32, VP, I32, I32, VP,
+                                       ctypes.POINTER(moe_replay_result)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -244,6 +258,30 @@ def expert_cache_resize(ctx: Ctx, new_n_slots, new_arena=None, new_arena_bytes=0
 
 def qstar_split(m: int, bw_pcie: int, bw_host: int, mode: int, evictable: int) -> int:
     return int(lib.qstar_split(m, bw_pcie, bw_host, mode, evictable))
+
+
+def moe_placement_replay(n_layers: int, n_experts: int, policy: int, capacity: int, decode, calib=None,
+                         ring_per_layer: int = 0, want_miss: bool = False):
+    """Replay a host routing trace (decode [steps, L, T*k], calib [tokens, L, k], int32
+    NumPy arrays) against one placement policy.  Returns a dict with keys, misses, reads
+    and, with want_miss, the per-pair miss flags [steps, L, T*k] (uint8)."""
+    import numpy as np
+    dec = np.ascontiguousarray(decode, dtype=np.int32)
+    steps, L, pairs = dec.shape
+    cal = None if calib is None else np.ascontiguousarray(calib, dtype=np.int32)
+    cfg = moe_replay_config(n_layers, n_experts, pairs, policy, capacity, ring_per_layer)
+    miss = np.zeros(dec.shape, np.uint8) if want_miss else None
+    res = moe_replay_result()
+    st = lib.moe_placement_replay(ctypes.byref(cfg), dec.ctypes.data, steps,
+                                  None if cal is None else cal.ctypes.data,
+                                  0 if cal is None else cal.shape[0], 1 if cal is None else cal.shape[2],
+                                  None if miss is None else miss.ctypes.data, ctypes.byref(res))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_placement_replay", "invalid shapes, ids or capacity")
+    out = {"keys": res.keys, "misses": res.misses, "reads": res.reads}
+    if want_miss:
+        out["miss"] = miss
+    return out
 
 
 def moe_bench_bw(ctx: Ctx):
