@@ -58,6 +58,9 @@ class moe_stats(ctypes.Structure):
         ("gemm_flops", ctypes.c_double), ("copy_ms", ctypes.c_double), ("copy_bytes", ctypes.c_uint64),
         ("cpu_ms", ctypes.c_double)]
 
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
 
 MOE_PLACE_LRU, MOE_PLACE_PREFILL, MOE_PLACE_STATIC, MOE_PLACE_PINNED_RING = 0, 1, 2, 3
 
@@ -69,9 +72,6 @@ class moe_replay_config(ctypes.Structure):
 
 class moe_replay_result(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("keys", "misses", "reads")]
-
-    def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 def _load():

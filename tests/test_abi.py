@@ -48,6 +48,15 @@ def test_record_bytes_match_pool_format():
     assert W.A3B_DECODE.record_bytes == 6 * 2 ** 20 and W.DSV4.record_bytes == 14155776
 
 
+def test_binding_structs_marshal():
+    """Every structure the binding returns converts to a dict of its fields."""
+    import routed_expert_ffn_02_amd as R
+    for cls in (R.moe_stats, R.moe_config, R.moe_trace_rec):
+        d = cls().as_dict() if hasattr(cls, "as_dict") else None
+        if cls is R.moe_stats:
+            assert d is not None and set(d) == {n for n, _ in cls._fields_}
+
+
 def test_struct_layouts():
     import routed_expert_ffn_02_amd as R
     assert ctypes.sizeof(R.moe_config) == 64
