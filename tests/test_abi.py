@@ -48,13 +48,11 @@ def test_record_bytes_match_pool_format():
     assert W.A3B_DECODE.record_bytes == 6 * 2 ** 20 and W.DSV4.record_bytes == 14155776
 
 
-def test_binding_structs_marshal():
-    """Every structure the binding returns converts to a dict of its fields."""
+def test_stats_struct_marshals():
+    """moe_get_stats returns the stats structure as a dict of all its fields."""
     import routed_expert_ffn_02_amd as R
-    for cls in (R.moe_stats, R.moe_config, R.moe_trace_rec):
-        d = cls().as_dict() if hasattr(cls, "as_dict") else None
-        if cls is R.moe_stats:
-            assert d is not None and set(d) == {n for n, _ in cls._fields_}
+    d = R.moe_stats().as_dict()
+    assert set(d) == {n for n, _ in R.moe_stats._fields_} and d["hits"] == 0
 
 
 def test_struct_layouts():
