@@ -31,7 +31,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--config", default="a3b", choices=["a3b", "dsv4"])
+    ap.add_argument("--config", default="a3b", choices=["a3b", "dsv4", "dsv4mx"],
+                    help="a3b: 35B-A3B shape, bf16; dsv4: DeepSeek-V4-Flash shape, e2m1 + bf16 scales; "
+                         "dsv4mx: the same shape as MXFP4 (E8M0 scales)")
     ap.add_argument("--mode", default="offload", choices=["offload", "hybrid", "fused"])
     ap.add_argument("--host-fills", action="store_true",
                     help="issue decode fills from the host (read the step's fill list, DMA copies) "
@@ -127,11 +129,11 @@ def main():
     import routed_expert_ffn_02_amd as R
     import workloads as W
 
-    wl = W.A3B_DECODE if args.config == "a3b" else W.DSV4
+    wl = {"a3b": W.A3B_DECODE, "dsv4": W.DSV4, "dsv4mx": W.DSV4_MX}[args.config]
     # The DSV4-shaped pool (155.8 GB) exceeds what the host lets us page-lock; by default
     # its keys are backed by key % 4500 records (63.7 GB): same record size and access
     # pattern, aliased contents (the oracle uses the same mapping).
-    alias = args.alias_records or (4500 if args.config == "dsv4" else 0)
+    alias = args.alias_records or (4500 if args.config != "a3b" else 0)
     if alias:
         wl = wl.with_(alias_records=alias)
     mode = {"offload": R.MOE_MODE_OFFLOAD, "hybrid": R.MOE_MODE_HYBRID, "fused": R.MOE_MODE_FUSED}[args.mode]
@@ -325,7 +327,9 @@ def main():
         "value": head_tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": head_ms, "higher_is_better": True, "scaling": "weak",
         "headline_leg": "graph-replayed decode step" if graph else "eager decode step",
-        "vs_baseline": None, "dtype": "bf16" if wl.wfmt == W.WFMT_BF16 else "fp4(e2m1)+bf16 scale",
+        "vs_baseline": None,
+        "dtype": {W.WFMT_BF16: "bf16", W.WFMT_FP4: "fp4(e2m1)+bf16 scale", W.WFMT_MXFP4: "mxfp4(e2m1)+e8m0 scale",
+                  W.WFMT_F32: "f32"}[wl.wfmt],
         "data": "synthetic (seeded; random-init weights of the stated shape)",
         "config": {"workload": f"{wl.name}: L={L} E={E} k={k} H={H} I={wl.inter}, batch {T}, "
                                f"{n_slots}-slot shared cache, {args.mode}, cold start",
@@ -357,7 +361,7 @@ def placement_curves(args):
     import routed_expert_ffn_02_amd as R
     import workloads as W
 
-    wl = W.A3B_DECODE if args.config == "a3b" else W.DSV4
+    wl = {"a3b": W.A3B_DECODE, "dsv4": W.DSV4, "dsv4mx": W.DSV4_MX}[args.config]
     L, E, k, H = wl.n_layers, wl.n_experts, wl.top_k, wl.hidden
     prompt = W.A3B_PREFILL.prefill_tokens if args.config == "a3b" else wl.prefill_tokens
     dev = torch.device("cuda:0")

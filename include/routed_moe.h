@@ -60,7 +60,10 @@ typedef enum {
 typedef enum {
   MOE_WFMT_F32 = 0,  /* fp32 gate | up | down */
   MOE_WFMT_BF16 = 1, /* bf16 gate | up | down */
-  MOE_WFMT_FP4 = 2   /* e2m1 codes + one bf16 scale per 32 elements along each row */
+  MOE_WFMT_FP4 = 2,  /* e2m1 codes + one bf16 scale per 32 elements along each row */
+  MOE_WFMT_MXFP4 = 3 /* e2m1 codes + one E8M0 scale byte per 32 elements (the MX format of the
+                        pages' DeepSeek-V4-Flash experts, [FT-KR] "실험 환경"); hidden and inter
+                        must be multiples of 256 */
 } moe_wfmt;
 
 typedef enum { MOE_AFMT_F32 = 0, MOE_AFMT_BF16 = 1 } moe_afmt;
@@ -138,6 +141,8 @@ MOE_API const char* moe_last_error(const moe_ctx* ctx);
  *                up scales | down scales]; element 2i of a row is the low nibble of byte i;
  *                one scale per 32 consecutive elements of a row (the reduction dimension);
  *                w = e2m1(code) * scale.
+ *   MXFP4:      as FP4 with one scale byte e per block (E8M0, bias 127): w = e2m1(code) * 2^(e-127);
+ *                e must lie in 1..254.
  * Returns -1 for an invalid config.  Pure host function.
  */
 MOE_API int64_t moe_record_bytes(const moe_config* cfg);

@@ -23,7 +23,7 @@ Sources (cited by page title and section in each function):
 Parity status of each function is stated in its docstring; readings of points
 the pages leave open are listed in the repository's design notes.
 """
-from .formats import bf16_to_f64, e2m1_decode, dequant_fp4, expert_weights_f64
+from .formats import bf16_to_f64, e2m1_decode, dequant_fp4, e8m0_decode, dequant_mxfp4, expert_weights_f64
 from .router import router_logits, topk_order, route
 from .qstar import MODE_FUSED, MODE_OFFLOAD, MODE_CPU, MODE_HYBRID, qstar_split, qstar_real
 from .cache import (ExpertCache, NaiveListCache, LookupResult, KIND_HIT, KIND_FILL, KIND_CPU, KIND_BUF)
@@ -33,7 +33,7 @@ from .placement import (POLICY_LRU, POLICY_PREFILL, POLICY_STATIC, POLICY_PINNED
                         routing_counts, top_keys, static_resident)
 
 __all__ = [
-    "bf16_to_f64", "e2m1_decode", "dequant_fp4", "expert_weights_f64",
+    "bf16_to_f64", "e2m1_decode", "dequant_fp4", "e8m0_decode", "dequant_mxfp4", "expert_weights_f64",
     "router_logits", "topk_order", "route",
     "MODE_FUSED", "MODE_OFFLOAD", "MODE_CPU", "MODE_HYBRID", "qstar_split", "qstar_real",
     "ExpertCache", "NaiveListCache", "LookupResult", "KIND_HIT", "KIND_FILL", "KIND_CPU", "KIND_BUF",

@@ -8,7 +8,11 @@ exponent 0 is subnormal with value 0.5 * mantissa.  The DeepSeek-V4-Flash
 experts on the pages are MXFP4 ([FT-KR] "실험 환경": routed experts quantised
 to MXFP4); the workload stores one bf16 scale per 32 consecutive elements of a
 row (the reduction dimension), a superset of the power-of-two MX scale.
-Parity: pinned by the exhaustive 16-code table test and by round trips.
+MXFP4 keeps the MX scale itself: one E8M0 byte e per 32-element block, an
+exponent with bias 127 and no sign or mantissa, so the scale is 2^(e - 127)
+(OCP Microscaling spec, "E8M0"; e = 255 encodes NaN).
+Parity: pinned by the exhaustive 16-code table test, by round trips, and MXFP4
+by equality with the bf16-scale path fed the same powers of two as bf16 bits.
 """
 import numpy as np
 
@@ -43,6 +47,23 @@ def dequant_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return vals * np.repeat(sc, 32, axis=1)
 
 
+def e8m0_decode(e: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> float64: 2^(e - 127); 255 is NaN."""
+    e = np.asarray(e).astype(np.int64)
+    return np.where(e == 255, np.nan, np.exp2((e - 127).astype(np.float64)))
+
+
+def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Packed codes [rows, cols/2] (element 2i in the low nibble of byte i) and E8M0 scale
+    bytes [rows, cols/32] -> float64 [rows, cols]; w = e2m1(code) * 2^(e - 127)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    nib = np.empty((rows, half * 2), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    return e2m1_decode(nib) * np.repeat(e8m0_decode(scales), 32, axis=1)
+
+
 def expert_weights_f64(workload, key: int):
     """(W_gate [I,H], W_up [I,H], W_down [H,I]) of expert `key` as float64.
 
@@ -50,7 +71,7 @@ def expert_weights_f64(workload, key: int):
     ([FT-KR] "FreeToken의 설계"); the expert's identity is the flattened id
     key = layer * E + expert ([FT-KR] "전문가 뱅크와 FTW 포맷").
     """
-    from workloads import WFMT_F32, WFMT_BF16
+    from workloads import WFMT_F32, WFMT_BF16, WFMT_FP4
     out = []
     for t in range(3):
         v = workload.expert_tensor(key, t)
@@ -58,8 +79,10 @@ def expert_weights_f64(workload, key: int):
             out.append(np.asarray(v, dtype=np.float64))
         elif workload.wfmt == WFMT_BF16:
             out.append(bf16_to_f64(v))
-        else:
+        elif workload.wfmt == WFMT_FP4:
             out.append(dequant_fp4(*v))
+        else:
+            out.append(dequant_mxfp4(*v))
     return tuple(out)
 
 

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libroutedmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE, MOE_ENOPIN, MOE_ENOTSUP = 0, -1, -2, -3, -4, -5, -6
-MOE_WFMT_F32, MOE_WFMT_BF16, MOE_WFMT_FP4 = 0, 1, 2
+MOE_WFMT_F32, MOE_WFMT_BF16, MOE_WFMT_FP4, MOE_WFMT_MXFP4 = 0, 1, 2, 3
 MOE_AFMT_F32, MOE_AFMT_BF16 = 0, 1
 MOE_MODE_FUSED, MOE_MODE_OFFLOAD, MOE_MODE_CPU, MOE_MODE_HYBRID = 0, 1, 2, 3
 MOE_KIND_HIT, MOE_KIND_FILL, MOE_KIND_CPU, MOE_KIND_BUF = 0, 1, 2, 3

@@ -207,6 +207,13 @@ static Dots pick_dots() {
   return Dots{dot_f32_generic, dot_bf16_generic, dot_fp4_generic};
 }
 
+// MXFP4 block scales of one row as bf16 bits: the E8M0 byte e (1..254) is the exponent
+// field of 2^(e - 127), so the bf16 pattern is e << 7 (bf16 shares fp32's exponent).
+static inline const uint16_t* mx_row_scales(const uint8_t* src, int nb, uint16_t* dst) {
+  for (int b = 0; b < nb; ++b) dst[b] = (uint16_t)(src[b] << 7);
+  return dst;
+}
+
 // ---------------------------------------------------------------- the branch
 void cpu_ffn(CpuPool& pool, const CpuFfnJob& job) {
   static const Dots D = pick_dots();
@@ -224,8 +231,10 @@ void cpu_ffn(CpuPool& pool, const CpuFfnJob& job) {
     }
   }
   // FP4 dots read de-interleaved activations
+  const bool fp4 = job.wfmt == MOE_WFMT_FP4 || job.wfmt == MOE_WFMT_MXFP4;
+  const bool mx = job.wfmt == MOE_WFMT_MXFP4;
   std::vector<float> xe, xo, he, ho;
-  if (job.wfmt == MOE_WFMT_FP4) {
+  if (fp4) {
     xe.resize((size_t)T * H / 2);
     xo.resize((size_t)T * H / 2);
     for (int t = 0; t < T; ++t)
@@ -239,6 +248,7 @@ void cpu_ffn(CpuPool& pool, const CpuFfnJob& job) {
   pool.run(ncpu * nrb_i, [&](int task) {
     const int c = task / nrb_i, i0 = (task % nrb_i) * RB, i1 = std::min(I, i0 + RB);
     const uint8_t* rec = job.rec[c];
+    std::vector<uint16_t> mg(mx ? H / 32 : 0), mu(mx ? H / 32 : 0);
     for (int p : pairs[c]) {
       const int t = p / k;
       const float* x = job.x + (size_t)t * H;
@@ -253,17 +263,26 @@ void cpu_ffn(CpuPool& pool, const CpuFfnJob& job) {
           g = D.bf16(W + (int64_t)i * H, x, H);
           u = D.bf16(W + n + (int64_t)i * H, x, H);
         } else {
-          const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2));
           const float* e = xe.data() + (size_t)t * H / 2;
           const float* o = xo.data() + (size_t)t * H / 2;
-          g = D.fp4(rec + (int64_t)i * (H / 2), sc + (int64_t)i * (H / 32), e, o, H);
-          u = D.fp4(rec + n / 2 + (int64_t)i * (H / 2), sc + n / 32 + (int64_t)i * (H / 32), e, o, H);
+          const uint16_t *sg, *su;
+          if (mx) {
+            const uint8_t* sb = rec + 3 * (n / 2);
+            sg = mx_row_scales(sb + (int64_t)i * (H / 32), H / 32, mg.data());
+            su = mx_row_scales(sb + n / 32 + (int64_t)i * (H / 32), H / 32, mu.data());
+          } else {
+            const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2));
+            sg = sc + (int64_t)i * (H / 32);
+            su = sc + n / 32 + (int64_t)i * (H / 32);
+          }
+          g = D.fp4(rec + (int64_t)i * (H / 2), sg, e, o, H);
+          u = D.fp4(rec + n / 2 + (int64_t)i * (H / 2), su, e, o, H);
         }
         job.h[(size_t)p * I + i] = (g / (1.0f + std::exp(-g))) * u;
       }
     }
   });
-  if (job.wfmt == MOE_WFMT_FP4) {
+  if (fp4) {
     he.resize((size_t)P * I / 2);
     ho.resize((size_t)P * I / 2);
     for (int c = 0; c < ncpu; ++c)
@@ -279,6 +298,7 @@ void cpu_ffn(CpuPool& pool, const CpuFfnJob& job) {
   const int nrb_h = (H + RB - 1) / RB;
   pool.run(nrb_h, [&](int task) {
     const int r0 = task * RB, r1 = std::min(H, r0 + RB);
+    std::vector<uint16_t> md(mx ? I / 32 : 0);
     for (int r = r0; r < r1; ++r) {
       for (int t = 0; t < T; ++t) {
         float acc = 0.f;
@@ -294,9 +314,10 @@ void cpu_ffn(CpuPool& pool, const CpuFfnJob& job) {
           } else if (job.wfmt == MOE_WFMT_BF16) {
             d = D.bf16(reinterpret_cast<const uint16_t*>(rec) + 2 * n + (int64_t)r * I, h, I);
           } else {
-            const uint16_t* sc = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2)) + 2 * (n / 32);
-            d = D.fp4(rec + n + (int64_t)r * (I / 2), sc + (int64_t)r * (I / 32), he.data() + (size_t)p * I / 2,
-                      ho.data() + (size_t)p * I / 2, I);
+            const uint16_t* sd =
+                mx ? mx_row_scales(rec + 3 * (n / 2) + 2 * (n / 32) + (int64_t)r * (I / 32), I / 32, md.data())
+                   : reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2)) + 2 * (n / 32) + (int64_t)r * (I / 32);
+            d = D.fp4(rec + n + (int64_t)r * (I / 2), sd, he.data() + (size_t)p * I / 2, ho.data() + (size_t)p * I / 2, I);
           }
           acc += job.w[p] * d;
         }

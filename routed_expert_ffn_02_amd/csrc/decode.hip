@@ -110,6 +110,36 @@ struct RowDot<MOE_WFMT_FP4> {
   }
 };
 
+// MXFP4: the same codes with one E8M0 scale byte per block, 2^(e - 127); the byte is
+// the exponent field of that power of two as an fp32 (bytes 1..254).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+
+template <>
+struct RowDot<MOE_WFMT_MXFP4> {
+  static constexpr int kElems = 32;
+  static __device__ __forceinline__ void unpack(const uint4& q, float* v) { fp4x32_to_f32(q, v); }
+  static __device__ __forceinline__ void chunk(const uint8_t* row, int c, const float*, float* v) {
+    unpack(reinterpret_cast<const uint4*>(row)[c], v);
+  }
+  static __device__ __forceinline__ float scale(const uint8_t* srow, int c) { return e8m0_to_f32(srow[c]); }
+};
+
+// e2m1 code formats: bf16 block scales (FP4) or E8M0 block scales (MXFP4)
+template <int WFMT>
+constexpr bool kIsFp4 = (WFMT == MOE_WFMT_FP4 || WFMT == MOE_WFMT_MXFP4);
+
+// Raw block scale c of a scale row (bf16 bits or the E8M0 byte) and its value.
+template <int WFMT>
+__device__ __forceinline__ uint32_t scale_raw(const uint8_t* srow, int c) {
+  if constexpr (WFMT == MOE_WFMT_MXFP4) return srow[c];
+  else return reinterpret_cast<const uint16_t*>(srow)[c];
+}
+template <int WFMT>
+__device__ __forceinline__ float scale_value(uint32_t raw) {
+  if constexpr (WFMT == MOE_WFMT_MXFP4) return e8m0_to_f32(raw);
+  else return bf16_to_f32((uint16_t)raw);
+}
+
 template <int WFMT>
 __device__ __forceinline__ int64_t row_bytes(int cols) {
   if constexpr (WFMT == MOE_WFMT_F32) return (int64_t)cols * 4;
@@ -135,10 +165,11 @@ __device__ __forceinline__ const uint8_t* tensor_row(const uint8_t* rec, int t, 
 
 template <int WFMT>
 __device__ __forceinline__ const uint8_t* scale_row(const uint8_t* rec, int t, int r, int H, int I) {
-  if constexpr (WFMT != MOE_WFMT_FP4) return nullptr;
+  if constexpr (!kIsFp4<WFMT>) return nullptr;
+  constexpr int SB = (WFMT == MOE_WFMT_MXFP4) ? 1 : 2;  // bytes per block scale
   const int64_t n = (int64_t)H * I;
   const int cols = (t < 2) ? H : I;
-  return rec + 3 * (n / 2) + (int64_t)t * (n / 32) * 2 + (int64_t)r * (cols / 32) * 2;
+  return rec + 3 * (n / 2) + (int64_t)t * (n / 32) * SB + (int64_t)r * (cols / 32) * SB;
 }
 
 // Pairs of group g, found by one wavefront with a ballot (no block barrier, so no
@@ -304,8 +335,8 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
   // FP4: activations as f16 pairs, once per chunk (exact for bf16 inputs inside the
   // f16 range; larger magnitudes overflow to infinity, as the prefill GEMM's f16
   // operands do)
-  f16x2 xh[MAXT][CPL][WFMT == MOE_WFMT_FP4 ? 16 : 1];
-  if constexpr (WFMT == MOE_WFMT_FP4) {
+  f16x2 xh[MAXT][CPL][kIsFp4<WFMT> ? 16 : 1];
+  if constexpr (kIsFp4<WFMT>) {
 #pragma unroll
     for (int t = 0; t < MAXT; ++t)
       if (t < n)
@@ -322,7 +353,7 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
     for (int t = 0; t < MAXT; ++t) { accg[t] = 0.f; accu[t] = 0.f; }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      if constexpr (WFMT == MOE_WFMT_FP4) {
+      if constexpr (kIsFp4<WFMT>) {
         // codes expand to f16 pairs (exact) and meet the activations in packed dot
         // products with fp32 accumulation: half the VALU work of fp32 FMAs
         f16x2 hg[16], hu[16];
@@ -387,18 +418,21 @@ __device__ __forceinline__ float dot_bf16x2(uint32_t w, uint32_t x, float c) {
 }
 
 // Dot product of one 16-byte weight chunk with the matching activation words (bf16
-// pairs: 16 for the 32 elements of an FP4 chunk, 4 for the 8 of a bf16 chunk).
+// pairs: 16 for the 32 elements of an e2m1 chunk, 4 for the 8 of a bf16 chunk).  `cs`
+// is the convert's scale: 1 for bf16-scaled codes (the block scale multiplies the
+// partial sum afterwards), the block's power of two for MXFP4, which the convert
+// applies exactly.
 template <int WFMT>
-__device__ __forceinline__ float chunk_dot_bf16(const u32x4n& q, const uint32_t* xw) {
+__device__ __forceinline__ float chunk_dot_bf16(const u32x4n& q, const uint32_t* xw, float cs = 1.0f) {
   float p = 0.f;
-  if constexpr (WFMT == MOE_WFMT_FP4) {
+  if constexpr (kIsFp4<WFMT>) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // byte j of word i holds elements 8i + 2j (low nibble) and 8i + 2j + 1
-      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 0)), xw[4 * i + 0], p);
-      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 1)), xw[4 * i + 1], p);
-      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 2)), xw[4 * i + 2], p);
-      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], 1.0f, 3)), xw[4 * i + 3], p);
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], cs, 0)), xw[4 * i + 0], p);
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], cs, 1)), xw[4 * i + 1], p);
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], cs, 2)), xw[4 * i + 2], p);
+      p = dot_bf16x2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], cs, 3)), xw[4 * i + 3], p);
     }
   } else {
 #pragma unroll
@@ -422,7 +456,7 @@ __device__ __forceinline__ void load_x_words(const void* x, int H, int t, int c,
 // RW results of a token leave in one store from lanes 0..RW-1.
 template <int WFMT, int CPL, int RW, int MAXT>
 __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
-  constexpr int XQ = (WFMT == MOE_WFMT_FP4) ? 4 : 1;
+  constexpr int XQ = kIsFp4<WFMT> ? 4 : 1;
   const int g = blockIdx.y;
   // issued with the count (grp_slot has E >= gridDim.y entries, so the read is in bounds
   // even for a group beyond the count, whose value is then unused)
@@ -445,7 +479,7 @@ __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
   if (row0 >= I) return;
   const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
   u32x4n qg[RW][CPL], qu[RW][CPL];
-  uint16_t sg[RW][CPL], su[RW][CPL];  // FP4 block scales (raw bf16)
+  uint16_t sg[RW][CPL], su[RW][CPL];  // block scales (raw bf16 bits or E8M0 bytes)
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int row = min(row0 + r, I - 1);
@@ -455,9 +489,9 @@ __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
     for (int c = 0; c < CPL; ++c) {
       qg[r][c] = gp[lane + 64 * c];
       qu[r][c] = up[lane + 64 * c];
-      if constexpr (WFMT == MOE_WFMT_FP4) {
-        sg[r][c] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 0, row, H, I))[lane + 64 * c];
-        su[r][c] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 1, row, H, I))[lane + 64 * c];
+      if constexpr (kIsFp4<WFMT>) {
+        sg[r][c] = (uint16_t)scale_raw<WFMT>(scale_row<WFMT>(rec, 0, row, H, I), lane + 64 * c);
+        su[r][c] = (uint16_t)scale_raw<WFMT>(scale_row<WFMT>(rec, 1, row, H, I), lane + 64 * c);
       }
     }
   }
@@ -489,14 +523,15 @@ __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
           uint32_t xw[4 * XQ];
 #pragma unroll
           for (int i = 0; i < 4 * XQ; ++i) xw[i] = xq[t][c][i / 4][i % 4];
-          const float pg = chunk_dot_bf16<WFMT>(qg[r][c], xw);
-          const float pu = chunk_dot_bf16<WFMT>(qu[r][c], xw);
-          if constexpr (WFMT == MOE_WFMT_FP4) {
-            accg += bf16_to_f32(sg[r][c]) * pg;
-            accu += bf16_to_f32(su[r][c]) * pu;
+          if constexpr (WFMT == MOE_WFMT_MXFP4) {
+            accg += chunk_dot_bf16<WFMT>(qg[r][c], xw, e8m0_to_f32(sg[r][c]));
+            accu += chunk_dot_bf16<WFMT>(qu[r][c], xw, e8m0_to_f32(su[r][c]));
+          } else if constexpr (WFMT == MOE_WFMT_FP4) {
+            accg += bf16_to_f32(sg[r][c]) * chunk_dot_bf16<WFMT>(qg[r][c], xw);
+            accu += bf16_to_f32(su[r][c]) * chunk_dot_bf16<WFMT>(qu[r][c], xw);
           } else {
-            accg += pg;
-            accu += pu;
+            accg += chunk_dot_bf16<WFMT>(qg[r][c], xw);
+            accu += chunk_dot_bf16<WFMT>(qu[r][c], xw);
           }
         }
         hv[r][t] = silu(wave_sum(accg)) * wave_sum(accu);
@@ -599,10 +634,9 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
   // the (small) block scales first, kept as raw bits until used: row r then waits
   // only for its own weights
   uint16_t scr[R2];
-  if constexpr (WFMT == MOE_WFMT_FP4) {
+  if constexpr (kIsFp4<WFMT>) {
 #pragma unroll
-    for (int r = 0; r < R2; ++r)
-      scr[r] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
+    for (int r = 0; r < R2; ++r) scr[r] = (uint16_t)scale_raw<WFMT>(scale_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I), lane);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -644,7 +678,7 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
         float p = 0.f;
 #pragma unroll
         for (int i = 0; i < EPC; ++i) p += v[i] * hv[t][i];
-        const float scale = (WFMT == MOE_WFMT_FP4) ? bf16_to_f32(scr[r]) : 1.f;
+        const float scale = kIsFp4<WFMT> ? scale_value<WFMT>(scr[r]) : 1.f;
         const float sum = wave_sum(scale * p);
         const int row = r0 + r;
         if (lane == 0 && row < H) a.d[(int64_t)pair[t] * H + row] = sum;
@@ -660,7 +694,7 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
 template <int WFMT, int MAXT>
 __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
   constexpr int R2 = kP2RowsPerWave;
-  constexpr int EPC = (WFMT == MOE_WFMT_FP4) ? 32 : 8;
+  constexpr int EPC = kIsFp4<WFMT> ? 32 : 8;
   const int g = blockIdx.y;
   const int slot = a.grp_slot[g];  // issued with the count (see phase 1)
   const int pair0 = (MAXT == 1) ? a.grp_pair0[g] : 0;
@@ -678,10 +712,9 @@ __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
     for (int i = 0; i < EPC / 4; ++i) hq[0][i] = hp[i];
   }
   uint16_t scr[R2];
-  if constexpr (WFMT == MOE_WFMT_FP4) {
+  if constexpr (kIsFp4<WFMT>) {
 #pragma unroll
-    for (int r = 0; r < R2; ++r)
-      scr[r] = reinterpret_cast<const uint16_t*>(scale_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
+    for (int r = 0; r < R2; ++r) scr[r] = (uint16_t)scale_raw<WFMT>(scale_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I), lane);
   }
   u32x4n q[R2];
 #pragma unroll
@@ -726,8 +759,10 @@ __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
     for (int t = 0; t < MAXT; ++t) {
       out[r][t] = 0.f;
       if (t < n) {
-        float p = chunk_dot_bf16<WFMT>(q[r], hw[t]);
-        if constexpr (WFMT == MOE_WFMT_FP4) p *= bf16_to_f32(scr[r]);
+        float p;
+        if constexpr (WFMT == MOE_WFMT_MXFP4) p = chunk_dot_bf16<WFMT>(q[r], hw[t], e8m0_to_f32(scr[r]));
+        else if constexpr (WFMT == MOE_WFMT_FP4) p = bf16_to_f32(scr[r]) * chunk_dot_bf16<WFMT>(q[r], hw[t]);
+        else p = chunk_dot_bf16<WFMT>(q[r], hw[t]);
         out[r][t] = wave_sum(p);
       }
     }
@@ -839,7 +874,7 @@ static void p1_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timing t
     launch_timed(dec_phase1_bf<W, CPL, RW, MAXT>, grid, dim3(256), 0, s, tm, a);
   } else {
     // about 16 in-flight 16-byte weight chunks per lane; wide FP4 rows unpack to many registers
-    constexpr int RW = (W == MOE_WFMT_FP4 && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : 8);
+    constexpr int RW = (kIsFp4<W> && CPL >= 4) ? 1 : (CPL >= 4) ? 2 : (CPL == 2 ? 4 : 8);
     dim3 grid((a.I + 4 * RW - 1) / (4 * RW), max_groups);
     launch_timed(dec_phase1_fast<W, A, CPL, RW, MAXT>, grid, dim3(256), 0, s, tm, a);
   }
@@ -851,7 +886,7 @@ static bool p1_try_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timi
     case 1: p1_fast<W, A, 1, MAXT>(a, max_groups, s, tm); return true;
     case 2: p1_fast<W, A, 2, MAXT>(a, max_groups, s, tm); return true;
     case 4:
-      if constexpr (W == MOE_WFMT_FP4 && MAXT > 1) return false;  // 8 KB of activations per token and lane
+      if constexpr (kIsFp4<W> && MAXT > 1) return false;  // 8 KB of activations per token and lane
       else { p1_fast<W, A, 4, MAXT>(a, max_groups, s, tm); return true; }
     default: return false;
   }
@@ -863,7 +898,7 @@ static void p1_dispatch(const DecodeArgs& a, int max_groups, size_t lds, hipStre
   bool done = false;
   if (small && a.T <= 1) {
     done = p1_try_fast<W, A, 1>(a, max_groups, s, tm);
-  } else if constexpr (W != MOE_WFMT_FP4 || A == MOE_AFMT_BF16) {
+  } else if constexpr (!kIsFp4<W> || A == MOE_AFMT_BF16) {
     // (FP4 rows with 4 fp32-activation tokens exceed the register file)
     if (small && a.T <= 4) done = p1_try_fast<W, A, 4>(a, max_groups, s, tm);
   }
@@ -878,10 +913,12 @@ void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_group
   if (afmt == MOE_AFMT_BF16) {
     if (wfmt == MOE_WFMT_BF16) p1_dispatch<MOE_WFMT_BF16, MOE_AFMT_BF16>(a, max_groups, lds, s, tm);
     else if (wfmt == MOE_WFMT_FP4) p1_dispatch<MOE_WFMT_FP4, MOE_AFMT_BF16>(a, max_groups, lds, s, tm);
+    else if (wfmt == MOE_WFMT_MXFP4) p1_dispatch<MOE_WFMT_MXFP4, MOE_AFMT_BF16>(a, max_groups, lds, s, tm);
     else p1_dispatch<MOE_WFMT_F32, MOE_AFMT_BF16>(a, max_groups, lds, s, tm);
   } else {
     if (wfmt == MOE_WFMT_BF16) p1_dispatch<MOE_WFMT_BF16, MOE_AFMT_F32>(a, max_groups, lds, s, tm);
     else if (wfmt == MOE_WFMT_FP4) p1_dispatch<MOE_WFMT_FP4, MOE_AFMT_F32>(a, max_groups, lds, s, tm);
+    else if (wfmt == MOE_WFMT_MXFP4) p1_dispatch<MOE_WFMT_MXFP4, MOE_AFMT_F32>(a, max_groups, lds, s, tm);
     else p1_dispatch<MOE_WFMT_F32, MOE_AFMT_F32>(a, max_groups, lds, s, tm);
   }
 }
@@ -907,6 +944,7 @@ static void p2_tokens(const DecodeArgs& a, int max_groups, hipStream_t s, Timing
 void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
   if (wfmt == MOE_WFMT_BF16) p2_tokens<MOE_WFMT_BF16>(a, max_groups, s, tm);
   else if (wfmt == MOE_WFMT_FP4) p2_tokens<MOE_WFMT_FP4>(a, max_groups, s, tm);
+  else if (wfmt == MOE_WFMT_MXFP4) p2_tokens<MOE_WFMT_MXFP4>(a, max_groups, s, tm);
   else p2_tokens<MOE_WFMT_F32>(a, max_groups, s, tm);
 }
 

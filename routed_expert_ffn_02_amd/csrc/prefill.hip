@@ -649,26 +649,56 @@ __device__ __forceinline__ void f4_store(const F4Chunk& st, uint16_t (*sA)[F4_AW
   for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 3) + 32 * j][(tid & 7) * 16]) = st.b[j];
 }
 
-// Scales of one weight row for chunk c: blocks [8c, 8c + 8); word w covers k in
-// [64w, 64w + 64) of the chunk, its low half the lanes of half 0, its high half half 1.
+// Scales of one weight row for chunk c: blocks [8c, 8c + 8).  bf16 scales: 16 bytes,
+// word w covers k in [64w, 64w + 64) of the chunk, its low half the lanes of half 0,
+// its high half half 1.  MXFP4 (MX): 8 E8M0 bytes, byte 2w + h for sub-step w and
+// lane half h (the upper two words of the vector are unused).
+template <bool MX>
 __device__ __forceinline__ u32x4 f4_scales(const uint8_t* rec, uint32_t soff, int c) {
-  return *reinterpret_cast<const u32x4*>(rec + 16 * c + soff);
+  if constexpr (MX) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(rec + 8 * c + soff);
+    return u32x4{v[0], v[1], 0u, 0u};
+  } else {
+    return *reinterpret_cast<const u32x4*>(rec + 16 * c + soff);
+  }
 }
 
 struct F4Scales {
-  uint32_t w0[4], w1[4];  // this lane's scale words for fragments rb0 and rb1
+  uint32_t w0[4], w1[4];  // this lane's scale of each sub-step for fragments rb0 and rb1 (low bits)
 };
 
+template <bool MX>
 __device__ __forceinline__ void f4_take(F4Scales& s, const u32x4& q0, const u32x4& q1, int h) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    s.w0[w] = q0[w] >> (16 * h);
-    s.w1[w] = q1[w] >> (16 * h);
+    if constexpr (MX) {
+      const int sh = 8 * (2 * (w & 1) + h);
+      s.w0[w] = (q0[w >> 1] >> sh) & 0xffu;
+      s.w1[w] = (q1[w >> 1] >> sh) & 0xffu;
+    } else {
+      s.w0[w] = q0[w] >> (16 * h);
+      s.w1[w] = q1[w] >> (16 * h);
+    }
+  }
+}
+
+// MFMA operands of a run of MXFP4 codes: the convert applies the block's power of
+// two 2^(e - 127) itself (exact in f16 inside its range), so no multiply follows.
+__device__ __forceinline__ void b_operands_mx(BOps<MOE_WFMT_FP4>& o, const BRun<MOE_WFMT_FP4>& r, uint32_t e) {
+  const float sc = __uint_as_float(e << 23);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = r.v[j];
+    o.op[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3))};
   }
 }
 
 // One chunk: four 64-k sub-steps; lane half h covers k in [32h, 32h + 32) of a
 // sub-step (one scale block) and MFMA j its slice [32h + 8j, + 8), in A and B alike.
+template <bool MX>
 __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const uint8_t (*sB)[F4_BP], int rb0, int rb1,
                                            const F4Scales& sc, int lane, f32x16 (&acc)[2][2]) {
   const int r = lane & 31, h = lane >> 5;
@@ -677,8 +707,13 @@ __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const ui
     BOps<MOE_WFMT_FP4> o0, o1;
     const BRun<MOE_WFMT_FP4> c0{*reinterpret_cast<const u32x4*>(&sB[rb0 + r][u * 32 + 16 * h])};
     const BRun<MOE_WFMT_FP4> c1{*reinterpret_cast<const u32x4*>(&sB[rb1 + r][u * 32 + 16 * h])};
-    b_operands<MOE_WFMT_FP4>(o0, c0, sc.w0[u]);
-    b_operands<MOE_WFMT_FP4>(o1, c1, sc.w1[u]);
+    if constexpr (MX) {
+      b_operands_mx(o0, c0, sc.w0[u]);
+      b_operands_mx(o1, c1, sc.w1[u]);
+    } else {
+      b_operands<MOE_WFMT_FP4>(o0, c0, sc.w0[u]);
+      b_operands<MOE_WFMT_FP4>(o1, c1, sc.w1[u]);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = u * 64 + 32 * h + 8 * j;
@@ -694,6 +729,7 @@ __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const ui
 
 // The k loop over nc = K / 256 chunks.  rb0 / rb1: the wavefront's two 32-row weight
 // fragments in the block's LDS rows; sc0 / sc1: byte offsets of their scale rows.
+template <bool MX>
 __device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0, uint32_t sc1,
                                          uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int rb0, int rb1, int tid,
                                          f32x16 (&acc)[2][2]) {
@@ -701,30 +737,33 @@ __device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0,
   F4Chunk N;
   F4Scales sc;
   f4_issue(N, src, 0);
-  u32x4 q0 = f4_scales(src.b, sc0, 0), q1 = f4_scales(src.b, sc1, 0);
+  u32x4 q0 = f4_scales<MX>(src.b, sc0, 0), q1 = f4_scales<MX>(src.b, sc1, 0);
   __builtin_amdgcn_sched_barrier(0);
   f4_store(N, sA, sB, tid);
-  f4_take(sc, q0, q1, h);
+  f4_take<MX>(sc, q0, q1, h);
   __syncthreads();
   f4_issue(N, src, min(1, nc - 1));
-  q0 = f4_scales(src.b, sc0, min(1, nc - 1));
-  q1 = f4_scales(src.b, sc1, min(1, nc - 1));
+  q0 = f4_scales<MX>(src.b, sc0, min(1, nc - 1));
+  q1 = f4_scales<MX>(src.b, sc1, min(1, nc - 1));
   __builtin_amdgcn_sched_barrier(0);
   for (int c = 0; c < nc; ++c) {
-    f4_compute(sA, sB, rb0, rb1, sc, lane, acc);
+    f4_compute<MX>(sA, sB, rb0, rb1, sc, lane, acc);
     __syncthreads();  // every wavefront is done with chunk c
     f4_store(N, sA, sB, tid);
-    f4_take(sc, q0, q1, h);
+    f4_take<MX>(sc, q0, q1, h);
     __syncthreads();
     f4_issue(N, src, min(c + 2, nc - 1));
-    q0 = f4_scales(src.b, sc0, min(c + 2, nc - 1));
-    q1 = f4_scales(src.b, sc1, min(c + 2, nc - 1));
+    q0 = f4_scales<MX>(src.b, sc0, min(c + 2, nc - 1));
+    q1 = f4_scales<MX>(src.b, sc1, min(c + 2, nc - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// GEMM1 (FP4): act columns n0 .. n0 + 127; block rows 0..127 gate rows n0.., 128..255 up.
+// GEMM1 (FP4; MX: MXFP4): act columns n0 .. n0 + 127; block rows 0..127 gate rows n0..,
+// 128..255 up.
+template <bool MX>
 __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
+  constexpr uint32_t SB = MX ? 1 : 2;  // bytes per block scale
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
@@ -750,8 +789,8 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   src.boff[1] = src.boff[0] + (uint32_t)(n / 2);
   src.bstep = (int64_t)32 * (H / 2);
   const int col = n0 + wave * 32 + (lane & 31);
-  const uint32_t sc_g = (uint32_t)(3 * (n / 2)) + 2u * (uint32_t)col * (uint32_t)(H / 32);
-  const uint32_t sc_u = sc_g + (uint32_t)(2 * (n / 32));
+  const uint32_t sc_g = (uint32_t)(3 * (n / 2)) + SB * (uint32_t)col * (uint32_t)(H / 32);
+  const uint32_t sc_u = sc_g + SB * (uint32_t)(n / 32);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -760,7 +799,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
-  f4_kloop(H / F4_KS, src, sc_g, sc_u, sA, sB, wave * 32, 128 + wave * 32, tid, acc);
+  f4_kloop<MX>(H / F4_KS, src, sc_g, sc_u, sA, sB, wave * 32, 128 + wave * 32, tid, acc);
 
   uint16_t* act = reinterpret_cast<uint16_t*>(a.act);
 #pragma unroll
@@ -777,8 +816,11 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   }
 }
 
-// GEMM2 (FP4): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64 of them.
+// GEMM2 (FP4; MX: MXFP4): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64
+// of them.
+template <bool MX>
 __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
+  constexpr uint32_t SB = MX ? 1 : 2;  // bytes per block scale
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
@@ -803,8 +845,8 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
   src.boff[1] = src.boff[0] + 128u * (uint32_t)(I / 2);
   src.bstep = (int64_t)32 * (I / 2);
   const int c0 = n0 + wave * 64 + (lane & 31);
-  const uint32_t sc0 = (uint32_t)(3 * (n / 2) + 2 * 2 * (n / 32)) + 2u * (uint32_t)c0 * (uint32_t)(I / 32);
-  const uint32_t sc1 = sc0 + 2u * 32u * (uint32_t)(I / 32);
+  const uint32_t sc0 = (uint32_t)(3 * (n / 2)) + SB * 2u * (uint32_t)(n / 32) + SB * (uint32_t)c0 * (uint32_t)(I / 32);
+  const uint32_t sc1 = sc0 + SB * 32u * (uint32_t)(I / 32);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -813,7 +855,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
-  f4_kloop(I / F4_KS, src, sc0, sc1, sA, sB, wave * 64, wave * 64 + 32, tid, acc);
+  f4_kloop<MX>(I / F4_KS, src, sc0, sc1, sA, sB, wave * 64, wave * 64 + 32, tid, acc);
 
   int pr[2][16];
 #pragma unroll
@@ -857,14 +899,14 @@ __global__ __launch_bounds__(256) void act_operands_kernel(const void* __restric
 }
 
 bool prefill_needs_act_operands(int wfmt, int afmt) {
-  return wfmt == MOE_WFMT_FP4 || (wfmt == MOE_WFMT_BF16 && afmt == MOE_AFMT_F32);
+  return wfmt == MOE_WFMT_FP4 || wfmt == MOE_WFMT_MXFP4 || (wfmt == MOE_WFMT_BF16 && afmt == MOE_AFMT_F32);
 }
 
 void launch_act_operands(int wfmt, int afmt, const void* x, void* xo, int64_t n, hipStream_t s) {
   const int64_t n8 = n / 8;
   const dim3 grid((unsigned)((n8 + 255) / 256));
   uint16_t* o = reinterpret_cast<uint16_t*>(xo);
-  if (wfmt == MOE_WFMT_FP4) {
+  if (wfmt == MOE_WFMT_FP4 || wfmt == MOE_WFMT_MXFP4) {
     if (afmt == MOE_AFMT_BF16) hipLaunchKernelGGL((act_operands_kernel<MOE_AFMT_BF16, true>), grid, dim3(256), 0, s, x, o, n8);
     else hipLaunchKernelGGL((act_operands_kernel<MOE_AFMT_F32, true>), grid, dim3(256), 0, s, x, o, n8);
   } else {
@@ -923,8 +965,8 @@ __global__ void gemm2_f32_kernel(PrefillArgs a) {
 
 // The LDS-staged FP4 kernels take two 128-k stages per 16-byte scale load.
 // The LDS-staged FP4 kernels take 256-k chunks and hold byte offsets (activations,
-// record) in 32 bits.
-static bool fp4_staged(const PrefillArgs& a) {
+// record) in 32 bits.  MXFP4 contexts are created only for shapes that meet this.
+bool fp4_staged(const PrefillArgs& a) {
   return a.H % 256 == 0 && a.I % 256 == 0 && (int64_t)a.T * a.H < (1ll << 31) &&
          (int64_t)a.T * a.k * a.I < (1ll << 31) && a.rec_bytes < (1ll << 32);
 }
@@ -944,7 +986,8 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
   }
   const dim3 grid(padded_grid(max_tiles_m, a.I / 128));
   if (wfmt == MOE_WFMT_BF16) launch_timed(gemm1_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
-  else if (fp4_staged(a)) launch_timed(gemm1_fp4_kernel, grid, dim3(256), 0, s, tm, a);
+  else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm1_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
+  else if (fp4_staged(a)) launch_timed(gemm1_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm1_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
 }
 
@@ -956,7 +999,8 @@ void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipSt
   }
   const dim3 grid(padded_grid(max_tiles_m, a.H / 256));
   if (wfmt == MOE_WFMT_BF16) launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
-  else if (fp4_staged(a)) launch_timed(gemm2_fp4_kernel, grid, dim3(256), 0, s, tm, a);
+  else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm2_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
+  else if (fp4_staged(a)) launch_timed(gemm2_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm2_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
 }
 

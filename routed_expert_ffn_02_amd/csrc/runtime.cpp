@@ -50,6 +50,7 @@ int64_t record_bytes(const moe_config& c) {
     case MOE_WFMT_F32: return 3 * n * 4;
     case MOE_WFMT_BF16: return 3 * n * 2;
     case MOE_WFMT_FP4: return 3 * (n / 2) + 3 * (n / 32) * 2;
+    case MOE_WFMT_MXFP4: return 3 * (n / 2) + 3 * (n / 32);
   }
   return -1;
 }
@@ -58,6 +59,7 @@ int64_t weight_row_bytes(const moe_config& c, int cols) {
   switch (c.wfmt) {
     case MOE_WFMT_F32: return (int64_t)cols * 4;
     case MOE_WFMT_BF16: return (int64_t)cols * 2;
+    case MOE_WFMT_MXFP4: return (int64_t)cols / 2 + (int64_t)cols / 32;
     default: return (int64_t)cols / 2 + (int64_t)cols / 32 * 2;
   }
 }
@@ -386,10 +388,15 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   const moe_config& c = *cfg;
   if (c.n_layers < 1 || c.n_experts < 1 || c.n_experts > kMaxExperts || c.top_k < 1 || c.top_k > c.n_experts ||
       c.hidden < 64 || c.hidden % 64 || c.inter < 64 || c.inter % 64 || c.max_tokens < 1 ||
-      (int64_t)c.n_layers * c.n_experts > (1 << 24) || c.wfmt < MOE_WFMT_F32 || c.wfmt > MOE_WFMT_FP4 ||
+      (int64_t)c.n_layers * c.n_experts > (1 << 24) || c.wfmt < MOE_WFMT_F32 || c.wfmt > MOE_WFMT_MXFP4 ||
       c.afmt < MOE_AFMT_F32 || c.afmt > MOE_AFMT_BF16 || !valid_mode(c.mode) ||
       (int64_t)c.max_tokens * c.top_k > (1 << 22))
     return MOE_EINVAL;
+  // MXFP4 runs the LDS-staged prefill GEMMs only: 256-k chunks, 32-bit byte offsets
+  if (c.wfmt == MOE_WFMT_MXFP4 &&
+      (c.hidden % 256 || c.inter % 256 || (int64_t)c.max_tokens * c.hidden >= (1ll << 31) ||
+       (int64_t)c.max_tokens * c.top_k * c.inter >= (1ll << 31) || record_bytes(c) >= (1ll << 32)))
+    return MOE_ENOTSUP;
   ctx = new moe_ctx();
   ctx->cfg = c;
   ctx->S = record_bytes(c);

@@ -41,11 +41,14 @@ def test_qstar_split_host_matches_oracle():
 
 def test_record_bytes_match_pool_format():
     import routed_expert_ffn_02_amd as R
-    for wl in (W.TINY, W.A3B_DECODE, W.DSV4):
+    for wl in (W.TINY, W.A3B_DECODE, W.DSV4, W.DSV4_MX):
         cfg = R.make_config(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.inter, wl.wfmt, wl.afmt, 1,
                             R.MOE_MODE_OFFLOAD)
         assert R.moe_record_bytes(cfg) == wl.record_bytes
     assert W.A3B_DECODE.record_bytes == 6 * 2 ** 20 and W.DSV4.record_bytes == 14155776
+    # MXFP4 needs hidden and inter in multiples of 256 (the staged prefill GEMMs)
+    bad = R.make_config(1, 8, 2, 256, 128, R.MOE_WFMT_MXFP4, R.MOE_AFMT_BF16, 1, R.MOE_MODE_OFFLOAD)
+    assert R.moe_record_bytes(bad) == 3 * (256 * 128 // 2) + 3 * (256 * 128 // 32)
 
 
 def test_stats_struct_marshals():

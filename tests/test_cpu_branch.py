@@ -42,8 +42,9 @@ def test_pool_destroy_never_blocks(shim):
 
 
 @pytest.mark.parametrize("wl", [W.TINY, W.A3B_DECODE.with_(n_layers=1, n_experts=8, hidden=256, inter=128),
-                                W.DSV4.with_(n_layers=1, n_experts=8, hidden=256, inter=128)],
-                         ids=["fp32", "bf16", "fp4"])
+                                W.DSV4.with_(n_layers=1, n_experts=8, hidden=256, inter=128),
+                                W.DSV4_MX.with_(n_layers=1, n_experts=8, hidden=256, inter=256)],
+                         ids=["fp32", "bf16", "fp4", "mxfp4"])
 @pytest.mark.parametrize("T", [1, 3])
 def test_cpu_branch_matches_oracle(shim, wl, T):
     k, H, I = wl.top_k, wl.hidden, wl.inter

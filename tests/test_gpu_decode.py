@@ -11,7 +11,8 @@ pytestmark = pytest.mark.gpu
 
 BF16 = W.A3B_DECODE.with_(name="dec_bf16", n_layers=2, n_experts=16, top_k=4, hidden=256, inter=128)
 FP4 = W.DSV4.with_(name="dec_fp4", n_layers=2, n_experts=16, top_k=3, hidden=256, inter=128)
-FMT = {"fp32": W.TINY, "bf16": BF16, "fp4": FP4}
+MX = W.DSV4_MX.with_(name="dec_mxfp4", n_layers=2, n_experts=16, top_k=3, hidden=256, inter=256)
+FMT = {"fp32": W.TINY, "bf16": BF16, "fp4": FP4, "mxfp4": MX}
 
 
 def _gates(wl, step, layer, T):
@@ -25,7 +26,7 @@ def _expected(wl, layer, x, idx, w):
     return oracle.moe_combine(outs, w)
 
 
-@pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4"])
+@pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4", "mxfp4"])
 @pytest.mark.parametrize("mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("T", [1, 4])
 def test_decode_matches_oracle(fmt, mode, T):
@@ -53,7 +54,7 @@ def test_decode_matches_oracle(fmt, mode, T):
         assert st["cpu_experts"] > 0
 
 
-@pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4"])
+@pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4", "mxfp4"])
 def test_full_residency_bit_identical_to_fused(fmt):
     """Once every expert is resident, the cached path equals the all-resident path bit for bit."""
     import routed_expert_ffn_02_amd as R
@@ -98,6 +99,7 @@ def test_decode_requires_lookup_first():
 REAL_ROWS = {
     "a3b_bf16": W.A3B_DECODE.with_(name="a3b_rows", n_layers=2, n_experts=16, n_slots=12),
     "dsv4_fp4": W.DSV4.with_(name="dsv4_rows", n_layers=2, n_experts=8, n_slots=6),
+    "dsv4_mxfp4": W.DSV4_MX.with_(name="dsv4mx_rows", n_layers=2, n_experts=8, n_slots=6),
     "wide_bf16": W.A3B_DECODE.with_(name="wide_rows", n_layers=1, n_experts=8, top_k=4, hidden=4096, inter=512,
                                     n_slots=6),
 }

@@ -14,6 +14,7 @@ PF_BF16 = W.A3B_PREFILL.with_(name="pf_bf16", n_layers=3, n_experts=16, top_k=4,
 PF_FP4 = W.DSV4.with_(name="pf_fp4", n_layers=3, n_experts=16, top_k=3, hidden=256, inter=128)
 # inter a multiple of 256 takes the LDS-staged FP4 kernels; 128 takes the register-streamed ones
 PF_FP4_256 = W.DSV4.with_(name="pf_fp4_256", n_layers=3, n_experts=16, top_k=3, hidden=512, inter=256)
+PF_MX = W.DSV4_MX.with_(name="pf_mxfp4", n_layers=3, n_experts=16, top_k=3, hidden=512, inter=256)
 
 
 def _route_np(wl, layer, x):
@@ -28,7 +29,7 @@ def _expected(wl, layer, x, idx, w):
     return oracle.moe_combine(outs, w)
 
 
-@pytest.mark.parametrize("wl", [PF_BF16, PF_FP4, PF_FP4_256], ids=["bf16", "fp4", "fp4_staged"])
+@pytest.mark.parametrize("wl", [PF_BF16, PF_FP4, PF_FP4_256, PF_MX], ids=["bf16", "fp4", "fp4_staged", "mxfp4"])
 @pytest.mark.parametrize("T", [1, 100, 257])
 def test_buffered_prefill_matches_oracle(wl, T):
     import routed_expert_ffn_02_amd as R

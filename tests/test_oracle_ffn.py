@@ -105,3 +105,35 @@ def test_full_residency_bitwise_and_exact_merge():
         rh = hyb.decode_layer(0, x)
         np.testing.assert_allclose(rh["y_split"], rh["y_exact"], rtol=1e-13, atol=1e-15)
         np.testing.assert_array_equal(rh["y"], rf["y"])
+
+
+def test_mxfp4_equals_bf16_scaled_path_on_powers_of_two():
+    """An E8M0 byte e is the bf16 bit pattern e << 7 (bf16 has fp32's 8-bit exponent and
+    a 7-bit mantissa), so MXFP4 must dequantise exactly like the bf16-scale path fed
+    those bits; and the E8M0 definition's fixed points: 127 -> 1, 0 -> 2^-127, 255 -> NaN."""
+    from oracle import dequant_mxfp4, e8m0_decode
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 256, size=(6, 64), dtype=np.uint8)     # 6 rows x 128 elements
+    e = rng.integers(1, 255, size=(6, 4)).astype(np.uint8)
+    e[0, 0], e[1, 1], e[2, 2] = 1, 127, 254
+    assert np.array_equal(dequant_mxfp4(codes, e), dequant_fp4(codes, (e.astype(np.uint16) << 7)))
+    assert e8m0_decode(np.array([127]))[0] == 1.0 and e8m0_decode(np.array([0]))[0] == 2.0 ** -127
+    assert e8m0_decode(np.array([130]))[0] == 8.0 and np.isnan(e8m0_decode(np.array([255]))[0])
+
+
+def test_mxfp4_workload_records():
+    """MXFP4 records: the FP4 codes of the same seed, one scale byte per 32 elements in the
+    configured exponent range, packed as [codes x3 | scale bytes x3]."""
+    import workloads as W
+    wl = W.DSV4_MX.with_(n_layers=1, n_experts=2, hidden=256, inter=256)
+    fp = W.DSV4.with_(n_layers=1, n_experts=2, hidden=256, inter=256)
+    n = wl.hidden * wl.inter
+    assert wl.record_bytes == 3 * (n // 2) + 3 * (n // 32)
+    rec = wl.pack_record(1)
+    for t in range(3):
+        codes, sc = wl.expert_tensor(1, t)
+        assert np.array_equal(codes, fp.expert_tensor(1, t)[0])
+        assert sc.dtype == np.uint8 and sc.min() >= wl.mx_exp_lo and sc.max() <= wl.mx_exp_hi
+        assert np.array_equal(rec[t * (n // 2):(t + 1) * (n // 2)], codes.reshape(-1))
+        assert np.array_equal(rec[3 * (n // 2) + t * (n // 32):3 * (n // 2) + (t + 1) * (n // 32)], sc.reshape(-1))
+    assert W.DSV4_MX.record_bytes == 13369344

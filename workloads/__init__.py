@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libwlgen.so")
 _lib = None
 
-WFMT_F32, WFMT_BF16, WFMT_FP4 = 0, 1, 2
+WFMT_F32, WFMT_BF16, WFMT_FP4, WFMT_MXFP4 = 0, 1, 2, 3
 AFMT_F32, AFMT_BF16 = 0, 1
 
 # Stream domains (high bits of the stream id); expert domains live in gen.c.
@@ -61,7 +61,8 @@ class _WlCfg(ctypes.Structure):
                 ("wfmt", ctypes.c_int32), ("pad", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("alias_records", ctypes.c_int64),
                 ("sigma", ctypes.c_float), ("fp4_scale_lo", ctypes.c_float),
-                ("fp4_scale_hi", ctypes.c_float), ("pad2", ctypes.c_float)]
+                ("fp4_scale_hi", ctypes.c_float), ("pad2", ctypes.c_float),
+                ("mx_exp_lo", ctypes.c_int32), ("mx_exp_hi", ctypes.c_int32)]
 
 
 def lib():
@@ -112,6 +113,8 @@ class Workload:
     alias_records: int = 0   # 0 = full pool; R > 0: key -> key % R backing record
     fp4_scale_lo: float = 0.5 * 0.02 / 2.926
     fp4_scale_hi: float = 1.5 * 0.02 / 2.926
+    mx_exp_lo: int = 119     # MXFP4 scale exponents: 2^-8 .. 2^-6 (weight rms ~0.03)
+    mx_exp_hi: int = 121
     resize_schedule: tuple = ()   # ((after_step, new_n_slots), ...)
     prefill_tokens: int = 0
 
@@ -135,7 +138,7 @@ class Workload:
     def _cfg(self) -> _WlCfg:
         return _WlCfg(self.n_layers, self.n_experts, self.hidden, self.inter, self.wfmt, 0,
                       self.seed, self.alias_records, self.sigma_w,
-                      self.fp4_scale_lo, self.fp4_scale_hi, 0.0)
+                      self.fp4_scale_lo, self.fp4_scale_hi, 0.0, self.mx_exp_lo, self.mx_exp_hi)
 
     # ---- expert weights -------------------------------------------------
     def backing_key(self, key: int) -> int:
@@ -145,7 +148,8 @@ class Workload:
         """Logical values of tensor t (0 gate [I,H], 1 up [I,H], 2 down [H,I]) of expert `key`.
 
         F32 -> float32 array; BF16 -> uint16 bf16 bit patterns;
-        FP4 -> (uint8 codes [rows, cols/2], uint16 bf16 scale bits [rows, cols/32]).
+        FP4 -> (uint8 codes [rows, cols/2], uint16 bf16 scale bits [rows, cols/32]);
+        MXFP4 -> (uint8 codes [rows, cols/2], uint8 E8M0 scale exponents [rows, cols/32]).
         """
         rows, cols = (self.inter, self.hidden) if t < 2 else (self.hidden, self.inter)
         cfg = self._cfg()
@@ -157,7 +161,7 @@ class Workload:
             rc = lib().wl_expert_tensor(ctypes.byref(cfg), key, t, out.ctypes.data, None)
         else:
             codes = np.empty((rows, cols // 2), np.uint8)
-            scales = np.empty((rows, cols // 32), np.uint16)
+            scales = np.empty((rows, cols // 32), np.uint16 if self.wfmt == WFMT_FP4 else np.uint8)
             rc = lib().wl_expert_tensor(ctypes.byref(cfg), key, t, codes.ctypes.data, scales.ctypes.data)
             out = (codes, scales)
         if rc != 0:
@@ -293,7 +297,11 @@ DSV4 = Workload(name="dsv4_fp4", seed=4, n_layers=43, n_experts=256, top_k=6, hi
                 wfmt=WFMT_FP4, afmt=AFMT_BF16, tokens=1, steps=512, n_slots=1695,
                 zipf_alpha=ZIPF_ALPHA, prev_bonus=PREV_BONUS, prefill_tokens=2048)
 
+# The pages' DeepSeek-V4-Flash experts as MXFP4: the same codes with one E8M0 scale byte
+# per 32 elements (13,369,344-byte records); the 24 GB cache then holds 1795 slots.
+DSV4_MX = DSV4.with_(name="dsv4_mxfp4", wfmt=WFMT_MXFP4, n_slots=1795)
+
 A3B_ELASTIC = A3B_DECODE.with_(name="a3b_elastic_hybrid", seed=5, tokens=4, steps=1024,
                                resize_schedule=((341, 640), (682, 960)))
 
-WORKLOADS = {w.name: w for w in (TINY, A3B_DECODE, A3B_PREFILL, DSV4, A3B_ELASTIC)}
+WORKLOADS = {w.name: w for w in (TINY, A3B_DECODE, A3B_PREFILL, DSV4, DSV4_MX, A3B_ELASTIC)}

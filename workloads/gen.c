@@ -87,6 +87,13 @@ void wl_bytes(uint8_t* out, int64_t n, uint64_t seed, uint64_t stream, uint64_t 
   }
 }
 
+/* lo + (top 32 bits of the draw) % (hi - lo + 1): integers in [lo, hi] (bytes). */
+void wl_uniform_u8(uint8_t* out, int64_t n, uint64_t seed, uint64_t stream, uint64_t ctr0, int32_t lo, int32_t hi) {
+  uint64_t k = stream_key(seed, stream);
+  uint64_t span = (uint64_t)(hi - lo + 1);
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)(lo + (int32_t)((draw(k, ctr0 + (uint64_t)i) >> 32) % span));
+}
+
 /* bf16(lo + (hi - lo) * u) with u = (top 16 bits of the draw) / 65536. */
 void wl_uniform_bf16(uint16_t* out, int64_t n, uint64_t seed, uint64_t stream, uint64_t ctr0, float lo, float hi) {
   uint64_t k = stream_key(seed, stream);
@@ -108,17 +115,19 @@ void wl_uniform_f64(double* out, int64_t n, uint64_t seed, uint64_t stream, uint
 #define DOMAIN_EXPERT (1ULL << 56)
 #define DOMAIN_SCALE  (2ULL << 56)
 
-enum { WL_F32 = 0, WL_BF16 = 1, WL_FP4 = 2 };
+enum { WL_F32 = 0, WL_BF16 = 1, WL_FP4 = 2, WL_MXFP4 = 3 };
 
 typedef struct {
   int32_t n_layers, n_experts, hidden, inter;
-  int32_t wfmt;        /* WL_F32, WL_BF16, WL_FP4 (e2m1 codes + bf16 scale per 32) */
+  int32_t wfmt;        /* WL_F32, WL_BF16, WL_FP4 (e2m1 codes + bf16 scale per 32),
+                          WL_MXFP4 (e2m1 codes + E8M0 scale byte per 32) */
   int32_t pad;
   uint64_t seed;
   int64_t alias_records;  /* 0: every key has its own values; R > 0: key -> key % R */
   float sigma;            /* weight standard deviation (F32/BF16) */
   float fp4_scale_lo, fp4_scale_hi;  /* FP4 block scales ~ U[lo, hi] */
   float pad2;
+  int32_t mx_exp_lo, mx_exp_hi;      /* MXFP4 block scale bytes ~ uniform integers in [lo, hi] */
 } wl_cfg;
 
 static inline int64_t backing(const wl_cfg* c, int64_t key) {
@@ -138,6 +147,7 @@ static inline void tensor_shape(const wl_cfg* c, int t, int64_t* rows, int64_t* 
  *  FP4:  values = uint8 codes [rows*cols/2], element 2i in the low nibble of byte i
  *        (elements run along a row, i.e. along the reduction dimension);
  *        scales = uint16 bf16 bits [rows*cols/32], one per 32 consecutive elements of a row.
+ *  MXFP4: codes as FP4; scales = uint8 E8M0 exponents [rows*cols/32] (scale 2^(e - 127)).
  */
 int wl_expert_tensor(const wl_cfg* c, int64_t key, int t, void* values, void* scales) {
   if (!c || t < 0 || t > 2 || key < 0 || key >= (int64_t)c->n_layers * c->n_experts) return -1;
@@ -154,6 +164,11 @@ int wl_expert_tensor(const wl_cfg* c, int64_t key, int t, void* values, void* sc
       if (scales)
         wl_uniform_bf16((uint16_t*)scales, n / 32, c->seed, DOMAIN_SCALE | sid, 0, c->fp4_scale_lo, c->fp4_scale_hi);
       return 0;
+    case WL_MXFP4:
+      if (cols % 32 || c->mx_exp_lo < 0 || c->mx_exp_hi > 255 || c->mx_exp_lo > c->mx_exp_hi) return -1;
+      wl_bytes((uint8_t*)values, n / 2, c->seed, DOMAIN_EXPERT | sid, 0);
+      if (scales) wl_uniform_u8((uint8_t*)scales, n / 32, c->seed, DOMAIN_SCALE | sid, 0, c->mx_exp_lo, c->mx_exp_hi);
+      return 0;
   }
   return -1;
 }
@@ -162,7 +177,8 @@ int wl_expert_tensor(const wl_cfg* c, int64_t key, int t, void* values, void* sc
  * Bytes of one packed expert record in the pool format the library reads:
  *  F32 / BF16: [gate I*H | up I*H | down H*I], each row-major, element size 4 / 2;
  *  FP4:        [gate codes I*H/2 | up codes | down codes H*I/2 |
- *               gate scales I*H/32 bf16 | up scales | down scales].
+ *               gate scales I*H/32 bf16 | up scales | down scales];
+ *  MXFP4:      as FP4 with one scale byte (E8M0) per 32 elements.
  */
 int64_t wl_record_bytes(const wl_cfg* c) {
   int64_t n = (int64_t)c->hidden * c->inter;
@@ -170,6 +186,7 @@ int64_t wl_record_bytes(const wl_cfg* c) {
     case WL_F32: return 3 * n * 4;
     case WL_BF16: return 3 * n * 2;
     case WL_FP4: return 3 * (n / 2) + 3 * (n / 32) * 2;
+    case WL_MXFP4: return 3 * (n / 2) + 3 * (n / 32);
   }
   return -1;
 }
@@ -184,6 +201,9 @@ int wl_pack_record(const wl_cfg* c, int64_t key, void* dst) {
       case WL_BF16: rc = wl_expert_tensor(c, key, t, p + (size_t)t * n * 2, NULL); break;
       case WL_FP4:
         rc = wl_expert_tensor(c, key, t, p + (size_t)t * (n / 2), p + 3 * (size_t)(n / 2) + (size_t)t * (n / 32) * 2);
+        break;
+      case WL_MXFP4:
+        rc = wl_expert_tensor(c, key, t, p + (size_t)t * (n / 2), p + 3 * (size_t)(n / 2) + (size_t)t * (n / 32));
         break;
       default: rc = -1;
     }
