@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--placement", action="store_true",
                     help="only replay the decode routing trace against the placement policies (miss rate vs "
                          "cache capacity) and print one JSON line of curves")
+    ap.add_argument("--bank", action="store_true",
+                    help="only time the expert bank file: write the first --bank-records records of the "
+                         "workload's pool, then load them into a page-locked pool with parallel direct I/O")
+    ap.add_argument("--bank-records", type=int, default=512)
+    ap.add_argument("--bank-dir", default=None, help="directory for the bank file (default: the temp dir)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 512 MiB device-to-device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -123,6 +128,9 @@ def main():
         return
     if args.placement:
         placement_curves(args)
+        return
+    if args.bank:
+        bank_load(args)
         return
 
     import torch
@@ -419,6 +427,57 @@ def placement_curves(args):
            "replay_ms_per_policy": round(rel * 1e3 / replays, 2),
            "reads_per_replay": int(decode.size)}
     print(json.dumps(out), flush=True)
+
+
+def bank_load(args):
+    """Engine bootstrap from an expert bank file: the first `--bank-records` records of
+    the workload's pool are generated, written as a bank file, and loaded into a fresh
+    context's page-locked pool by `moe_pool_load` with 1, 4 and 16 reader threads
+    (O_DIRECT where the file system allows it: the page cache holds the freshly written
+    file, which buffered reads would hit)."""
+    import ctypes
+    import shutil
+    import tempfile
+    import routed_expert_ffn_02_amd as R
+    import workloads as W
+
+    base = {"a3b": W.A3B_DECODE, "dsv4": W.DSV4, "dsv4mx": W.DSV4_MX}[args.config]
+    n = min(args.bank_records, base.n_keys)
+    wl = base.with_(alias_records=n)
+    L, E = wl.n_layers, wl.n_experts
+    cfg = R.make_config(L, E, wl.top_k, wl.hidden, wl.inter, wl.wfmt, wl.afmt, 1, R.MOE_MODE_OFFLOAD)
+    S = R.moe_record_bytes(cfg)
+    d = tempfile.mkdtemp(prefix="rmoe_bank_", dir=args.bank_dir)
+    path = os.path.join(d, "experts.bank")
+    try:
+        src = np.empty(n * S, np.uint8)
+        t0 = time.perf_counter()
+        wl.fill_pool(src.ctypes.data, 0, n, threads=min(16, len(os.sched_getaffinity(0))))
+        gen_s = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        R.moe_bank_write(path, cfg, src, n)
+        write_s = time.perf_counter() - t0
+        loads = []
+        for threads in (1, 4, 16):
+            ctx = R.moe_create(cfg)
+            t0 = time.perf_counter()
+            ptr, st = R.moe_pool_load(ctx, path, threads)
+            total_s = time.perf_counter() - t0
+            view = np.ctypeslib.as_array((ctypes.c_uint8 * (n * S)).from_address(ptr))
+            ok = bool(np.array_equal(view, src))
+            loads.append({"threads": threads, "mode": st["mode"], "direct_errno": st["direct_errno"],
+                          "read_GBps": round(st["bytes"] / st["seconds"] / 1e9, 2),
+                          "alloc_plus_read_s": round(total_s, 3), "bytes_match": ok})
+            R.moe_destroy(ctx)
+            log(f"bank load: {loads[-1]}")
+        fs = os.popen(f"df -T {d} | tail -1").read().split()
+        out = {"bank": f"{wl.name}: {n} records of {S} B ({n * S / 1e9:.2f} GB)",
+               "file_system": fs[1] if len(fs) > 1 else "?",
+               "generate_GBps": round(n * S / gen_s / 1e9, 2), "write_GBps": round(n * S / write_s / 1e9, 2),
+               "loads": loads}
+        print(json.dumps(out), flush=True)
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
 
 
 def oracle_baseline(wl, seconds):

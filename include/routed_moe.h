@@ -368,6 +368,58 @@ MOE_API moe_status moe_placement_replay(const moe_replay_config* cfg, const int3
                                         const int32_t* calib, int32_t calib_tokens, int32_t calib_k,
                                         uint8_t* miss_out, moe_replay_result* out);
 
+/* ------------------------------------------------------------------ expert bank file */
+
+/* Header of an expert bank file: the host pool stored in its runtime layout ([FT-KR]
+ * "전문가 뱅크와 FTW 포맷"; [FT-CN] 05 Implementation): a 4 KiB header block, then
+ * n_records records of record_bytes each in key order (key = l*E + e, or key % n_records
+ * for an aliased pool), exactly the layout moe_record_bytes defines. */
+typedef struct {
+  int32_t n_layers, n_experts, hidden, inter, wfmt, pad;
+  int64_t record_bytes, n_records;
+} moe_bank_header;
+
+typedef struct {
+  uint64_t bytes;        /* record bytes read */
+  double seconds;        /* wall time of the reads */
+  int32_t mode;          /* 0: O_DIRECT straight into the destination; 1: O_DIRECT into per-thread
+                            page-aligned buffers, then copied (destinations the kernel cannot do
+                            direct I/O into); 2: buffered reads (no O_DIRECT on the file system) */
+  int32_t threads;       /* reader threads */
+  int32_t direct_errno;  /* errno of the first failed attempt of a faster mode, or 0 */
+  int32_t pad;
+} moe_bank_stats;
+
+/* Write n_records records from `pool` (host memory, caller-owned) as a bank file for the
+ * shape and format of cfg.  MOE_EINVAL for a bad shape or path, MOE_EHIP for an I/O error. */
+MOE_API moe_status moe_bank_write(const char* path, const moe_config* cfg, const void* pool, int64_t n_records);
+
+/* Read and check a bank file's header (MOE_EINVAL: missing, malformed or truncated file). */
+MOE_API moe_status moe_bank_info(const char* path, moe_bank_header* out);
+
+/*
+ * Read every record of a bank file into dst (host memory of at least record_bytes *
+ * n_records bytes, caller-owned) with `threads` (1..256) parallel readers in 64 MiB pieces:
+ * O_DIRECT straight into dst when dst and the data size are 4 KiB-aligned and the kernel
+ * accepts dst, else O_DIRECT through page-aligned per-thread buffers, else (no O_DIRECT on
+ * the file system) buffered reads; `out` reports which.  cfg, when not NULL, must match the file's shape, format and
+ * record size.  MOE_EINVAL for a mismatch or a short buffer, MOE_EHIP for a read error.
+ * Pure host function.
+ */
+MOE_API moe_status moe_bank_read(const char* path, const moe_config* cfg, void* dst, int64_t dst_bytes,
+                                 int32_t threads, moe_bank_stats* out);
+
+/*
+ * Engine bootstrap ([FT-KR] "탄력적 메모리 관리", fast engine bootstrap): allocate the
+ * context's page-locked pool at exactly the file's record count (as moe_pool_alloc) and
+ * read the bank into it; serving then starts from an empty cache, whose misses the
+ * ordinary decode path fills.  The pages pin after filling; on machines that refuse to
+ * page-lock existing memory the pool is allocated page-locked and filled in place.  On a
+ * read error the pool is released again.  *host_pool receives the pool (owned by ctx).
+ */
+MOE_API moe_status moe_pool_load(moe_ctx* ctx, const char* path, int32_t threads, void** host_pool,
+                                 moe_bank_stats* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,19 @@ class moe_replay_result(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("keys", "misses", "reads")]
 
 
+class moe_bank_header(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "n_experts", "hidden", "inter", "wfmt", "pad")] + [
+        ("record_bytes", ctypes.c_int64), ("n_records", ctypes.c_int64)]
+
+
+class moe_bank_stats(ctypes.Structure):
+    _fields_ = [("bytes", ctypes.c_uint64), ("seconds", ctypes.c_double), ("mode", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("direct_errno", ctypes.c_int32), ("pad", ctypes.c_int32)]
+
+
+BANK_READ_MODES = {0: "direct", 1: "direct_bounce", 2: "buffered"}
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python routed_expert_ffn_02_amd/_build.py` "
@@ -108,6 +121,11 @@ def _load():
         "moe_sync": (I32, [P, VP]),
         "moe_placement_replay": (I32, [ctypes.POINTER(moe_replay_config), VP, I32, VP, I32, I32, VP,
                                        ctypes.POINTER(moe_replay_result)]),
+        "moe_bank_write": (I32, [ctypes.c_char_p, ctypes.POINTER(moe_config), VP, I64]),
+        "moe_bank_info": (I32, [ctypes.c_char_p, ctypes.POINTER(moe_bank_header)]),
+        "moe_bank_read": (I32, [ctypes.c_char_p, ctypes.POINTER(moe_config), VP, I64, I32,
+                                ctypes.POINTER(moe_bank_stats)]),
+        "moe_pool_load": (I32, [P, ctypes.c_char_p, I32, ctypes.POINTER(VP), ctypes.POINTER(moe_bank_stats)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -282,6 +300,51 @@ def moe_placement_replay(n_layers: int, n_experts: int, policy: int, capacity: i
     if want_miss:
         out["miss"] = miss
     return out
+
+
+def _stats_dict(st: "moe_bank_stats") -> dict:
+    return {"bytes": st.bytes, "seconds": st.seconds, "mode": BANK_READ_MODES.get(st.mode, st.mode),
+            "threads": st.threads, "direct_errno": st.direct_errno}
+
+
+def moe_bank_write(path: str, cfg: moe_config, pool, n_records: int) -> None:
+    """Write n_records records from host memory `pool` (address or NumPy array) as a bank file."""
+    st = lib.moe_bank_write(os.fsencode(path), ctypes.byref(cfg), _host_ptr(pool), n_records)
+    if st != MOE_OK:
+        raise MoeError(st, "moe_bank_write", f"cannot write {path}")
+
+
+def moe_bank_info(path: str) -> dict:
+    h = moe_bank_header()
+    st = lib.moe_bank_info(os.fsencode(path), ctypes.byref(h))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_bank_info", f"{path}: missing, malformed or truncated bank file")
+    return {n: getattr(h, n) for n, _ in h._fields_ if n != "pad"}
+
+
+def moe_bank_read(path: str, cfg, dst, dst_bytes: int, threads: int = 8) -> dict:
+    """Read a bank file's records into host memory `dst` (address or NumPy array)."""
+    out = moe_bank_stats()
+    st = lib.moe_bank_read(os.fsencode(path), None if cfg is None else ctypes.byref(cfg), _host_ptr(dst), dst_bytes,
+                           threads, ctypes.byref(out))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_bank_read", f"{path}: header mismatch, short buffer or read error")
+    return _stats_dict(out)
+
+
+def moe_pool_load(ctx: Ctx, path: str, threads: int = 8):
+    """Allocate the context's page-locked pool from a bank file and fill it; returns (pool address, stats)."""
+    p = ctypes.c_void_p()
+    out = moe_bank_stats()
+    _check(ctx, lib.moe_pool_load(ctx.handle, os.fsencode(path), threads, ctypes.byref(p), ctypes.byref(out)),
+           "moe_pool_load")
+    return p.value, _stats_dict(out)
+
+
+def _host_ptr(a):
+    if a is None or isinstance(a, int):
+        return a
+    return a.ctypes.data
 
 
 def moe_bench_bw(ctx: Ctx):

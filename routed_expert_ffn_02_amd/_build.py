@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libroutedmoe.so")
 ARCH = os.environ.get("RMOE_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["route.hip", "lookup.hip", "decode.hip", "prefill.hip", "fill.hip"]
-CPP_SOURCES = ["runtime.cpp", "cpu_ffn.cpp", "placement.cpp"]
+CPP_SOURCES = ["runtime.cpp", "cpu_ffn.cpp", "placement.cpp", "bank.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code (the host pass warns that it
 # does not know the feature; that is harmless).
