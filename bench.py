@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode leg")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-hybrid", action="store_true")
+    ap.add_argument("--no-fused", action="store_true", help="skip the all-resident (FUSED) graph-replayed decode leg")
+    ap.add_argument("--no-elastic", action="store_true",
+                    help="skip the batch-4 hybrid leg with elastic cache resizes (A3B shape only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--alias-records", type=int, default=0,
@@ -179,9 +182,9 @@ def main():
     Xd = torch.from_numpy(X.view(np.int16)).to(dev)
     zipf = torch.from_numpy(np.stack([wl.zipf_bias(l) for l in range(L)])).to(dev)        # [L, E]
     bias = torch.empty((L, T, E), dtype=torch.float32, device=dev)
-    bonus = torch.full((T, k), float(wl.prev_bonus), dtype=torch.float32, device=dev)
+    bonus = torch.full((L, T, k), float(wl.prev_bonus), dtype=torch.float32, device=dev)
     idx = torch.zeros((L, T, k), dtype=torch.int32, device=dev)
-    idx64 = torch.zeros((T, k), dtype=torch.int64, device=dev)
+    idx64 = torch.zeros((L, T, k), dtype=torch.int64, device=dev)
     wts = torch.zeros((L, T, k), dtype=torch.float32, device=dev)
     slot = torch.zeros((L, T, k), dtype=torch.int32, device=dev)
     y = torch.zeros((L, T, H), dtype=torch.float32, device=dev)
@@ -189,27 +192,34 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     log(f"set-up {time.time() - t0:.1f}s")
 
-    def step(s, xsrc=None, strm=None):
+    def step(s, xsrc=None, strm=None, c=None):
         xsrc = Xd[s] if xsrc is None else xsrc
         strm = stream if strm is None else strm
+        c = ctx if c is None else c
+        # the synthetic routing bias of every layer (Zipf popularity plus the bonus for
+        # the previous token's experts at that layer) depends only on the previous step,
+        # so it is prepared for all layers at once before the step's layers run
+        bias.copy_(zipf[:, None, :].expand(L, T, E))
+        if s > 0 and wl.prev_bonus:
+            idx64.copy_(idx)
+            bias.scatter_add_(2, idx64, bonus)
         for l in range(L):
             b = bias[l]
-            b.copy_(zipf[l].expand(T, E))
-            if s > 0 and wl.prev_bonus:
-                idx64.copy_(idx[l])
-                b.scatter_add_(1, idx64, bonus)
             x = xsrc[l]
-            R.moe_route(ctx, l, x, T, b, None, idx[l], wts[l], strm)
-            R.expert_cache_lookup(ctx, l, idx[l], T, slot[l], None, None, strm)
-            R.moe_ffn_decode(ctx, l, x, T, idx[l], wts[l], slot[l], y[l], strm)
+            R.moe_route_lookup(c, l, x, T, b, None, idx[l], wts[l], slot[l], None, None, strm)
+            R.moe_ffn_decode(c, l, x, T, idx[l], wts[l], slot[l], y[l], strm)
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
     R.moe_reset_stats(ctx)
+    cold_steps = min(64, args.steps)
     t1 = time.perf_counter()
     for s in range(args.warmup, total_steps):
         step(s)
+        if s == args.warmup + cold_steps - 1:
+            torch.cuda.synchronize()
+            cold_elapsed = time.perf_counter() - t1
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t1
     st = R.moe_get_stats(ctx)
@@ -228,6 +238,9 @@ def main():
     decode_detail = {
         "fill_path": "host DMA" if args.host_fills else "device copy kernel",
         "eager_tokens_per_s": round(tok_s, 2), "eager_ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "cold_first_steps": cold_steps, "cold_tokens_per_s": round(cold_steps * T / cold_elapsed, 2),
+        "steady_tokens_per_s": round((args.steps - cold_steps) * T / max(1e-9, elapsed - cold_elapsed), 2)
+        if args.steps > cold_steps else None,
         "miss_rate": round(miss_rate, 4), "fills": st["fills"], "cpu_experts": st["cpu_experts"],
         "fill_GBps_wall": round(st["fill_bytes"] / elapsed / 1e9, 2),
         "copy_engine_ms": round(st["copy_ms"], 2),
@@ -284,7 +297,8 @@ def main():
         hs = R.moe_get_stats(ctx)
         hybrid = {"tokens_per_s": round(args.steps * T / hel, 2), "ms_per_step": round(hel * 1e3 / args.steps, 3),
                   "fills": hs["fills"], "cpu_experts": hs["cpu_experts"],
-                  "cpu_branch_ms_per_step": round(hs["cpu_ms"] / args.steps, 3)}
+                  "cpu_branch_ms_per_step": round(hs["cpu_ms"] / args.steps, 3),
+                  "fill_copy_ms_per_step": round(hs["copy_ms"] / args.steps, 3)}
         log(f"hybrid: {hybrid}")
         R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)
 
@@ -321,6 +335,53 @@ def main():
         }
         log(f"prefill: {prefill}")
 
+    # ---------------------------------------------------------------- elastic leg
+    # The batch-4 hybrid run of the elastic configuration on the same pool: four
+    # sequences, each with its own previous-token bonus, misses split by q* (B_P, B_H
+    # measured above), the cache resized 1280 -> 640 -> 960 slots at safe points a third
+    # and two thirds into the run without reloading the host pool.
+    elastic = None
+    if mode == R.MOE_MODE_OFFLOAD and args.config == "a3b" and not args.no_elastic:
+        elastic = elastic_leg(args, R, W, ctx, router, arena, n_slots, zipf, stream, dev)
+        log(f"elastic: {elastic}")
+
+    # ---------------------------------------------------------------- fused leg
+    # Every record resident (a second context over the same page-locked pool): the
+    # all-hit decode step, captured once and replayed per token, against the whole
+    # step's algorithmic HBM bytes (each routed expert's record, the router weights,
+    # x and y of every layer).
+    fused = None
+    if mode == R.MOE_MODE_OFFLOAD and not args.no_fused and not args.no_graph:
+        del arena
+        torch.cuda.empty_cache()
+        cfg_f = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, 8, R.MOE_MODE_FUSED, wl.renorm)
+        ctx_f = R.moe_create(cfg_f)
+        R.moe_pool_register(ctx_f, pool, wl.pool_records, 1)
+        arena_f = torch.empty(L * E * S, dtype=torch.uint8, device=dev)
+        R.moe_bind(ctx_f, router, arena_f, arena_f.numel(), L * E)
+        R.moe_fused_load(ctx_f)
+        Xs = torch.empty_like(Xd[0])
+        for s in range(args.warmup):
+            step(s, c=ctx_f)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(1, Xs, torch.cuda.current_stream().cuda_stream, c=ctx_f)
+        tf = time.perf_counter()
+        for s in range(args.warmup, total_steps):
+            Xs.copy_(Xd[s])
+            g.replay()
+        torch.cuda.synchronize()
+        fel = time.perf_counter() - tf
+        del g
+        step_bytes = L * (k * S + E * H * 4 + T * H * (2 + 4))
+        fused = {"tokens_per_s": round(args.steps * T / fel, 2), "ms_per_step": round(fel * 1e3 / args.steps, 3),
+                 "step_bytes": step_bytes, "step_GBps": round(step_bytes * args.steps / fel / 1e9, 1),
+                 "step_hbm_frac": round(step_bytes * args.steps / fel / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"fused: {fused}")
+        R.moe_destroy(ctx_f)
+        del arena_f
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu_baseline = None
     if not args.no_cpu_baseline:
@@ -351,10 +412,61 @@ def main():
         "decode": decode_detail,
         "graph_decode": graph,
         "hybrid_decode": hybrid,
+        "fused_decode": fused,
+        "elastic_hybrid_batch4": elastic,
         "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
     R.moe_destroy(ctx)
+
+
+def elastic_leg(args, R, W, ctx, router, arena, n_slots, zipf, stream, dev):
+    """Batch 4, hybrid q* split, resizes at a third and two thirds of 2 x --steps steps."""
+    import torch
+    wl = W.A3B_DECODE.with_(tokens=4)
+    L, E, k, H, T = wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, 4
+    steps = 2 * args.steps
+    sched = {steps // 3: 640, (2 * steps) // 3: 960}
+    X = np.empty((steps, L, T, H), np.uint16)
+    for s in range(steps):
+        for l in range(L):
+            X[s, l] = wl.decode_activations(s, l, T)
+    Xd = torch.from_numpy(X.view(np.int16)).to(dev)
+    bias = torch.empty((L, T, E), dtype=torch.float32, device=dev)
+    bonus = torch.full((L, T, k), float(wl.prev_bonus), dtype=torch.float32, device=dev)
+    idx = torch.zeros((L, T, k), dtype=torch.int32, device=dev)
+    idx64 = torch.zeros((L, T, k), dtype=torch.int64, device=dev)
+    wts = torch.zeros((L, T, k), dtype=torch.float32, device=dev)
+    slot = torch.zeros((L, T, k), dtype=torch.int32, device=dev)
+    y = torch.zeros((T, H), dtype=torch.float32, device=dev)
+    R.moe_bind(ctx, router, arena, arena.numel(), n_slots)
+    R.moe_set_mode(ctx, R.MOE_MODE_HYBRID)
+    R.moe_reset_stats(ctx)
+    torch.cuda.synchronize()
+    resize_s = 0.0
+    t0 = time.perf_counter()
+    for s in range(steps):
+        bias.copy_(zipf[:, None, :].expand(L, T, E))
+        if s > 0:
+            idx64.copy_(idx)
+            bias.scatter_add_(2, idx64, bonus)
+        for l in range(L):
+            R.moe_route_lookup(ctx, l, Xd[s, l], T, bias[l], None, idx[l], wts[l], slot[l], None, None, stream)
+            R.moe_ffn_decode(ctx, l, Xd[s, l], T, idx[l], wts[l], slot[l], y, stream)
+        if s + 1 in sched:
+            tr = time.perf_counter()
+            R.expert_cache_resize(ctx, sched[s + 1], None, 0, stream)
+            resize_s += time.perf_counter() - tr
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    st = R.moe_get_stats(ctx)
+    R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)
+    distinct = st["hits"] + st["fills"] + st["cpu_experts"]
+    return {"tokens_per_s": round(steps * T / el, 2), "ms_per_step": round(el * 1e3 / steps, 3), "steps": steps,
+            "batch": T, "resizes": [[k_, v] for k_, v in sorted(sched.items())], "resize_ms_total": round(resize_s * 1e3, 2),
+            "miss_rate": round((st["fills"] + st["cpu_experts"]) / max(1, distinct), 4), "fills": st["fills"],
+            "cpu_experts": st["cpu_experts"], "cpu_branch_ms_per_step": round(st["cpu_ms"] / steps, 3),
+            "fill_copy_ms_per_step": round(st["copy_ms"] / steps, 3)}
 
 
 def placement_curves(args):

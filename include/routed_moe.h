@@ -246,6 +246,17 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
  * launches, and a step that would read the host while the stream is capturing returns
  * MOE_ESTATE.
  */
+/*
+ * moe_route followed by expert_cache_lookup of the same layer and tokens, in two launches
+ * instead of three: for decode-sized steps (T*k <= 64, T <= 16) the cache-control kernel
+ * takes the top k from the logits itself, with the selection and gates of moe_route.
+ * Arguments are those of the two calls (topk_idx and topk_w are outputs, as in
+ * moe_route); the same errors.  Asynchronous on the stream.
+ */
+MOE_API moe_status moe_route_lookup(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
+                                    float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* slot_idx,
+                                    moe_trace_rec* trace, int32_t* counts, moe_stream_t stream);
+
 MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);
 

@@ -107,6 +107,7 @@ def _load():
         "moe_route": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP]),
         "moe_topk": (I32, [P, VP, I32, VP, VP, VP]),
         "expert_cache_lookup": (I32, [P, I32, VP, I32, VP, VP, VP, VP]),
+        "moe_route_lookup": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP, VP, VP, VP]),
         "moe_ffn_decode": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP]),
         "moe_prefill_begin": (I32, [P, VP]),
         "moe_ffn_prefill": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP, VP]),
@@ -244,6 +245,13 @@ def moe_topk(ctx: Ctx, logits, T, topk_idx, topk_w, stream=None) -> None:
 def expert_cache_lookup(ctx: Ctx, layer, topk_idx, T, slot_idx, trace=None, counts=None, stream=None) -> None:
     _check(ctx, lib.expert_cache_lookup(ctx.handle, layer, _ptr(topk_idx), T, _ptr(slot_idx), _ptr(trace),
                                         _ptr(counts), _stream(stream)), "expert_cache_lookup")
+
+
+def moe_route_lookup(ctx: Ctx, layer, x, T, logit_bias, logits_out, topk_idx, topk_w, slot_idx, trace=None,
+                     counts=None, stream=None) -> None:
+    _check(ctx, lib.moe_route_lookup(ctx.handle, layer, _ptr(x), T, _ptr(logit_bias), _ptr(logits_out), _ptr(topk_idx),
+                                     _ptr(topk_w), _ptr(slot_idx), _ptr(trace), _ptr(counts), _stream(stream)),
+           "moe_route_lookup")
 
 
 def moe_ffn_decode(ctx: Ctx, layer, x, T, topk_idx, topk_w, slot_idx, y, stream=None) -> None:

@@ -95,6 +95,67 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// ---------------------------------------------------------------------------
+// Softmax over E logits and the top k of one token, by one wavefront.  Selection order:
+// the larger logit, then the lower index (-0 and +0 compare equal).  Gates are the
+// softmax values at the chosen experts, renormalised over the k when renorm is set.
+// Writes idx_out[j], w_out[j] (global) and, when lds_idx is given, lds_idx[j].
+constexpr int kTopkPerLane = kMaxExperts / 64;
+
+__device__ __forceinline__ bool topk_better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, int k, int renorm,
+                                          int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                          int* lds_idx = nullptr) {
+  const int lane = threadIdx.x & 63;
+  float v[kTopkPerLane];
+  bool taken[kTopkPerLane];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kTopkPerLane; ++i) {
+    int e = lane + 64 * i;
+    v[i] = (e < E) ? z[e] : -INFINITY;
+    taken[i] = (e >= E);
+    mx = fmaxf(mx, v[i]);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kTopkPerLane; ++i)
+    if (lane + 64 * i < E) sum += __expf(v[i] - mx);
+  sum = wave_sum(sum);
+  float sel_sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kTopkPerLane; ++i) {
+      int e = lane + 64 * i;
+      if (!taken[i] && topk_better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+    }
+    // wave arg-max under the same order: the largest value, then the lowest index
+    // among the lanes holding it
+    const float wv = wave_max(bv);
+    bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
+    bv = wv;
+#pragma unroll
+    for (int i = 0; i < kTopkPerLane; ++i)
+      if (lane + 64 * i == bi) taken[i] = true;
+    float p = __expf(bv - mx) / sum;
+    sel_sum += p;
+    if (lane == 0) {
+      idx_out[j] = bi;
+      w_out[j] = p;
+      if (lds_idx) lds_idx[j] = bi;
+    }
+  }
+  if (renorm && lane == 0) {
+    for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sel_sum;
+  }
+}
+
 // Two e2m1 codes (byte `sel` of w, low nibble first) -> two fp32 values, exact.
 template <int SEL>
 __device__ __forceinline__ void fp4x2_to_f32(uint32_t w, float& a, float& b) {

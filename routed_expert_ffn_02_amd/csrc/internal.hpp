@@ -24,6 +24,7 @@ constexpr int kLookupThreads = 1024;
 constexpr int kSlotsPerThread = kMaxCachedSlots / kLookupThreads;
 constexpr int kDecodeMaxTH = 16384;     // decode: T * H fp32 activations staged in 64 KiB of LDS
 constexpr int kDecodeMaxTok = 8;        // decode: tokens routed to one expert within a call
+constexpr int kSmallLookupPairs = 64;   // lookup steps of at most this many pairs take the one-wavefront path
 
 // lookup counters (device int32 array)
 enum {
@@ -37,7 +38,11 @@ enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D
 enum LookupMode { LK_FUSED = 0, LK_OFFLOAD = 1, LK_CPU = 2, LK_HYBRID = 3, LK_BUFFER = 4 };
 
 struct LookupArgs {
-  const int32_t* topk_idx;   // [T,k] experts (or nullptr when cand is used)
+  const int32_t* topk_idx;   // [T,k] experts (or nullptr when cand is used or logits is set)
+  const float* logits;       // [T,E]: the kernel takes the top k itself (decode-sized steps), or nullptr
+  int32_t* topk_out;         // [T,k] experts and
+  float* topk_w;             // [T,k] gates written with the top k (logits set)
+  int32_t renorm;
   const int32_t* cand;       // candidate key list (on-demand prefill rounds) or nullptr
   int32_t n_cand;
   int32_t T, k, E, layer;

@@ -58,7 +58,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {  // set bi
   return __popcll(mask & ((1ull << lane) - 1ull));
 }
 
-constexpr int kSmallP = 64;  // pairs a step may have for the one-wavefront path
+constexpr int kSmallP = kSmallLookupPairs;  // pairs a step may have for the one-wavefront path
 
 // Decode-sized steps (T*k <= 64, routed ids given): wavefront 0 holds one (token,
 // rank) pair per lane and does every per-key step (dedupe, classify, miss ranks,
@@ -67,7 +67,7 @@ constexpr int kSmallP = 64;  // pairs a step may have for the one-wavefront path
 // (stamp, slot) candidates).  Three block barriers in all; the decisions and their
 // order are those of the general path below.
 __device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, unsigned char* s_prot,
-                             uint64_t (*s_cand)[kSmallP], int* s_evc, int* s_ufirst, int* s_sc) {
+                             uint64_t (*s_cand)[kSmallP], int* s_evc, int* s_ufirst, int* s_sc, int* s_tk) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.T * a.k;
   const int kbase = a.layer * E;
@@ -80,7 +80,7 @@ __device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, 
   int ko_r[kSlotsPerThread];
   uint64_t c0 = 0;
   int e = -1;
-  if (wave == 0 && lane < P) e = a.topk_idx[lane];
+  if (!a.logits && wave == 0 && lane < P) e = a.topk_idx[lane];
   if (cached) {
     if (tid < E) slotrow_r = a.slot_of[kbase + tid];
 #pragma unroll
@@ -93,6 +93,11 @@ __device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, 
     }
     if (wave == 0) c0 = *a.counter;
   }
+  // routing fused in: wavefront t takes token t's top k from its logits while the state
+  // loads above are in flight (the same selection and gates as the top-k kernel)
+  if (a.logits && wave < a.T)
+    topk_wave(a.logits + (size_t)wave * E, E, a.k, a.renorm, a.topk_out + wave * a.k, a.topk_w + wave * a.k,
+              s_tk + wave * a.k);
   reinterpret_cast<uint32_t*>(s_prot)[tid] = 0u;  // kMaxCachedSlots bytes = one word per thread
   if (cached) {
     if (tid < E) s_slotrow[tid] = slotrow_r;
@@ -106,6 +111,7 @@ __device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, 
 
   // ---- 1. wavefront 0: U, classification, miss ranks
   const bool valid = lane < P;
+  if (a.logits && wave == 0 && valid) e = s_tk[lane];
   int nU = 0, m = 0, upos_p = 0;       // pair lanes: U position of the pair's expert
   int key = -1, slot = -1, kind = 9, p0 = 0;  // U lanes (lane < nU)
   uint64_t missmask = 0;
@@ -330,7 +336,8 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
     __shared__ uint64_t s_cand[kWaves][kSmallP];
     __shared__ int s_evc[kWaves];
     __shared__ int s_ufirst[kSmallP];
-    lookup_small(a, s_slotrow, s_keyof, s_prot, s_cand, s_evc, s_ufirst, s_sc);
+    __shared__ int s_tk[kSmallP];
+    lookup_small(a, s_slotrow, s_keyof, s_prot, s_cand, s_evc, s_ufirst, s_sc, s_tk);
     return;
   }
 

@@ -176,62 +176,11 @@ void launch_route_logits(const void* x, int afmt, const float* wr, const float* 
 // ---------------------------------------------------------------------------
 // Top-k + gates: one wavefront per token.  Each lane holds E/64 logits; k rounds
 // of a wave arg-max under the total order (value descending, index ascending).
-constexpr int kTopkPerLane = kMaxExperts / 64;
-
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k, int renorm,
                                                    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* z = logits + (size_t)t * E;
-  float v[kTopkPerLane];
-  bool taken[kTopkPerLane];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kTopkPerLane; ++i) {
-    int e = lane + 64 * i;
-    v[i] = (e < E) ? z[e] : -INFINITY;
-    taken[i] = (e >= E);
-    mx = fmaxf(mx, v[i]);
-  }
-  mx = wave_max(mx);
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < kTopkPerLane; ++i)
-    if (lane + 64 * i < E) sum += __expf(v[i] - mx);
-  sum = wave_sum(sum);
-  float sel_sum = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
-      int e = lane + 64 * i;
-      if (!taken[i] && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
-    }
-    // wave arg-max under the same order: the largest value, then the lowest index
-    // among the lanes holding it (-0 and +0 compare equal, as in `better`)
-    const float wv = wave_max(bv);
-    bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
-    bv = wv;
-    // bi is the same on every lane; mark it taken
-#pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i)
-      if (lane + 64 * i == bi) taken[i] = true;
-    float p = __expf(bv - mx) / sum;
-    sel_sum += p;
-    if (lane == 0) {
-      idx_out[(size_t)t * k + j] = bi;
-      w_out[(size_t)t * k + j] = p;
-    }
-  }
-  if (renorm && lane == 0) {
-    for (int j = 0; j < k; ++j) w_out[(size_t)t * k + j] = w_out[(size_t)t * k + j] / sel_sum;
-  }
+  topk_wave(logits + (size_t)t * E, E, k, renorm, idx_out + (size_t)t * k, w_out + (size_t)t * k);
 }
 
 void launch_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w, hipStream_t s) {

@@ -645,6 +645,41 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
   return MOE_OK;
 }
 
+MOE_API moe_status moe_route_lookup(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
+                                    float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* slot_idx,
+                                    moe_trace_rec* trace, int32_t* counts, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(ctx->bound && ctx->router_w, "bind first");
+  CHECK_ARG(!ctx->in_prefill, "decode lookup inside prefill");
+  CHECK_ARG(layer >= 0 && layer < ctx->cfg.n_layers, "layer out of range");
+  CHECK_ARG(T >= 1 && T <= ctx->cfg.max_tokens, "T out of range");
+  CHECK_ARG(x && topk_idx && topk_w && slot_idx, "null pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = ctx->cfg.n_experts, H = ctx->cfg.hidden, k = ctx->cfg.top_k;
+  float* z = logits_out ? logits_out : ctx->logits;
+  launch_route_logits(x, ctx->cfg.afmt, ctx->router_w + (int64_t)layer * E * H, logit_bias, z, T, E, H, s);
+  LookupArgs a;
+  fill_lookup_args(ctx, a, layer, topk_idx, T, lookup_mode_of(ctx->cfg.mode));
+  if (T * k <= kSmallLookupPairs && T <= kLookupThreads / 64) {
+    // the lookup kernel takes the top k from the logits itself: one launch fewer
+    a.topk_idx = nullptr;
+    a.logits = z;
+    a.topk_out = topk_idx;
+    a.topk_w = topk_w;
+    a.renorm = ctx->cfg.renorm;
+  } else {
+    launch_topk(z, T, E, k, ctx->cfg.renorm, topk_idx, topk_w, s);
+  }
+  a.slot_idx = slot_idx;
+  a.trace = trace;
+  a.counts_out = counts;
+  launch_lookup(a, s);
+  HIPCHK(hipGetLastError());
+  ctx->last_lookup_layer = layer;
+  ctx->last_lookup_T = T;
+  return MOE_OK;
+}
+
 MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream) {
   if (!ctx) return MOE_EINVAL;

@@ -1,0 +1,57 @@
+"""GPU: moe_route_lookup (router GEMV, then the cache-control kernel taking the top k
+from the logits itself) equals moe_route followed by expert_cache_lookup bit for bit:
+indices, gates, logits, slot ids, traces, counts and the decode output that follows."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from moe_harness import Harness, dev_act
+
+pytestmark = pytest.mark.gpu
+
+BF16 = W.A3B_DECODE.with_(name="rl_bf16", n_layers=2, n_experts=32, top_k=4, hidden=256, inter=128)
+MX = W.DSV4_MX.with_(name="rl_mx", n_layers=2, n_experts=16, top_k=3, hidden=512, inter=256)
+# 8 tokens x top-10 = 80 pairs: beyond the one-wavefront lookup, so the top-k kernel runs
+K10 = W.A3B_DECODE.with_(name="rl_k10", n_layers=2, n_experts=32, top_k=10, hidden=256, inter=128)
+
+
+def _run(h, fused_call, layer, x_np, bias, T):
+    R = h.R
+    wl = h.wl
+    k, E = wl.top_k, wl.n_experts
+    x = dev_act(wl, x_np)
+    idx = torch.full((T, k), -5, dtype=torch.int32, device="cuda")
+    w = torch.full((T, k), -1.0, dtype=torch.float32, device="cuda")
+    z = torch.full((T, E), -1.0, dtype=torch.float32, device="cuda")
+    slot = torch.full((T, k), -9, dtype=torch.int32, device="cuda")
+    tr = torch.full((min(T * k, E), 4), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+    if fused_call:
+        R.moe_route_lookup(h.ctx, layer, x, T, bias, z, idx, w, slot, tr, cnt)
+    else:
+        R.moe_route(h.ctx, layer, x, T, bias, z, idx, w)
+        R.expert_cache_lookup(h.ctx, layer, idx, T, slot, tr, cnt)
+    y = torch.full((T, wl.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    R.moe_ffn_decode(h.ctx, layer, x, T, idx, w, slot, y)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in (idx, w, z, slot, tr, cnt, y)]
+
+
+@pytest.mark.parametrize("wl,T", [(BF16, 1), (BF16, 4), (MX, 1), (MX, 8), (K10, 8)],
+                         ids=["bf16-1", "bf16-4", "mxfp4-1", "mxfp4-8", "k10-8-fallback"])
+@pytest.mark.parametrize("mode", [0, 1, 3])
+def test_route_lookup_equals_route_then_lookup(wl, mode, T):
+    n_slots = max(2 * wl.top_k * T, wl.n_keys // 3)
+    bw = (25_000_000_000, 100_000_000_000)
+    a = Harness(wl, mode, n_slots=n_slots, max_tokens=T, bw=bw)
+    b = Harness(wl, mode, n_slots=n_slots, max_tokens=T, bw=bw)
+    for step in range(5):
+        for layer in range(wl.n_layers):
+            x_np = wl.decode_activations(step, layer, T)
+            bias = torch.from_numpy(np.tile(wl.zipf_bias(layer), (T, 1)).astype(np.float32)).cuda()
+            ra = _run(a, True, layer, x_np, bias, T)
+            rb = _run(b, False, layer, x_np, bias, T)
+            for name, u, v in zip(("idx", "w", "logits", "slot", "trace", "counts", "y"), ra, rb):
+                assert np.array_equal(u.view(np.uint32) if u.dtype == np.float32 else u,
+                                      v.view(np.uint32) if v.dtype == np.float32 else v), (name, step, layer)
