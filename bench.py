@@ -206,8 +206,7 @@ def main():
         for l in range(L):
             b = bias[l]
             x = xsrc[l]
-            R.moe_route_lookup(c, l, x, T, b, None, idx[l], wts[l], slot[l], None, None, strm)
-            R.moe_ffn_decode(c, l, x, T, idx[l], wts[l], slot[l], y[l], strm)
+            R.moe_decode_layer(c, l, x, T, b, idx[l], wts[l], slot[l], y[l], strm)
 
     for s in range(args.warmup):
         step(s)

@@ -257,6 +257,17 @@ MOE_API moe_status moe_route_lookup(moe_ctx* ctx, int32_t layer, const void* x, 
                                     float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* slot_idx,
                                     moe_trace_rec* trace, int32_t* counts, moe_stream_t stream);
 
+/*
+ * One decode layer step: moe_route_lookup, then moe_ffn_decode, with their arguments,
+ * outputs and errors (y [T,H] fp32 out; topk_idx, topk_w, slot_idx [T,k] out).  In
+ * MOE_MODE_FUSED at T = 1 the lookup is the identity (slot = key, group g = rank g), so
+ * phase 1 takes the top k from the logits itself and the step runs in four launches
+ * (router GEMV, phase 1, phase 2, combine) with results bit-identical to the two calls.
+ * Asynchronous on the stream; capturable wherever moe_ffn_decode is.
+ */
+MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
+                                    int32_t* topk_idx, float* topk_w, int32_t* slot_idx, float* y, moe_stream_t stream);
+
 MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);
 

@@ -108,6 +108,7 @@ def _load():
         "moe_topk": (I32, [P, VP, I32, VP, VP, VP]),
         "expert_cache_lookup": (I32, [P, I32, VP, I32, VP, VP, VP, VP]),
         "moe_route_lookup": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP, VP, VP, VP]),
+        "moe_decode_layer": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP, VP]),
         "moe_ffn_decode": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP]),
         "moe_prefill_begin": (I32, [P, VP]),
         "moe_ffn_prefill": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP, VP]),
@@ -252,6 +253,11 @@ def moe_route_lookup(ctx: Ctx, layer, x, T, logit_bias, logits_out, topk_idx, to
     _check(ctx, lib.moe_route_lookup(ctx.handle, layer, _ptr(x), T, _ptr(logit_bias), _ptr(logits_out), _ptr(topk_idx),
                                      _ptr(topk_w), _ptr(slot_idx), _ptr(trace), _ptr(counts), _stream(stream)),
            "moe_route_lookup")
+
+
+def moe_decode_layer(ctx: Ctx, layer, x, T, logit_bias, topk_idx, topk_w, slot_idx, y, stream=None) -> None:
+    _check(ctx, lib.moe_decode_layer(ctx.handle, layer, _ptr(x), T, _ptr(logit_bias), _ptr(topk_idx), _ptr(topk_w),
+                                     _ptr(slot_idx), _ptr(y), _stream(stream)), "moe_decode_layer")
 
 
 def moe_ffn_decode(ctx: Ctx, layer, x, T, topk_idx, topk_w, slot_idx, y, stream=None) -> None:

@@ -454,27 +454,62 @@ __device__ __forceinline__ void load_x_words(const void* x, int H, int t, int c,
 // wavefront owns RW consecutive (gate, up) row pairs of one expert; all its loads are
 // issued before any is used, activations first (loads return in issue order), and the
 // RW results of a token leave in one store from lanes 0..RW-1.
-template <int WFMT, int CPL, int RW, int MAXT>
+template <int WFMT, int CPL, int RW, int MAXT, bool ROUTE = false>
 __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
   constexpr int XQ = kIsFp4<WFMT> ? 4 : 1;
   const int g = blockIdx.y;
-  // issued with the count (grp_slot has E >= gridDim.y entries, so the read is in bounds
-  // even for a group beyond the count, whose value is then unused)
-  const int slot = a.grp_slot[g];
   const int H = a.H, I = a.I;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   u32x4n xq[MAXT][CPL][XQ];
   int pair[MAXT];
   int n = 0;
-  if constexpr (MAXT == 1) {
-    // one token: its activation chunks need no other load, so they go first; the
-    // group's single pair (needed only for the store) comes with the slot
-    pair[0] = a.grp_pair0[g];
-    n = 1;
+  int slot;
+  if constexpr (ROUTE) {
+    // all resident, one token: the activations are requested first, then wavefront 0
+    // takes the top k from the logits (the selection and gates of the top-k kernel);
+    // group g is rank g and its slot is the key.  Workgroup (0, 0) publishes the step.
+    static_assert(MAXT == 1, "routed phase 1 is for one token");
+    __shared__ int s_idx[kSmallLookupPairs];
+    __shared__ int s_tk[kSmallLookupPairs];
+    __shared__ float s_tw[kSmallLookupPairs];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) load_x_words<XQ>(a.x, H, 0, lane + 64 * c, xq[0][c]);
+    const bool first = blockIdx.x == 0 && blockIdx.y == 0;
+    if (wave == 0)
+      topk_wave(a.logits, a.E, a.k, a.renorm, first ? a.topk_out : s_tk, first ? a.topk_w_out : s_tw, s_idx);
+    __syncthreads();
+    const int base = a.layer * a.E;
+    if (first && wave == 0 && lane < a.k) {
+      const int sl = base + s_idx[lane];
+      a.grp_slot_out[lane] = sl;
+      a.grp_pair0_out[lane] = lane;
+      a.pair_grp_out[lane] = lane;
+      if (a.slot_out) a.slot_out[lane] = sl;
+      if (lane == 0) {
+        a.cnt_out[C_NGRP] = a.k;
+        a.cnt_out[C_NPAIR_GPU] = a.k;
+        a.cnt_out[C_ERR] = 0;
+        a.cnt_out[C_T] = 1;
+      }
+    }
+    if (g >= a.k) return;
+    slot = base + s_idx[g];
+    pair[0] = g;
+    n = 1;
+  } else {
+    // issued with the count (grp_slot has E >= gridDim.y entries, so the read is in bounds
+    // even for a group beyond the count, whose value is then unused)
+    slot = a.grp_slot[g];
+    if constexpr (MAXT == 1) {
+      // one token: its activation chunks need no other load, so they go first; the
+      // group's single pair (needed only for the store) comes with the slot
+      pair[0] = a.grp_pair0[g];
+      n = 1;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) load_x_words<XQ>(a.x, H, 0, lane + 64 * c, xq[0][c]);
+    }
+    if (g >= a.cnt[C_NGRP]) return;
   }
-  if (g >= a.cnt[C_NGRP]) return;
   const int row0 = (blockIdx.x * 4 + wave) * RW;
   if (row0 >= I) return;
   const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
@@ -878,6 +913,39 @@ static void p1_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timing t
     dim3 grid((a.I + 4 * RW - 1) / (4 * RW), max_groups);
     launch_timed(dec_phase1_fast<W, A, CPL, RW, MAXT>, grid, dim3(256), 0, s, tm, a);
   }
+}
+
+template <int W, int CPL>
+static void p1_routed(const DecodeArgs& a, hipStream_t s, Timing tm) {
+  constexpr int RW = 4 / CPL;
+  dim3 grid((a.I + 4 * RW - 1) / (4 * RW), a.k);
+  launch_timed(dec_phase1_bf<W, CPL, RW, 1, true>, grid, dim3(256), 0, s, tm, a);
+}
+
+template <int W>
+static bool p1_routed_try(const DecodeArgs& a, hipStream_t s, Timing tm) {
+  switch (lane_chunks(W, a.H)) {
+    case 1: p1_routed<W, 1>(a, s, tm); return true;
+    case 2: p1_routed<W, 2>(a, s, tm); return true;
+    case 4: p1_routed<W, 4>(a, s, tm); return true;
+    default: return false;
+  }
+}
+
+// All-resident batch-1 phase 1 with the routing taken inside (bf16 activations, bf16 or
+// e2m1 weights, rows of 1, 2 or 4 wavefront-wide chunks, k <= 64).
+bool decode_phase1_routed_ok(int wfmt, int afmt, int H, int k) {
+  if (afmt != MOE_AFMT_BF16 || k > kSmallLookupPairs || wfmt == MOE_WFMT_F32) return false;
+  const int c = lane_chunks(wfmt, H);
+  return c == 1 || c == 2 || c == 4;
+}
+
+bool launch_decode_phase1_routed(int wfmt, int afmt, const DecodeArgs& a, hipStream_t s, Timing tm) {
+  if (a.T != 1 || !decode_phase1_routed_ok(wfmt, afmt, a.H, a.k)) return false;
+  if (wfmt == MOE_WFMT_BF16) return p1_routed_try<MOE_WFMT_BF16>(a, s, tm);
+  if (wfmt == MOE_WFMT_FP4) return p1_routed_try<MOE_WFMT_FP4>(a, s, tm);
+  if (wfmt == MOE_WFMT_MXFP4) return p1_routed_try<MOE_WFMT_MXFP4>(a, s, tm);
+  return false;
 }
 
 template <int W, int A, int MAXT>

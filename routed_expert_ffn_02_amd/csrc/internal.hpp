@@ -81,6 +81,17 @@ struct DecodeArgs {
   float* h;                  // [T*k, I] scratch
   float* d;                  // [T*k, H] scratch (per-pair expert outputs)
   float* y;                  // [T,H]
+  // all-resident batch-1 steps routed inside phase 1 (logits != nullptr): every workgroup
+  // takes the top k itself; group g is rank g, its slot layer * E + expert
+  const float* logits;       // [E]
+  int32_t E, renorm, layer;
+  int32_t* topk_out;         // [k] written by workgroup (0, 0), with
+  float* topk_w_out;         // [k] the gates,
+  int32_t* slot_out;         // [k] the slot ids (or nullptr),
+  int32_t* grp_slot_out;     // [k] and the group tables phase 2 and the combine read
+  int32_t* grp_pair0_out;    // [k]
+  int32_t* pair_grp_out;     // [k]
+  int32_t* cnt_out;          // C_NGRP, C_NPAIR_GPU, C_ERR, C_T
 };
 
 struct FillArgs {
@@ -133,6 +144,8 @@ struct Timing {
 };
 void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
+bool decode_phase1_routed_ok(int wfmt, int afmt, int H, int k);
+bool launch_decode_phase1_routed(int wfmt, int afmt, const DecodeArgs& a, hipStream_t s, Timing tm = {});
 int decode_phase2_rowblocks(int H);
 void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s);
 int fill_blocks_per_record(int64_t rec_bytes);

@@ -680,6 +680,80 @@ MOE_API moe_status moe_route_lookup(moe_ctx* ctx, int32_t layer, const void* x, 
   return MOE_OK;
 }
 
+MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
+                                    int32_t* topk_idx, float* topk_w, int32_t* slot_idx, float* y, moe_stream_t stream) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(ctx->bound && ctx->router_w, "bind first");
+  CHECK_ARG(!ctx->in_prefill, "decode inside prefill");
+  CHECK_ARG(layer >= 0 && layer < ctx->cfg.n_layers, "layer out of range");
+  CHECK_ARG(x && topk_idx && topk_w && slot_idx && y, "null pointer");
+  CHECK_ARG(T >= 1 && T <= kDecodeMaxTok && T <= ctx->cfg.max_tokens && (int64_t)T * ctx->cfg.hidden <= kDecodeMaxTH,
+            "decode needs T <= 8, T <= max_tokens and T*H <= 16384");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int k = ctx->cfg.top_k, E = ctx->cfg.n_experts, H = ctx->cfg.hidden, I = ctx->cfg.inter;
+  if (ctx->cfg.mode == MOE_MODE_FUSED && T == 1 && decode_phase1_routed_ok(ctx->cfg.wfmt, ctx->cfg.afmt, H, k)) {
+    // all resident, one token: the lookup is the identity, so phase 1 routes itself and
+    // the step takes four launches: router GEMV, phase 1, phase 2, combine
+    DecodeArgs d{};
+    d.x = x;
+    d.w = topk_w;
+    d.arena = ctx->arena;
+    d.rec_bytes = ctx->S;
+    d.T = 1;
+    d.k = k;
+    d.H = H;
+    d.I = I;
+    d.grp_slot = ctx->grp_slot;
+    d.grp_pair0 = ctx->grp_pair0;
+    d.pair_grp = ctx->pair_grp;
+    d.cnt = ctx->cnt;
+    d.h = ctx->h;
+    d.d = ctx->dpair;
+    d.y = y;
+    d.logits = ctx->logits;
+    d.E = E;
+    d.renorm = ctx->cfg.renorm;
+    d.layer = layer;
+    d.topk_out = topk_idx;
+    d.topk_w_out = topk_w;
+    d.slot_out = slot_idx;
+    d.grp_slot_out = ctx->grp_slot;
+    d.grp_pair0_out = ctx->grp_pair0;
+    d.pair_grp_out = ctx->pair_grp;
+    d.cnt_out = ctx->cnt;
+    launch_route_logits(x, ctx->cfg.afmt, ctx->router_w + (int64_t)layer * E * H, logit_bias, ctx->logits, 1, E, H, s);
+    bool routed;
+    {
+      TimedScope t1(ctx, s, TK_P1);
+      routed = launch_decode_phase1_routed(ctx->cfg.wfmt, ctx->cfg.afmt, d, s, t1.tm);
+    }
+    if (routed) {
+      {
+        TimedScope t2(ctx, s, TK_P2);
+        launch_decode_phase2(ctx->cfg.wfmt, d, k, s, t2.tm);
+      }
+      launch_decode_combine(d, nullptr, s);
+      HIPCHK(hipGetLastError());
+      if ((ctx->cfg.flags & MOE_FLAG_PROFILE) && !capturing(s)) {
+        const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
+        ctx->stats.phase1_launches += 1;
+        ctx->stats.phase2_launches += 1;
+        ctx->stats.phase1_bytes += (uint64_t)k * 2 * I * wrow_h + (uint64_t)H * act_bytes(ctx->cfg) + (uint64_t)k * I * 4;
+        ctx->stats.phase2_bytes += (uint64_t)k * H * wrow_i + (uint64_t)k * I * 4 + (uint64_t)H * 4;
+      }
+      ctx->stats.lookups += 1;
+      ctx->stats.hits += k;
+      ctx->stats.decode_calls += 1;
+      ctx->last_lookup_layer = -1;
+      return MOE_OK;
+    }
+  }
+  moe_status st = moe_route_lookup(ctx, layer, x, T, logit_bias, nullptr, topk_idx, topk_w, slot_idx, nullptr, nullptr,
+                                   stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_decode(ctx, layer, x, T, topk_idx, topk_w, slot_idx, y, stream);
+}
+
 MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
                                   const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream) {
   if (!ctx) return MOE_EINVAL;

@@ -55,3 +55,42 @@ def test_route_lookup_equals_route_then_lookup(wl, mode, T):
             for name, u, v in zip(("idx", "w", "logits", "slot", "trace", "counts", "y"), ra, rb):
                 assert np.array_equal(u.view(np.uint32) if u.dtype == np.float32 else u,
                                       v.view(np.uint32) if v.dtype == np.float32 else v), (name, step, layer)
+
+
+FUSED_WL = {"bf16": W.A3B_DECODE.with_(name="dl_bf16", n_layers=2, n_experts=16, top_k=8, hidden=2048, inter=512),
+            "fp4": W.DSV4.with_(name="dl_fp4", n_layers=2, n_experts=16, top_k=6, hidden=4096, inter=512),
+            "mxfp4": W.DSV4_MX.with_(name="dl_mx", n_layers=2, n_experts=16, top_k=6, hidden=4096, inter=512),
+            "fp32": W.TINY.with_(n_layers=2)}
+
+
+@pytest.mark.parametrize("fmt", list(FUSED_WL))
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("T", [1, 2])
+def test_decode_layer_equals_the_two_calls(fmt, mode, T):
+    """moe_decode_layer (all-resident batch 1: phase 1 routes itself) against
+    moe_route_lookup + moe_ffn_decode: indices, gates, slot ids and y bit for bit."""
+    import routed_expert_ffn_02_amd as R
+    wl = FUSED_WL[fmt]
+    n_slots = wl.n_keys if mode == 1 else None
+    a = Harness(wl, mode, n_slots=n_slots, max_tokens=T)
+    b = Harness(wl, mode, n_slots=n_slots, max_tokens=T)
+    k, E, H = wl.top_k, wl.n_experts, wl.hidden
+    for step in range(4):
+        for layer in range(wl.n_layers):
+            x = dev_act(wl, wl.decode_activations(step, layer, T))
+            bias = torch.from_numpy(np.tile(wl.zipf_bias(layer), (T, 1)).astype(np.float32)).cuda()
+            outs = []
+            for h, one in ((a, True), (b, False)):
+                idx = torch.full((T, k), -5, dtype=torch.int32, device="cuda")
+                w = torch.full((T, k), -1.0, dtype=torch.float32, device="cuda")
+                slot = torch.full((T, k), -9, dtype=torch.int32, device="cuda")
+                y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+                if one:
+                    R.moe_decode_layer(h.ctx, layer, x, T, bias, idx, w, slot, y)
+                else:
+                    R.moe_route_lookup(h.ctx, layer, x, T, bias, None, idx, w, slot)
+                    R.moe_ffn_decode(h.ctx, layer, x, T, idx, w, slot, y)
+                torch.cuda.synchronize()
+                outs.append([t.cpu().numpy() for t in (idx, w.view(torch.int32), slot, y.view(torch.int32))])
+            for name, u, v in zip(("idx", "w", "slot", "y"), *outs):
+                assert np.array_equal(u, v), (name, step, layer)
