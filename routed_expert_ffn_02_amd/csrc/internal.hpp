@@ -78,6 +78,7 @@ struct DecodeArgs {
   const int32_t* grp_pair0;  // [G] first pair routed to group g (the only one when T == 1)
   const int32_t* pair_grp;   // [T*k]
   const int32_t* cnt;        // device counters (C_NGRP)
+  const int32_t* slot_idx;   // [T,k] slot of each pair (or a CPU flag), as the lookup wrote it
   float* h;                  // [T*k, I] scratch
   float* d;                  // [T*k, H] scratch (per-pair expert outputs)
   float* y;                  // [T,H]
@@ -145,6 +146,7 @@ struct Timing {
 void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 bool decode_phase1_routed_ok(int wfmt, int afmt, int H, int k);
+bool launch_decode_phase2_combine(int wfmt, const DecodeArgs& a, hipStream_t s, Timing tm = {});
 bool launch_decode_phase1_routed(int wfmt, int afmt, const DecodeArgs& a, hipStream_t s, Timing tm = {});
 int decode_phase2_rowblocks(int H);
 void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s);

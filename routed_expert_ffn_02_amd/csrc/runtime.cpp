@@ -707,6 +707,7 @@ MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, 
     d.grp_pair0 = ctx->grp_pair0;
     d.pair_grp = ctx->pair_grp;
     d.cnt = ctx->cnt;
+    d.slot_idx = slot_idx;
     d.h = ctx->h;
     d.d = ctx->dpair;
     d.y = y;
@@ -730,9 +731,11 @@ MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, 
     if (routed) {
       {
         TimedScope t2(ctx, s, TK_P2);
-        launch_decode_phase2(ctx->cfg.wfmt, d, k, s, t2.tm);
+        if (!launch_decode_phase2_combine(ctx->cfg.wfmt, d, s, t2.tm)) {
+          launch_decode_phase2(ctx->cfg.wfmt, d, k, s, t2.tm);
+          launch_decode_combine(d, nullptr, s);
+        }
       }
-      launch_decode_combine(d, nullptr, s);
       HIPCHK(hipGetLastError());
       if ((ctx->cfg.flags & MOE_FLAG_PROFILE) && !capturing(s)) {
         const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
@@ -791,7 +794,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     moe_status st = read_step(ctx, s, true, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
   }
-  DecodeArgs d;
+  DecodeArgs d{};
   d.x = x;
   d.w = topk_w;
   d.arena = ctx->arena;
@@ -804,6 +807,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   d.grp_pair0 = ctx->grp_pair0;
   d.pair_grp = ctx->pair_grp;
   d.cnt = ctx->cnt;
+  d.slot_idx = slot_idx;
   d.h = ctx->h;
   d.d = ctx->dpair;
   d.y = y;
@@ -838,9 +842,13 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     TimedScope t1(ctx, s, TK_P1);
     launch_decode_phase1(ctx->cfg.wfmt, ctx->cfg.afmt, d, max_groups, s, t1.tm);
   }
+  // one token with no CPU branch possible: phase 2 and the combine in one launch
+  const bool p2c = T == 1 && !inputs && !has_cpu && !async_cpu;
+  bool combined = false;
   {
     TimedScope t2(ctx, s, TK_P2);
-    launch_decode_phase2(ctx->cfg.wfmt, d, max_groups, s, t2.tm);
+    if (p2c) combined = launch_decode_phase2_combine(ctx->cfg.wfmt, d, s, t2.tm);
+    if (!combined) launch_decode_phase2(ctx->cfg.wfmt, d, max_groups, s, t2.tm);
   }
   if (has_cpu) {
     // the GPU path is enqueued; the CPU branch runs now, concurrently, then merges exactly
@@ -848,7 +856,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     if (st != MOE_OK) return st;
   }
   if (async_cpu) HIPCHK(hipStreamWaitEvent(s, ctx->ev_join, 0));
-  launch_decode_combine(d, y_cpu, s);
+  if (!combined) launch_decode_combine(d, y_cpu, s);
   HIPCHK(hipGetLastError());
   if (profile && devfill) {  // bytes are added on the device
     ctx->stats.phase1_launches += 1;

@@ -94,3 +94,33 @@ def test_decode_layer_equals_the_two_calls(fmt, mode, T):
                 outs.append([t.cpu().numpy() for t in (idx, w.view(torch.int32), slot, y.view(torch.int32))])
             for name, u, v in zip(("idx", "w", "slot", "y"), *outs):
                 assert np.array_equal(u, v), (name, step, layer)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp4", "mxfp4"])
+def test_fused_phase2_combine_equals_separate_kernels(fmt):
+    """Batch 1 with no CPU branch possible (offload) takes phase 2 and the combine in one
+    kernel; hybrid mode with B_H <= B_P fills every miss too but keeps the separate
+    kernels.  Same routing, same fills: y must agree bit for bit."""
+    import routed_expert_ffn_02_amd as R
+    wl = FUSED_WL[fmt]
+    n_slots = wl.n_keys // 2
+    a = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n_slots, max_tokens=1)
+    b = Harness(wl, R.MOE_MODE_HYBRID, n_slots=n_slots, max_tokens=1, bw=(100, 50))
+    k, H = wl.top_k, wl.hidden
+    for step in range(5):
+        for layer in range(wl.n_layers):
+            x = dev_act(wl, wl.decode_activations(step, layer, 1))
+            bias = torch.from_numpy(wl.zipf_bias(layer)[None, :].astype(np.float32)).cuda()
+            ys = []
+            for h in (a, b):
+                idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+                w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+                slot = torch.empty((1, k), dtype=torch.int32, device="cuda")
+                cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+                y = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
+                R.moe_route_lookup(h.ctx, layer, x, 1, bias, None, idx, w, slot, None, cnt)
+                R.moe_ffn_decode(h.ctx, layer, x, 1, idx, w, slot, y)
+                torch.cuda.synchronize()
+                assert int(cnt[2]) == 0          # nothing ran on the CPU
+                ys.append(y.view(torch.int32).cpu().numpy())
+            assert np.array_equal(ys[0], ys[1]), (step, layer)
