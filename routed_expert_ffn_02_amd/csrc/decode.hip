@@ -814,87 +814,71 @@ __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
 }
 
 // Phase 2 with the combine, one token and no CPU branch (every pair is a GPU pair; pair
-// j's expert is found through its slot id, whatever the lookup's group numbering): a
-// workgroup owns 4 * R2 rows of the output.  The k
-// activated rows are rounded to bf16 once per workgroup into LDS (as dec_phase2_bf does
-// per wavefront); each wavefront streams its rows of all k experts' W_down (all loads
-// issued first) and sums w_j * d_j in rank order with one fused multiply-add per pair, the
-// arithmetic of dec_phase2_bf followed by dec_combine, so the result is bit-identical.
+// j's expert is found through its slot id, whatever the lookup's group numbering).  A
+// workgroup owns R2 rows of the output and has one wavefront per pair: wavefront j
+// computes its expert's R2 rows of W_down h_j exactly as dec_phase2_bf does (the same
+// loads, bf16 rounding of h_j and dot path), parks them in LDS, and wavefront 0 sums
+// w_j * d_j in rank order with one fused multiply-add per pair, the arithmetic of
+// dec_combine, so the result is bit-identical to the two separate kernels.
 constexpr int kP2cMaxK = 8;
 
-template <int WFMT, int R2>
-__global__ __launch_bounds__(256) void dec_phase2_combine_bf(DecodeArgs a) {
+template <int WFMT>
+__global__ __launch_bounds__(64 * kP2cMaxK) void dec_phase2_combine_bf(DecodeArgs a) {
+  constexpr int R2 = kP2RowsPerWave;
   constexpr int EPC = kIsFp4<WFMT> ? 32 : 8;  // elements per lane chunk (one 16-byte weight load)
-  constexpr int HW = EPC / 2;                  // bf16 pair words of h per lane chunk
-  extern __shared__ uint32_t s_h[];            // [k][64 * HW] bf16 pairs
+  __shared__ float s_d[kP2cMaxK][R2];
   const int H = a.H, I = a.I, k = a.k;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = (blockIdx.x * 4 + wave) * R2;
-  // the group count, gates and pair slots first (scalar loads issued together); a step
-  // whose lookup did not place every pair (an expert id out of range: no groups) has
-  // stale slot entries, so nothing is read through them and y is 0, as the separate
+  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;  // blockDim.x = 64 * k
+  const int r0 = blockIdx.x * R2;
+  // a step whose lookup did not place every pair (an expert id out of range: no groups)
+  // has stale slot entries, so nothing is read through them and y is 0, as the separate
   // kernels give
   const int ngrp = a.cnt[C_NGRP];
-  float wj[kP2cMaxK];
-  int slot[kP2cMaxK];
-#pragma unroll
-  for (int j = 0; j < kP2cMaxK; ++j) {
-    wj[j] = j < k ? a.w[j] : 0.f;
-    slot[j] = j < k ? a.slot_idx[j] : 0;
-  }
+  const int slot = a.slot_idx[j];
   if (ngrp != k) {
-    if (lane < R2 && r0 + lane < H) a.y[r0 + lane] = 0.f;
+    if (j == 0 && lane < R2 && r0 + lane < H) a.y[r0 + lane] = 0.f;
     return;
   }
-  u32x4n q[kP2cMaxK][R2];
-  uint16_t scr[kP2cMaxK][R2];
+  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  f32x4n hq[EPC / 4];
+  const f32x4n* hp = reinterpret_cast<const f32x4n*>(a.h + (int64_t)j * I + lane * EPC);
 #pragma unroll
-  for (int j = 0; j < kP2cMaxK; ++j) {
-    if (j < k) {
-      const uint8_t* rec = a.arena + (int64_t)slot[j] * a.rec_bytes;
+  for (int i = 0; i < EPC / 4; ++i) hq[i] = hp[i];
+  uint16_t scr[R2];
+  if constexpr (kIsFp4<WFMT>) {
 #pragma unroll
-      for (int r = 0; r < R2; ++r) {
-        const int row = min(r0 + r, H - 1);
-        if constexpr (kIsFp4<WFMT>) scr[j][r] = (uint16_t)scale_raw<WFMT>(scale_row<WFMT>(rec, 2, row, H, I), lane);
-        q[j][r] = reinterpret_cast<const u32x4n*>(tensor_row<WFMT>(rec, 2, row, H, I))[lane];
-      }
-    }
+    for (int r = 0; r < R2; ++r) scr[r] = (uint16_t)scale_raw<WFMT>(scale_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I), lane);
   }
-  // stage h: pair j's I values as bf16 pairs (round to nearest even)
-  for (int i = threadIdx.x; i < k * (I / 4); i += 256) {
-    const int j = i / (I / 4), c = i % (I / 4);
-    const f32x4n v = reinterpret_cast<const f32x4n*>(a.h + (int64_t)j * I)[c];
-    const bf16x2 b0 = {(__bf16)v[0], (__bf16)v[1]}, b1 = {(__bf16)v[2], (__bf16)v[3]};
-    s_h[j * (I / 2) + 2 * c] = __builtin_bit_cast(uint32_t, b0);
-    s_h[j * (I / 2) + 2 * c + 1] = __builtin_bit_cast(uint32_t, b1);
+  u32x4n q[R2];
+#pragma unroll
+  for (int r = 0; r < R2; ++r)
+    q[r] = reinterpret_cast<const u32x4n*>(tensor_row<WFMT>(rec, 2, min(r0 + r, H - 1), H, I))[lane];
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before any use
+  uint32_t hw[EPC / 2];
+#pragma unroll
+  for (int i = 0; i < EPC / 2; ++i) {
+    const bf16x2 b = {(__bf16)hq[i / 2][2 * (i % 2)], (__bf16)hq[i / 2][2 * (i % 2) + 1]};
+    hw[i] = __builtin_bit_cast(uint32_t, b);
   }
+  float out[R2];
+#pragma unroll
+  for (int r = 0; r < R2; ++r) {
+    float p;
+    if constexpr (WFMT == MOE_WFMT_MXFP4) p = chunk_dot_bf16<WFMT>(q[r], hw, e8m0_to_f32(scr[r]));
+    else if constexpr (WFMT == MOE_WFMT_FP4) p = bf16_to_f32(scr[r]) * chunk_dot_bf16<WFMT>(q[r], hw);
+    else p = chunk_dot_bf16<WFMT>(q[r], hw);
+    out[r] = wave_sum(p);
+  }
+  float v = out[0];
+#pragma unroll
+  for (int r = 1; r < R2; ++r) v = (lane == r) ? out[r] : v;
+  if (lane < R2) s_d[j][lane] = v;
   __syncthreads();
-  float y[R2];
-#pragma unroll
-  for (int r = 0; r < R2; ++r) y[r] = 0.f;
-#pragma unroll
-  for (int j = 0; j < kP2cMaxK; ++j) {
-    if (j < k) {
-      uint32_t hw[HW];
-#pragma unroll
-      for (int i = 0; i < HW; i += 4) {
-        const u32x4n v = *reinterpret_cast<const u32x4n*>(&s_h[j * (I / 2) + lane * HW + i]);
-        hw[i] = v[0]; hw[i + 1] = v[1]; hw[i + 2] = v[2]; hw[i + 3] = v[3];
-      }
-#pragma unroll
-      for (int r = 0; r < R2; ++r) {
-        float p;
-        if constexpr (WFMT == MOE_WFMT_MXFP4) p = chunk_dot_bf16<WFMT>(q[j][r], hw, e8m0_to_f32(scr[j][r]));
-        else if constexpr (WFMT == MOE_WFMT_FP4) p = bf16_to_f32(scr[j][r]) * chunk_dot_bf16<WFMT>(q[j][r], hw);
-        else p = chunk_dot_bf16<WFMT>(q[j][r], hw);
-        y[r] = fmaf(wj[j], wave_sum(p), y[r]);
-      }
-    }
+  if (j == 0 && lane < R2 && r0 + lane < H) {
+    float y = 0.f;
+    for (int t = 0; t < k; ++t) y = fmaf(a.w[t], s_d[t][lane], y);
+    a.y[r0 + lane] = y;
   }
-  float v = y[0];
-#pragma unroll
-  for (int r = 1; r < R2; ++r) v = (lane == r) ? y[r] : v;
-  if (lane < R2 && r0 + lane < H) a.y[r0 + lane] = v;
 }
 
 // Phase 2, generic shapes.
@@ -1104,13 +1088,11 @@ void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStre
 // Phase 2 and the combine in one launch for one token with no CPU branch (see
 // dec_phase2_combine_bf); false: the shape or format needs the separate kernels.
 bool launch_decode_phase2_combine(int wfmt, const DecodeArgs& a, hipStream_t s, Timing tm) {
-  if (a.T != 1 || a.k > kP2cMaxK || wfmt == MOE_WFMT_F32 || lane_chunks(wfmt, a.I) != 1) return false;
-  constexpr int R2 = 2;
-  const dim3 grid((a.H + 4 * R2 - 1) / (4 * R2));
-  const uint32_t lds = (uint32_t)a.k * (uint32_t)a.I * 2;
-  if (wfmt == MOE_WFMT_BF16) launch_timed(dec_phase2_combine_bf<MOE_WFMT_BF16, R2>, grid, dim3(256), lds, s, tm, a);
-  else if (wfmt == MOE_WFMT_FP4) launch_timed(dec_phase2_combine_bf<MOE_WFMT_FP4, R2>, grid, dim3(256), lds, s, tm, a);
-  else launch_timed(dec_phase2_combine_bf<MOE_WFMT_MXFP4, R2>, grid, dim3(256), lds, s, tm, a);
+  if (a.T != 1 || a.k < 1 || a.k > kP2cMaxK || wfmt == MOE_WFMT_F32 || lane_chunks(wfmt, a.I) != 1) return false;
+  const dim3 grid((a.H + kP2RowsPerWave - 1) / kP2RowsPerWave), block(64 * a.k);
+  if (wfmt == MOE_WFMT_BF16) launch_timed(dec_phase2_combine_bf<MOE_WFMT_BF16>, grid, block, 0, s, tm, a);
+  else if (wfmt == MOE_WFMT_FP4) launch_timed(dec_phase2_combine_bf<MOE_WFMT_FP4>, grid, block, 0, s, tm, a);
+  else launch_timed(dec_phase2_combine_bf<MOE_WFMT_MXFP4>, grid, block, 0, s, tm, a);
   return true;
 }
 
