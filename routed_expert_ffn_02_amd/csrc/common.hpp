@@ -106,15 +106,16 @@ __device__ __forceinline__ bool topk_better(float va, int ia, float vb, int ib) 
   return va > vb || (va == vb && ia < ib);
 }
 
-__device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, int k, int renorm,
-                                          int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                          int* lds_idx = nullptr) {
+// PL logits per lane (E <= 64 * PL): the scan and the selection rounds touch only those.
+template <int PL>
+__device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E, int k, int renorm,
+                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out, int* lds_idx) {
   const int lane = threadIdx.x & 63;
-  float v[kTopkPerLane];
-  bool taken[kTopkPerLane];
+  float v[PL];
+  bool taken[PL];
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kTopkPerLane; ++i) {
+  for (int i = 0; i < PL; ++i) {
     int e = lane + 64 * i;
     v[i] = (e < E) ? z[e] : -INFINITY;
     taken[i] = (e >= E);
@@ -123,7 +124,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   mx = wave_max(mx);
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kTopkPerLane; ++i)
+  for (int i = 0; i < PL; ++i)
     if (lane + 64 * i < E) sum += __expf(v[i] - mx);
   sum = wave_sum(sum);
   float sel_sum = 0.f;
@@ -131,17 +132,21 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
       int e = lane + 64 * i;
       if (!taken[i] && topk_better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
     }
-    // wave arg-max under the same order: the largest value, then the lowest index
-    // among the lanes holding it
+    // wave arg-max under the same order: the largest value, then the lowest index among
+    // the lanes holding it (a single holder, the usual case, is read from its lane)
     const float wv = wave_max(bv);
-    bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
+    const uint64_t holders = __ballot(bv == wv);
+    if (__popcll(holders) == 1)
+      bi = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)holders) - 1);
+    else
+      bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
     bv = wv;
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i)
+    for (int i = 0; i < PL; ++i)
       if (lane + 64 * i == bi) taken[i] = true;
     float p = __expf(bv - mx) / sum;
     sel_sum += p;
@@ -154,6 +159,16 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   if (renorm && lane == 0) {
     for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sel_sum;
   }
+}
+
+__device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, int k, int renorm,
+                                          int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                          int* lds_idx = nullptr) {
+  if (E <= 64) topk_wave_pl<1>(z, E, k, renorm, idx_out, w_out, lds_idx);
+  else if (E <= 128) topk_wave_pl<2>(z, E, k, renorm, idx_out, w_out, lds_idx);
+  else if (E <= 256) topk_wave_pl<4>(z, E, k, renorm, idx_out, w_out, lds_idx);
+  else if (E <= 512) topk_wave_pl<8>(z, E, k, renorm, idx_out, w_out, lds_idx);
+  else topk_wave_pl<kTopkPerLane>(z, E, k, renorm, idx_out, w_out, lds_idx);
 }
 
 // Two e2m1 codes (byte `sel` of w, low nibble first) -> two fp32 values, exact.

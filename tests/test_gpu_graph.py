@@ -44,21 +44,25 @@ class StepBuffers:
         return [t.cpu().numpy().copy() for t in (self.y, self.idx, self.slot, self.trace, self.cnt)]
 
 
-def run_step(R, h, b, stream):
+def run_step(R, h, b, stream, layer_call=False):
     for l in range(h.wl.n_layers):
+        if layer_call:  # one call per layer (all resident at batch 1: router + top k in one launch)
+            R.moe_decode_layer(h.ctx, l, b.x[l], b.T, None, b.idx[l], b.w[l], b.slot[l], b.y[l], stream)
+            continue
         R.moe_route(h.ctx, l, b.x[l], b.T, None, None, b.idx[l], b.w[l], stream)
         R.expert_cache_lookup(h.ctx, l, b.idx[l], b.T, b.slot[l], b.trace[l], b.cnt[l], stream)
         R.moe_ffn_decode(h.ctx, l, b.x[l], b.T, b.idx[l], b.w[l], b.slot[l], b.y[l], stream)
 
 
 @pytest.mark.parametrize("wl", [BF16, FP4, ROWS], ids=["bf16", "fp4", "rows"])
-@pytest.mark.parametrize("mode", ["offload_device_fills", "hybrid_device_fills", "fused"])
+@pytest.mark.parametrize("mode", ["offload_device_fills", "hybrid_device_fills", "fused", "fused_layer_call"])
 def test_captured_step_replays_like_eager(wl, mode):
     import routed_expert_ffn_02_amd as R
     import torch
     T = 1
     bw = (0, 0)
-    if mode == "fused":
+    lc = mode == "fused_layer_call"
+    if mode.startswith("fused"):
         kw = dict(mode=R.MOE_MODE_FUSED)
         flags = 0
     elif mode == "hybrid_device_fills":  # few slots: the CPU branch runs as host nodes
@@ -75,12 +79,12 @@ def test_captured_step_replays_like_eager(wl, mode):
     # step 0 eagerly on both
     be.load(wl, 0)
     bg.load(wl, 0)
-    run_step(R, eager, be, None)
-    run_step(R, graph, bg, None)
+    run_step(R, eager, be, None, lc)
+    run_step(R, graph, bg, None, lc)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        run_step(R, graph, bg, torch.cuda.current_stream().cuda_stream)
+        run_step(R, graph, bg, torch.cuda.current_stream().cuda_stream, lc)
     scratch = torch.randn(1 << 16, device="cuda")
     for step in range(1, 9):
         bg.load(wl, step)
@@ -88,14 +92,14 @@ def test_captured_step_replays_like_eager(wl, mode):
         scratch.mul_(0.5).add_(1.0)  # unrelated eager work between replays
         torch.cuda.synchronize()
         be.load(wl, step)
-        run_step(R, eager, be, None)
+        run_step(R, eager, be, None, lc)
         torch.cuda.synchronize()
         for a, b_, name in zip(bg.outputs(), be.outputs(), ("y", "idx", "slot", "trace", "cnt")):
             assert np.array_equal(a.view(np.uint8), b_.view(np.uint8)), (step, name)
     R.moe_sync(graph.ctx)
     R.moe_sync(eager.ctx)
     sg, se = R.moe_get_stats(graph.ctx), R.moe_get_stats(eager.ctx)
-    if mode != "fused":
+    if not mode.startswith("fused"):
         assert sg["fills"] == se["fills"] > 0 and sg["hits"] == se["hits"] and sg["lookups"] == se["lookups"]
         assert sg["cpu_experts"] == se["cpu_experts"]
         if mode == "hybrid_device_fills":

@@ -16,7 +16,7 @@ SMALL_BF16 = W.A3B_DECODE.with_(name="small_bf16", n_layers=2, n_experts=64, top
 def test_topk_bitexact_on_identical_logits():
     """Decisions taken on the same fp32 logits: indices bit-exact, ties to the lower index."""
     import routed_expert_ffn_02_amd as R
-    for E, k in ((8, 2), (256, 8), (256, 6), (1024, 16)):
+    for E, k in ((8, 2), (100, 5), (256, 8), (256, 6), (512, 8), (1024, 16)):
         wl = W.TINY.with_(n_experts=E, top_k=k)
         h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=1)
         rng = np.random.default_rng(E + k)
