@@ -15,6 +15,9 @@ PF_FP4 = W.DSV4.with_(name="pf_fp4", n_layers=3, n_experts=16, top_k=3, hidden=2
 # inter a multiple of 256 takes the LDS-staged FP4 kernels; 128 takes the register-streamed ones
 PF_FP4_256 = W.DSV4.with_(name="pf_fp4_256", n_layers=3, n_experts=16, top_k=3, hidden=512, inter=256)
 PF_MX = W.DSV4_MX.with_(name="pf_mxfp4", n_layers=3, n_experts=16, top_k=3, hidden=512, inter=256)
+# hidden a multiple of 512 takes the down-projection blocks of 512 columns; 768 the 256-column ones
+PF_FP4_768 = W.DSV4.with_(name="pf_fp4_768", n_layers=2, n_experts=16, top_k=3, hidden=768, inter=256)
+PF_MX_768 = W.DSV4_MX.with_(name="pf_mxfp4_768", n_layers=2, n_experts=16, top_k=3, hidden=768, inter=256)
 
 
 def _route_np(wl, layer, x):
@@ -29,7 +32,8 @@ def _expected(wl, layer, x, idx, w):
     return oracle.moe_combine(outs, w)
 
 
-@pytest.mark.parametrize("wl", [PF_BF16, PF_FP4, PF_FP4_256, PF_MX], ids=["bf16", "fp4", "fp4_staged", "mxfp4"])
+@pytest.mark.parametrize("wl", [PF_BF16, PF_FP4, PF_FP4_256, PF_MX, PF_FP4_768, PF_MX_768],
+                         ids=["bf16", "fp4", "fp4_staged", "mxfp4", "fp4_staged_h768", "mxfp4_h768"])
 @pytest.mark.parametrize("T", [1, 100, 257])
 def test_buffered_prefill_matches_oracle(wl, T):
     import routed_expert_ffn_02_amd as R
