@@ -127,7 +127,10 @@ __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E,
   for (int i = 0; i < PL; ++i)
     if (lane + 64 * i < E) sum += __expf(v[i] - mx);
   sum = wave_sum(sum);
-  float sel_sum = 0.f;
+  // selection rounds carry only the arg-max; lane j keeps the j-th winner (k <= 64) and
+  // the gates are formed after the loop, all lanes at once
+  int my_idx = 0;
+  float my_v = -INFINITY;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
@@ -144,19 +147,32 @@ __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E,
       bi = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)holders) - 1);
     else
       bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
-    bv = wv;
 #pragma unroll
     for (int i = 0; i < PL; ++i)
       if (lane + 64 * i == bi) taken[i] = true;
-    float p = __expf(bv - mx) / sum;
-    sel_sum += p;
-    if (lane == 0) {
+    if (k <= 64) {
+      if (lane == j) { my_idx = bi; my_v = wv; }
+    } else if (lane == 0) {  // more than one selection per lane: written as found
       idx_out[j] = bi;
-      w_out[j] = p;
+      w_out[j] = __expf(wv - mx) / sum;
       if (lds_idx) lds_idx[j] = bi;
     }
   }
-  if (renorm && lane == 0) {
+  if (k <= 64) {
+    const float p = __expf(my_v - mx) / sum;
+    if (lane < k) {
+      idx_out[lane] = my_idx;
+      w_out[lane] = p;
+      if (lds_idx) lds_idx[lane] = my_idx;
+    }
+    if (renorm) {
+      float sel_sum = 0.f;  // in rank order
+      for (int j = 0; j < k; ++j) sel_sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
+      if (lane < k) w_out[lane] = p / sel_sum;
+    }
+  } else if (renorm && lane == 0) {
+    float sel_sum = 0.f;
+    for (int j = 0; j < k; ++j) sel_sum += w_out[j];
     for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sel_sum;
   }
 }
