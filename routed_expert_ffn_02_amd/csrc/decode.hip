@@ -986,7 +986,9 @@ static void p1_fast(const DecodeArgs& a, int max_groups, hipStream_t s, Timing t
 
 template <int W, int CPL>
 static void p1_routed(const DecodeArgs& a, hipStream_t s, Timing tm) {
-  constexpr int RW = 4 / CPL;
+  // every workgroup pays the top-k latency before its loads, so the grid should fit the
+  // chip in one round: e2m1 rows take twice the rows per wavefront of the plain kernel
+  constexpr int RW = kIsFp4<W> ? 8 / CPL : 4 / CPL;
   dim3 grid((a.I + 4 * RW - 1) / (4 * RW), a.k);
   launch_timed(dec_phase1_bf<W, CPL, RW, 1, true>, grid, dim3(256), 0, s, tm, a);
 }
