@@ -260,7 +260,7 @@ def main():
             step(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, capture_error_mode="thread_local"):
             step(1, Xs, torch.cuda.current_stream().cuda_stream)
         R.moe_reset_stats(ctx)
         tg = time.perf_counter()
@@ -297,7 +297,8 @@ def main():
         hybrid = {"tokens_per_s": round(args.steps * T / hel, 2), "ms_per_step": round(hel * 1e3 / args.steps, 3),
                   "fills": hs["fills"], "cpu_experts": hs["cpu_experts"],
                   "cpu_branch_ms_per_step": round(hs["cpu_ms"] / args.steps, 3),
-                  "fill_copy_ms_per_step": round(hs["copy_ms"] / args.steps, 3)}
+                  "fill_path": "host DMA" if args.host_fills else "device copy kernel",
+                  "fill_GBps_wall": round(hs["fill_bytes"] / hel / 1e9, 2)}
         if not args.host_fills and not args.no_graph:
             # the same hybrid steps from a cold cache, replayed from one captured graph: fills
             # by the device copy kernel, the CPU branch as host nodes on the library's stream
@@ -307,7 +308,7 @@ def main():
                 step(s)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+            with torch.cuda.graph(g, capture_error_mode="thread_local"):
                 step(1, Xs, torch.cuda.current_stream().cuda_stream)
             R.moe_reset_stats(ctx)
             th = time.perf_counter()
@@ -386,7 +387,7 @@ def main():
             step(s, c=ctx_f)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, capture_error_mode="thread_local"):
             step(1, Xs, torch.cuda.current_stream().cuda_stream, c=ctx_f)
         tf = time.perf_counter()
         for s in range(args.warmup, total_steps):
@@ -487,7 +488,7 @@ def elastic_leg(args, R, W, ctx, router, arena, n_slots, zipf, stream, dev):
             "batch": T, "resizes": [[k_, v] for k_, v in sorted(sched.items())], "resize_ms_total": round(resize_s * 1e3, 2),
             "miss_rate": round((st["fills"] + st["cpu_experts"]) / max(1, distinct), 4), "fills": st["fills"],
             "cpu_experts": st["cpu_experts"], "cpu_branch_ms_per_step": round(st["cpu_ms"] / steps, 3),
-            "fill_copy_ms_per_step": round(st["copy_ms"] / steps, 3)}
+            "fill_GBps_wall": round(st["fill_bytes"] / el / 1e9, 2)}
 
 
 def placement_curves(args):

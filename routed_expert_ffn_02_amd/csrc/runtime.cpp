@@ -209,8 +209,10 @@ int lookup_mode_of(int mode) {
 // Copy the step's counts and work lists (one contiguous block) to pinned host memory,
 // with the CPU branch's inputs when `inputs` is set, and wait: the one device -> host
 // decision point of a cached step.
-moe_status read_step(moe_ctx* ctx, hipStream_t s, bool inputs, const void* x, const float* w, const int32_t* slot_idx,
-                     int T) {
+// The step block (and, with inputs, x, gates and slot ids for the CPU branch) copied to
+// pinned staging behind the lookup on stream s; read_step_finish waits for the copies.
+moe_status read_step_issue(moe_ctx* ctx, hipStream_t s, bool inputs, const void* x, const float* w,
+                           const int32_t* slot_idx, int T) {
   const int E = ctx->cfg.n_experts;
   HIPCHK(hipMemcpyAsync(ctx->step_host, ctx->step_dev, (size_t)(C_COUNT + 5 * E) * sizeof(int32_t),
                         hipMemcpyDeviceToHost, s));
@@ -222,6 +224,10 @@ moe_status read_step(moe_ctx* ctx, hipStream_t s, bool inputs, const void* x, co
     HIPCHK(hipMemcpyAsync(ctx->h_slot_idx, slot_idx, (size_t)P * sizeof(int32_t), hipMemcpyDeviceToHost, s));
   }
   HIPCHK(hipEventRecord(ctx->ev_sync, s));
+  return MOE_OK;
+}
+
+moe_status read_step_finish(moe_ctx* ctx) {
   HIPCHK(hipEventSynchronize(ctx->ev_sync));
   if (ctx->h_cnt[C_ERR]) return fail(ctx, MOE_EINVAL, "expert id out of range in topk_idx");
   ctx->stats.lookups += 1;
@@ -230,6 +236,12 @@ moe_status read_step(moe_ctx* ctx, hipStream_t s, bool inputs, const void* x, co
   ctx->stats.cpu_experts += ctx->h_cnt[C_CPU];
   ctx->stats.evictions += ctx->h_cnt[C_EVICT];
   return MOE_OK;
+}
+
+moe_status read_step(moe_ctx* ctx, hipStream_t s, bool inputs, const void* x, const float* w, const int32_t* slot_idx,
+                     int T) {
+  moe_status st = read_step_issue(ctx, s, inputs, x, w, slot_idx, T);
+  return st != MOE_OK ? st : read_step_finish(ctx);
 }
 
 // Fills of the current step: pinned pool -> victim slots on the copy stream; the
@@ -774,22 +786,27 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   float* y_cpu = nullptr;
   const bool inputs = !fused && may_use_cpu(ctx, P);
   // device fills: no host read of the step (its counts and profiled bytes stay on the
-  // device).  A step that may send work to the CPU does so only while the stream is being
-  // captured, running its branch as host nodes; eagerly it takes the host path (the
-  // calling thread reads the step, issues the fills and runs the branch itself, which
-  // measured faster than a host function competing with the enqueuing thread).
+  // device).  A step that may send work to the CPU does so as host nodes while the stream
+  // is being captured.  Eagerly the calling thread reads the step and runs the branch
+  // itself (faster than a host function competing with the enqueuing thread); the fill
+  // kernel, queued behind the step's copies to the host, moves the records meanwhile, so
+  // no host round trip precedes the fills.
   const bool devfill_flag = (ctx->cfg.flags & MOE_FLAG_DEVICE_FILLS) && !fused;
   const bool async_cpu = devfill_flag && inputs && captured;
   const bool devfill = devfill_flag && (!inputs || captured);
+  const bool devfill_host = devfill_flag && inputs && !captured && ctx->pool_dev;
   if (devfill && !ctx->pool_dev) return fail(ctx, MOE_ENOPIN, "device fills need a mapped page-locked pool");
   if (captured && !fused && !devfill)
     return fail(ctx, MOE_ESTATE, "a captured decode step reads nothing on the host: use FUSED mode or a cached "
                                  "mode with MOE_FLAG_DEVICE_FILLS");
-  if ((!fused && !devfill) || (fused && profile)) {
+  if (devfill_host) {
+    moe_status st = read_step_issue(ctx, s, true, x, topk_w, slot_idx, T);
+    if (st != MOE_OK) return st;
+  } else if ((!fused && !devfill) || (fused && profile)) {
     moe_status st = read_step(ctx, s, inputs, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
   }
-  const bool has_cpu = !fused && !devfill && ctx->h_cnt[C_CPU] > 0;
+  bool has_cpu = !fused && !devfill && !devfill_host && ctx->h_cnt[C_CPU] > 0;
   if (has_cpu && !inputs) {  // unexpected CPU work (e.g. every slot protected): fetch its inputs
     moe_status st = read_step(ctx, s, true, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
@@ -817,7 +834,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     if (st != MOE_OK) return st;
     y_cpu = ctx->y_cpu_dev;
   }
-  if (devfill) {
+  if (devfill || devfill_host) {
     FillArgs f;
     f.cnt = ctx->cnt;
     f.fill_key = ctx->fill_key;
@@ -826,13 +843,14 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     f.pool_records = ctx->pool_records;
     f.arena = ctx->arena;
     f.rec_bytes = ctx->S;
-    f.dstats = ctx->dstats;
+    f.dstats = devfill ? ctx->dstats : nullptr;  // a step the host reads is counted there
     const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
-    f.p1_grp = profile ? (uint64_t)2 * I * wrow_h : 0;
-    f.p1_fixed = profile ? (uint64_t)T * H * act_bytes(ctx->cfg) : 0;
-    f.p2_grp = profile ? (uint64_t)H * wrow_i : 0;
-    f.p2_fixed = profile ? (uint64_t)T * H * 4 : 0;
-    f.pair_bytes = profile ? (uint64_t)I * 4 : 0;
+    const bool dprof = profile && devfill;
+    f.p1_grp = dprof ? (uint64_t)2 * I * wrow_h : 0;
+    f.p1_fixed = dprof ? (uint64_t)T * H * act_bytes(ctx->cfg) : 0;
+    f.p2_grp = dprof ? (uint64_t)H * wrow_i : 0;
+    f.p2_fixed = dprof ? (uint64_t)T * H * 4 : 0;
+    f.pair_bytes = dprof ? (uint64_t)I * 4 : 0;
     launch_fill_pull(f, max_groups, s);
   } else if (!fused) {
     moe_status st = issue_fills(ctx, s);
@@ -849,6 +867,12 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     TimedScope t2(ctx, s, TK_P2);
     if (p2c) combined = launch_decode_phase2_combine(ctx->cfg.wfmt, d, s, t2.tm);
     if (!combined) launch_decode_phase2(ctx->cfg.wfmt, d, max_groups, s, t2.tm);
+  }
+  if (devfill_host) {  // the GPU path (fills included) is enqueued: read the step now
+    moe_status st = read_step_finish(ctx);
+    if (st != MOE_OK) return st;
+    has_cpu = ctx->h_cnt[C_CPU] > 0;
+    if (ctx->h_cnt[C_FILL] > 0) ctx->stats.fill_bytes += (uint64_t)ctx->h_cnt[C_FILL] * ctx->S;
   }
   if (has_cpu) {
     // the GPU path is enqueued; the CPU branch runs now, concurrently, then merges exactly

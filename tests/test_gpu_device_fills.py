@@ -60,9 +60,10 @@ def test_device_fills_match_oracle(fmt, T):
 @pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp4"])
 @pytest.mark.parametrize("mode", [2, 3])
 def test_device_fill_steps_with_cpu_branch(fmt, mode):
-    """CPU and HYBRID modes with the device-fill flag, eagerly: such steps take the host
-    path; outputs, traces and counts as in the oracle (the captured form, with the CPU
-    branch as host nodes, is checked against this eager form in test_gpu_graph)."""
+    """CPU and HYBRID modes with the device-fill flag, eagerly: the fill kernel moves the
+    records while the calling thread reads the step and runs the CPU branch; outputs,
+    traces and counts as in the oracle (the captured form, with the CPU branch as host
+    nodes, is checked against this eager form in test_gpu_graph)."""
     import routed_expert_ffn_02_amd as R
     wl = FMT[fmt]
     T = 2
@@ -120,6 +121,35 @@ def test_device_fills_bit_identical_to_host_fills(fmt):
     for s_, key in enumerate(key_dev[:n_slots]):
         if key >= 0:
             assert bool((dev.arena[s_ * S:(s_ + 1) * S] == host.arena[s_ * S:(s_ + 1) * S]).all()), s_
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp4"])
+def test_hybrid_device_fills_bit_identical_to_host_fills(fmt):
+    """HYBRID steps (fills and a CPU branch) through the fill kernel and through host-issued
+    copies: identical bytes in every output and the same counts."""
+    import routed_expert_ffn_02_amd as R
+    wl = FMT[fmt]
+    T = 2
+    bw = (25_000_000_000, 100_000_000_000)
+    n_slots = max(2, wl.n_keys // 3)
+    dev = Harness(wl, R.MOE_MODE_HYBRID, n_slots=n_slots, bw=bw, flags=R.MOE_FLAG_DEVICE_FILLS | R.MOE_FLAG_PROFILE)
+    host = Harness(wl, R.MOE_MODE_HYBRID, n_slots=n_slots, bw=bw, flags=R.MOE_FLAG_PROFILE)
+    routes = {l: wl.synthetic_routing(8, l, T) for l in range(wl.n_layers)}
+    for step in range(8):
+        for layer in range(wl.n_layers):
+            idx = routes[layer][step]
+            x = wl.decode_activations(step, layer, T)
+            w = _gates(wl, step, layer, T)
+            ya, sa, ta, ca = dev.decode(layer, x, idx, w)
+            yb, sb, tb, cb = host.decode(layer, x, idx, w)
+            assert ta == tb and np.array_equal(sa, sb) and np.array_equal(ca, cb), (step, layer)
+            assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), (step, layer)
+    R.moe_sync(dev.ctx)
+    sd, sh = R.moe_get_stats(dev.ctx), R.moe_get_stats(host.ctx)
+    assert sd["cpu_experts"] > 0 and sd["fills"] > 0
+    for key in ("lookups", "hits", "fills", "cpu_experts", "evictions", "fill_bytes", "phase1_launches",
+                "phase2_launches", "phase1_bytes", "phase2_bytes"):
+        assert sd[key] == sh[key], key
 
 
 def test_device_fill_range_error_is_deferred_to_sync():

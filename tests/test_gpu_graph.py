@@ -83,7 +83,9 @@ def test_captured_step_replays_like_eager(wl, mode):
     run_step(R, graph, bg, None, lc)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    # thread-local capture: only this thread's calls are checked against the capture
+    # (host nodes and the CPU worker pool run on threads of their own)
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
         run_step(R, graph, bg, torch.cuda.current_stream().cuda_stream, lc)
     scratch = torch.randn(1 << 16, device="cuda")
     for step in range(1, 9):
