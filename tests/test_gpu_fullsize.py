@@ -54,13 +54,16 @@ def _near_tie_flips(z_ref, idx_gpu, k):
 
 
 class DecodeRun:
-    """Drives the library's decode step like the benchmark and checks it against the oracle."""
+    """Drives the library's decode step as the benchmark does (device fills; router and
+    lookup in one call, the top k taken inside the lookup, then the expert FFN) and checks
+    it against the oracle."""
 
     def __init__(self, wl, mode, n_slots, bw=None, measure_bw=False):
         import routed_expert_ffn_02_amd as R
         self.R, self.wl, self.mode = R, wl, mode
         self.T = wl.tokens
-        self.h = Harness(wl, mode, n_slots=n_slots, max_tokens=max(8, self.T), bw=bw or (1, 1))
+        self.h = Harness(wl, mode, n_slots=n_slots, max_tokens=max(8, self.T), bw=bw or (1, 1),
+                         flags=R.MOE_FLAG_DEVICE_FILLS)
         if measure_bw:
             bp, bh = R.moe_bench_bw(self.h.ctx)
             bw = (max(int(bp), 1), max(int(bh), 1))
@@ -86,8 +89,7 @@ class DecodeRun:
         bias_np = self.orc.decode_bias(layer, self.prev.get(layer), T)
         x = dev_act(wl, x_np)
         bias = torch.from_numpy(bias_np).cuda()
-        R.moe_route(self.h.ctx, layer, x, T, bias, self.z, self.idx, self.w)
-        R.expert_cache_lookup(self.h.ctx, layer, self.idx, T, self.slot, self.tr, self.cnt)
+        R.moe_route_lookup(self.h.ctx, layer, x, T, bias, self.z, self.idx, self.w, self.slot, self.tr, self.cnt)
         R.moe_ffn_decode(self.h.ctx, layer, x, T, self.idx, self.w, self.slot, self.y)
         torch.cuda.synchronize()
         z, idx, w = self.z.cpu().numpy(), self.idx.cpu().numpy(), self.w.cpu().numpy()
@@ -124,6 +126,7 @@ class DecodeRun:
         assert np.array_equal(stamp, self.orc.cache.stamp.astype(np.uint64))
 
     def close(self):
+        self.R.moe_sync(self.h.ctx)  # deferred errors of device-fill steps
         self.R.moe_destroy(self.h.ctx)
 
 
