@@ -177,6 +177,65 @@ def test_elastic_hybrid_fullsize():
     assert run.flips <= 4
 
 
+def _run_fused(wl, steps, sample):
+    """All resident (FUSED), batch 1, one moe_decode_layer call per layer as the
+    benchmark's all-resident leg makes them: the router launch, phase 1 taking the top k
+    itself, the down projection with the combine.  Indices are checked against the
+    oracle's top k of its own logits (differences must be near-ties), gates against its
+    softmax at the chosen experts, slot ids against the identity lookup, and sampled
+    outputs against the oracle's FFN with the GPU's choice and gates."""
+    import routed_expert_ffn_02_amd as R
+    L, E, k, H = wl.n_layers, wl.n_experts, wl.top_k, wl.hidden
+    h = Harness(wl, R.MOE_MODE_FUSED, max_tokens=8)
+    orc = oracle.OracleMoE(wl, n_slots=L * E, weight_cache=False)
+    idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    slot = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    prev, flips, checked, n = {}, 0, 0, 0
+    try:
+        for step in range(steps):
+            for layer in range(L):
+                x_np = wl.decode_activations(step, layer, 1)
+                bias_np = orc.decode_bias(layer, prev.get(layer), 1)
+                R.moe_decode_layer(h.ctx, layer, dev_act(wl, x_np), 1, torch.from_numpy(bias_np).cuda(), idx, w, slot,
+                                   y)
+                torch.cuda.synchronize()
+                gi, gw = idx.cpu().numpy(), w.cpu().numpy()
+                where = (step, layer)
+                z_ref = oracle.router_logits(oracle.formats.activations_f64(x_np), orc.router(layer), bias_np)
+                flips += _near_tie_flips(z_ref, gi, k)
+                zr = np.asarray(z_ref[0], np.float64)
+                p_ref = np.exp(zr - zr.max())
+                p_ref /= p_ref.sum()
+                # gates from logits within 1e-5 of the row's largest magnitude: relative error
+                # at most twice that in the exponent
+                bound = 2.5 * TOL_LOGIT * max(1.0, np.abs(zr).max()) + 1e-6
+                assert np.abs(gw[0] / p_ref[gi[0]] - 1.0).max() <= bound, where
+                assert np.array_equal(slot.cpu().numpy(), layer * E + gi), where
+                prev[layer] = gi
+                if n % sample == 0:
+                    ref = oracle.moe_combine(orc.expert_outputs(layer, x_np, gi), gw)
+                    assert row_rel_err(y.cpu().numpy(), ref) <= TOL_OUT, where
+                    checked += 1
+                n += 1
+    finally:
+        R.moe_destroy(h.ctx)
+    return flips, checked
+
+
+def test_a3b_fused_decode_fullsize():
+    """35B-A3B shape, every one of the 10240 records resident (60 GiB arena), batch 1."""
+    flips, checked = _run_fused(W.A3B_DECODE, steps=8, sample=16)
+    assert checked >= 20 and flips <= 2
+
+
+def test_dsv4_fused_decode_fullsize():
+    """DeepSeek-V4-Flash shape, all 11008 records resident (156 GB arena, aliased pool)."""
+    flips, checked = _run_fused(W.DSV4.with_(alias_records=4500), steps=4, sample=43)
+    assert checked >= 4 and flips <= 2
+
+
 def _run_prefill(wl, n_slots, sample_layers, sample_tokens):
     import routed_expert_ffn_02_amd as R
     T, k, E, H = wl.prefill_tokens, wl.top_k, wl.n_experts, wl.hidden
