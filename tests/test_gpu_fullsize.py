@@ -186,6 +186,7 @@ def _run_fused(wl, steps, sample):
     outputs against the oracle's FFN with the GPU's choice and gates."""
     import routed_expert_ffn_02_amd as R
     L, E, k, H = wl.n_layers, wl.n_experts, wl.top_k, wl.hidden
+    torch.cuda.empty_cache()  # the arena holds every record: return earlier tests' cached blocks first
     h = Harness(wl, R.MOE_MODE_FUSED, max_tokens=8)
     orc = oracle.OracleMoE(wl, n_slots=L * E, weight_cache=False)
     idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
@@ -221,6 +222,8 @@ def _run_fused(wl, steps, sample):
                 n += 1
     finally:
         R.moe_destroy(h.ctx)
+        del h
+        torch.cuda.empty_cache()
     return flips, checked
 
 
