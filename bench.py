@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed decode leg")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-hybrid", action="store_true")
+    ap.add_argument("--no-cpu-mode", action="store_true", help="skip the CPU-backend decode leg")
     ap.add_argument("--no-fused", action="store_true", help="skip the all-resident (FUSED) graph-replayed decode leg")
     ap.add_argument("--no-elastic", action="store_true",
                     help="skip the batch-4 hybrid leg with elastic cache resizes (A3B shape only)")
@@ -324,6 +325,33 @@ def main():
         log(f"hybrid: {hybrid}")
         R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)
 
+    # ---------------------------------------------------------------- CPU leg
+    # Every routed expert evaluated by the library's CPU branch (the pages' cpu backend:
+    # q = 0), a bounded number of steps: host-DRAM-bound tokens/s beside the GPU legs.
+    cpu_mode = None
+    if mode == R.MOE_MODE_OFFLOAD and not args.no_cpu_mode:
+        R.moe_bind(ctx, router, arena, arena.numel(), n_slots)  # cold cache: with q = 0 nothing becomes resident
+        R.moe_set_mode(ctx, R.MOE_MODE_CPU)
+        n_cpu = min(args.steps, 64)
+        for s in range(min(args.warmup, 2)):
+            step(s)
+        torch.cuda.synchronize()
+        R.moe_reset_stats(ctx)
+        tc = time.perf_counter()
+        for s in range(n_cpu):
+            step(s)
+        torch.cuda.synchronize()
+        cel = time.perf_counter() - tc
+        cs = R.moe_get_stats(ctx)
+        cpu_bytes = cs["cpu_experts"] * S
+        cpu_mode = {"tokens_per_s": round(n_cpu * T / cel, 2), "ms_per_step": round(cel * 1e3 / n_cpu, 3),
+                    "steps": n_cpu, "cpu_experts": cs["cpu_experts"],
+                    "cpu_branch_ms_per_step": round(cs["cpu_ms"] / n_cpu, 3),
+                    "host_GBps": round(cpu_bytes / (cs["cpu_ms"] * 1e-3) / 1e9, 1) if cs["cpu_ms"] > 0 else None,
+                    "bw_host_GBps": round(bw_h / 1e9, 2)}
+        log(f"cpu mode: {cpu_mode}")
+        R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)
+
     # ---------------------------------------------------------------- prefill leg
     prefill = None
     if not args.no_prefill and mode != R.MOE_MODE_FUSED:
@@ -434,6 +462,7 @@ def main():
         "decode": decode_detail,
         "graph_decode": graph,
         "hybrid_decode": hybrid,
+        "cpu_mode_decode": cpu_mode,
         "fused_decode": fused,
         "elastic_hybrid_batch4": elastic,
         "prefill": prefill,
