@@ -237,15 +237,21 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
  * on the device); while `stream` is being captured, a step that may (CPU or HYBRID mode, or
  * fewer slots) also forks the library's CPU stream: the step block and inputs are copied to
  * pinned staging, a host function runs the CPU branch there, its partial sum is copied back,
- * and the combine waits for it (eagerly such a step takes the host path above).  Nothing is
- * read on the calling thread, the call only enqueues work, and an out-of-range id in
- * topk_idx (the step then computes y = 0) is reported by the next moe_sync.  Needs a pool from moe_pool_alloc or a registered
+ * and the combine waits for it.  Nothing is read on the calling thread, the call only
+ * enqueues work, and an out-of-range id in topk_idx (the step then computes y = 0) is
+ * reported by the next moe_sync.  Eagerly, a device-fill step that may send work to the CPU
+ * queues the copy kernel behind the copies of the step block and inputs to pinned staging,
+ * then the calling thread waits for those copies only, runs the CPU branch while the
+ * records move, and copies its partial sum back (an out-of-range id returns MOE_EINVAL).  Needs a pool from moe_pool_alloc or a registered
  * page-locked pool with a device mapping (MOE_ENOPIN).  Such steps, and FUSED steps, may be
  * captured with route and lookup for every layer into one HIP graph on `stream` and replayed
  * (the CPU branch becomes host nodes); MOE_FLAG_PROFILE timing is skipped for captured
  * launches, and a step that would read the host while the stream is capturing returns
  * MOE_ESTATE.
  */
+MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
+                                  const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);
+
 /*
  * moe_route followed by expert_cache_lookup of the same layer and tokens, in two launches
  * instead of three: for decode-sized steps (T*k <= 64, T <= 16) the cache-control kernel
@@ -260,16 +266,14 @@ MOE_API moe_status moe_route_lookup(moe_ctx* ctx, int32_t layer, const void* x, 
 /*
  * One decode layer step: moe_route_lookup, then moe_ffn_decode, with their arguments,
  * outputs and errors (y [T,H] fp32 out; topk_idx, topk_w, slot_idx [T,k] out).  In
- * MOE_MODE_FUSED at T = 1 the lookup is the identity (slot = key, group g = rank g), so
- * phase 1 takes the top k from the logits itself and the step runs in four launches
- * (router GEMV, phase 1, phase 2, combine) with results bit-identical to the two calls.
+ * MOE_MODE_FUSED at T = 1 (bf16 activations, bf16 or e2m1 weights) the lookup is the
+ * identity (slot = key, group g = rank g), so phase 1 takes the top k from the logits
+ * itself and the step runs in three launches (router GEMV, phase 1, the down projection
+ * with the combine) with results bit-identical to the two calls.
  * Asynchronous on the stream; capturable wherever moe_ffn_decode is.
  */
 MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
                                     int32_t* topk_idx, float* topk_w, int32_t* slot_idx, float* y, moe_stream_t stream);
-
-MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* topk_idx,
-                                  const float* topk_w, const int32_t* slot_idx, float* y, moe_stream_t stream);
 
 /*
  * Prefill over layers 0..L-1 in ascending order ([FT-KR] "전층 이중 버퍼링"; [FT-CN] 04 Design,
