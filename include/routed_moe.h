@@ -269,7 +269,7 @@ MOE_API moe_status moe_route_lookup(moe_ctx* ctx, int32_t layer, const void* x, 
  * MOE_MODE_FUSED at T = 1 (bf16 activations, bf16 or e2m1 weights) the lookup is the
  * identity (slot = key, group g = rank g), so phase 1 takes the top k from the logits
  * itself and the step runs in three launches (router GEMV, phase 1, the down projection
- * with the combine) with results bit-identical to the two calls.
+ * with the combine; four when k > 8) with results bit-identical to the two calls.
  * Asynchronous on the stream; capturable wherever moe_ffn_decode is.
  */
 MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
