@@ -68,7 +68,41 @@ __global__ __launch_bounds__(256) void fill_pull_kernel(FillArgs a) {
     for (int64_t b = (n16 << 4) + threadIdx.x; b < a.rec_bytes; b += 256) dst[b] = src[b];
 }
 
+// The step block and the CPU branch's inputs to pinned host staging: one grid-stride pass
+// over the concatenated ranges, each 32-bit word stored at system scope (written through
+// to host memory), so the host reads them once the launch has completed.
+__global__ __launch_bounds__(256) void stage_step_kernel(StageArgs a) {
+  const int total = a.n_step + a.n_x + 2 * a.P;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+    uint32_t v;
+    uint32_t* dst;
+    if (i < a.n_step) {
+      v = (uint32_t)a.step[i];
+      dst = reinterpret_cast<uint32_t*>(a.step_h) + i;
+    } else if (i < a.n_step + a.n_x) {
+      const int j = i - a.n_step;
+      v = a.x[j];
+      dst = a.x_h + j;
+    } else if (i < a.n_step + a.n_x + a.P) {
+      const int j = i - a.n_step - a.n_x;
+      v = __float_as_uint(a.w[j]);
+      dst = reinterpret_cast<uint32_t*>(a.w_h) + j;
+    } else {
+      const int j = i - a.n_step - a.n_x - a.P;
+      v = (uint32_t)a.slot[j];
+      dst = reinterpret_cast<uint32_t*>(a.slot_h) + j;
+    }
+    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 }  // namespace
+
+void launch_stage_step(const StageArgs& a, hipStream_t s) {
+  const int total = a.n_step + a.n_x + 2 * a.P;
+  const int blocks = std::max(1, std::min(64, (total + 255) / 256));
+  hipLaunchKernelGGL(stage_step_kernel, dim3(blocks), dim3(256), 0, s, a);
+}
 
 int fill_blocks_per_record(int64_t rec_bytes) {
   // about 256 KiB per workgroup

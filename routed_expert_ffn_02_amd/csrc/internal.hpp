@@ -151,6 +151,22 @@ bool launch_decode_phase1_routed(int wfmt, int afmt, const DecodeArgs& a, hipStr
 int decode_phase2_rowblocks(int H);
 void launch_decode_combine(const DecodeArgs& a, const float* y_cpu, hipStream_t s);
 int fill_blocks_per_record(int64_t rec_bytes);
+// One launch writing the step block and the CPU branch's inputs into pinned host staging
+// through its device mapping (system-scope stores), in place of four device-to-host copies.
+struct StageArgs {
+  const int32_t* step;  // [n_step] device step block
+  int32_t* step_h;      // its pinned mirror (device address)
+  int n_step;
+  const uint32_t* x;    // [n_x] activations as 32-bit words
+  uint32_t* x_h;
+  int n_x;
+  const float* w;       // [P] gates
+  float* w_h;
+  const int32_t* slot;  // [P] slot ids
+  int32_t* slot_h;
+  int P;
+};
+void launch_stage_step(const StageArgs& a, hipStream_t s);
 void launch_fill_pull(const FillArgs& a, int max_fills, hipStream_t s);
 void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
                     int32_t* inv, int32_t* offsets, int32_t* tile_base, int bm, hipStream_t s);
@@ -266,6 +282,11 @@ struct moe_ctx {
   float* h_xf = nullptr;         // [max_tokens*H] fp32
   float* h_y = nullptr;          // [max_tokens*H] fp32 (pinned, CPU partial)
   float* h_hbuf = nullptr;       // [Pmax*I] fp32 (CPU intermediate)
+  // device addresses of step_host, h_x, h_w, h_slot_idx (nullptr: no mapping, copies instead)
+  int32_t* step_host_dev = nullptr;
+  void* h_x_dev = nullptr;
+  float* h_w_dev = nullptr;
+  int32_t* h_slot_idx_dev = nullptr;
 
   hipStream_t copy_stream = nullptr;
   // device-fill steps with CPU work: the branch runs as a host function on cpu_stream,

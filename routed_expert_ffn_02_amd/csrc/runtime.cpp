@@ -340,6 +340,24 @@ void cpu_branch_host_fn(void* user) {
   ctx->stats.cpu_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
+// The step block and the CPU branch's inputs written into the pinned staging by one
+// launch on s (through the staging's device mapping), in place of four copies.
+void stage_step(moe_ctx* ctx, const void* x, const float* w, const int32_t* slot_idx, int T, hipStream_t s) {
+  StageArgs sa;
+  sa.step = ctx->step_dev;
+  sa.step_h = ctx->step_host_dev;
+  sa.n_step = C_COUNT + 5 * ctx->cfg.n_experts;
+  sa.x = static_cast<const uint32_t*>(x);
+  sa.x_h = static_cast<uint32_t*>(ctx->h_x_dev);
+  sa.n_x = (int)((int64_t)T * ctx->cfg.hidden * act_bytes(ctx->cfg) / 4);
+  sa.w = w;
+  sa.w_h = ctx->h_w_dev;
+  sa.slot = slot_idx;
+  sa.slot_h = ctx->h_slot_idx_dev;
+  sa.P = T * ctx->cfg.top_k;
+  launch_stage_step(sa, s);
+}
+
 // Enqueue the CPU branch of a device-fill step on cpu_stream (forked from s after the
 // lookup): step block and inputs to the pinned staging, the host function, the
 // partial sum back to y_cpu_dev.  s must wait for ev_join before the combine.
@@ -347,13 +365,16 @@ moe_status enqueue_cpu_branch(moe_ctx* ctx, const void* x, const float* w, const
                               hipStream_t s) {
   const int E = ctx->cfg.n_experts, H = ctx->cfg.hidden, P = T * ctx->cfg.top_k;
   hipStream_t c = ctx->cpu_stream;
+  if (ctx->step_host_dev) stage_step(ctx, x, w, slot_idx, T, s);  // one launch instead of four copy nodes
   HIPCHK(hipEventRecord(ctx->ev_fork, s));
   HIPCHK(hipStreamWaitEvent(c, ctx->ev_fork, 0));
-  HIPCHK(hipMemcpyAsync(ctx->step_host, ctx->step_dev, (size_t)(C_COUNT + 5 * E) * sizeof(int32_t),
-                        hipMemcpyDeviceToHost, c));
-  HIPCHK(hipMemcpyAsync(ctx->h_x, x, (size_t)T * H * act_bytes(ctx->cfg), hipMemcpyDeviceToHost, c));
-  HIPCHK(hipMemcpyAsync(ctx->h_w, w, (size_t)P * sizeof(float), hipMemcpyDeviceToHost, c));
-  HIPCHK(hipMemcpyAsync(ctx->h_slot_idx, slot_idx, (size_t)P * sizeof(int32_t), hipMemcpyDeviceToHost, c));
+  if (!ctx->step_host_dev) {
+    HIPCHK(hipMemcpyAsync(ctx->step_host, ctx->step_dev, (size_t)(C_COUNT + 5 * E) * sizeof(int32_t),
+                          hipMemcpyDeviceToHost, c));
+    HIPCHK(hipMemcpyAsync(ctx->h_x, x, (size_t)T * H * act_bytes(ctx->cfg), hipMemcpyDeviceToHost, c));
+    HIPCHK(hipMemcpyAsync(ctx->h_w, w, (size_t)P * sizeof(float), hipMemcpyDeviceToHost, c));
+    HIPCHK(hipMemcpyAsync(ctx->h_slot_idx, slot_idx, (size_t)P * sizeof(int32_t), hipMemcpyDeviceToHost, c));
+  }
   HIPCHK(hipLaunchHostFunc(c, cpu_branch_host_fn, ctx));
   HIPCHK(hipMemcpyAsync(ctx->y_cpu_dev, ctx->h_y, (size_t)T * H * sizeof(float), hipMemcpyHostToDevice, c));
   HIPCHK(hipEventRecord(ctx->ev_join, c));
@@ -461,6 +482,18 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       hipHostMalloc(reinterpret_cast<void**>(&ctx->h_y), (size_t)c.max_tokens * H * 4, 0) ||
       hipHostMalloc(reinterpret_cast<void**>(&ctx->h_hbuf), (size_t)Pmax * I * 4, 0))
     return cleanup_fail(MOE_ENOMEM);
+  {  // device addresses of the staging the step-staging kernel writes (optional)
+    void *a = nullptr, *b = nullptr, *c2 = nullptr, *d = nullptr;
+    if (hipHostGetDevicePointer(&a, ctx->step_host, 0) == hipSuccess &&
+        hipHostGetDevicePointer(&b, ctx->h_x, 0) == hipSuccess && hipHostGetDevicePointer(&c2, ctx->h_w, 0) == hipSuccess &&
+        hipHostGetDevicePointer(&d, ctx->h_slot_idx, 0) == hipSuccess) {
+      ctx->step_host_dev = static_cast<int32_t*>(a);
+      ctx->h_x_dev = b;
+      ctx->h_w_dev = static_cast<float*>(c2);
+      ctx->h_slot_idx_dev = static_cast<int32_t*>(d);
+    }
+    (void)hipGetLastError();
+  }
   ctx->h_cnt = ctx->step_host;
   ctx->h_fill_key = ctx->h_cnt + C_COUNT;
   ctx->h_fill_slot = ctx->h_fill_key + E;
@@ -799,7 +832,13 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   if (captured && !fused && !devfill)
     return fail(ctx, MOE_ESTATE, "a captured decode step reads nothing on the host: use FUSED mode or a cached "
                                  "mode with MOE_FLAG_DEVICE_FILLS");
-  if (devfill_host) {
+  if (devfill_host && ctx->step_host_dev) {
+    // one staging launch writes the step block and the CPU branch's inputs straight into
+    // the pinned staging, and the fill kernel follows it at once
+    HIPCHK(hipEventSynchronize(ctx->ev_ycpu));  // the previous partial sum has left h_y's staging
+    stage_step(ctx, x, topk_w, slot_idx, T, s);
+    HIPCHK(hipEventRecord(ctx->ev_sync, s));
+  } else if (devfill_host) {
     moe_status st = read_step_issue(ctx, s, true, x, topk_w, slot_idx, T);
     if (st != MOE_OK) return st;
   } else if ((!fused && !devfill) || (fused && profile)) {
