@@ -124,7 +124,7 @@ def copy_probe():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not part of this build",
+        print(json.dumps({"error": "this benchmark measures one GPU; runs on several GPUs are not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.copy_probe:
