@@ -13,7 +13,7 @@ bonus for the previous token's experts at the same layer.
 After the timed decode, a prefill leg streams a 4096-token prompt through all
 layers with full-layer double buffering (reported beside the headline value).
 
-Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
