@@ -33,18 +33,28 @@ def e2m1_decode(codes: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
+# The value of every 4-bit code, from the bit-field definition above (evaluated once;
+# indexing it is the same map as calling e2m1_decode on each code).
+_E2M1_TABLE = e2m1_decode(np.arange(16))
+
+
+def _e2m1_values(codes: np.ndarray) -> np.ndarray:
+    """Packed codes [rows, cols/2] (element 2i in the low nibble of byte i) -> float64 [rows, cols]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    nib = np.empty((rows, half * 2), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    return _E2M1_TABLE[nib]
+
+
 def dequant_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """Packed codes [rows, cols/2] (element 2i in the low nibble of byte i) and bf16 scale
     bits [rows, cols/32] -> float64 [rows, cols]; w = e2m1(code) * scale of its 32-block."""
-    codes = np.asarray(codes, dtype=np.uint8)
-    rows, half = codes.shape
-    cols = half * 2
-    nib = np.empty((rows, cols), dtype=np.uint8)
-    nib[:, 0::2] = codes & 0x0F
-    nib[:, 1::2] = codes >> 4
-    vals = e2m1_decode(nib)
+    vals = _e2m1_values(codes)                     # [rows, cols]
     sc = bf16_to_f64(scales)                       # [rows, cols/32]
-    return vals * np.repeat(sc, 32, axis=1)
+    rows, cols = vals.shape
+    return (vals.reshape(rows, cols // 32, 32) * sc[:, :, None]).reshape(rows, cols)
 
 
 def e8m0_decode(e: np.ndarray) -> np.ndarray:
@@ -56,12 +66,10 @@ def e8m0_decode(e: np.ndarray) -> np.ndarray:
 def dequant_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """Packed codes [rows, cols/2] (element 2i in the low nibble of byte i) and E8M0 scale
     bytes [rows, cols/32] -> float64 [rows, cols]; w = e2m1(code) * 2^(e - 127)."""
-    codes = np.asarray(codes, dtype=np.uint8)
-    rows, half = codes.shape
-    nib = np.empty((rows, half * 2), dtype=np.uint8)
-    nib[:, 0::2] = codes & 0x0F
-    nib[:, 1::2] = codes >> 4
-    return e2m1_decode(nib) * np.repeat(e8m0_decode(scales), 32, axis=1)
+    vals = _e2m1_values(codes)
+    rows, cols = vals.shape
+    sc = e8m0_decode(scales)
+    return (vals.reshape(rows, cols // 32, 32) * sc[:, :, None]).reshape(rows, cols)
 
 
 def expert_weights_f64(workload, key: int):
