@@ -3,15 +3,21 @@
 
 A step is one decode token through every MoE layer: router softmax/top-k, cache
 lookup with LRU update, fills of misses from the pinned host pool, the SwiGLU
-expert GEMVs and the rank-order combine.  Default workload: the 35B-A3B shape
-(40 layers, 256 experts, top-8, hidden 2048, expert intermediate 512, bf16
-weights, a 64,424,509,440-byte pinned host pool), batch 1, a 1280-slot cache
-(12.5% of the pool), cold start, misses filled over PCIe (offload mode).
-Routing has temporal locality: a per-layer Zipf(1.1) popularity bias plus a
-bonus for the previous token's experts at the same layer.
+expert GEMVs and the rank-order combine.  Default workload: the DeepSeek-V4-Flash
+shape (43 layers, 256 experts, top-6, hidden 4096, expert intermediate 2048, e2m1
+weights with a bf16 scale per 32 elements, 14,155,776-byte records), batch 1, a
+1695-slot (24 GB) cache, cold start, misses filled over PCIe (offload mode); the
+155.8 GB pool is backed by 4500 page-locked records (key % 4500: the same record
+size and access pattern, aliased contents).  Routing has temporal locality: a
+per-layer Zipf(1.1) popularity bias plus a bonus for the previous token's experts
+at the same layer.  The 35B-A3B shape (40 layers, top-8 of 256, hidden 2048,
+intermediate 512, bf16, the 64.4 GB pool whole, 1280 slots) runs afterwards as a
+secondary section with the batch-4 elastic hybrid leg.
 
-After the timed decode, a prefill leg streams a 4096-token prompt through all
-layers with full-layer double buffering (reported beside the headline value).
+Beside the timed decode: a prefill leg (2048 / 4096-token prompt through all layers
+with full-layer double buffering), hybrid (q* split) and CPU-backend decode legs
+with the per-step split balance, an all-resident decode leg, and plain HBM reads at
+the kernels' transfer sizes (the practical ceiling).
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: the benchmark measures one GPU.
 """
@@ -31,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--config", default="a3b", choices=["a3b", "dsv4", "dsv4mx"],
+    ap.add_argument("--config", default="dsv4", choices=["a3b", "dsv4", "dsv4mx"],
                     help="a3b: 35B-A3B shape, bf16; dsv4: DeepSeek-V4-Flash shape, e2m1 + bf16 scales; "
                          "dsv4mx: the same shape as MXFP4 (E8M0 scales)")
     ap.add_argument("--mode", default="offload", choices=["offload", "hybrid", "fused"])
@@ -47,6 +53,12 @@ def parse():
                     help="skip the batch-4 hybrid leg with elastic cache resizes (A3B shape only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="runs of the headline (graph-replayed) and hybrid decode legs; the median is reported")
+    ap.add_argument("--secondary", default="a3b", choices=["a3b", "none"],
+                    help="a second workload run after the first (its own context and pool), reported under "
+                         "'secondary'")
+    ap.add_argument("--no-hbm-probe", action="store_true", help="skip the plain HBM read legs")
     ap.add_argument("--alias-records", type=int, default=0,
                     help="back keys by key %% R records (smaller host pool; same transfer sizes)")
     ap.add_argument("--placement", action="store_true",
@@ -136,16 +148,31 @@ def main():
     if args.bank:
         bank_load(args)
         return
+    out = run_workload(args, args.config, primary=True)
+    if args.secondary != "none" and args.secondary != args.config:
+        sec = run_workload(args, args.secondary, primary=False)
+        keep = ("value", "unit", "ms_per_step", "headline_leg", "dtype", "config", "roofline", "repeats")
+        out["secondary"] = {k_: sec[k_] for k_ in keep}
+        out["secondary"].update({k_: v for k_, v in sec.items() if isinstance(v, dict) and k_ not in keep})
+    print(json.dumps(out), flush=True)
 
+
+def median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+
+def run_workload(args, config, primary):
+    """Every leg of one workload on its own context and pool; returns the JSON fields."""
     import torch
     import routed_expert_ffn_02_amd as R
     import workloads as W
 
-    wl = {"a3b": W.A3B_DECODE, "dsv4": W.DSV4, "dsv4mx": W.DSV4_MX}[args.config]
+    wl = {"a3b": W.A3B_DECODE, "dsv4": W.DSV4, "dsv4mx": W.DSV4_MX}[config]
     # The DSV4-shaped pool (155.8 GB) exceeds what the host lets us page-lock; by default
     # its keys are backed by key % 4500 records (63.7 GB): same record size and access
     # pattern, aliased contents (the oracle uses the same mapping).
-    alias = args.alias_records or (4500 if args.config != "a3b" else 0)
+    alias = args.alias_records or (4500 if config != "a3b" else 0)
     if alias:
         wl = wl.with_(alias_records=alias)
     mode = {"offload": R.MOE_MODE_OFFLOAD, "hybrid": R.MOE_MODE_HYBRID, "fused": R.MOE_MODE_FUSED}[args.mode]
@@ -153,10 +180,11 @@ def main():
     T = wl.tokens
     total_steps = args.warmup + args.steps
     dev = torch.device("cuda:0")
+    reps = max(1, args.repeats)
 
     # ---------------------------------------------------------------- set-up (untimed)
     t0 = time.time()
-    prompt = W.A3B_PREFILL.prefill_tokens if args.config == "a3b" else wl.prefill_tokens
+    prompt = W.A3B_PREFILL.prefill_tokens if config == "a3b" else wl.prefill_tokens
     max_tokens = 8 if args.no_prefill else max(8, prompt)
     flags = R.MOE_FLAG_PROFILE | (0 if args.host_fills else R.MOE_FLAG_DEVICE_FILLS)
     cfg = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, max_tokens, mode, wl.renorm, flags=flags)
@@ -164,7 +192,8 @@ def main():
     S = R.moe_record_bytes(cfg)
     pool = R.moe_pool_alloc(ctx, wl.pool_records)
     wl.fill_pool(pool, 0, wl.pool_records, threads=min(16, len(os.sched_getaffinity(0))))
-    log(f"pool: {wl.pool_records} records x {S} B = {wl.pool_records * S / 1e9:.1f} GB in {time.time() - t0:.1f}s")
+    log(f"[{config}] pool: {wl.pool_records} records x {S} B = {wl.pool_records * S / 1e9:.1f} GB in "
+        f"{time.time() - t0:.1f}s")
     router = torch.from_numpy(np.stack([wl.router_weight(l) for l in range(L)])).to(dev)
     n_slots = L * E if mode == R.MOE_MODE_FUSED else wl.n_slots
     arena = torch.empty(n_slots * S, dtype=torch.uint8, device=dev)
@@ -173,7 +202,7 @@ def main():
         R.moe_fused_load(ctx)
     bw_p, bw_h = R.moe_bench_bw(ctx)
     R.moe_set_bandwidths(ctx, max(bw_p, 1), max(bw_h, 1))
-    log(f"B_P = {bw_p / 1e9:.1f} GB/s, B_H = {bw_h / 1e9:.1f} GB/s")
+    log(f"[{config}] B_P = {bw_p / 1e9:.1f} GB/s, B_H = {bw_h / 1e9:.1f} GB/s")
 
     # activations for every (step, layer), resident in HBM before timing
     X = np.empty((total_steps, L, T, H), np.uint16)
@@ -191,7 +220,7 @@ def main():
     y = torch.zeros((L, T, H), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
-    log(f"set-up {time.time() - t0:.1f}s")
+    log(f"[{config}] set-up {time.time() - t0:.1f}s")
 
     def step(s, xsrc=None, strm=None, c=None):
         xsrc = Xd[s] if xsrc is None else xsrc
@@ -233,7 +262,7 @@ def main():
     p2_bytes = st["phase2_bytes"] / max(1, st["phase2_launches"])
     p1_gbs = p1_bytes / (p1_avg_ms * 1e-3) / 1e9 if p1_avg_ms > 0 else 0.0
     p2_gbs = p2_bytes / (p2_avg_ms * 1e-3) / 1e9 if p2_avg_ms > 0 else 0.0
-    log(f"decode: {tok_s:.1f} tok/s, miss rate {miss_rate:.3f}, phase1 {p1_avg_ms * 1e3:.1f} us "
+    log(f"[{config}] decode: {tok_s:.1f} tok/s, miss rate {miss_rate:.3f}, phase1 {p1_avg_ms * 1e3:.1f} us "
         f"{p1_gbs:.0f} GB/s, phase2 {p2_avg_ms * 1e3:.1f} us {p2_gbs:.0f} GB/s")
     decode_detail = {
         "fill_path": "host DMA" if args.host_fills else "device copy kernel",
@@ -246,60 +275,75 @@ def main():
         "copy_engine_ms": round(st["copy_ms"], 2),
         "phase1_avg_us": round(p1_avg_ms * 1e3, 2), "phase1_GBps": round(p1_gbs, 1),
         "phase2_avg_us": round(p2_avg_ms * 1e3, 2), "phase2_GBps": round(p2_gbs, 1),
+        "phase2_bytes_per_launch": int(p2_bytes),
         "bw_pcie_GBps": round(bw_p / 1e9, 2), "bw_host_GBps": round(bw_h / 1e9, 2), "lookups": lookups,
     }
 
-    # ---------------------------------------------------------------- graph leg
+    # ---------------------------------------------------------------- graph leg (headline)
     # The same steps from a cold cache, each step (every layer's bias, route, lookup,
     # device fills and GEMVs) replayed from one captured HIP graph; the step's
-    # activations are copied into the graph's static input first.
+    # activations are copied into the graph's static input first.  Repeated from a cold
+    # cache; the median run is the headline.
     graph = None
     if mode == R.MOE_MODE_OFFLOAD and not args.host_fills and not args.no_graph:
-        R.moe_bind(ctx, router, arena, arena.numel(), n_slots)
-        Xs = torch.empty_like(Xd[0])
-        for s in range(args.warmup):
-            step(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, capture_error_mode="thread_local"):
-            step(1, Xs, torch.cuda.current_stream().cuda_stream)
-        R.moe_reset_stats(ctx)
-        tg = time.perf_counter()
-        for s in range(args.warmup, total_steps):
-            Xs.copy_(Xd[s])
-            g.replay()
-        torch.cuda.synchronize()
-        gel = time.perf_counter() - tg
-        R.moe_sync(ctx, stream)
-        gs = R.moe_get_stats(ctx)
-        graph = {"tokens_per_s": round(args.steps * T / gel, 2), "ms_per_step": round(gel * 1e3 / args.steps, 3),
-                 "fills": gs["fills"], "lookups": gs["lookups"],
-                 "miss_rate": round(gs["fills"] / max(1, gs["hits"] + gs["fills"]), 4)}
-        log(f"graph: {graph}")
-        del g
+        runs = []
+        for _ in range(reps):
+            R.moe_bind(ctx, router, arena, arena.numel(), n_slots)
+            Xs = torch.empty_like(Xd[0])
+            for s in range(args.warmup):
+                step(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, capture_error_mode="thread_local"):
+                step(1, Xs, torch.cuda.current_stream().cuda_stream)
+            R.moe_reset_stats(ctx)
+            tg = time.perf_counter()
+            for s in range(args.warmup, total_steps):
+                Xs.copy_(Xd[s])
+                g.replay()
+            torch.cuda.synchronize()
+            gel = time.perf_counter() - tg
+            R.moe_sync(ctx, stream)
+            gs = R.moe_get_stats(ctx)
+            runs.append({"tokens_per_s": round(args.steps * T / gel, 2), "ms_per_step": round(gel * 1e3 / args.steps, 3),
+                         "fills": gs["fills"], "lookups": gs["lookups"],
+                         "miss_rate": round(gs["fills"] / max(1, gs["hits"] + gs["fills"]), 4)})
+            del g
+        graph = dict(sorted(runs, key=lambda r: r["tokens_per_s"])[len(runs) // 2])
+        graph["runs_tokens_per_s"] = [r["tokens_per_s"] for r in runs]
+        log(f"[{config}] graph: {graph}")
 
     # ---------------------------------------------------------------- hybrid leg
     # Same steps from a cold cache with the misses split by q* between fills and the
-    # host CPU branch (B_P and B_H measured above).
+    # host CPU branch (B_P and B_H measured above), repeated; the first run's per-step
+    # log gives the split's balance (fill-kernel time against CPU-branch time).
     hybrid = None
+    qstar = None
     if mode == R.MOE_MODE_OFFLOAD and not args.no_hybrid:
-        R.moe_bind(ctx, router, arena, arena.numel(), n_slots)
+        runs, logs = [], []
         R.moe_set_mode(ctx, R.MOE_MODE_HYBRID)
-        for s in range(args.warmup):
-            step(s)
-        torch.cuda.synchronize()
-        R.moe_reset_stats(ctx)
-        th = time.perf_counter()
-        for s in range(args.warmup, total_steps):
-            step(s)
-        torch.cuda.synchronize()
-        hel = time.perf_counter() - th
-        hs = R.moe_get_stats(ctx)
-        hybrid = {"tokens_per_s": round(args.steps * T / hel, 2), "ms_per_step": round(hel * 1e3 / args.steps, 3),
-                  "fills": hs["fills"], "cpu_experts": hs["cpu_experts"],
-                  "cpu_branch_ms_per_step": round(hs["cpu_ms"] / args.steps, 3),
-                  "fill_path": "host DMA" if args.host_fills else "device copy kernel",
-                  "fill_GBps_wall": round(hs["fill_bytes"] / hel / 1e9, 2)}
+        for _ in range(reps):
+            R.moe_bind(ctx, router, arena, arena.numel(), n_slots)
+            for s in range(args.warmup):
+                step(s)
+            torch.cuda.synchronize()
+            R.moe_reset_stats(ctx)
+            th = time.perf_counter()
+            for s in range(args.warmup, total_steps):
+                step(s)
+            torch.cuda.synchronize()
+            hel = time.perf_counter() - th
+            hs = R.moe_get_stats(ctx)
+            logs.append(R.moe_step_log(ctx))
+            runs.append({"tokens_per_s": round(args.steps * T / hel, 2), "ms_per_step": round(hel * 1e3 / args.steps, 3),
+                         "fills": hs["fills"], "cpu_experts": hs["cpu_experts"],
+                         "cpu_branch_ms_per_step": round(hs["cpu_ms"] / args.steps, 3),
+                         "fill_path": "host DMA" if args.host_fills else "device copy kernel",
+                         "fill_GBps_wall": round(hs["fill_bytes"] / hel / 1e9, 2)})
+        mid = sorted(range(len(runs)), key=lambda i: runs[i]["tokens_per_s"])[len(runs) // 2]
+        hybrid = dict(runs[mid])
+        hybrid["runs_tokens_per_s"] = [r["tokens_per_s"] for r in runs]
+        qstar = qstar_balance(logs[mid], S, bw_p, bw_h, args.steps, L)
         if not args.host_fills and not args.no_graph:
             # the same hybrid steps from a cold cache, replayed from one captured graph: fills
             # by the device copy kernel, the CPU branch as host nodes on the library's stream
@@ -322,7 +366,8 @@ def main():
             del g
             hybrid["graph_tokens_per_s"] = round(args.steps * T / hg, 2)
             hybrid["graph_ms_per_step"] = round(hg * 1e3 / args.steps, 3)
-        log(f"hybrid: {hybrid}")
+        log(f"[{config}] hybrid: {hybrid}")
+        log(f"[{config}] q*: {qstar}")
         R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)
 
     # ---------------------------------------------------------------- CPU leg
@@ -343,13 +388,15 @@ def main():
         torch.cuda.synchronize()
         cel = time.perf_counter() - tc
         cs = R.moe_get_stats(ctx)
+        clog = R.moe_step_log(ctx)
         cpu_bytes = cs["cpu_experts"] * S
         cpu_mode = {"tokens_per_s": round(n_cpu * T / cel, 2), "ms_per_step": round(cel * 1e3 / n_cpu, 3),
                     "steps": n_cpu, "cpu_experts": cs["cpu_experts"],
                     "cpu_branch_ms_per_step": round(cs["cpu_ms"] / n_cpu, 3),
+                    "cpu_branch_ms_per_layer_step": round(float(np.mean(clog["cpu_ms"])), 4) if len(clog) else None,
                     "host_GBps": round(cpu_bytes / (cs["cpu_ms"] * 1e-3) / 1e9, 1) if cs["cpu_ms"] > 0 else None,
                     "bw_host_GBps": round(bw_h / 1e9, 2)}
-        log(f"cpu mode: {cpu_mode}")
+        log(f"[{config}] cpu mode: {cpu_mode}")
         R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)
 
     # ---------------------------------------------------------------- prefill leg
@@ -379,11 +426,14 @@ def main():
         prefill = {
             "tokens": Tp, "tokens_per_s": round(Tp / pel, 1), "wall_s": round(pel, 3),
             "copy_GBps": round(ps["copy_bytes"] / (ps["copy_ms"] * 1e-3) / 1e9, 2) if ps["copy_ms"] > 0 else None,
-            "copy_bytes": ps["copy_bytes"], "gemm_ms_per_layer": round(gemm_ms / L, 3),
+            "copy_bytes": ps["copy_bytes"], "copy_ms_per_layer": round(ps["copy_ms"] / L, 3),
+            "gemm_ms_per_layer": round(gemm_ms / L, 3),
+            "gemm1_ms_per_layer": round(ps["gemm1_ms"] / L, 3), "gemm2_ms_per_layer": round(ps["gemm2_ms"] / L, 3),
             "gemm_TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "gemm_weight_GBps": round(E * S / (gemm_ms / L * 1e-3) / 1e9, 1) if gemm_ms > 0 else None,
             "overlap": round(max(0.0, (ps["copy_ms"] + gemm_ms - pel * 1e3) / max(1e-9, min(ps["copy_ms"], gemm_ms))), 3),
         }
-        log(f"prefill: {prefill}")
+        log(f"[{config}] prefill: {prefill}")
 
     # ---------------------------------------------------------------- elastic leg
     # The batch-4 hybrid run of the elastic configuration on the same pool: four
@@ -391,9 +441,28 @@ def main():
     # measured above), the cache resized 1280 -> 640 -> 960 slots at safe points a third
     # and two thirds into the run without reloading the host pool.
     elastic = None
-    if mode == R.MOE_MODE_OFFLOAD and args.config == "a3b" and not args.no_elastic:
+    if mode == R.MOE_MODE_OFFLOAD and config == "a3b" and not args.no_elastic:
         elastic = elastic_leg(args, R, W, ctx, router, arena, n_slots, zipf, stream, dev)
-        log(f"elastic: {elastic}")
+        log(f"[{config}] elastic: {elastic}")
+
+    # ---------------------------------------------------------------- HBM ceiling legs
+    # Plain streaming reads of the sizes the kernels move per launch (phase 1, phase 2 of
+    # a decode step, one prefill layer's records), from a region of the arena not read in
+    # the previous passes (no cache reuse): the practical HBM read rate each kernel is
+    # measured against beside the vendor peak.
+    hbm = None
+    if not args.no_hbm_probe and mode == R.MOE_MODE_OFFLOAD:
+        hbm = {}
+        sizes = {"phase1": int(p1_bytes), "phase2": int(p2_bytes), "prefill_layer": int(E * S)}
+        for name, nb in sizes.items():
+            nb = min(nb, arena.numel() // 2)
+            if nb < (1 << 20):
+                continue
+            secs = R.moe_bench_hbm(arena, arena.numel(), nb, 40 if nb < (1 << 30) else 6, stream)[1:]
+            hbm[name] = {"bytes": nb, "median_us": round(median(list(secs)) * 1e6, 2),
+                         "median_GBps": round(nb / median(list(secs)) / 1e9, 1),
+                         "best_GBps": round(nb / float(np.min(secs)) / 1e9, 1)}
+        log(f"[{config}] hbm reads: {hbm}")
 
     # ---------------------------------------------------------------- fused leg
     # Every record resident (a second context over the same page-locked pool): the
@@ -404,7 +473,8 @@ def main():
     if mode == R.MOE_MODE_OFFLOAD and not args.no_fused and not args.no_graph:
         del arena
         torch.cuda.empty_cache()
-        cfg_f = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, 8, R.MOE_MODE_FUSED, wl.renorm)
+        cfg_f = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, 8, R.MOE_MODE_FUSED, wl.renorm,
+                              flags=R.MOE_FLAG_PROFILE)
         ctx_f = R.moe_create(cfg_f)
         R.moe_pool_register(ctx_f, pool, wl.pool_records, 1)
         arena_f = torch.empty(L * E * S, dtype=torch.uint8, device=dev)
@@ -414,6 +484,13 @@ def main():
         for s in range(args.warmup):
             step(s, c=ctx_f)
         torch.cuda.synchronize()
+        # eager all-resident steps with per-launch events: the routed phase 1 and the fused
+        # down projection + combine as the graph below runs them
+        R.moe_reset_stats(ctx_f)
+        for s in range(args.warmup, min(total_steps, args.warmup + 8)):
+            step(s, c=ctx_f)
+        torch.cuda.synchronize()
+        fs = R.moe_get_stats(ctx_f)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, capture_error_mode="thread_local"):
             step(1, Xs, torch.cuda.current_stream().cuda_stream, c=ctx_f)
@@ -425,18 +502,26 @@ def main():
         fel = time.perf_counter() - tf
         del g
         step_bytes = L * (k * S + E * H * 4 + T * H * (2 + 4))
+        f1 = fs["phase1_ms"] / max(1, fs["phase1_launches"])
+        f2 = fs["phase2_ms"] / max(1, fs["phase2_launches"])
         fused = {"tokens_per_s": round(args.steps * T / fel, 2), "ms_per_step": round(fel * 1e3 / args.steps, 3),
                  "step_bytes": step_bytes, "step_GBps": round(step_bytes * args.steps / fel / 1e9, 1),
-                 "step_hbm_frac": round(step_bytes * args.steps / fel / 1e9 / PEAK_HBM_GBS, 4)}
-        log(f"fused: {fused}")
+                 "step_hbm_frac": round(step_bytes * args.steps / fel / 1e9 / PEAK_HBM_GBS, 4),
+                 "routed_phase1_avg_us": round(f1 * 1e3, 2),
+                 "routed_phase1_GBps": round(fs["phase1_bytes"] / max(1, fs["phase1_launches"]) / (f1 * 1e-3) / 1e9, 1)
+                 if f1 > 0 else None,
+                 "phase2_combine_avg_us": round(f2 * 1e3, 2),
+                 "phase2_combine_GBps": round(fs["phase2_bytes"] / max(1, fs["phase2_launches"]) / (f2 * 1e-3) / 1e9, 1)
+                 if f2 > 0 else None}
+        log(f"[{config}] fused: {fused}")
         R.moe_destroy(ctx_f)
         del arena_f
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu_baseline = None
-    if not args.no_cpu_baseline:
+    if primary and not args.no_cpu_baseline:
         cpu_baseline = oracle_baseline(wl, args.cpu_baseline_seconds)
-        log(f"cpu baseline: {cpu_baseline}")
+        log(f"[{config}] cpu baseline: {cpu_baseline}")
 
     # headline: the graph-replayed step when it ran (the production path), else the eager one
     head_tok_s, head_ms = (graph["tokens_per_s"], graph["ms_per_step"]) if graph else \
@@ -446,29 +531,70 @@ def main():
         "value": head_tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": head_ms, "higher_is_better": True, "scaling": "weak",
         "headline_leg": "graph-replayed decode step" if graph else "eager decode step",
+        "repeats": reps if graph else 1,
         "vs_baseline": None,
         "dtype": {W.WFMT_BF16: "bf16", W.WFMT_FP4: "fp4(e2m1)+bf16 scale", W.WFMT_MXFP4: "mxfp4(e2m1)+e8m0 scale",
                   W.WFMT_F32: "f32"}[wl.wfmt],
         "data": "synthetic (seeded; random-init weights of the stated shape)",
         "config": {"workload": f"{wl.name}: L={L} E={E} k={k} H={H} I={wl.inter}, batch {T}, "
-                               f"{n_slots}-slot shared cache, {args.mode}, cold start",
+                               f"{n_slots}-slot shared cache, {args.mode}, cold start"
+                               + (f", pool aliased to {wl.alias_records} records" if wl.alias_records else ""),
                    "pool_records": wl.pool_records, "record_bytes": S,
                    "pool_aliased": bool(wl.alias_records)},
         "roofline": {"bound": "hbm", "kernel": "dec_phase1 (gate/up GEMV + SwiGLU)",
                      "achieved": round(p1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(p1_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(args.config),
-                     "bytes_per_launch": int(p1_bytes), "avg_launch_us": round(p1_avg_ms * 1e3, 3)},
+                     "frac": round(p1_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(config),
+                     "bytes_per_launch": int(p1_bytes), "avg_launch_us": round(p1_avg_ms * 1e3, 3),
+                     "practical_read_GBps": hbm["phase1"]["median_GBps"] if hbm and "phase1" in hbm else None},
         "cpu_baseline": cpu_baseline,
         "decode": decode_detail,
         "graph_decode": graph,
         "hybrid_decode": hybrid,
+        "qstar": qstar,
         "cpu_mode_decode": cpu_mode,
         "fused_decode": fused,
         "elastic_hybrid_batch4": elastic,
         "prefill": prefill,
+        "hbm_ceiling": hbm,
     }
-    print(json.dumps(out), flush=True)
     R.moe_destroy(ctx)
+    del ctx
+    torch.cuda.empty_cache()
+    return out
+
+
+def qstar_balance(rec, S, bw_p, bw_h, steps, L):
+    """The q* split per layer step (the library's step log of one hybrid run): how many
+    misses went to fills and to the CPU, and the two branches' measured times against
+    the closed form's T_fill = q S / B_P and T_cpu = (m - q) S / B_H."""
+    if rec is None or len(rec) == 0:
+        return None
+    m = rec["misses"]
+    q = rec["fills"]
+    c = rec["cpu"]
+    both = (q > 0) & (c > 0)
+    hist = {int(v): int(n) for v, n in zip(*np.unique(q, return_counts=True))}
+    mhist = {int(v): int(n) for v, n in zip(*np.unique(m, return_counts=True))}
+    tf, tc = rec["fill_ms"], rec["cpu_ms"]
+    out = {"layer_steps": int(len(rec)), "with_misses": int(np.sum(m > 0)),
+           "q_hist": hist, "m_hist": mhist,
+           "fills": int(q.sum()), "cpu_experts": int(c.sum()),
+           "fill_ms_mean": round(float(tf[q > 0].mean()), 4) if np.any(q > 0) else None,
+           "cpu_ms_mean": round(float(tc[c > 0].mean()), 4) if np.any(c > 0) else None,
+           "model_fill_ms_per_record": round(S / bw_p * 1e3, 4) if bw_p else None,
+           "model_cpu_ms_per_record": round(S / bw_h * 1e3, 4) if bw_h else None,
+           "measured_fill_ms_per_record": round(float(tf[q > 0].sum() / max(1, q[q > 0].sum())), 4)
+           if np.any(q > 0) else None,
+           "measured_cpu_ms_per_record": round(float(tc[c > 0].sum() / max(1, c[c > 0].sum())), 4)
+           if np.any(c > 0) else None}
+    if np.any(both):
+        r = tf[both] / np.maximum(tc[both], 1e-9)
+        out["fill_over_cpu_median"] = round(float(np.median(r)), 3)
+        out["steps_fill_longer"] = int(np.sum(tf[both] > tc[both]))
+        out["steps_cpu_longer"] = int(np.sum(tf[both] <= tc[both]))
+    out["exposed_ms_per_step"] = round(float(np.maximum(tf, tc).sum()) / steps, 3)
+    out["serial_ms_per_step"] = round(float((tf + tc).sum()) / steps, 3)
+    return out
 
 
 def elastic_leg(args, R, W, ctx, router, arena, n_slots, zipf, stream, dev):

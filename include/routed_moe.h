@@ -181,10 +181,21 @@ MOE_API moe_status moe_bind(moe_ctx* ctx, const float* router_w, void* arena, si
 /* FUSED mode: copy every pool record into arena slot = key (enqueued on stream). */
 MOE_API moe_status moe_fused_load(moe_ctx* ctx, moe_stream_t stream);
 
-/* Set B_P and B_H (bytes/s) used by the q* split from now on. */
+/*
+ * Set B_P and B_H (bytes/s) used by the q* split from now on.  Waits for all work on the
+ * device.  The kernels read the slot arena, the slot count, the mode and the bandwidths from
+ * a device-side control block when they run, so decode steps captured into a graph before
+ * this call, moe_set_mode or expert_cache_resize follow the new values on replay.
+ */
 MOE_API moe_status moe_set_bandwidths(moe_ctx* ctx, uint64_t bw_pcie, uint64_t bw_host);
 
-/* Change the backend mode between steps (not FUSED <-> cached: that needs a new bind). */
+/*
+ * Change the backend mode between steps (not FUSED <-> cached: that needs a new bind).  Waits
+ * for all work on the device; captured steps follow it on replay (see moe_set_bandwidths).  A
+ * step captured without a CPU branch (OFFLOAD with n_slots >= 2*T*k) whose lookup now sends
+ * experts to the CPU leaves them out of y and makes the next moe_sync return MOE_ESTATE:
+ * capture such steps again after the change.
+ */
 MOE_API moe_status moe_set_mode(moe_ctx* ctx, int32_t mode);
 
 /* ---- the hot path ------------------------------------------------------ */
@@ -310,8 +321,12 @@ MOE_API moe_status moe_permute(moe_ctx* ctx, const int32_t* slot_idx, int32_t T,
  * ([FT-KR] "탄력적 메모리 관리").  Shrinking keeps the n_slots' most recently used entries,
  * packed into slots 0..n_slots'-1 in ascending old-slot order (recency kept); growing adds empty
  * slots.  new_arena = NULL resizes in the bound arena (needs arena_bytes >= n_slots' * S);
- * otherwise records move to new_arena, which becomes the bound arena.  Synchronises stream.
- * MOE_ESTATE inside prefill; MOE_ENOTSUP in FUSED mode.
+ * otherwise records move to new_arena, which becomes the bound arena.  Synchronises stream, then
+ * waits for all work on the device before it publishes the new arena and slot count to the
+ * device-side control block the kernels read when they run: decode steps captured into a graph
+ * before the resize use the resized cache on replay.  A captured step without a CPU branch
+ * whose lookup finds too few slots after a shrink is reported by moe_sync (MOE_ESTATE; see
+ * moe_set_mode).  MOE_ESTATE inside prefill; MOE_ENOTSUP in FUSED mode.
  */
 MOE_API moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_n_slots, void* new_arena, size_t new_arena_bytes,
                                        moe_stream_t stream);
@@ -333,6 +348,20 @@ MOE_API int32_t qstar_split(int32_t m, uint64_t bw_pcie, uint64_t bw_host, int32
  */
 MOE_API moe_status moe_bench_bw(moe_ctx* ctx, uint64_t* bw_pcie, uint64_t* bw_host);
 
+/*
+ * The practical HBM read rate of the current device at one transfer size: the ceiling the
+ * memory-bound kernels of this library (decode GEMVs: the routed experts' records read once
+ * per step; prefill GEMMs: a layer's records) are measured against.  Pass r (0 <= r < reps)
+ * reads read_bytes of buf (device memory of buf_bytes, caller-owned, read only) at offset
+ * (r * read_bytes) mod (buf_bytes - read_bytes + 1), rounded down to 256 bytes, with a plain
+ * streaming kernel (16-byte loads, four in flight per thread), so with buf_bytes far above
+ * the last-level caches every pass comes from HBM.  seconds_out[r] (host) receives pass r's
+ * kernel duration.  Synchronises stream.  MOE_EINVAL: null pointers, reps < 1, read_bytes < 16
+ * or above buf_bytes.
+ */
+MOE_API moe_status moe_bench_hbm(const void* buf, size_t buf_bytes, size_t read_bytes, int32_t reps,
+                                 double* seconds_out, moe_stream_t stream);
+
 /* Copy the residency tables to host memory (any pointer may be NULL):
  * slot_of [L*E], key_of [n_slots], stamp [n_slots]; *counter = the recency counter. */
 MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, uint64_t* stamp,
@@ -340,9 +369,33 @@ MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* k
 
 /*
  * Wait for `stream` and report what device-fill steps could not report when they were
- * enqueued: MOE_EINVAL if a step since the last moe_sync saw an expert id out of range.
+ * enqueued: MOE_EINVAL if a step since the last moe_sync saw an expert id out of range;
+ * MOE_ESTATE if a step without a CPU branch had experts sent to the CPU by its lookup (a
+ * graph captured before a shrink or a mode change; those experts are missing from y).
  */
 MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream);
+
+/*
+ * One layer step whose work lists the host read, logged when the context was created with
+ * MOE_FLAG_PROFILE (eager decode steps that may send experts to the CPU, and steps with
+ * host-issued fills): the inputs and the outcome of the q* split ([FT-KR] "측정된 대역폭이
+ * 분할을 결정합니다": T_fill = q S / B_P against T_cpu for the other m - q misses).
+ *   misses  m, the step's distinct routed experts not resident;  fills  q;  cpu  m - q
+ *   fill_ms the fill copy of the q records: the copy kernel's duration (device fills) or the
+ *           span of the host-issued copies on the copy stream; 0 when q = 0
+ *   cpu_ms  wall time of the CPU branch over the cpu list; 0 when it is empty
+ */
+typedef struct {
+  int32_t layer, misses, fills, cpu;
+  double fill_ms, cpu_ms;
+} moe_step_rec;
+
+/*
+ * Move up to `capacity` logged steps (oldest first) into out (host memory) and clear the log;
+ * *n_out receives the number written.  Synchronises the context's streams (the fill times are
+ * kernel timestamps).  At most 2^20 steps are kept between calls; later ones are dropped.
+ */
+MOE_API moe_status moe_step_log(moe_ctx* ctx, moe_step_rec* out, int32_t capacity, int32_t* n_out);
 
 /* Accumulated statistics (synchronises the context's streams to read kernel timings). */
 MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);

@@ -62,6 +62,11 @@ class moe_stats(ctypes.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
+class moe_step_rec(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("layer", "misses", "fills", "cpu")] + [
+        ("fill_ms", ctypes.c_double), ("cpu_ms", ctypes.c_double)]
+
+
 MOE_PLACE_LRU, MOE_PLACE_PREFILL, MOE_PLACE_STATIC, MOE_PLACE_PINNED_RING = 0, 1, 2, 3
 
 
@@ -121,6 +126,8 @@ def _load():
         "moe_get_stats": (I32, [P, ctypes.POINTER(moe_stats)]),
         "moe_reset_stats": (I32, [P]),
         "moe_sync": (I32, [P, VP]),
+        "moe_step_log": (I32, [P, VP, I32, ctypes.POINTER(I32)]),
+        "moe_bench_hbm": (I32, [VP, ctypes.c_size_t, ctypes.c_size_t, I32, VP, VP]),
         "moe_placement_replay": (I32, [ctypes.POINTER(moe_replay_config), VP, I32, VP, I32, I32, VP,
                                        ctypes.POINTER(moe_replay_result)]),
         "moe_bank_write": (I32, [ctypes.c_char_p, ctypes.POINTER(moe_config), VP, I64]),
@@ -395,3 +402,24 @@ def moe_reset_stats(ctx: Ctx) -> None:
 
 def moe_sync(ctx: Ctx, stream=None) -> None:
     _check(ctx, lib.moe_sync(ctx.handle, _stream(stream)), "moe_sync")
+
+
+def moe_step_log(ctx: Ctx, capacity: int = 1 << 20):
+    """The logged steps (oldest first) as a numpy record array; clears the log."""
+    import numpy as np
+    buf = (moe_step_rec * capacity)()
+    n = ctypes.c_int32()
+    _check(ctx, lib.moe_step_log(ctx.handle, ctypes.addressof(buf), capacity, ctypes.byref(n)), "moe_step_log")
+    dt = np.dtype([("layer", np.int32), ("misses", np.int32), ("fills", np.int32), ("cpu", np.int32),
+                   ("fill_ms", np.float64), ("cpu_ms", np.float64)])
+    return np.frombuffer(bytes(buf)[: n.value * ctypes.sizeof(moe_step_rec)], dtype=dt).copy()
+
+
+def moe_bench_hbm(buf, buf_bytes: int, read_bytes: int, reps: int, stream=None):
+    """Per-pass kernel seconds of reps plain reads of read_bytes from the device buffer buf."""
+    import numpy as np
+    out = np.zeros(reps, np.float64)
+    st = lib.moe_bench_hbm(_ptr(buf), buf_bytes, read_bytes, reps, out.ctypes.data, _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_bench_hbm", "bad arguments or device error")
+    return out

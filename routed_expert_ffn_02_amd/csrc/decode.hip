@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
   if (g >= a.cnt[C_NGRP]) return;
   const int row0 = (blockIdx.x * 4 + wave) * RW;
   if (row0 >= I) return;
-  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  const uint8_t* rec = a.ctrl->arena + (int64_t)slot * a.rec_bytes;
   uint4 qg[RW][CPL], qu[RW][CPL];
   float sg[RW][CPL], su[RW][CPL];
 #pragma unroll
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
   }
   const int row0 = (blockIdx.x * 4 + wave) * RW;
   if (row0 >= I) return;
-  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  const uint8_t* rec = a.ctrl->arena + (int64_t)slot * a.rec_bytes;
   u32x4n qg[RW][CPL], qu[RW][CPL];
   uint16_t sg[RW][CPL], su[RW][CPL];  // block scales (raw bf16 bits or E8M0 bytes)
 #pragma unroll
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
   const int H = a.H, I = a.I;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
+  const uint8_t* rec = a.ctrl->arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
   using RD = RowDot<WFMT>;
   constexpr int EPC = RD::kElems;
   const int n = group_pairs(a, g, s_pair, &s_n);
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r0 = blockIdx.x * kP2Rows + wave * R2;
   if (r0 >= H) return;
-  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  const uint8_t* rec = a.ctrl->arena + (int64_t)slot * a.rec_bytes;
   using RD = RowDot<WFMT>;
   constexpr int EPC = RD::kElems;
   // one token: the group's activated row is requested before the weights (loads
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r0 = blockIdx.x * kP2Rows + wave * R2;
   if (r0 >= H) return;
-  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  const uint8_t* rec = a.ctrl->arena + (int64_t)slot * a.rec_bytes;
   // one token: the group's activated row is requested before the weights
   f32x4n hq[MAXT][EPC / 4];
   if constexpr (MAXT == 1) {
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(64 * kP2cMaxK) void dec_phase2_combine_bf(DecodeArg
     if (j == 0 && lane < R2 && r0 + lane < H) a.y[r0 + lane] = 0.f;
     return;
   }
-  const uint8_t* rec = a.arena + (int64_t)slot * a.rec_bytes;
+  const uint8_t* rec = a.ctrl->arena + (int64_t)slot * a.rec_bytes;
   f32x4n hq[EPC / 4];
   const f32x4n* hp = reinterpret_cast<const f32x4n*>(a.h + (int64_t)j * I + lane * EPC);
 #pragma unroll
@@ -891,7 +891,7 @@ __global__ __launch_bounds__(256) void dec_phase2(DecodeArgs a) {
   __shared__ int s_pair[kDecodeMaxTok];
   __shared__ int s_n;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
+  const uint8_t* rec = a.ctrl->arena + (int64_t)a.grp_slot[g] * a.rec_bytes;
   using RD = RowDot<WFMT>;
   constexpr int EPC = RD::kElems;
   const int r0 = blockIdx.x * kP2Rows + wave * R2;

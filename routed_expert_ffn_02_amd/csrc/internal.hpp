@@ -33,7 +33,20 @@ enum {
 };
 
 // device-side step statistics of device-fill steps (uint64 array)
-enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_P1_BYTES = 6, D_P2_BYTES = 7, D_COUNT = 8 };
+// D_NOCPU: steps whose lookup sent experts to the CPU although the step, as enqueued or
+// captured, had no CPU branch (a graph replayed after a shrink or a mode change)
+enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_P1_BYTES = 6, D_P2_BYTES = 7,
+       D_NOCPU = 8, D_COUNT = 9 };
+
+// Cache parameters the kernels read on the device when they run, not from their launch
+// arguments, so a step captured into a graph and replayed sees the current values after
+// expert_cache_resize, moe_set_mode and moe_set_bandwidths.
+struct DevCtrl {
+  uint8_t* arena;      // the bound slot arena
+  int32_t n_slots;
+  int32_t lk_mode;     // LookupMode of decode lookups (the context's backend mode)
+  uint64_t bw_pcie, bw_host;
+};
 
 enum LookupMode { LK_FUSED = 0, LK_OFFLOAD = 1, LK_CPU = 2, LK_HYBRID = 3, LK_BUFFER = 4 };
 
@@ -48,6 +61,10 @@ struct LookupArgs {
   int32_t T, k, E, layer;
   int32_t mode;              // LookupMode
   int32_t n_slots;
+  // decode lookups: n_slots, mode and bandwidths are read from the control block when the
+  // kernel runs (prefill lookups: n_slots only, the mode as given)
+  const DevCtrl* ctrl;
+  int32_t mode_from_ctrl;
   int32_t buffer_base;       // LK_BUFFER: slot of expert 0 of this layer
   uint64_t bw_pcie, bw_host;
   // cache tables
@@ -71,7 +88,7 @@ struct LookupArgs {
 struct DecodeArgs {
   const void* x;             // [T,H] afmt
   const float* w;            // [T,k]
-  const uint8_t* arena;
+  const DevCtrl* ctrl;       // the arena base is read from here when the kernel runs
   int64_t rec_bytes;
   int32_t T, k, H, I;
   const int32_t* grp_slot;   // [G]
@@ -101,7 +118,8 @@ struct FillArgs {
   const int32_t* fill_slot;  // [E]
   const uint8_t* pool;       // device address of the page-locked host pool
   int64_t pool_records;      // the pool holds records key % pool_records
-  uint8_t* arena;
+  const DevCtrl* ctrl;       // the arena base is read from here when the kernel runs
+  int32_t no_cpu_branch;     // the step has no CPU branch: CPU work from the lookup is an error
   int64_t rec_bytes;
   uint64_t* dstats;          // [D_COUNT] accumulated step counts, or nullptr
   // algorithmic bytes of the step's GEMV phases (zero unless profiling):
@@ -167,7 +185,8 @@ struct StageArgs {
   int P;
 };
 void launch_stage_step(const StageArgs& a, hipStream_t s);
-void launch_fill_pull(const FillArgs& a, int max_fills, hipStream_t s);
+void launch_fill_pull(const FillArgs& a, int max_fills, hipStream_t s, Timing tm = {});
+void launch_read_probe(const void* p, int64_t bytes, hipStream_t s, Timing tm);
 void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
                     int32_t* inv, int32_t* offsets, int32_t* tile_base, int bm, hipStream_t s);
 void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp, int32_t* grp_slot, int32_t* cnt,
@@ -267,6 +286,7 @@ struct moe_ctx {
   float* ypair = nullptr;
   int32_t* flags = nullptr;
   uint64_t* dstats = nullptr;    // [D_COUNT] counts of device-fill steps
+  rmoe::DevCtrl* ctrl = nullptr; // device control block (arena, n_slots, mode, bandwidths)
 
   // pinned host staging; h_cnt .. h_u_kind mirror step_dev
   int32_t* step_host = nullptr;
@@ -307,7 +327,8 @@ struct moe_ctx {
 
   // stats and profiling
   moe_stats stats{};
-  struct Timed { hipEvent_t a, b; int kind; };
+  std::vector<moe_step_rec> step_log;   // profiled steps read on the host (moe_step_log)
+  struct Timed { hipEvent_t a, b; int kind; int64_t rec; };
   std::vector<Timed> pending_timed;
   std::vector<hipEvent_t> event_pool;
 

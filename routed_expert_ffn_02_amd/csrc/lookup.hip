@@ -66,7 +66,7 @@ constexpr int kSmallP = kSmallLookupPairs;  // pairs a step may have for the one
 // joins only for the per-slot scan (evictable count and each wavefront's smallest
 // (stamp, slot) candidates).  Three block barriers in all; the decisions and their
 // order are those of the general path below.
-__device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, unsigned char* s_prot,
+__device__ __forceinline__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, unsigned char* s_prot,
                              uint64_t (*s_cand)[kSmallP], int* s_evc, int* s_ufirst, int* s_sc, int* s_tk) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, P = a.T * a.k;
@@ -313,7 +313,18 @@ __device__ void lookup_small(const LookupArgs& a, int* s_slotrow, int* s_keyof, 
   }
 }
 
-__global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs a) {
+__global__ __launch_bounds__(kLookupThreads) void lookup_kernel(LookupArgs args) {
+  // the cache's current size (and for decode lookups mode and bandwidths) as they are when
+  // the kernel runs: a replayed graph follows resizes and mode changes made after capture
+  LookupArgs a = args;
+  if (args.ctrl) {
+    a.n_slots = args.ctrl->n_slots;
+    if (args.mode_from_ctrl) {
+      a.mode = args.ctrl->lk_mode;
+      a.bw_pcie = args.ctrl->bw_pcie;
+      a.bw_host = args.ctrl->bw_host;
+    }
+  }
   __shared__ int s_first[kMaxExperts];   // first pair index of expert e, or INT_MAX
   __shared__ int s_upos[kMaxExperts];    // position of expert e in U, or -1
   __shared__ int s_ukey[kMaxExperts];

@@ -103,7 +103,8 @@ hipEvent_t take_event(moe_ctx* c) {
   return e;
 }
 
-enum TimedKind { TK_P1 = 0, TK_P2 = 1, TK_G1 = 2, TK_G2 = 3, TK_COPY = 4 };
+enum TimedKind { TK_P1 = 0, TK_P2 = 1, TK_G1 = 2, TK_G2 = 3, TK_COPY = 4, TK_FILL = 5 };
+constexpr size_t kStepLogMax = size_t(1) << 20;
 
 // Work enqueued while `s` is being captured into a graph runs later, at each replay:
 // nothing may be read on the host then, and per-launch profiling is skipped.
@@ -120,10 +121,11 @@ struct TimedScope {
   hipStream_t s;
   int kind;
   bool record;
+  int64_t rec;  // TK_FILL: the step-log record the interval belongs to
   Timing tm;
-  TimedScope(moe_ctx* c_, hipStream_t s_, int kind_, bool record_around = false)
-      : c(c_), s(s_), kind(kind_), record(record_around) {
-    if ((c->cfg.flags & MOE_FLAG_PROFILE) && !capturing(s)) {
+  TimedScope(moe_ctx* c_, hipStream_t s_, int kind_, bool record_around = false, int64_t rec_ = -1)
+      : c(c_), s(s_), kind(kind_), record(record_around), rec(rec_) {
+    if (kind >= 0 && (c->cfg.flags & MOE_FLAG_PROFILE) && !capturing(s)) {
       tm.start = take_event(c);
       tm.stop = take_event(c);
       if (record && tm.start) hipEventRecord(tm.start, s);
@@ -132,7 +134,7 @@ struct TimedScope {
   ~TimedScope() {
     if (tm.start && tm.stop) {
       if (record) hipEventRecord(tm.stop, s);
-      c->pending_timed.push_back({tm.start, tm.stop, kind});
+      c->pending_timed.push_back({tm.start, tm.stop, kind, rec});
     }
   }
 };
@@ -147,6 +149,10 @@ void drain_timed(moe_ctx* c) {
         case TK_G1: c->stats.gemm1_ms += ms; break;
         case TK_G2: c->stats.gemm2_ms += ms; break;
         case TK_COPY: c->stats.copy_ms += ms; break;
+        case TK_FILL:
+          if (t.rec >= 0 && t.rec < (int64_t)c->step_log.size() && c->step_log[t.rec].fills > 0)
+            c->step_log[t.rec].fill_ms += ms;
+          break;
       }
     }
     c->event_pool.push_back(t.a);
@@ -179,6 +185,8 @@ void fill_lookup_args(moe_ctx* c, LookupArgs& a, int layer, const int32_t* idx, 
   a.n_slots = c->n_slots;
   a.bw_pcie = c->cfg.bw_pcie;
   a.bw_host = c->cfg.bw_host;
+  a.ctrl = c->ctrl;
+  a.mode_from_ctrl = 0;
   a.slot_of = c->slot_of;
   a.key_of = c->key_of;
   a.stamp = c->stamp;
@@ -204,6 +212,20 @@ int lookup_mode_of(int mode) {
     case MOE_MODE_CPU: return LK_CPU;
     default: return LK_HYBRID;
   }
+}
+
+// The device control block from the host state, once all work on the device has finished
+// (kernels read it when they run, so it changes only between steps).
+moe_status write_ctrl(moe_ctx* ctx) {
+  DevCtrl h{};
+  h.arena = ctx->arena;
+  h.n_slots = ctx->n_slots;
+  h.lk_mode = lookup_mode_of(ctx->cfg.mode);
+  h.bw_pcie = ctx->cfg.bw_pcie;
+  h.bw_host = ctx->cfg.bw_host;
+  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(hipMemcpy(ctx->ctrl, &h, sizeof h, hipMemcpyHostToDevice));
+  return MOE_OK;
 }
 
 // Copy the step's counts and work lists (one contiguous block) to pinned host memory,
@@ -247,11 +269,12 @@ moe_status read_step(moe_ctx* ctx, hipStream_t s, bool inputs, const void* x, co
 // Fills of the current step: pinned pool -> victim slots on the copy stream; the
 // compute stream waits for them.  The compute stream is idle up to the lookup here
 // (read_step synchronised it), so no kernel still reads a victim slot.
-moe_status issue_fills(moe_ctx* ctx, hipStream_t s) {
+moe_status issue_fills(moe_ctx* ctx, hipStream_t s, int64_t log_rec = -1) {
   const int nf = ctx->h_cnt[C_FILL];
   if (nf <= 0) return MOE_OK;
   if (!ctx->pool_pinned) return fail(ctx, MOE_ENOPIN, "fills need a page-locked host pool");
   TimedScope ts(ctx, ctx->copy_stream, TK_COPY, true);
+  TimedScope tl(ctx, ctx->copy_stream, log_rec >= 0 ? TK_FILL : -1, true, log_rec);
   for (int i = 0; i < nf; ++i) {
     const int key = ctx->h_fill_key[i], slot = ctx->h_fill_slot[i];
     HIPCHK(hipMemcpyAsync(ctx->arena + (int64_t)slot * ctx->S, pool_record(ctx, key), ctx->S, hipMemcpyHostToDevice,
@@ -457,7 +480,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->hist, (size_t)((Pmax + 255) / 256) * kMaxExperts) || dev_alloc(&ctx->cand, E) ||
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->act), (size_t)Pmax * I * 4) ||
       dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)) ||
-      dev_alloc(&ctx->dstats, D_COUNT))
+      dev_alloc(&ctx->dstats, D_COUNT) || dev_alloc(&ctx->ctrl, 1))
     return cleanup_fail(MOE_ENOMEM);
   if (prefill_needs_act_operands(c.wfmt, c.afmt) &&
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->xo), (size_t)c.max_tokens * H * 2))
@@ -513,7 +536,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       hipEventCreateWithFlags(&ctx->ev_layer_done[0], hipEventDisableTiming) ||
       hipEventCreateWithFlags(&ctx->ev_layer_done[1], hipEventDisableTiming))
     return cleanup_fail(MOE_EHIP);
-  if (hipDeviceSynchronize() != hipSuccess) return cleanup_fail(MOE_EHIP);
+  if (write_ctrl(ctx) != MOE_OK) return cleanup_fail(MOE_EHIP);
   *out = ctx;
   return MOE_OK;
 }
@@ -533,7 +556,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
                  ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
-                 ctx->flags, ctx->xo, ctx->dstats};
+                 ctx->flags, ctx->xo, ctx->dstats, ctx->ctrl};
   for (void* p : dev)
     if (p) hipFree(p);
   void* host[] = {ctx->step_host, ctx->h_slot_idx, ctx->h_w, ctx->h_x, ctx->h_xf, ctx->h_y, ctx->h_hbuf};
@@ -615,7 +638,7 @@ MOE_API moe_status moe_bind(moe_ctx* ctx, const float* router_w, void* arena, si
   ctx->n_slots = n_slots;
   ctx->bound = true;
   ctx->last_lookup_layer = -1;
-  return MOE_OK;
+  return write_ctrl(ctx);
 }
 
 MOE_API moe_status moe_fused_load(moe_ctx* ctx, moe_stream_t stream) {
@@ -632,7 +655,7 @@ MOE_API moe_status moe_set_bandwidths(moe_ctx* ctx, uint64_t bw_pcie, uint64_t b
   CHECK_ARG(bw_pcie > 0 && bw_host > 0 && bw_pcie < (1ull << 53) && bw_host < (1ull << 53), "bandwidths out of range");
   ctx->cfg.bw_pcie = bw_pcie;
   ctx->cfg.bw_host = bw_host;
-  return MOE_OK;
+  return write_ctrl(ctx);
 }
 
 MOE_API moe_status moe_set_mode(moe_ctx* ctx, int32_t mode) {
@@ -641,7 +664,7 @@ MOE_API moe_status moe_set_mode(moe_ctx* ctx, int32_t mode) {
   CHECK_ARG((mode == MOE_MODE_FUSED) == (ctx->cfg.mode == MOE_MODE_FUSED), "FUSED <-> cached needs a new context");
   CHECK_ARG(ctx->pool_pinned || mode == MOE_MODE_CPU, "pageable pool: only MOE_MODE_CPU");
   ctx->cfg.mode = mode;
-  return MOE_OK;
+  return write_ctrl(ctx);
 }
 
 MOE_API moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const float* logit_bias,
@@ -680,6 +703,7 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
   CHECK_ARG(topk_idx && slot_idx, "null pointer");
   LookupArgs a;
   fill_lookup_args(ctx, a, layer, topk_idx, T, lookup_mode_of(ctx->cfg.mode));
+  a.mode_from_ctrl = 1;
   a.slot_idx = slot_idx;
   a.trace = trace;
   a.counts_out = counts;
@@ -705,6 +729,7 @@ MOE_API moe_status moe_route_lookup(moe_ctx* ctx, int32_t layer, const void* x, 
   launch_route_logits(x, ctx->cfg.afmt, ctx->router_w + (int64_t)layer * E * H, logit_bias, z, T, E, H, s);
   LookupArgs a;
   fill_lookup_args(ctx, a, layer, topk_idx, T, lookup_mode_of(ctx->cfg.mode));
+  a.mode_from_ctrl = 1;
   if (T * k <= kSmallLookupPairs && T <= kLookupThreads / 64) {
     // the lookup kernel takes the top k from the logits itself: one launch fewer
     a.topk_idx = nullptr;
@@ -742,7 +767,7 @@ MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, 
     DecodeArgs d{};
     d.x = x;
     d.w = topk_w;
-    d.arena = ctx->arena;
+    d.ctrl = ctx->ctrl;
     d.rec_bytes = ctx->S;
     d.T = 1;
     d.k = k;
@@ -829,6 +854,13 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   const bool devfill = devfill_flag && (!inputs || captured);
   const bool devfill_host = devfill_flag && inputs && !captured && ctx->pool_dev;
   if (devfill && !ctx->pool_dev) return fail(ctx, MOE_ENOPIN, "device fills need a mapped page-locked pool");
+  // a profiled step whose lists the host reads is logged with its split and branch times
+  int64_t log_rec = -1;
+  if (profile && !fused && !devfill && ctx->step_log.size() < kStepLogMax) {
+    ctx->step_log.push_back(moe_step_rec{layer, 0, 0, 0, 0.0, 0.0});
+    log_rec = (int64_t)ctx->step_log.size() - 1;
+  }
+  const double cpu_ms0 = ctx->stats.cpu_ms;
   if (captured && !fused && !devfill)
     return fail(ctx, MOE_ESTATE, "a captured decode step reads nothing on the host: use FUSED mode or a cached "
                                  "mode with MOE_FLAG_DEVICE_FILLS");
@@ -853,7 +885,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   DecodeArgs d{};
   d.x = x;
   d.w = topk_w;
-  d.arena = ctx->arena;
+  d.ctrl = ctx->ctrl;
   d.rec_bytes = ctx->S;
   d.T = T;
   d.k = k;
@@ -880,7 +912,8 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     f.fill_slot = ctx->fill_slot;
     f.pool = ctx->pool_dev;
     f.pool_records = ctx->pool_records;
-    f.arena = ctx->arena;
+    f.ctrl = ctx->ctrl;
+    f.no_cpu_branch = devfill && !async_cpu;
     f.rec_bytes = ctx->S;
     f.dstats = devfill ? ctx->dstats : nullptr;  // a step the host reads is counted there
     const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
@@ -890,9 +923,10 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     f.p2_grp = dprof ? (uint64_t)H * wrow_i : 0;
     f.p2_fixed = dprof ? (uint64_t)T * H * 4 : 0;
     f.pair_bytes = dprof ? (uint64_t)I * 4 : 0;
-    launch_fill_pull(f, max_groups, s);
+    TimedScope tf(ctx, s, log_rec >= 0 ? TK_FILL : -1, false, log_rec);
+    launch_fill_pull(f, max_groups, s, tf.tm);
   } else if (!fused) {
-    moe_status st = issue_fills(ctx, s);
+    moe_status st = issue_fills(ctx, s, log_rec);
     if (st != MOE_OK) return st;
   }
   {
@@ -920,6 +954,13 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   }
   if (async_cpu) HIPCHK(hipStreamWaitEvent(s, ctx->ev_join, 0));
   if (!combined) launch_decode_combine(d, y_cpu, s);
+  if (log_rec >= 0) {
+    moe_step_rec& r = ctx->step_log[log_rec];
+    r.fills = ctx->h_cnt[C_FILL];
+    r.cpu = ctx->h_cnt[C_CPU];
+    r.misses = r.fills + r.cpu;
+    r.cpu_ms = ctx->stats.cpu_ms - cpu_ms0;
+  }
   HIPCHK(hipGetLastError());
   if (profile && devfill) {  // bytes are added on the device
     ctx->stats.phase1_launches += 1;
@@ -1302,7 +1343,7 @@ MOE_API moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_n_slots, void* 
   ctx->arena_bytes = dst_bytes;
   ctx->n_slots = new_n_slots;
   ctx->last_lookup_layer = -1;
-  return MOE_OK;
+  return write_ctrl(ctx);
 }
 
 MOE_API moe_status moe_bench_bw(moe_ctx* ctx, uint64_t* bw_pcie, uint64_t* bw_host) {
@@ -1364,6 +1405,32 @@ MOE_API moe_status moe_bench_bw(moe_ctx* ctx, uint64_t* bw_pcie, uint64_t* bw_ho
   return MOE_OK;
 }
 
+MOE_API moe_status moe_bench_hbm(const void* buf, size_t buf_bytes, size_t read_bytes, int32_t reps,
+                                 double* seconds_out, moe_stream_t stream) {
+  if (!buf || !seconds_out || reps < 1 || read_bytes < 16 || read_bytes > buf_bytes) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Timing tm;
+  if (hipEventCreate(&tm.start) != hipSuccess) return MOE_EHIP;
+  if (hipEventCreate(&tm.stop) != hipSuccess) {
+    hipEventDestroy(tm.start);
+    return MOE_EHIP;
+  }
+  moe_status st = MOE_OK;
+  const size_t span = buf_bytes - read_bytes + 1;
+  for (int r = 0; r < reps && st == MOE_OK; ++r) {
+    const size_t off = (size_t)(((unsigned __int128)r * read_bytes) % span) & ~(size_t)255;
+    launch_read_probe(static_cast<const uint8_t*>(buf) + off, (int64_t)read_bytes, s, tm);
+    float ms = 0.f;
+    if (hipGetLastError() != hipSuccess || hipEventSynchronize(tm.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, tm.start, tm.stop) != hipSuccess)
+      st = MOE_EHIP;
+    seconds_out[r] = ms * 1e-3;
+  }
+  hipEventDestroy(tm.start);
+  hipEventDestroy(tm.stop);
+  return st;
+}
+
 MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* key_of, uint64_t* stamp,
                                       uint64_t* counter, int32_t* n_slots) {
   if (!ctx) return MOE_EINVAL;
@@ -1382,12 +1449,18 @@ MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* k
 MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream) {
   if (!ctx) return MOE_EINVAL;
   HIPCHK(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  uint64_t err = 0;
+  uint64_t err = 0, nocpu = 0;
   HIPCHK(hipMemcpy(&err, ctx->dstats + D_ERR, 8, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(&nocpu, ctx->dstats + D_NOCPU, 8, hipMemcpyDeviceToHost));
+  const uint64_t zero = 0;
   if (err) {
-    const uint64_t zero = 0;
     HIPCHK(hipMemcpy(ctx->dstats + D_ERR, &zero, 8, hipMemcpyHostToDevice));
     return fail(ctx, MOE_EINVAL, "expert id out of range in topk_idx (device-fill step)");
+  }
+  if (nocpu) {
+    HIPCHK(hipMemcpy(ctx->dstats + D_NOCPU, &zero, 8, hipMemcpyHostToDevice));
+    return fail(ctx, MOE_ESTATE, "a step without a CPU branch had experts sent to the CPU (a graph captured "
+                                 "before a shrink or a mode change: capture it again)");
   }
   return MOE_OK;
 }
@@ -1411,16 +1484,30 @@ MOE_API moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
   return MOE_OK;
 }
 
+MOE_API moe_status moe_step_log(moe_ctx* ctx, moe_step_rec* out, int32_t capacity, int32_t* n_out) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(n_out && capacity >= 0 && (out || capacity == 0), "bad arguments");
+  HIPCHK(hipDeviceSynchronize());
+  drain_timed(ctx);
+  const int32_t n = (int32_t)std::min<size_t>((size_t)capacity, ctx->step_log.size());
+  if (n > 0) std::memcpy(out, ctx->step_log.data(), (size_t)n * sizeof(moe_step_rec));
+  ctx->step_log.clear();
+  *n_out = n;
+  return MOE_OK;
+}
+
 MOE_API moe_status moe_reset_stats(moe_ctx* ctx) {
   if (!ctx) return MOE_EINVAL;
   drain_timed(ctx);
   ctx->stats = moe_stats{};
+  ctx->step_log.clear();
   HIPCHK(hipDeviceSynchronize());
   uint64_t d[D_COUNT];
   HIPCHK(hipMemcpy(d, ctx->dstats, sizeof d, hipMemcpyDeviceToHost));
-  const uint64_t err = d[D_ERR];  // a pending error stays pending for moe_sync
+  const uint64_t err = d[D_ERR], nocpu = d[D_NOCPU];  // pending errors stay pending for moe_sync
   for (auto& v : d) v = 0;
   d[D_ERR] = err;
+  d[D_NOCPU] = nocpu;
   HIPCHK(hipMemcpy(ctx->dstats, d, sizeof d, hipMemcpyHostToDevice));
   return MOE_OK;
 }

@@ -3,9 +3,13 @@ plus small marshalling helpers.  Inputs come from `workloads`; expected values c
 from `oracle`; nothing flows from the GPU into the oracle."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
+import oracle
 import workloads as W
 
 
@@ -16,6 +20,39 @@ def row_rel_err(y, ref):
     num = np.abs(y - ref).max(axis=1)
     den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
     return float((num / den).max())
+
+
+def oracle_outputs(wl, layer, x_np, idx, threads=None):
+    """Per-pair expert outputs [T,k,H] (float64) of the oracle's all-resident definition,
+    with the distinct experts evaluated in parallel threads (each runs the oracle's own
+    dequantisation and SwiGLU for its rows; numpy releases the GIL in both)."""
+    x64 = oracle.formats.activations_f64(x_np)
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    out = np.zeros((T, k, wl.hidden), np.float64)
+    experts = sorted(set(idx.reshape(-1).tolist()))
+
+    def one(e):
+        rows = np.argwhere(idx == e)
+        ys = oracle.expert_ffn(x64[rows[:, 0]], *oracle.expert_weights_f64(wl, layer * wl.n_experts + e))
+        return rows, ys
+
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for rows, ys in ex.map(one, experts):
+            out[rows[:, 0], rows[:, 1]] = ys
+    return out
+
+
+def exact_f32(y64):
+    """The fp32 value of an oracle result that the exact-arithmetic inputs make
+    representable: asserts the premise (the fp64 value is an fp32 number up to the fp64
+    rounding of silu(g) = g / (1 + e^-g) at g >= 32, a relative 2^-46), returns it as fp32."""
+    y64 = np.asarray(y64, np.float64)
+    y32 = y64.astype(np.float32)
+    assert np.all(np.abs(y64 - y32.astype(np.float64)) <= 1e-12 * np.maximum(1.0, np.abs(y64))), \
+        "exact-input premise broken: the oracle result is not an fp32 number"
+    return y32
 
 
 def tol_for(wl) -> float:

@@ -1,12 +1,14 @@
 """GPU: a whole decode step (route + lookup + decode of every layer) captured into one
 HIP graph and replayed must reproduce eager execution bit for bit, replay after replay,
-with the cache state advancing on the device.  Two paths qualify: OFFLOAD with device
-fills, and FUSED."""
+with the cache state advancing on the device, and every replayed step must match the
+oracle (top-k indices and gates, cache trace and slot ids, outputs).  Paths that
+qualify: OFFLOAD and HYBRID with device fills (the CPU branch as host nodes), FUSED."""
 import numpy as np
 import pytest
 
+import oracle
 import workloads as W
-from moe_harness import Harness
+from moe_harness import Harness, oracle_outputs, row_rel_err, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +43,28 @@ class StepBuffers:
             self.x[l].copy_(torch.from_numpy(xs.copy()))
 
     def outputs(self):
-        return [t.cpu().numpy().copy() for t in (self.y, self.idx, self.slot, self.trace, self.cnt)]
+        return [t.cpu().numpy().copy() for t in (self.y, self.idx, self.slot, self.trace, self.cnt, self.w)]
+
+
+def check_against_oracle(wl, b, step, cache, mode, bw, fused):
+    """One executed step (buffers b) against the oracle: routing on its own logits, the
+    LRU trace and slot ids of its cache simulation, outputs from its FFN and combine."""
+    y, idx, slot, trace, cnt, w = b.outputs()
+    for l in range(wl.n_layers):
+        x = wl.decode_activations(step, l, b.T)
+        z_ref = oracle.router_logits(oracle.formats.activations_f64(x), wl.router_weight(l))
+        i_ref, w_ref = oracle.route(z_ref, wl.top_k, wl.renorm)
+        assert np.array_equal(idx[l], i_ref), (step, l)
+        assert np.abs(w[l] - w_ref).max() <= 1e-5, (step, l)
+        ref = oracle.moe_combine(oracle_outputs(wl, l, x, idx[l]), w[l])
+        assert row_rel_err(y[l], ref) <= tol_for(wl), (step, l)
+        if fused:
+            assert np.array_equal(slot[l], l * wl.n_experts + idx[l])
+            continue
+        r = cache.lookup(l, idx[l], mode, *bw)
+        n_u = int(cnt[l][0] + cnt[l][1] + cnt[l][2])
+        assert [tuple(int(v) for v in t) for t in trace[l][:n_u]] == r.trace, (step, l)
+        assert np.array_equal(slot[l], r.slot_idx), (step, l)
 
 
 def run_step(R, h, b, stream, layer_call=False):
@@ -76,12 +99,15 @@ def test_captured_step_replays_like_eager(wl, mode):
     # profiling is requested on the captured context: captured launches must skip it
     graph = Harness(wl, kw["mode"], n_slots=kw.get("n_slots"), flags=flags | R.MOE_FLAG_PROFILE, bw=bw)
     be, bg = StepBuffers(wl, T), StepBuffers(wl, T)
+    fused = mode.startswith("fused")
+    cache = None if fused else oracle.ExpertCache(wl.n_layers, wl.n_experts, graph.n_slots)
     # step 0 eagerly on both
     be.load(wl, 0)
     bg.load(wl, 0)
     run_step(R, eager, be, None, lc)
     run_step(R, graph, bg, None, lc)
     torch.cuda.synchronize()
+    check_against_oracle(wl, bg, 0, cache, kw["mode"], bw, fused)
     g = torch.cuda.CUDAGraph()
     # thread-local capture: only this thread's calls are checked against the capture
     # (host nodes and the CPU worker pool run on threads of their own)
@@ -96,8 +122,9 @@ def test_captured_step_replays_like_eager(wl, mode):
         be.load(wl, step)
         run_step(R, eager, be, None, lc)
         torch.cuda.synchronize()
-        for a, b_, name in zip(bg.outputs(), be.outputs(), ("y", "idx", "slot", "trace", "cnt")):
+        for a, b_, name in zip(bg.outputs(), be.outputs(), ("y", "idx", "slot", "trace", "cnt", "w")):
             assert np.array_equal(a.view(np.uint8), b_.view(np.uint8)), (step, name)
+        check_against_oracle(wl, bg, step, cache, kw["mode"], bw, fused)
     R.moe_sync(graph.ctx)
     R.moe_sync(eager.ctx)
     sg, se = R.moe_get_stats(graph.ctx), R.moe_get_stats(eager.ctx)
@@ -123,3 +150,73 @@ def test_capture_refuses_host_issued_fills():
         with torch.cuda.graph(g):
             run_step(R, h, b, torch.cuda.current_stream().cuda_stream)
     assert e.value.status == R.MOE_ESTATE
+
+
+@pytest.mark.parametrize("new_arena", [False, True], ids=["in_place", "new_arena"])
+def test_replay_follows_resize(new_arena):
+    """A step captured before expert_cache_resize replays on the resized cache: shrink
+    (in place, or into a new arena) and grow between replays, every replayed step and the
+    final tables checked against the oracle's cache with the same resizes."""
+    import routed_expert_ffn_02_amd as R
+    import torch
+    wl, T = BF16, 1
+    n0 = 4 * T * wl.top_k + 4
+    h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=n0, flags=R.MOE_FLAG_DEVICE_FILLS)
+    b = StepBuffers(wl, T)
+    cache = oracle.ExpertCache(wl.n_layers, wl.n_experts, n0)
+    b.load(wl, 0)
+    run_step(R, h, b, None)
+    torch.cuda.synchronize()
+    check_against_oracle(wl, b, 0, cache, R.MOE_MODE_OFFLOAD, (0, 0), False)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        run_step(R, h, b, torch.cuda.current_stream().cuda_stream)
+    sizes = {4: 2 * T * wl.top_k + 1, 8: 3 * T * wl.top_k}
+    arena2 = torch.empty(max(sizes.values()) * h.S, dtype=torch.uint8, device="cuda") if new_arena else None
+    for step in range(1, 12):
+        if step in sizes:
+            if arena2 is not None:
+                R.expert_cache_resize(h.ctx, sizes[step], arena2, arena2.numel())
+            else:
+                R.expert_cache_resize(h.ctx, sizes[step])
+            cache.resize(sizes[step])
+            slot_of, key_of, stamp, _ = h.snapshot()
+            assert np.array_equal(slot_of, cache.slot_of.astype(np.int32)) and np.array_equal(
+                key_of, cache.key_of.astype(np.int32)) and np.array_equal(stamp, cache.stamp.astype(np.uint64))
+        b.load(wl, step)
+        g.replay()
+        torch.cuda.synchronize()
+        check_against_oracle(wl, b, step, cache, R.MOE_MODE_OFFLOAD, (0, 0), False)
+    R.moe_sync(h.ctx)
+    slot_of, key_of, stamp, counter = h.snapshot()
+    assert np.array_equal(slot_of, cache.slot_of.astype(np.int32)) and counter == cache.counter
+    assert np.array_equal(key_of, cache.key_of.astype(np.int32)) and np.array_equal(stamp, cache.stamp.astype(np.uint64))
+    del g
+
+
+def test_replay_after_shrink_below_capture_is_reported():
+    """A step captured without a CPU branch (OFFLOAD, n_slots >= 2*T*k) replayed after a
+    shrink that leaves too few slots: the lookup sends misses to the CPU, which the graph
+    cannot run, and moe_sync reports it instead of returning silently short outputs."""
+    import routed_expert_ffn_02_amd as R
+    import torch
+    wl, T = BF16, 1
+    h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=2 * T * wl.top_k + 2, flags=R.MOE_FLAG_DEVICE_FILLS)
+    b = StepBuffers(wl, T)
+    b.load(wl, 0)
+    run_step(R, h, b, None)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        run_step(R, h, b, torch.cuda.current_stream().cuda_stream)
+    R.moe_sync(h.ctx)
+    R.expert_cache_resize(h.ctx, 1)
+    for step in range(1, 4):
+        b.load(wl, step)
+        g.replay()
+    torch.cuda.synchronize()
+    with pytest.raises(R.MoeError) as e:
+        R.moe_sync(h.ctx)
+    assert e.value.status == R.MOE_ESTATE
+    R.moe_sync(h.ctx)  # reported once
+    del g

@@ -58,7 +58,7 @@ def build(force: bool = False) -> str:
 class _WlCfg(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("wfmt", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("wfmt", ctypes.c_int32), ("exact", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("alias_records", ctypes.c_int64),
                 ("sigma", ctypes.c_float), ("fp4_scale_lo", ctypes.c_float),
                 ("fp4_scale_hi", ctypes.c_float), ("pad2", ctypes.c_float),
@@ -84,6 +84,8 @@ def lib():
         L.wl_record_bytes.argtypes = [ctypes.POINTER(_WlCfg)]
         L.wl_pack_record.argtypes = [ctypes.POINTER(_WlCfg), i64, vp]
         L.wl_fill_pool.argtypes = [ctypes.POINTER(_WlCfg), vp, i64, i64, ctypes.c_int]
+        L.wl_exact_act.argtypes = [vp, i64, ctypes.c_int, u64, u64, u64]
+        L.wl_exact_router.argtypes = [vp, i64, i64, u64, u64]
         _lib = L
     return _lib
 
@@ -117,6 +119,10 @@ class Workload:
     mx_exp_hi: int = 121
     resize_schedule: tuple = ()   # ((after_step, new_n_slots), ...)
     prefill_tokens: int = 0
+    # exact-arithmetic inputs: sparse few-bit expert and router weights, activations in
+    # {0, 1, 2} (gen.c, wl_exact_tensor): every sum of products is exact in fp32 and the
+    # SwiGLU intermediate exact in bf16 / f16, so results can be compared bit for bit
+    exact: bool = False
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -136,7 +142,7 @@ class Workload:
         return replace(self, **kw)
 
     def _cfg(self) -> _WlCfg:
-        return _WlCfg(self.n_layers, self.n_experts, self.hidden, self.inter, self.wfmt, 0,
+        return _WlCfg(self.n_layers, self.n_experts, self.hidden, self.inter, self.wfmt, int(self.exact),
                       self.seed, self.alias_records, self.sigma_w,
                       self.fp4_scale_lo, self.fp4_scale_hi, 0.0, self.mx_exp_lo, self.mx_exp_hi)
 
@@ -183,11 +189,18 @@ class Workload:
     # ---- router, activations, biases ------------------------------------
     def router_weight(self, layer: int) -> np.ndarray:
         out = np.empty((self.n_experts, self.hidden), np.float32)
-        lib().wl_normal_f32(out.ctypes.data, out.size, self.seed, DOMAIN_ROUTER | layer, 0, self.sigma_r)
+        if self.exact:
+            lib().wl_exact_router(out.ctypes.data, self.n_experts, self.hidden, self.seed, DOMAIN_ROUTER | layer)
+        else:
+            lib().wl_normal_f32(out.ctypes.data, out.size, self.seed, DOMAIN_ROUTER | layer, 0, self.sigma_r)
         return out
 
     def _act(self, domain: int, index: int, tokens: int):
         n = tokens * self.hidden
+        if self.exact:
+            out = np.empty((tokens, self.hidden), np.float32 if self.afmt == AFMT_F32 else np.uint16)
+            lib().wl_exact_act(out.ctypes.data, n, int(self.afmt == AFMT_BF16), self.seed, domain | index, 0)
+            return out
         if self.afmt == AFMT_F32:
             out = np.empty((tokens, self.hidden), np.float32)
             lib().wl_normal_f32(out.ctypes.data, n, self.seed, domain | index, 0, self.sigma_x)

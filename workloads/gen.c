@@ -121,7 +121,8 @@ typedef struct {
   int32_t n_layers, n_experts, hidden, inter;
   int32_t wfmt;        /* WL_F32, WL_BF16, WL_FP4 (e2m1 codes + bf16 scale per 32),
                           WL_MXFP4 (e2m1 codes + E8M0 scale byte per 32) */
-  int32_t pad;
+  int32_t exact;       /* 0: dense random values; 1: the sparse few-bit values of
+                          wl_exact_tensor (every sum of products exact in fp32) */
   uint64_t seed;
   int64_t alias_records;  /* 0: every key has its own values; R > 0: key -> key % R */
   float sigma;            /* weight standard deviation (F32/BF16) */
@@ -141,6 +142,85 @@ static inline void tensor_shape(const wl_cfg* c, int t, int64_t* rows, int64_t* 
 }
 
 /*
+ * Exact-arithmetic expert tensors (exact = 1).  Sparse rows of few-bit values whose
+ * products with the exact activations below, and every partial sum of those products,
+ * are representable in fp32, so any summation order gives the same result:
+ *   gate rows  one nonzero (1 row in 8 all zero): a positive code 1..7, block scale
+ *              2^6 or 2^7;
+ *   up rows    one nonzero: a code of either sign, block scale 2^-3 or 2^-2;
+ *   down rows  four nonzeros (positions may coincide; the last drawn wins): codes of
+ *              either sign, block scale 2^-4 or 2^-3.
+ * Every 32-element block of a row has its own power-of-two scale (drawn per block, also
+ * for all-zero blocks).  FP4 stores the 4-bit code and the scale (bf16 bits of the power
+ * of two); MXFP4 stores the code and the E8M0 byte 127 + exponent; F32 / BF16 store the
+ * value itself, from the magnitudes {0.5, 1, 1.5, 2, 3, 4, 6} (indexed by the code's low
+ * three bits minus one; bit 3 is the sign) times the block's power of two.
+ */
+static const float kMag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+static int exact_tensor(const wl_cfg* c, int64_t key, int t, void* values, void* scales) {
+  int64_t rows, cols;
+  tensor_shape(c, t, &rows, &cols);
+  if (cols % 32) return -1;
+  const int64_t nb = cols / 32;
+  const uint64_t sid = ((uint64_t)backing(c, key) << 2) | (uint64_t)t;
+  const uint64_t kv = stream_key(c->seed, DOMAIN_EXPERT | sid), ks = stream_key(c->seed, DOMAIN_SCALE | sid);
+  const int base = t == 0 ? 6 : (t == 1 ? -3 : -4);
+  const int fp4 = c->wfmt == WL_FP4 || c->wfmt == WL_MXFP4;
+  if (fp4) memset(values, 0, (size_t)(rows * cols / 2));
+  else memset(values, 0, (size_t)(rows * cols * (c->wfmt == WL_F32 ? 4 : 2)));
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const int e = base + (int)(draw(ks, (uint64_t)(r * nb + b)) & 1);
+      if (c->wfmt == WL_FP4) ((uint16_t*)scales)[r * nb + b] = (uint16_t)((uint32_t)(127 + e) << 7);
+      else if (c->wfmt == WL_MXFP4) ((uint8_t*)scales)[r * nb + b] = (uint8_t)(127 + e);
+    }
+    const int nnz = t == 2 ? 4 : 1;
+    for (int i = 0; i < nnz; ++i) {
+      const uint64_t d = draw(kv, (uint64_t)(r * 4 + i));
+      if (t == 0 && (d & 7) == 0) break;  /* an all-zero gate row */
+      const int64_t p = (int64_t)((d >> 3) % (uint64_t)cols);
+      const uint32_t mag = 1u + (uint32_t)((d >> 40) % 7u);
+      const uint32_t code = mag | (t == 0 ? 0u : (uint32_t)((d >> 47) & 1u) << 3);
+      if (fp4) {
+        uint8_t* byte = (uint8_t*)values + r * (cols / 2) + p / 2;
+        *byte = (p & 1) ? (uint8_t)((*byte & 0x0F) | (code << 4)) : (uint8_t)((*byte & 0xF0) | code);
+      } else {
+        const int e = base + (int)(draw(ks, (uint64_t)(r * nb + p / 32)) & 1);
+        const float v = (code & 8u ? -kMag[mag] : kMag[mag]) * ldexpf(1.0f, e);
+        if (c->wfmt == WL_F32) ((float*)values)[r * cols + p] = v;
+        else ((uint16_t*)values)[r * cols + p] = f32_to_bf16_rne(v);  /* exact: at most 2 significant bits */
+      }
+    }
+  }
+  return 0;
+}
+
+/* Exact-arithmetic activations: 0 with probability 1/8, else 1 or 2 (fp32, or bf16 bits). */
+void wl_exact_act(void* out, int64_t n, int bf16, uint64_t seed, uint64_t stream, uint64_t ctr0) {
+  uint64_t k = stream_key(seed, stream);
+  for (int64_t i = 0; i < n; ++i) {
+    const uint64_t d = draw(k, ctr0 + (uint64_t)i);
+    const float v = (d & 7) == 0 ? 0.0f : (float)(1 + ((d >> 3) & 1));
+    if (bf16) ((uint16_t*)out)[i] = f32_to_bf16_rne(v);
+    else ((float*)out)[i] = v;
+  }
+}
+
+/* Exact-arithmetic router weights [rows, cols]: eight nonzeros per row (positions may
+ * coincide), values +-{1, 2, 4} * 2^-6. */
+void wl_exact_router(float* out, int64_t rows, int64_t cols, uint64_t seed, uint64_t stream) {
+  uint64_t k = stream_key(seed, stream);
+  memset(out, 0, (size_t)(rows * cols) * sizeof(float));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int i = 0; i < 8; ++i) {
+      const uint64_t d = draw(k, (uint64_t)(r * 8 + i));
+      const float v = ldexpf((float)(1u << ((d >> 40) % 3u)), -6);
+      out[r * cols + (int64_t)((d >> 3) % (uint64_t)cols)] = (d >> 47) & 1 ? -v : v;
+    }
+}
+
+/*
  * Logical values of one expert tensor.
  *  F32:  values = float[rows*cols]
  *  BF16: values = uint16 bf16 bits [rows*cols]
@@ -155,6 +235,7 @@ int wl_expert_tensor(const wl_cfg* c, int64_t key, int t, void* values, void* sc
   tensor_shape(c, t, &rows, &cols);
   int64_t n = rows * cols;
   uint64_t sid = ((uint64_t)backing(c, key) << 2) | (uint64_t)t;
+  if (c->exact) return (c->wfmt == WL_FP4 || c->wfmt == WL_MXFP4) && !scales ? -1 : exact_tensor(c, key, t, values, scales);
   switch (c->wfmt) {
     case WL_F32: wl_normal_f32((float*)values, n, c->seed, DOMAIN_EXPERT | sid, 0, c->sigma); return 0;
     case WL_BF16: wl_normal_bf16((uint16_t*)values, n, c->seed, DOMAIN_EXPERT | sid, 0, c->sigma); return 0;
