@@ -62,7 +62,11 @@ def test_exact_inputs_keep_every_result_representable(fmt):
 
 
 def test_exact_premise_detects_a_planted_error():
-    """exact_f32 refuses a result that is not an fp32 number (a planted 1e-9 error)."""
+    """exact_f32 refuses a result off the 2^-16 grid (a planted 1e-6 error) or one that is
+    not an fp32 number, and absorbs only fp64 noise (a cancelled sum left at 1e-14)."""
     with pytest.raises(AssertionError):
-        exact_f32(np.array([[1.0 + 1e-9]]))
-    assert exact_f32(np.array([[1.5, -2.0 ** -20]])).dtype == np.float32
+        exact_f32(np.array([[1.0 + 1e-6]]))
+    with pytest.raises(AssertionError):
+        exact_f32(np.array([[2.0 ** 30 + 2.0 ** -10]]))
+    got = exact_f32(np.array([[1.5, -2.0 ** -10, 1.4e-14]]))
+    assert got.dtype == np.float32 and got.tolist() == [[1.5, -2.0 ** -10, 0.0]]
