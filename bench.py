@@ -363,9 +363,13 @@ def run_workload(args, config, primary):
             torch.cuda.synchronize()
             hg = time.perf_counter() - th
             R.moe_sync(ctx, stream)
+            gs = R.moe_get_stats(ctx)
             del g
             hybrid["graph_tokens_per_s"] = round(args.steps * T / hg, 2)
             hybrid["graph_ms_per_step"] = round(hg * 1e3 / args.steps, 3)
+            hybrid["graph_fills"] = gs["fills"]
+            hybrid["graph_cpu_experts"] = gs["cpu_experts"]
+            hybrid["graph_cpu_branch_ms_per_step"] = round(gs["cpu_ms"] / args.steps, 3)
         log(f"[{config}] hybrid: {hybrid}")
         log(f"[{config}] q*: {qstar}")
         R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)

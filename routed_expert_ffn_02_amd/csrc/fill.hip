@@ -15,6 +15,9 @@
 
 namespace rmoe {
 
+// written by the HBM read probe only when its fold of the data equals a launch argument
+__device__ uint32_t g_read_sink;
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -99,10 +102,9 @@ __global__ __launch_bounds__(256) void stage_step_kernel(StageArgs a) {
 
 // Plain streaming read of n16 16-byte units (the HBM read probe): grid-stride, four
 // independent loads in flight per thread, folded into one word that is stored only if
-// it equals a constant no run is expected to produce (so the loads cannot be dropped).
-__device__ uint32_t g_read_sink;
-
-__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ p, int64_t n16) {
+// it equals a value passed in at launch (never produced in practice).  The sink has
+// external linkage, so the compiler cannot prove the store, and with it the loads, dead.
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ p, int64_t n16, uint32_t magic) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__
   }
   for (; i < n16; i += stride) acc ^= p[i];
   const uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-  if (v == 0x9E3779B9u) g_read_sink = v;
+  if (v == magic) g_read_sink = v;
 }
 
 }  // namespace
@@ -120,7 +122,8 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__
 void launch_read_probe(const void* p, int64_t bytes, hipStream_t s, Timing tm) {
   const int64_t n16 = bytes >> 4;
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(8192, (n16 + 1023) / 1024));
-  launch_timed(hbm_read_kernel, dim3(blocks), dim3(256), 0, s, tm, reinterpret_cast<const u32x4*>(p), n16);
+  launch_timed(hbm_read_kernel, dim3(blocks), dim3(256), 0, s, tm, reinterpret_cast<const u32x4*>(p), n16,
+               0x9E3779B9u);
 }
 
 void launch_stage_step(const StageArgs& a, hipStream_t s) {
