@@ -317,6 +317,29 @@ MOE_API moe_status moe_permute(moe_ctx* ctx, const int32_t* slot_idx, int32_t T,
                                int32_t* group_slot, int32_t* n_groups, moe_stream_t stream);
 
 /*
+ * moe_permute for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): no context, no allocation, no host read.  Its
+ * kernels' scratch (per-slot flags, per-pair group ids, the inverse permutation, per-chunk
+ * group histograms, tile bases, counters: 2 MiB) is one array in the library's device code,
+ * a copy on each device, which every call on that device shares and which keeps the last
+ * call's contents: calls that overlap on one device (concurrent streams, or threads) race
+ * and must be serialised by the caller.  The library looks up the array's address on a
+ * device at the first call there.
+ *   slot_idx     device int32 [P]: a slot id per (token, rank) pair (P = T*k, pair order
+ *                t*k + j); negative entries are not GPU pairs and are left out
+ *   n_slot_range every slot id must be < n_slot_range
+ *   perm, offsets, group_slot  as in moe_permute: device int32 [P], [P+1], [P]
+ *   n_groups     device int32 [1]: the number of groups, or -1 (the outputs are then
+ *                unspecified) when a slot id is >= n_slot_range or the pairs use more than
+ *                1024 distinct slots
+ * Limits: 1 <= P <= 65536 and 1 <= n_slot_range <= 65536, else MOE_EINVAL (nothing is
+ * enqueued).  Asynchronous on stream; MOE_EHIP if a launch fails.
+ */
+MOE_API moe_status moe_permute_noalloc(const int32_t* slot_idx, int32_t P, int32_t n_slot_range, int32_t* perm,
+                                       int32_t* offsets, int32_t* group_slot, int32_t* n_groups,
+                                       moe_stream_t stream);
+
+/*
  * Rebuild the cache for n_slots' slots at a safe point, without touching the host pool
  * ([FT-KR] "탄력적 메모리 관리").  Shrinking keeps the n_slots' most recently used entries,
  * packed into slots 0..n_slots'-1 in ascending old-slot order (recency kept); growing adds empty

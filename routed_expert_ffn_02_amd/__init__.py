@@ -127,6 +127,7 @@ def _load():
         "moe_reset_stats": (I32, [P]),
         "moe_sync": (I32, [P, VP]),
         "moe_step_log": (I32, [P, VP, I32, ctypes.POINTER(I32)]),
+        "moe_permute_noalloc": (I32, [VP, I32, I32, VP, VP, VP, VP, VP]),
         "moe_bench_hbm": (I32, [VP, ctypes.c_size_t, ctypes.c_size_t, I32, VP, VP]),
         "moe_placement_replay": (I32, [ctypes.POINTER(moe_replay_config), VP, I32, VP, I32, I32, VP,
                                        ctypes.POINTER(moe_replay_result)]),
@@ -423,3 +424,10 @@ def moe_bench_hbm(buf, buf_bytes: int, read_bytes: int, reps: int, stream=None):
     if st != MOE_OK:
         raise MoeError(st, "moe_bench_hbm", "bad arguments or device error")
     return out
+
+
+def moe_permute_noalloc(slot_idx, P: int, n_slot_range: int, perm, offsets, group_slot, n_groups, stream=None):
+    st = lib.moe_permute_noalloc(_ptr(slot_idx), P, n_slot_range, _ptr(perm), _ptr(offsets), _ptr(group_slot),
+                                 _ptr(n_groups), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_permute_noalloc", "sizes out of range, null pointer or launch failure")

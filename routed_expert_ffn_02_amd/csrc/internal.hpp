@@ -190,7 +190,8 @@ void launch_read_probe(const void* p, int64_t bytes, hipStream_t s, Timing tm);
 void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
                     int32_t* inv, int32_t* offsets, int32_t* tile_base, int bm, hipStream_t s);
 void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp, int32_t* grp_slot, int32_t* cnt,
-                              int32_t* scratch_flags, int n_slot_range, hipStream_t s);
+                              int32_t* scratch_flags, int n_slot_range, int gmax, int32_t* n_groups_out,
+                              hipStream_t s);
 int prefill_bm();
 bool prefill_needs_act_operands(int wfmt, int afmt);
 void launch_act_operands(int wfmt, int afmt, const void* x, void* xo, int64_t n, hipStream_t s);

@@ -116,10 +116,14 @@ void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_ma
 }
 
 // Groups from raw slot ids (the exported moe_permute): distinct slots >= 0, ascending.
+// A slot id >= nrange (cnt[C_ERR] = 1) or more than gmax distinct slots (cnt[C_ERR] = 2)
+// leaves every pair without a group and no groups, so the permutation kernels that follow
+// index nothing out of range; n_groups_out (optional) receives the group count, or -1.
 __global__ __launch_bounds__(1024) void groups_from_slots_kernel(const int32_t* __restrict__ slot_idx, int P,
                                                                  int32_t* __restrict__ pair_grp,
                                                                  int32_t* __restrict__ grp_slot,
-                                                                 int32_t* __restrict__ cnt, int32_t* flags, int nrange) {
+                                                                 int32_t* __restrict__ cnt, int32_t* flags, int nrange,
+                                                                 int gmax, int32_t* n_groups_out) {
   __shared__ int s_tmp[64];
   for (int i = threadIdx.x; i < nrange; i += 1024) flags[i] = 0;
   __syncthreads();
@@ -137,12 +141,16 @@ __global__ __launch_bounds__(1024) void groups_from_slots_kernel(const int32_t* 
   for (int i = i0; i < i1; ++i) local += flags[i];
   int total;
   int pos = block_excl_scan(local, s_tmp, &total);
-  __syncthreads();
-  for (int i = i0; i < i1; ++i) {
-    if (flags[i]) {
-      grp_slot[pos] = i;
-      flags[i] = pos + 1;
-      ++pos;
+  int nbad;
+  block_excl_scan(bad, s_tmp, &nbad);
+  const int err = nbad ? 1 : (total > gmax ? 2 : 0);
+  if (!err) {
+    for (int i = i0; i < i1; ++i) {
+      if (flags[i]) {
+        grp_slot[pos] = i;
+        flags[i] = pos + 1;
+        ++pos;
+      }
     }
   }
   __threadfence_block();
@@ -150,25 +158,25 @@ __global__ __launch_bounds__(1024) void groups_from_slots_kernel(const int32_t* 
   int npairs = 0;
   for (int p = threadIdx.x; p < P; p += 1024) {
     const int sl = slot_idx[p];
-    const int g = (sl >= 0 && sl < nrange) ? flags[sl] - 1 : -1;
+    const int g = (!err && sl >= 0 && sl < nrange) ? flags[sl] - 1 : -1;
     pair_grp[p] = g;
     npairs += (g >= 0);
   }
   int np;
   block_excl_scan(npairs, s_tmp, &np);
-  int nbad;
-  block_excl_scan(bad, s_tmp, &nbad);
   if (threadIdx.x == 0) {
-    cnt[C_NGRP] = total;
+    cnt[C_NGRP] = err ? 0 : total;
     cnt[C_NPAIR_GPU] = np;
-    cnt[C_ERR] = nbad ? 1 : 0;
+    cnt[C_ERR] = err;
+    if (n_groups_out) *n_groups_out = err ? -1 : total;
   }
 }
 
 void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp, int32_t* grp_slot, int32_t* cnt,
-                              int32_t* scratch_flags, int n_slot_range, hipStream_t s) {
+                              int32_t* scratch_flags, int n_slot_range, int gmax, int32_t* n_groups_out,
+                              hipStream_t s) {
   hipLaunchKernelGGL(groups_from_slots_kernel, dim3(1), dim3(1024), 0, s, slot_idx, P, pair_grp, grp_slot, cnt,
-                     scratch_flags, n_slot_range);
+                     scratch_flags, n_slot_range, gmax, n_groups_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1033,4 +1041,62 @@ void launch_prefill_combine(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 
+// ---------------------------------------------------------------------------
+// The permutation with no allocation: moe_permute_noalloc keeps the scratch its kernels
+// use (slot flags, group ids per pair, the inverse permutation, per-chunk group
+// histograms, tile bases, counters) in one file-scope device array instead of context
+// memory, for callers that cannot allocate.  Each device holds its own copy; its device
+// address is looked up once per device (hipGetSymbolAddress) and every call on that
+// device shares it.
+constexpr int kNoAllocMaxPairs = 1 << 16;   // P = T * k
+constexpr int kNoAllocMaxSlots = 1 << 16;   // n_slot_range
+constexpr size_t kNaFlags = 0;
+constexpr size_t kNaPairGrp = kNaFlags + kNoAllocMaxSlots;
+constexpr size_t kNaInv = kNaPairGrp + kNoAllocMaxPairs;
+constexpr size_t kNaHist = kNaInv + kNoAllocMaxPairs;
+constexpr size_t kNaTileBase = kNaHist + (size_t)(kNoAllocMaxPairs / kChunk) * kMaxExperts;
+constexpr size_t kNaCnt = kNaTileBase + kMaxExperts + 64;
+constexpr size_t kNaInts = kNaCnt + C_COUNT;   // 524,368 ints: 2 MiB
+
+static __device__ __align__(256) int32_t scratch[kNaInts];
+
+namespace {
+constexpr int kNaMaxDevices = 64;
+std::mutex g_na_mu;
+int32_t* g_na_ptr[kNaMaxDevices] = {};  // device address of `scratch` on each device
+
+moe_status noalloc_scratch(int32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNaMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_na_mu);
+  if (!g_na_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    g_na_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_na_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
 }  // namespace rmoe
+
+extern "C" MOE_API moe_status moe_permute_noalloc(const int32_t* slot_idx, int32_t P, int32_t n_slot_range,
+                                                  int32_t* perm, int32_t* offsets, int32_t* group_slot,
+                                                  int32_t* n_groups, moe_stream_t stream) {
+  using namespace rmoe;
+  if (!slot_idx || !perm || !offsets || !group_slot || !n_groups) return MOE_EINVAL;
+  if (P < 1 || P > kNoAllocMaxPairs || n_slot_range < 1 || n_slot_range > kNoAllocMaxSlots) return MOE_EINVAL;
+  int32_t* base = nullptr;
+  const moe_status st = noalloc_scratch(&base);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int gmax = std::min(P, kMaxExperts);
+  // every scratch word a kernel reads is written earlier in the same call: the flags are
+  // cleared first, each chunk's histogram row and the tile bases are written in full
+  launch_groups_from_slots(slot_idx, P, base + kNaPairGrp, group_slot, base + kNaCnt, base + kNaFlags, n_slot_range,
+                           gmax, n_groups, s);
+  launch_permute(base + kNaPairGrp, base + kNaCnt, P, gmax, base + kNaHist, perm, base + kNaInv, offsets,
+                 base + kNaTileBase, prefill_bm(), s);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}

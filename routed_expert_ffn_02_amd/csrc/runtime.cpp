@@ -1268,13 +1268,13 @@ MOE_API moe_status moe_permute(moe_ctx* ctx, const int32_t* slot_idx, int32_t T,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int P = T * ctx->cfg.top_k;
   const int nrange = (int)std::max<int64_t>((int64_t)ctx->cfg.n_layers * ctx->cfg.n_experts, kMaxCachedSlots);
-  // groups are indexed by distinct slot; up to min(P, nrange) of them
-  launch_groups_from_slots(slot_idx, P, ctx->pair_grp, group_slot, ctx->cnt, ctx->flags, nrange, s);
+  // groups are indexed by distinct slot; up to min(P, 1024) of them
   const int gmax = std::min(P, kMaxExperts);
+  launch_groups_from_slots(slot_idx, P, ctx->pair_grp, group_slot, ctx->cnt, ctx->flags, nrange, gmax, nullptr, s);
   HIPCHK(hipMemcpyAsync(ctx->h_cnt, ctx->cnt, C_COUNT * 4, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
-  if (ctx->h_cnt[C_ERR]) return fail(ctx, MOE_EINVAL, "slot id out of range");
-  if (ctx->h_cnt[C_NGRP] > gmax) return fail(ctx, MOE_ENOTSUP, "more than 1024 distinct slots");
+  if (ctx->h_cnt[C_ERR] == 1) return fail(ctx, MOE_EINVAL, "slot id out of range");
+  if (ctx->h_cnt[C_ERR] == 2) return fail(ctx, MOE_ENOTSUP, "more than 1024 distinct slots");
   launch_permute(ctx->pair_grp, ctx->cnt, P, gmax, ctx->hist, perm, ctx->inv, offsets, ctx->tile_base, prefill_bm(), s);
   HIPCHK(hipMemcpyAsync(n_groups, ctx->cnt + C_NGRP, 4, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipGetLastError());
