@@ -639,10 +639,13 @@ struct F4Src {
   int64_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
 };
 
+// MR: 32-row activation fragments in the tile (1 for a tile of at most 32 rows, else 2);
+// only their rows are fetched and stored.
+template <int MR>
 __device__ __forceinline__ void f4_issue(F4Chunk& st, const F4Src& src, int c) {
   const uint8_t* ab = src.a + c * (2 * F4_KS);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(ab + src.aoff[i]);
+  for (int i = 0; i < 4 * MR; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(ab + src.aoff[i]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint8_t* bb = src.b + (j & 3) * src.bstep + c * (F4_KS / 2);
@@ -650,9 +653,10 @@ __device__ __forceinline__ void f4_issue(F4Chunk& st, const F4Src& src, int c) {
   }
 }
 
+template <int MR>
 __device__ __forceinline__ void f4_store(const F4Chunk& st, uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&sA[(tid >> 5) + 8 * i][(tid & 31) * 8]) = st.a[i];
+  for (int i = 0; i < 4 * MR; ++i) *reinterpret_cast<u32x4*>(&sA[(tid >> 5) + 8 * i][(tid & 31) * 8]) = st.a[i];
 #pragma unroll
   for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 3) + 32 * j][(tid & 7) * 16]) = st.b[j];
 }
@@ -706,9 +710,9 @@ __device__ __forceinline__ void b_operands_mx(BOps<MOE_WFMT_FP4>& o, const BRun<
 
 // One chunk: four 64-k sub-steps; lane half h covers k in [32h, 32h + 32) of a
 // sub-step (one scale block) and MFMA j its slice [32h + 8j, + 8), in A and B alike.
-template <bool MX>
+template <bool MX, int MR>
 __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const uint8_t (*sB)[F4_BP], int rb0, int rb1,
-                                           const F4Scales& sc, int lane, f32x16 (&acc)[2][2]) {
+                                           const F4Scales& sc, int lane, f32x16 (&acc)[MR][2]) {
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -725,57 +729,55 @@ __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const ui
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = u * 64 + 32 * h + 8 * j;
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sA[r][k]);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sA[32 + r][k]);
-      acc[0][0] = mfma32<true>(a0, o0.op[j], acc[0][0]);
-      acc[0][1] = mfma32<true>(a0, o1.op[j], acc[0][1]);
-      acc[1][0] = mfma32<true>(a1, o0.op[j], acc[1][0]);
-      acc[1][1] = mfma32<true>(a1, o1.op[j], acc[1][1]);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const u32x4 am = *reinterpret_cast<const u32x4*>(&sA[32 * m + r][k]);
+        acc[m][0] = mfma32<true>(am, o0.op[j], acc[m][0]);
+        acc[m][1] = mfma32<true>(am, o1.op[j], acc[m][1]);
+      }
     }
   }
 }
 
 // The k loop over nc = K / 256 chunks.  rb0 / rb1: the wavefront's two 32-row weight
 // fragments in the block's LDS rows; sc0 / sc1: byte offsets of their scale rows.
-template <bool MX>
+template <bool MX, int MR>
 __device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0, uint32_t sc1,
                                          uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int rb0, int rb1, int tid,
-                                         f32x16 (&acc)[2][2]) {
+                                         f32x16 (&acc)[MR][2]) {
   const int lane = tid & 63, h = lane >> 5;
+  auto chunk = [&](int c) { return min(c, nc - 1); };
   F4Chunk N;
   F4Scales sc;
-  f4_issue(N, src, 0);
-  u32x4 q0 = f4_scales<MX>(src.b, sc0, 0), q1 = f4_scales<MX>(src.b, sc1, 0);
+  f4_issue<MR>(N, src, chunk(0));
+  u32x4 q0 = f4_scales<MX>(src.b, sc0, chunk(0)), q1 = f4_scales<MX>(src.b, sc1, chunk(0));
   __builtin_amdgcn_sched_barrier(0);
-  f4_store(N, sA, sB, tid);
+  f4_store<MR>(N, sA, sB, tid);
   f4_take<MX>(sc, q0, q1, h);
   __syncthreads();
-  f4_issue(N, src, min(1, nc - 1));
-  q0 = f4_scales<MX>(src.b, sc0, min(1, nc - 1));
-  q1 = f4_scales<MX>(src.b, sc1, min(1, nc - 1));
+  f4_issue<MR>(N, src, chunk(1));
+  q0 = f4_scales<MX>(src.b, sc0, chunk(1));
+  q1 = f4_scales<MX>(src.b, sc1, chunk(1));
   __builtin_amdgcn_sched_barrier(0);
   for (int c = 0; c < nc; ++c) {
-    f4_compute<MX>(sA, sB, rb0, rb1, sc, lane, acc);
+    f4_compute<MX, MR>(sA, sB, rb0, rb1, sc, lane, acc);
     __syncthreads();  // every wavefront is done with chunk c
-    f4_store(N, sA, sB, tid);
+    f4_store<MR>(N, sA, sB, tid);
     f4_take<MX>(sc, q0, q1, h);
     __syncthreads();
-    f4_issue(N, src, min(c + 2, nc - 1));
-    q0 = f4_scales<MX>(src.b, sc0, min(c + 2, nc - 1));
-    q1 = f4_scales<MX>(src.b, sc1, min(c + 2, nc - 1));
+    f4_issue<MR>(N, src, chunk(c + 2));
+    q0 = f4_scales<MX>(src.b, sc0, chunk(c + 2));
+    q1 = f4_scales<MX>(src.b, sc1, chunk(c + 2));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // GEMM1 (FP4; MX: MXFP4): act columns n0 .. n0 + 127; block rows 0..127 gate rows n0..,
 // 128..255 up.
-template <bool MX>
-__global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
+template <bool MX, int MR>
+__device__ __forceinline__ void gemm1_fp4_tile(const PrefillArgs& a, const TileInfo& ti, uint16_t (*sA)[F4_AW],
+                                               uint8_t (*sB)[F4_BP]) {
   constexpr uint32_t SB = MX ? 1 : 2;  // bytes per block scale
-  __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
-  TileInfo ti;
-  if (!decode_tile(a, a.I / 128, ti)) return;
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = ti.nt * 128;
@@ -786,7 +788,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   F4Src src;
   src.a = reinterpret_cast<const uint8_t*>(a.xa);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4 * MR; ++i) {
     const int row = (tid >> 5) + 8 * i;
     const uint32_t tok = (uint32_t)(a.perm[ti.row0 + (row < ti.rows ? row : 0)] / a.k);
     src.aoff[i] = 2u * (tok * (uint32_t)H + (uint32_t)(tid & 31) * 8u);
@@ -800,18 +802,18 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   const uint32_t sc_g = (uint32_t)(3 * (n / 2)) + SB * (uint32_t)col * (uint32_t)(H / 32);
   const uint32_t sc_u = sc_g + SB * (uint32_t)(n / 32);
 
-  f32x16 acc[2][2];
+  f32x16 acc[MR][2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
-  f4_kloop<MX>(H / F4_KS, src, sc_g, sc_u, sA, sB, wave * 32, 128 + wave * 32, tid, acc);
+  f4_kloop<MX, MR>(H / F4_KS, src, sc_g, sc_u, sA, sB, wave * 32, 128 + wave * 32, tid, acc);
 
   uint16_t* act = reinterpret_cast<uint16_t*>(a.act);
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < MR; ++m) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * m + frag_row(lane, i);
@@ -824,15 +826,24 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   }
 }
 
-// GEMM2 (FP4; MX: MXFP4): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64
-// of them.
+// A tile of at most 32 rows runs one 32-row fragment per wavefront (half the MFMAs of
+// the padded 64-row tile).
 template <bool MX>
-__global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
-  constexpr uint32_t SB = MX ? 1 : 2;  // bytes per block scale
+__global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
-  if (!decode_tile(a, a.H / 256, ti)) return;
+  if (!decode_tile(a, a.I / 128, ti)) return;
+  if (ti.rows <= 32) gemm1_fp4_tile<MX, 1>(a, ti, sA, sB);
+  else gemm1_fp4_tile<MX, 2>(a, ti, sA, sB);
+}
+
+// GEMM2 (FP4; MX: MXFP4): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64
+// of them.
+template <bool MX, int MR>
+__device__ __forceinline__ void gemm2_fp4_tile(const PrefillArgs& a, const TileInfo& ti, uint16_t (*sA)[F4_AW],
+                                               uint8_t (*sB)[F4_BP]) {
+  constexpr uint32_t SB = MX ? 1 : 2;  // bytes per block scale
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = ti.nt * 256;
@@ -844,7 +855,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
   F4Src src;
   src.a = reinterpret_cast<const uint8_t*>(a.act);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4 * MR; ++i) {
     const int row = (tid >> 5) + 8 * i;
     src.aoff[i] = 2u * ((uint32_t)(ti.row0 + (row < ti.rows ? row : 0)) * (uint32_t)I + (uint32_t)(tid & 31) * 8u);
   }
@@ -856,25 +867,25 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
   const uint32_t sc0 = (uint32_t)(3 * (n / 2)) + SB * 2u * (uint32_t)(n / 32) + SB * (uint32_t)c0 * (uint32_t)(I / 32);
   const uint32_t sc1 = sc0 + SB * 32u * (uint32_t)(I / 32);
 
-  f32x16 acc[2][2];
+  f32x16 acc[MR][2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
-  f4_kloop<MX>(I / F4_KS, src, sc0, sc1, sA, sB, wave * 64, wave * 64 + 32, tid, acc);
+  f4_kloop<MX, MR>(I / F4_KS, src, sc0, sc1, sA, sB, wave * 64, wave * 64 + 32, tid, acc);
 
-  int pr[2][16];
+  int pr[MR][16];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * m + frag_row(lane, i);
       pr[m][i] = a.perm[ti.row0 + (r < ti.rows ? r : 0)];
     }
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * m + frag_row(lane, i);
@@ -884,6 +895,16 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
         dst[c0 + 32] = acc[m][1][i];
       }
     }
+}
+
+template <bool MX>
+__global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
+  TileInfo ti;
+  if (!decode_tile(a, a.H / 256, ti)) return;
+  if (ti.rows <= 32) gemm2_fp4_tile<MX, 1>(a, ti, sA, sB);
+  else gemm2_fp4_tile<MX, 2>(a, ti, sA, sB);
 }
 
 // ---------------------------------------------------------------------------
