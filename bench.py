@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-elastic", action="store_true",
                     help="skip the batch-4 hybrid leg with elastic cache resizes (A3B shape only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the library's CPU branch (0: the library's default)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--repeats", type=int, default=3,
                     help="runs of the headline (graph-replayed) and hybrid decode legs; the median is reported")
@@ -187,7 +189,8 @@ def run_workload(args, config, primary):
     prompt = W.A3B_PREFILL.prefill_tokens if config == "a3b" else wl.prefill_tokens
     max_tokens = 8 if args.no_prefill else max(8, prompt)
     flags = R.MOE_FLAG_PROFILE | (0 if args.host_fills else R.MOE_FLAG_DEVICE_FILLS)
-    cfg = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, max_tokens, mode, wl.renorm, flags=flags)
+    cfg = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, max_tokens, mode, wl.renorm,
+                        cpu_threads=args.cpu_threads, flags=flags)
     ctx = R.moe_create(cfg)
     S = R.moe_record_bytes(cfg)
     pool = R.moe_pool_alloc(ctx, wl.pool_records)
@@ -346,7 +349,7 @@ def run_workload(args, config, primary):
         qstar = qstar_balance(logs[mid], S, bw_p, bw_h, args.steps, L)
         if not args.host_fills and not args.no_graph:
             # the same hybrid steps from a cold cache, replayed from one captured graph: fills
-            # by the device copy kernel, the CPU branch as host nodes on the library's stream
+            # by the device copy kernel, the CPU branch on the library's branch thread
             R.moe_bind(ctx, router, arena, arena.numel(), n_slots)
             Xs = torch.empty_like(Xd[0])
             for s in range(args.warmup):

@@ -53,7 +53,8 @@ typedef enum {
   MOE_EHIP = -3,    /* HIP runtime error (includes device faults) */
   MOE_ESTATE = -4,  /* call-order violation (e.g. decode without lookup, resize in prefill) */
   MOE_ENOPIN = -5,  /* the host pool is not page-locked: only MOE_MODE_CPU can use it */
-  MOE_ENOTSUP = -6  /* combination not supported */
+  MOE_ENOTSUP = -6, /* combination not supported */
+  MOE_ETIMEDOUT = -7 /* a captured step's bounded wait for its CPU branch expired (moe_sync) */
 } moe_status;
 
 /* Expert weight formats of a pool record (see moe_record_bytes for the layout). */
@@ -82,8 +83,8 @@ typedef enum { MOE_KIND_HIT = 0, MOE_KIND_FILL = 1, MOE_KIND_CPU = 2, MOE_KIND_B
 
 #define MOE_FLAG_PROFILE 1 /* time the FFN kernels with HIP events (moe_get_stats) */
 /* Cached decode steps copy their fills with a kernel that reads the page-locked pool through
- * its device mapping and run their CPU branch as a host function on a side stream, so
- * moe_ffn_decode never waits for the device (see moe_ffn_decode). */
+ * its device mapping; captured steps hand their CPU branch to a library thread, so replay
+ * has no host node (see moe_ffn_decode). */
 #define MOE_FLAG_DEVICE_FILLS 2
 
 typedef struct {
@@ -95,7 +96,7 @@ typedef struct {
   int32_t mode;        /* moe_mode */
   uint64_t bw_pcie;    /* B_P, bytes/s (host -> device expert transfer) */
   uint64_t bw_host;    /* B_H, bytes/s (host CPU expert processing) */
-  int32_t cpu_threads; /* CPU branch threads; 0 = every CPU in the process affinity mask */
+  int32_t cpu_threads; /* CPU branch threads; 0 = the CPUs of the process affinity mask but two */
   int32_t flags;       /* MOE_FLAG_* */
 } moe_config;
 
@@ -198,6 +199,16 @@ MOE_API moe_status moe_set_bandwidths(moe_ctx* ctx, uint64_t bw_pcie, uint64_t b
  */
 MOE_API moe_status moe_set_mode(moe_ctx* ctx, int32_t mode);
 
+/*
+ * Bound of a captured step's device-side wait for its CPU branch (see moe_ffn_decode), in
+ * milliseconds, (0, 60000]; default 5000.  A wait that expires leaves the step's CPU experts
+ * out of y and makes the next moe_sync return MOE_ETIMEDOUT.  Waits for all work on the
+ * device; captured steps follow the new bound on replay.  (Failure tests make the library's
+ * branch worker answer late by setting RMOE_CPU_BRANCH_DELAY_US, in microseconds, in the
+ * environment before the first captured step with a CPU branch.)
+ */
+MOE_API moe_status moe_set_cpu_wait(moe_ctx* ctx, double timeout_ms);
+
 /* ---- the hot path ------------------------------------------------------ */
 
 /*
@@ -246,17 +257,22 @@ MOE_API moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_
  * n_slots >= 2*T*k) instead enqueues a copy kernel that executes the lookup's fill list from
  * the mapped pool ([FT-KR] "CUDA Graph와 공존하는 LRU 캐시": cache control and transfer stay
  * on the device); while `stream` is being captured, a step that may (CPU or HYBRID mode, or
- * fewer slots) also forks the library's CPU stream: the step block and inputs are copied to
- * pinned staging, a host function runs the CPU branch there, its partial sum is copied back,
- * and the combine waits for it.  Nothing is read on the calling thread, the call only
- * enqueues work, and an out-of-range id in topk_idx (the step then computes y = 0) is
- * reported by the next moe_sync.  Eagerly, a device-fill step that may send work to the CPU
+ * fewer slots) also hands its CPU branch to a library thread without a host node in the
+ * graph: a one-workgroup kernel writes the step block and inputs into pinned staging through
+ * its device mapping and, when the lookup sent experts to the CPU, publishes a sequence
+ * number in a pinned word; the thread (started by the first such step, spinning while steps
+ * come, and stopped by moe_destroy) runs the branch and answers with the same number; after
+ * the step's GPU experts a one-workgroup kernel polls for that answer, bounded in time (see
+ * moe_set_cpu_wait), and copies the partial sum out of pinned memory for the combine.
+ * Nothing is read on the calling thread, the call only enqueues work, and an out-of-range id
+ * in topk_idx (the step then computes y = 0) and an expired wait are reported by the next
+ * moe_sync.  Eagerly, a device-fill step that may send work to the CPU
  * queues the copy kernel behind the copies of the step block and inputs to pinned staging,
  * then the calling thread waits for those copies only, runs the CPU branch while the
  * records move, and copies its partial sum back (an out-of-range id returns MOE_EINVAL).  Needs a pool from moe_pool_alloc or a registered
  * page-locked pool with a device mapping (MOE_ENOPIN).  Such steps, and FUSED steps, may be
  * captured with route and lookup for every layer into one HIP graph on `stream` and replayed
- * (the CPU branch becomes host nodes); MOE_FLAG_PROFILE timing is skipped for captured
+ * (the CPU branch is served by the library thread); MOE_FLAG_PROFILE timing is skipped for captured
  * launches, and a step that would read the host while the stream is capturing returns
  * MOE_ESTATE.
  */
@@ -394,7 +410,8 @@ MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* k
  * Wait for `stream` and report what device-fill steps could not report when they were
  * enqueued: MOE_EINVAL if a step since the last moe_sync saw an expert id out of range;
  * MOE_ESTATE if a step without a CPU branch had experts sent to the CPU by its lookup (a
- * graph captured before a shrink or a mode change; those experts are missing from y).
+ * graph captured before a shrink or a mode change; those experts are missing from y);
+ * MOE_ETIMEDOUT if a captured step's wait for its CPU branch expired (see moe_set_cpu_wait).
  */
 MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream);
 

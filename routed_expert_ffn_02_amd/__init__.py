@@ -16,7 +16,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library links against)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libroutedmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE, MOE_ENOPIN, MOE_ENOTSUP = 0, -1, -2, -3, -4, -5, -6
+MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE, MOE_ENOPIN, MOE_ENOTSUP, MOE_ETIMEDOUT = 0, -1, -2, -3, -4, -5, -6, -7
 MOE_WFMT_F32, MOE_WFMT_BF16, MOE_WFMT_FP4, MOE_WFMT_MXFP4 = 0, 1, 2, 3
 MOE_AFMT_F32, MOE_AFMT_BF16 = 0, 1
 MOE_MODE_FUSED, MOE_MODE_OFFLOAD, MOE_MODE_CPU, MOE_MODE_HYBRID = 0, 1, 2, 3
@@ -25,7 +25,7 @@ MOE_FLAG_PROFILE = 1
 MOE_FLAG_DEVICE_FILLS = 2
 
 _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ESTATE",
-           -5: "MOE_ENOPIN", -6: "MOE_ENOTSUP"}
+           -5: "MOE_ENOPIN", -6: "MOE_ENOTSUP", -7: "MOE_ETIMEDOUT"}
 
 
 class MoeError(RuntimeError):
@@ -109,6 +109,7 @@ def _load():
         "moe_fused_load": (I32, [P, VP]),
         "moe_set_bandwidths": (I32, [P, U64, U64]),
         "moe_set_mode": (I32, [P, I32]),
+        "moe_set_cpu_wait": (I32, [P, ctypes.c_double]),
         "moe_route": (I32, [P, I32, VP, I32, VP, VP, VP, VP, VP]),
         "moe_topk": (I32, [P, VP, I32, VP, VP, VP]),
         "expert_cache_lookup": (I32, [P, I32, VP, I32, VP, VP, VP, VP]),
@@ -239,6 +240,10 @@ def moe_set_bandwidths(ctx: Ctx, bw_pcie: int, bw_host: int) -> None:
 
 def moe_set_mode(ctx: Ctx, mode: int) -> None:
     _check(ctx, lib.moe_set_mode(ctx.handle, mode), "moe_set_mode")
+
+
+def moe_set_cpu_wait(ctx: Ctx, timeout_ms: float) -> None:
+    _check(ctx, lib.moe_set_cpu_wait(ctx.handle, float(timeout_ms)), "moe_set_cpu_wait")
 
 
 def moe_route(ctx: Ctx, layer, x, T, logit_bias, logits_out, topk_idx, topk_w, stream=None) -> None:

@@ -72,31 +72,95 @@ __global__ __launch_bounds__(256) void fill_pull_kernel(FillArgs a) {
     for (int64_t b = (n16 << 4) + threadIdx.x; b < a.rec_bytes; b += 256) dst[b] = src[b];
 }
 
-// The step block and the CPU branch's inputs to pinned host staging: one grid-stride pass
-// over the concatenated ranges, each 32-bit word stored at system scope (written through
-// to host memory), so the host reads them once the launch has completed.
+// Word i of the concatenated ranges (step block, activations, gates, slot ids) to its
+// place in the pinned staging, stored at system scope (written through to host memory).
+__device__ __forceinline__ void stage_word(const StageArgs& a, int i) {
+  uint32_t v;
+  uint32_t* dst;
+  if (i < a.n_step) {
+    v = (uint32_t)a.step[i];
+    dst = reinterpret_cast<uint32_t*>(a.step_h) + i;
+  } else if (i < a.n_step + a.n_x) {
+    const int j = i - a.n_step;
+    v = a.x[j];
+    dst = a.x_h + j;
+  } else if (i < a.n_step + a.n_x + a.P) {
+    const int j = i - a.n_step - a.n_x;
+    v = __float_as_uint(a.w[j]);
+    dst = reinterpret_cast<uint32_t*>(a.w_h) + j;
+  } else {
+    const int j = i - a.n_step - a.n_x - a.P;
+    v = (uint32_t)a.slot[j];
+    dst = reinterpret_cast<uint32_t*>(a.slot_h) + j;
+  }
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// The step block and the CPU branch's inputs to pinned host staging in one grid-stride
+// pass, so the host reads them once the launch has completed.
 __global__ __launch_bounds__(256) void stage_step_kernel(StageArgs a) {
   const int total = a.n_step + a.n_x + 2 * a.P;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-    uint32_t v;
-    uint32_t* dst;
-    if (i < a.n_step) {
-      v = (uint32_t)a.step[i];
-      dst = reinterpret_cast<uint32_t*>(a.step_h) + i;
-    } else if (i < a.n_step + a.n_x) {
-      const int j = i - a.n_step;
-      v = a.x[j];
-      dst = a.x_h + j;
-    } else if (i < a.n_step + a.n_x + a.P) {
-      const int j = i - a.n_step - a.n_x;
-      v = __float_as_uint(a.w[j]);
-      dst = reinterpret_cast<uint32_t*>(a.w_h) + j;
-    } else {
-      const int j = i - a.n_step - a.n_x - a.P;
-      v = (uint32_t)a.slot[j];
-      dst = reinterpret_cast<uint32_t*>(a.slot_h) + j;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) stage_word(a, i);
+}
+
+// The same staging by one workgroup, then the signal: every thread releases its stores at
+// system scope before the barrier, so when thread 0 publishes the step's sequence number
+// in the go word, a host thread that reads that number (acquire) sees the whole staging.
+__global__ __launch_bounds__(1024) void stage_signal_kernel(StageArgs a) {
+  if (a.cnt[C_ERR] || a.cnt[C_CPU] <= 0) return;  // no CPU work: no signal, no wait
+  const int total = a.n_step + a.n_x + 2 * a.P;
+  for (int i = threadIdx.x; i < total; i += 1024) stage_word(a, i);
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t q = *a.seq + 1;
+    *a.seq = q;
+    __hip_atomic_store(a.go_h, q, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+// The join of a captured step with its CPU branch.  Thread 0 polls the pinned done word
+// (system-scope acquire loads, a short sleep between polls) until it holds the step's
+// sequence number or the bound of device wall-clock ticks has passed; the workgroup then
+// copies the partial sum out of pinned memory (system-scope loads, which no GPU cache
+// serves stale), or zeros y when there is none to take.
+__global__ __launch_bounds__(1024) void cpu_wait_kernel(CpuWaitArgs a) {
+  __shared__ int ok;
+  const bool work = !a.cnt[C_ERR] && a.cnt[C_CPU] > 0;
+  if (threadIdx.x == 0) {
+    int done = 0;
+    if (work) {
+      const uint32_t want = *a.seq;
+      const uint64_t limit = a.ctrl->cpu_wait_ticks;
+      const uint64_t t0 = wall_clock64();
+      for (;;) {
+        if (__hip_atomic_load(a.done_h, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) == want) {
+          done = 1;
+          break;
+        }
+        if ((uint64_t)wall_clock64() - t0 > limit) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (!done) a.dstats[D_CPUWAIT] += 1;
     }
-    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    ok = done;
+  }
+  __syncthreads();
+  constexpr int kU = 4;
+  for (int base = 0; base < a.n; base += 1024 * kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * 1024 + threadIdx.x;
+      v[u] = (ok && i < a.n)
+                 ? __uint_as_float(__hip_atomic_load(a.y_h + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
+                 : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * 1024 + threadIdx.x;
+      if (i < a.n) a.y[i] = v[u];
+    }
   }
 }
 
@@ -124,6 +188,14 @@ void launch_read_probe(const void* p, int64_t bytes, hipStream_t s, Timing tm) {
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(8192, (n16 + 1023) / 1024));
   launch_timed(hbm_read_kernel, dim3(blocks), dim3(256), 0, s, tm, reinterpret_cast<const u32x4*>(p), n16,
                0x9E3779B9u);
+}
+
+void launch_stage_signal(const StageArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(stage_signal_kernel, dim3(1), dim3(1024), 0, s, a);
+}
+
+void launch_cpu_wait(const CpuWaitArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(cpu_wait_kernel, dim3(1), dim3(1024), 0, s, a);
 }
 
 void launch_stage_step(const StageArgs& a, hipStream_t s) {

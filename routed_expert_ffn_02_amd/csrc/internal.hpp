@@ -35,17 +35,21 @@ enum {
 // device-side step statistics of device-fill steps (uint64 array)
 // D_NOCPU: steps whose lookup sent experts to the CPU although the step, as enqueued or
 // captured, had no CPU branch (a graph replayed after a shrink or a mode change)
+// D_CPUWAIT: captured steps whose bounded wait for the CPU branch's partial sum expired
 enum { D_LOOKUP = 0, D_HIT = 1, D_FILL = 2, D_CPU = 3, D_EVICT = 4, D_ERR = 5, D_P1_BYTES = 6, D_P2_BYTES = 7,
-       D_NOCPU = 8, D_COUNT = 9 };
+       D_NOCPU = 8, D_CPUWAIT = 9, D_COUNT = 10 };
 
 // Cache parameters the kernels read on the device when they run, not from their launch
 // arguments, so a step captured into a graph and replayed sees the current values after
 // expert_cache_resize, moe_set_mode and moe_set_bandwidths.
+constexpr int kSigGo = 0, kSigDone = 32;  // words, 128 bytes apart
+
 struct DevCtrl {
   uint8_t* arena;      // the bound slot arena
   int32_t n_slots;
   int32_t lk_mode;     // LookupMode of decode lookups (the context's backend mode)
   uint64_t bw_pcie, bw_host;
+  uint64_t cpu_wait_ticks;  // bound of a captured step's wait for its CPU branch (wall-clock ticks)
 };
 
 enum LookupMode { LK_FUSED = 0, LK_OFFLOAD = 1, LK_CPU = 2, LK_HYBRID = 3, LK_BUFFER = 4 };
@@ -183,8 +187,31 @@ struct StageArgs {
   const int32_t* slot;  // [P] slot ids
   int32_t* slot_h;
   int P;
+  // signalling variant only: the step's counts (nothing is staged without CPU work), the
+  // device sequence number of signalled steps, and the pinned go word (device address)
+  const int32_t* cnt = nullptr;
+  uint32_t* seq = nullptr;
+  uint32_t* go_h = nullptr;
 };
 void launch_stage_step(const StageArgs& a, hipStream_t s);
+// The staging of a captured step with CPU work followed by its signal to the library's
+// CPU-branch worker (sequence number to the go word); a step without CPU work stages nothing.
+void launch_stage_signal(const StageArgs& a, hipStream_t s);
+// The captured step's join with its CPU branch: waits (bounded by ctrl->cpu_wait_ticks) for
+// the worker to publish the step's sequence number in the pinned done word, then copies the
+// partial sum from pinned memory to y; zeros y when the step has no CPU work or the wait
+// expires (counted in dstats[D_CPUWAIT]).
+struct CpuWaitArgs {
+  const int32_t* cnt;
+  const uint32_t* seq;
+  uint32_t* done_h;   // pinned done word (device address)
+  uint32_t* y_h;      // [n] the partial sum in pinned memory (device address), fp32 bits
+  float* y;           // [n] device copy read by the combine
+  int n;
+  const DevCtrl* ctrl;
+  uint64_t* dstats;
+};
+void launch_cpu_wait(const CpuWaitArgs& a, hipStream_t s);
 void launch_fill_pull(const FillArgs& a, int max_fills, hipStream_t s, Timing tm = {});
 void launch_read_probe(const void* p, int64_t bytes, hipStream_t s, Timing tm);
 void launch_permute(const int32_t* pair_grp, const int32_t* cnt, int P, int G_max, int32_t* hist, int32_t* perm,
@@ -309,11 +336,18 @@ struct moe_ctx {
   float* h_w_dev = nullptr;
   int32_t* h_slot_idx_dev = nullptr;
 
+  // captured steps with CPU work: a library thread runs the branch when the device publishes
+  // a step's sequence number in the pinned go word, and answers in the done word
+  uint32_t* sig_host = nullptr;   // pinned: go word at [kSigGo], done word at [kSigDone]
+  uint32_t* sig_dev = nullptr;    // its device mapping
+  float* h_y_dev = nullptr;       // device mapping of h_y
+  uint32_t* seq_dev = nullptr;    // [1] sequence number of the last signalled step (device)
+  int64_t wall_khz = 0;           // device wall-clock rate
+  double cpu_wait_ms = 5000.0;    // bound of the device's wait for the branch
+  std::thread branch_thread;
+  std::atomic<bool> branch_stop{false};
+
   hipStream_t copy_stream = nullptr;
-  // device-fill steps with CPU work: the branch runs as a host function on cpu_stream,
-  // forked from and joined to the caller's stream with events
-  hipStream_t cpu_stream = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t ev_sync = nullptr, ev_fill = nullptr, ev_ycpu = nullptr;
   hipEvent_t ev_layer_copied[2] = {nullptr, nullptr};
   hipEvent_t ev_layer_done[2] = {nullptr, nullptr};

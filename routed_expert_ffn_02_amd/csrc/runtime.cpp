@@ -13,10 +13,12 @@
 //   resize   rebuild the cache for a new slot budget at a safe point without
 //            touching the host pool (FreeToken summary, "탄력적 메모리 관리").
 #include <hip/hip_runtime.h>
+#include <immintrin.h>
 #include <sched.h>
 
 #include <algorithm>
 #include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 #include <string>
@@ -161,13 +163,20 @@ void drain_timed(moe_ctx* c) {
   c->pending_timed.clear();
 }
 
+// The CPU branch's pool.  By default it leaves two of the process's CPUs free: one for the
+// application thread, which keeps a core busy while it waits on the stream as a replayed
+// step's branch runs on the library's branch thread, and one for the runtime's own threads.
+// Measured on a 16-CPU process replaying DSV4-shaped hybrid steps: with 16 pool threads
+// the branch took 4x as long as eagerly (it ends with its slowest task, and a worker
+// sharing a core stalls it), with 15 1.7x, with 14 the same as eagerly.
 rmoe::CpuPool& cpu_pool(moe_ctx* c) {
   if (!c->cpu) {
     int n = c->cfg.cpu_threads;
     if (n <= 0) {
       cpu_set_t set;
       CPU_ZERO(&set);
-      n = (sched_getaffinity(0, sizeof(set), &set) == 0) ? CPU_COUNT(&set) : 1;
+      const int cpus = (sched_getaffinity(0, sizeof(set), &set) == 0) ? CPU_COUNT(&set) : 1;
+      n = std::max(1, cpus - 2);
     }
     c->cpu = new rmoe::CpuPool(n);
   }
@@ -223,6 +232,7 @@ moe_status write_ctrl(moe_ctx* ctx) {
   h.lk_mode = lookup_mode_of(ctx->cfg.mode);
   h.bw_pcie = ctx->cfg.bw_pcie;
   h.bw_host = ctx->cfg.bw_host;
+  h.cpu_wait_ticks = (uint64_t)(ctx->cpu_wait_ms * (double)ctx->wall_khz);
   HIPCHK(hipDeviceSynchronize());
   HIPCHK(hipMemcpy(ctx->ctrl, &h, sizeof h, hipMemcpyHostToDevice));
   return MOE_OK;
@@ -326,12 +336,11 @@ moe_status run_cpu_branch(moe_ctx* ctx, int T, hipStream_t s, float** y_cpu_dev_
   return MOE_OK;
 }
 
-// The CPU branch of a device-fill step, run by the HIP runtime as a host function on
-// cpu_stream once the step block and the inputs have landed in the pinned staging: it
-// reads the CPU list there and leaves the partial sum (zeros without CPU work) in h_y,
-// which the next node copies to the device.  It calls no HIP API.
-void cpu_branch_host_fn(void* user) {
-  moe_ctx* ctx = static_cast<moe_ctx*>(user);
+// The CPU branch of a captured step, run by the branch worker once the step block and the
+// inputs are in the pinned staging: it reads the CPU list there and leaves the partial sum
+// (zeros without CPU work) in h_y, which the device reads through its mapping.  It calls
+// no HIP API.
+void cpu_branch_staged(moe_ctx* ctx) {
   const int T = ctx->h_cnt[C_T], H = ctx->cfg.hidden;
   std::memset(ctx->h_y, 0, (size_t)T * H * sizeof(float));
   const int ncpu = ctx->h_cnt[C_ERR] ? 0 : ctx->h_cnt[C_CPU];
@@ -363,9 +372,39 @@ void cpu_branch_host_fn(void* user) {
   ctx->stats.cpu_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
+// The branch worker of captured steps: it waits for the device to publish a new sequence
+// number in the pinned go word, runs that step's CPU branch from the staging, and answers
+// with the same number in the done word, which the step's wait kernel polls.  It spins
+// while steps keep coming (the branch then starts within a microsecond of the signal) and
+// sleeps in short naps after 2 ms without one.  Numbers only grow; a number the device
+// publishes while the previous branch still runs is taken next (the device waits for each
+// branch before it stages the next step, so a step is never overwritten while it is read).
+void branch_worker(moe_ctx* ctx) {
+  uint32_t* go = ctx->sig_host + kSigGo;
+  uint32_t* done = ctx->sig_host + kSigDone;
+  // failure tests only: a delay before each answer, so that a short wait bound expires
+  const char* env = std::getenv("RMOE_CPU_BRANCH_DELAY_US");
+  const long delay_us = env ? std::max(0L, std::atol(env)) : 0L;
+  uint32_t last = __atomic_load_n(done, __ATOMIC_ACQUIRE);
+  auto idle = std::chrono::steady_clock::now();
+  while (!ctx->branch_stop.load(std::memory_order_acquire)) {
+    const uint32_t g = __atomic_load_n(go, __ATOMIC_ACQUIRE);
+    if (g != last) {
+      if (delay_us) std::this_thread::sleep_for(std::chrono::microseconds(delay_us));
+      cpu_branch_staged(ctx);
+      __atomic_store_n(done, g, __ATOMIC_RELEASE);
+      last = g;
+      idle = std::chrono::steady_clock::now();
+      continue;
+    }
+    if (std::chrono::steady_clock::now() - idle < std::chrono::milliseconds(2)) _mm_pause();
+    else std::this_thread::sleep_for(std::chrono::microseconds(50));
+  }
+}
+
 // The step block and the CPU branch's inputs written into the pinned staging by one
 // launch on s (through the staging's device mapping), in place of four copies.
-void stage_step(moe_ctx* ctx, const void* x, const float* w, const int32_t* slot_idx, int T, hipStream_t s) {
+StageArgs stage_args(moe_ctx* ctx, const void* x, const float* w, const int32_t* slot_idx, int T) {
   StageArgs sa;
   sa.step = ctx->step_dev;
   sa.step_h = ctx->step_host_dev;
@@ -378,30 +417,43 @@ void stage_step(moe_ctx* ctx, const void* x, const float* w, const int32_t* slot
   sa.slot = slot_idx;
   sa.slot_h = ctx->h_slot_idx_dev;
   sa.P = T * ctx->cfg.top_k;
-  launch_stage_step(sa, s);
+  return sa;
 }
 
-// Enqueue the CPU branch of a device-fill step on cpu_stream (forked from s after the
-// lookup): step block and inputs to the pinned staging, the host function, the
-// partial sum back to y_cpu_dev.  s must wait for ev_join before the combine.
+void stage_step(moe_ctx* ctx, const void* x, const float* w, const int32_t* slot_idx, int T, hipStream_t s) {
+  launch_stage_step(stage_args(ctx, x, w, slot_idx, T), s);
+}
+
+// The CPU branch of a captured step, first half (right after the lookup on s): the step
+// block and inputs to the pinned staging and the signal to the branch worker, which starts
+// with the first such step.  The GPU work enqueued next runs while the CPU computes;
+// join_cpu_branch then makes s wait for the partial sum.
 moe_status enqueue_cpu_branch(moe_ctx* ctx, const void* x, const float* w, const int32_t* slot_idx, int T,
                               hipStream_t s) {
-  const int E = ctx->cfg.n_experts, H = ctx->cfg.hidden, P = T * ctx->cfg.top_k;
-  hipStream_t c = ctx->cpu_stream;
-  if (ctx->step_host_dev) stage_step(ctx, x, w, slot_idx, T, s);  // one launch instead of four copy nodes
-  HIPCHK(hipEventRecord(ctx->ev_fork, s));
-  HIPCHK(hipStreamWaitEvent(c, ctx->ev_fork, 0));
-  if (!ctx->step_host_dev) {
-    HIPCHK(hipMemcpyAsync(ctx->step_host, ctx->step_dev, (size_t)(C_COUNT + 5 * E) * sizeof(int32_t),
-                          hipMemcpyDeviceToHost, c));
-    HIPCHK(hipMemcpyAsync(ctx->h_x, x, (size_t)T * H * act_bytes(ctx->cfg), hipMemcpyDeviceToHost, c));
-    HIPCHK(hipMemcpyAsync(ctx->h_w, w, (size_t)P * sizeof(float), hipMemcpyDeviceToHost, c));
-    HIPCHK(hipMemcpyAsync(ctx->h_slot_idx, slot_idx, (size_t)P * sizeof(int32_t), hipMemcpyDeviceToHost, c));
-  }
-  HIPCHK(hipLaunchHostFunc(c, cpu_branch_host_fn, ctx));
-  HIPCHK(hipMemcpyAsync(ctx->y_cpu_dev, ctx->h_y, (size_t)T * H * sizeof(float), hipMemcpyHostToDevice, c));
-  HIPCHK(hipEventRecord(ctx->ev_join, c));
+  if (!ctx->step_host_dev || !ctx->sig_dev || !ctx->h_y_dev)
+    return fail(ctx, MOE_ENOTSUP, "a captured step with a CPU branch needs device-mapped pinned staging");
+  if (!ctx->branch_thread.joinable()) ctx->branch_thread = std::thread(branch_worker, ctx);
+  StageArgs sa = stage_args(ctx, x, w, slot_idx, T);
+  sa.cnt = ctx->cnt;
+  sa.seq = ctx->seq_dev;
+  sa.go_h = ctx->sig_dev + kSigGo;
+  launch_stage_signal(sa, s);
   return MOE_OK;
+}
+
+// Second half, before the combine: the bounded wait for the worker's answer and the copy of
+// the partial sum to y_cpu_dev.
+void join_cpu_branch(moe_ctx* ctx, int T, hipStream_t s) {
+  CpuWaitArgs w;
+  w.cnt = ctx->cnt;
+  w.seq = ctx->seq_dev;
+  w.done_h = ctx->sig_dev + kSigDone;
+  w.y_h = reinterpret_cast<uint32_t*>(ctx->h_y_dev);
+  w.y = ctx->y_cpu_dev;
+  w.n = T * ctx->cfg.hidden;
+  w.ctrl = ctx->ctrl;
+  w.dstats = ctx->dstats;
+  launch_cpu_wait(w, s);
 }
 
 // A step may send experts to the CPU: CPU and HYBRID modes, or too few slots.
@@ -480,7 +532,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->hist, (size_t)((Pmax + 255) / 256) * kMaxExperts) || dev_alloc(&ctx->cand, E) ||
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->act), (size_t)Pmax * I * 4) ||
       dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)) ||
-      dev_alloc(&ctx->dstats, D_COUNT) || dev_alloc(&ctx->ctrl, 1))
+      dev_alloc(&ctx->dstats, D_COUNT) || dev_alloc(&ctx->ctrl, 1) || dev_alloc(&ctx->seq_dev, 1))
     return cleanup_fail(MOE_ENOMEM);
   if (prefill_needs_act_operands(c.wfmt, c.afmt) &&
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->xo), (size_t)c.max_tokens * H * 2))
@@ -493,7 +545,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ctx->u_kind = ctx->u_key + E;
   if (hipMemset(ctx->slot_of, 0xff, (size_t)L * E * 4) || hipMemset(ctx->key_of, 0xff, kMaxCachedSlots * 4) ||
       hipMemset(ctx->stamp, 0, kMaxCachedSlots * 8) || hipMemset(ctx->reserved, 0, kMaxCachedSlots) ||
-      hipMemset(ctx->counter, 0, 8) || hipMemset(ctx->dstats, 0, D_COUNT * 8) ||
+      hipMemset(ctx->counter, 0, 8) || hipMemset(ctx->dstats, 0, D_COUNT * 8) || hipMemset(ctx->seq_dev, 0, 4) ||
       hipMemset(ctx->step_dev, 0, (C_COUNT + 5 * E) * 4))
     return cleanup_fail(MOE_EHIP);
   // pinned host staging
@@ -503,8 +555,10 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       hipHostMalloc(&ctx->h_x, (size_t)c.max_tokens * H * 4, 0) ||
       hipHostMalloc(reinterpret_cast<void**>(&ctx->h_xf), (size_t)c.max_tokens * H * 4, 0) ||
       hipHostMalloc(reinterpret_cast<void**>(&ctx->h_y), (size_t)c.max_tokens * H * 4, 0) ||
-      hipHostMalloc(reinterpret_cast<void**>(&ctx->h_hbuf), (size_t)Pmax * I * 4, 0))
+      hipHostMalloc(reinterpret_cast<void**>(&ctx->h_hbuf), (size_t)Pmax * I * 4, 0) ||
+      hipHostMalloc(reinterpret_cast<void**>(&ctx->sig_host), 256, 0))
     return cleanup_fail(MOE_ENOMEM);
+  std::memset(ctx->sig_host, 0, 256);
   {  // device addresses of the staging the step-staging kernel writes (optional)
     void *a = nullptr, *b = nullptr, *c2 = nullptr, *d = nullptr;
     if (hipHostGetDevicePointer(&a, ctx->step_host, 0) == hipSuccess &&
@@ -515,7 +569,19 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       ctx->h_w_dev = static_cast<float*>(c2);
       ctx->h_slot_idx_dev = static_cast<int32_t*>(d);
     }
+    void *g = nullptr, *yh = nullptr;
+    if (hipHostGetDevicePointer(&g, ctx->sig_host, 0) == hipSuccess &&
+        hipHostGetDevicePointer(&yh, ctx->h_y, 0) == hipSuccess) {
+      ctx->sig_dev = static_cast<uint32_t*>(g);
+      ctx->h_y_dev = static_cast<float*>(yh);
+    }
     (void)hipGetLastError();
+  }
+  {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, ctx->device) != hipSuccess || khz <= 0)
+      khz = 100000;  // 100 MHz, the rate of the device's constant wall clock
+    ctx->wall_khz = khz;
   }
   ctx->h_cnt = ctx->step_host;
   ctx->h_fill_key = ctx->h_cnt + C_COUNT;
@@ -525,9 +591,6 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ctx->h_u_kind = ctx->h_u_key + E;
   std::memset(ctx->h_cnt, 0, C_COUNT * 4);
   if (hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking) ||
-      hipStreamCreateWithFlags(&ctx->cpu_stream, hipStreamNonBlocking) ||
-      hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming) ||
-      hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming) ||
       hipEventCreateWithFlags(&ctx->ev_sync, hipEventDisableTiming) ||
       hipEventCreateWithFlags(&ctx->ev_fill, hipEventDisableTiming) ||
       hipEventCreateWithFlags(&ctx->ev_ycpu, hipEventDisableTiming) ||
@@ -544,8 +607,11 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
 MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   if (!ctx) return MOE_EINVAL;
   if (ctx->copy_stream) hipStreamSynchronize(ctx->copy_stream);
-  if (ctx->cpu_stream) hipStreamSynchronize(ctx->cpu_stream);
-  hipDeviceSynchronize();
+  hipDeviceSynchronize();  // a captured step's wait for its branch ends first (bounded)
+  if (ctx->branch_thread.joinable()) {
+    ctx->branch_stop.store(true, std::memory_order_release);
+    ctx->branch_thread.join();
+  }
   delete ctx->cpu;
   ctx->cpu = nullptr;
   for (auto& t : ctx->pending_timed) {
@@ -556,20 +622,19 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
                  ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
-                 ctx->flags, ctx->xo, ctx->dstats, ctx->ctrl};
+                 ctx->flags, ctx->xo, ctx->dstats, ctx->ctrl, ctx->seq_dev};
   for (void* p : dev)
     if (p) hipFree(p);
-  void* host[] = {ctx->step_host, ctx->h_slot_idx, ctx->h_w, ctx->h_x, ctx->h_xf, ctx->h_y, ctx->h_hbuf};
+  void* host[] = {ctx->step_host, ctx->h_slot_idx, ctx->h_w, ctx->h_x, ctx->h_xf, ctx->h_y, ctx->h_hbuf, ctx->sig_host};
   for (void* p : host)
     if (p) hipHostFree(p);
   if (ctx->pool_owned && ctx->pool) hipHostFree(ctx->pool);
-  hipEvent_t evs[] = {ctx->ev_sync, ctx->ev_fill, ctx->ev_ycpu, ctx->ev_fork, ctx->ev_join, ctx->ev_layer_copied[0],
+  hipEvent_t evs[] = {ctx->ev_sync, ctx->ev_fill, ctx->ev_ycpu, ctx->ev_layer_copied[0],
                       ctx->ev_layer_copied[1],
                       ctx->ev_layer_done[0], ctx->ev_layer_done[1]};
   for (auto e : evs)
     if (e) hipEventDestroy(e);
   if (ctx->copy_stream) hipStreamDestroy(ctx->copy_stream);
-  if (ctx->cpu_stream) hipStreamDestroy(ctx->cpu_stream);
   delete ctx;
   return MOE_OK;
 }
@@ -664,6 +729,13 @@ MOE_API moe_status moe_set_mode(moe_ctx* ctx, int32_t mode) {
   CHECK_ARG((mode == MOE_MODE_FUSED) == (ctx->cfg.mode == MOE_MODE_FUSED), "FUSED <-> cached needs a new context");
   CHECK_ARG(ctx->pool_pinned || mode == MOE_MODE_CPU, "pageable pool: only MOE_MODE_CPU");
   ctx->cfg.mode = mode;
+  return write_ctrl(ctx);
+}
+
+MOE_API moe_status moe_set_cpu_wait(moe_ctx* ctx, double timeout_ms) {
+  if (!ctx) return MOE_EINVAL;
+  CHECK_ARG(timeout_ms > 0.0 && timeout_ms <= 60000.0, "timeout_ms must be in (0, 60000]");
+  ctx->cpu_wait_ms = timeout_ms;
   return write_ctrl(ctx);
 }
 
@@ -844,11 +916,11 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   float* y_cpu = nullptr;
   const bool inputs = !fused && may_use_cpu(ctx, P);
   // device fills: no host read of the step (its counts and profiled bytes stay on the
-  // device).  A step that may send work to the CPU does so as host nodes while the stream
-  // is being captured.  Eagerly the calling thread reads the step and runs the branch
-  // itself (faster than a host function competing with the enqueuing thread); the fill
-  // kernel, queued behind the step's copies to the host, moves the records meanwhile, so
-  // no host round trip precedes the fills.
+  // device).  A step that may send work to the CPU hands it to the branch thread while the
+  // stream is being captured (signal and bounded wait on the device, no host node).
+  // Eagerly the calling thread reads the step and runs the branch itself; the fill kernel,
+  // queued behind the step's copies to the host, moves the records meanwhile, so no host
+  // round trip precedes the fills.
   const bool devfill_flag = (ctx->cfg.flags & MOE_FLAG_DEVICE_FILLS) && !fused;
   const bool async_cpu = devfill_flag && inputs && captured;
   const bool devfill = devfill_flag && (!inputs || captured);
@@ -952,7 +1024,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     moe_status st = run_cpu_branch(ctx, T, s, &y_cpu);
     if (st != MOE_OK) return st;
   }
-  if (async_cpu) HIPCHK(hipStreamWaitEvent(s, ctx->ev_join, 0));
+  if (async_cpu) join_cpu_branch(ctx, T, s);
   if (!combined) launch_decode_combine(d, y_cpu, s);
   if (log_rec >= 0) {
     moe_step_rec& r = ctx->step_log[log_rec];
@@ -1449,9 +1521,10 @@ MOE_API moe_status moe_cache_snapshot(moe_ctx* ctx, int32_t* slot_of, int32_t* k
 MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream) {
   if (!ctx) return MOE_EINVAL;
   HIPCHK(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  uint64_t err = 0, nocpu = 0;
+  uint64_t err = 0, nocpu = 0, waits = 0;
   HIPCHK(hipMemcpy(&err, ctx->dstats + D_ERR, 8, hipMemcpyDeviceToHost));
   HIPCHK(hipMemcpy(&nocpu, ctx->dstats + D_NOCPU, 8, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(&waits, ctx->dstats + D_CPUWAIT, 8, hipMemcpyDeviceToHost));
   const uint64_t zero = 0;
   if (err) {
     HIPCHK(hipMemcpy(ctx->dstats + D_ERR, &zero, 8, hipMemcpyHostToDevice));
@@ -1461,6 +1534,11 @@ MOE_API moe_status moe_sync(moe_ctx* ctx, moe_stream_t stream) {
     HIPCHK(hipMemcpy(ctx->dstats + D_NOCPU, &zero, 8, hipMemcpyHostToDevice));
     return fail(ctx, MOE_ESTATE, "a step without a CPU branch had experts sent to the CPU (a graph captured "
                                  "before a shrink or a mode change: capture it again)");
+  }
+  if (waits) {
+    HIPCHK(hipMemcpy(ctx->dstats + D_CPUWAIT, &zero, 8, hipMemcpyHostToDevice));
+    return fail(ctx, MOE_ETIMEDOUT, "a captured step's wait for its CPU branch expired (its CPU experts are "
+                                    "missing from y)");
   }
   return MOE_OK;
 }

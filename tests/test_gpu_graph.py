@@ -2,7 +2,8 @@
 HIP graph and replayed must reproduce eager execution bit for bit, replay after replay,
 with the cache state advancing on the device, and every replayed step must match the
 oracle (top-k indices and gates, cache trace and slot ids, outputs).  Paths that
-qualify: OFFLOAD and HYBRID with device fills (the CPU branch as host nodes), FUSED."""
+qualify: OFFLOAD and HYBRID with device fills (the CPU branch served by the library's
+branch thread, joined on the device by a bounded wait), FUSED."""
 import numpy as np
 import pytest
 
@@ -88,7 +89,7 @@ def test_captured_step_replays_like_eager(wl, mode):
     if mode.startswith("fused"):
         kw = dict(mode=R.MOE_MODE_FUSED)
         flags = 0
-    elif mode == "hybrid_device_fills":  # few slots: the CPU branch runs as host nodes
+    elif mode == "hybrid_device_fills":  # few slots: the CPU branch runs on the branch thread
         kw = dict(mode=R.MOE_MODE_HYBRID, n_slots=wl.top_k + 1)
         flags = R.MOE_FLAG_DEVICE_FILLS
         bw = (25_000_000_000, 100_000_000_000)
@@ -110,7 +111,7 @@ def test_captured_step_replays_like_eager(wl, mode):
     check_against_oracle(wl, bg, 0, cache, kw["mode"], bw, fused)
     g = torch.cuda.CUDAGraph()
     # thread-local capture: only this thread's calls are checked against the capture
-    # (host nodes and the CPU worker pool run on threads of their own)
+    # (the branch thread and the CPU worker pool run on threads of their own)
     with torch.cuda.graph(g, capture_error_mode="thread_local"):
         run_step(R, graph, bg, torch.cuda.current_stream().cuda_stream, lc)
     scratch = torch.randn(1 << 16, device="cuda")
@@ -219,4 +220,53 @@ def test_replay_after_shrink_below_capture_is_reported():
         R.moe_sync(h.ctx)
     assert e.value.status == R.MOE_ESTATE
     R.moe_sync(h.ctx)  # reported once
+    del g
+
+
+def test_expired_cpu_branch_wait_is_reported(monkeypatch):
+    """A captured HYBRID step whose CPU branch answers after the wait bound (the branch
+    thread is told to answer 100 ms late, the bound is 50 us): the wait kernel gives up and
+    ends, the step's CPU experts are left out, and moe_sync reports MOE_ETIMEDOUT once.  With
+    the bound raised, the following replays match the oracle again."""
+    import routed_expert_ffn_02_amd as R
+    import torch
+    wl, T = BF16, 1
+    bw = (25_000_000_000, 100_000_000_000)
+    monkeypatch.setenv("RMOE_CPU_BRANCH_DELAY_US", "100000")  # read when the branch thread starts
+    h = Harness(wl, R.MOE_MODE_HYBRID, n_slots=wl.top_k + 1, flags=R.MOE_FLAG_DEVICE_FILLS, bw=bw)
+    b = StepBuffers(wl, T)
+    cache = oracle.ExpertCache(wl.n_layers, wl.n_experts, h.n_slots)
+    b.load(wl, 0)
+    run_step(R, h, b, None)
+    torch.cuda.synchronize()
+    check_against_oracle(wl, b, 0, cache, R.MOE_MODE_HYBRID, bw, False)
+    R.moe_set_cpu_wait(h.ctx, 0.05)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        run_step(R, h, b, torch.cuda.current_stream().cuda_stream)
+    step, expired = 0, False
+    while step < 6 and not expired:
+        step += 1
+        b.load(wl, step)
+        g.replay()
+        torch.cuda.synchronize()
+        _, idx, _, _, cnt, _ = b.outputs()
+        for l in range(wl.n_layers):  # the tables advance on the device all the same
+            cache.lookup(l, idx[l], R.MOE_MODE_HYBRID, *bw)
+        if int(cnt[:, 2].sum()) > 0:  # a step with CPU work
+            with pytest.raises(R.MoeError) as e:
+                R.moe_sync(h.ctx)
+            assert e.value.status == R.MOE_ETIMEDOUT
+            expired = True
+        else:
+            R.moe_sync(h.ctx)
+    assert expired, "no replayed step sent experts to the CPU"
+    R.moe_sync(h.ctx)  # reported once
+    R.moe_set_cpu_wait(h.ctx, 5000.0)
+    for step in range(step + 1, step + 3):
+        b.load(wl, step)
+        g.replay()
+        torch.cuda.synchronize()
+        check_against_oracle(wl, b, step, cache, R.MOE_MODE_HYBRID, bw, False)
+    R.moe_sync(h.ctx)
     del g
