@@ -128,6 +128,14 @@ struct RowDot<MOE_WFMT_MXFP4> {
 template <int WFMT>
 constexpr bool kIsFp4 = (WFMT == MOE_WFMT_FP4 || WFMT == MOE_WFMT_MXFP4);
 
+// An activated value v = h[pair, row] is stored twice: fp32 in h (the fp32 phase-2 paths)
+// and rounded to bf16 (to nearest even) in h16, the operand of the bf16 phase-2 paths,
+// which read half the bytes and convert nothing.
+__device__ __forceinline__ void store_h(const DecodeArgs& a, int64_t i, float v) {
+  a.h[i] = v;
+  a.h16[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 // Raw block scale c of a scale row (bf16 bits or the E8M0 byte) and its value.
 template <int WFMT>
 __device__ __forceinline__ uint32_t scale_raw(const uint8_t* srow, int c) {
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(256) void dec_phase1_fast(DecodeArgs a) {
       if (t < n) {
         const float gs = wave_sum(accg[t]);
         const float us = wave_sum(accu[t]);
-        if (lane == 0 && row < I) a.h[(int64_t)pair[t] * I + row] = silu(gs) * us;
+        if (lane == 0 && row < I) store_h(a, (int64_t)pair[t] * I + row, silu(gs) * us);
       }
     }
   }
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
       float v = hv[0][t];
 #pragma unroll
       for (int r = 1; r < RW; ++r) v = (lane == r) ? hv[r][t] : v;
-      if (lane < RW && row0 + lane < I) a.h[(int64_t)pair[t] * I + row0 + lane] = v;
+      if (lane < RW && row0 + lane < I) store_h(a, (int64_t)pair[t] * I + row0 + lane, v);
     }
   }
 }
@@ -632,7 +640,7 @@ __global__ __launch_bounds__(256) void dec_phase1(DecodeArgs a) {
     if (t < n) {
       const float gs = wave_sum(accg[t]);
       const float us = wave_sum(accu[t]);
-      if (lane == 0) a.h[(int64_t)s_pair[t] * I + row] = silu(gs) * us;
+      if (lane == 0) store_h(a, (int64_t)s_pair[t] * I + row, silu(gs) * us);
     }
   }
 }
@@ -723,9 +731,9 @@ __global__ __launch_bounds__(256) void dec_phase2_fast(DecodeArgs a) {
 }
 
 // Phase 2, bf16 dot path (I = 64 chunks per row, P <= 64, bf16 or FP4 weights): each
-// wavefront owns R2 rows of W_down of one expert.  The fp32 activated rows h are
-// rounded to bf16 once per wavefront (the 16-bit operand rounding the prefill GEMM
-// applies to the same values) and meet the weights in v_dot2_f32_bf16.
+// wavefront owns R2 rows of W_down of one expert.  The activated rows come as h16, the
+// bf16 rounding phase 1 stored (the 16-bit operand rounding the prefill GEMM applies to
+// the same values), and meet the weights in v_dot2_f32_bf16.
 template <int WFMT, int MAXT>
 __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
   constexpr int R2 = kP2RowsPerWave;
@@ -740,11 +748,12 @@ __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
   if (r0 >= H) return;
   const uint8_t* rec = a.ctrl->arena + (int64_t)slot * a.rec_bytes;
   // one token: the group's activated row is requested before the weights
-  f32x4n hq[MAXT][EPC / 4];
+  constexpr int HQ = EPC / 8;  // 16-byte loads of the lane's bf16 h elements
+  u32x4n hq[MAXT][HQ];
   if constexpr (MAXT == 1) {
-    const f32x4n* hp = reinterpret_cast<const f32x4n*>(a.h + (int64_t)pair0 * I + lane * EPC);
+    const u32x4n* hp = reinterpret_cast<const u32x4n*>(a.h16 + (int64_t)pair0 * I + lane * EPC);
 #pragma unroll
-    for (int i = 0; i < EPC / 4; ++i) hq[0][i] = hp[i];
+    for (int i = 0; i < HQ; ++i) hq[0][i] = hp[i];
   }
   uint16_t scr[R2];
   if constexpr (kIsFp4<WFMT>) {
@@ -771,22 +780,19 @@ __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
       if (t < n) {
-        const f32x4n* hp = reinterpret_cast<const f32x4n*>(a.h + (int64_t)pair[t] * I + lane * EPC);
+        const u32x4n* hp = reinterpret_cast<const u32x4n*>(a.h16 + (int64_t)pair[t] * I + lane * EPC);
 #pragma unroll
-        for (int i = 0; i < EPC / 4; ++i) hq[t][i] = hp[i];
+        for (int i = 0; i < HQ; ++i) hq[t][i] = hp[i];
       }
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // every load in flight before any use
-  uint32_t hw[MAXT][EPC / 2];
+  uint32_t hw[MAXT][EPC / 2];  // word i: elements 2i (low half) and 2i + 1
 #pragma unroll
   for (int t = 0; t < MAXT; ++t)
     if (t < n)
 #pragma unroll
-      for (int i = 0; i < EPC / 2; ++i) {
-        const bf16x2 b = {(__bf16)hq[t][i / 2][2 * (i % 2)], (__bf16)hq[t][i / 2][2 * (i % 2) + 1]};
-        hw[t][i] = __builtin_bit_cast(uint32_t, b);
-      }
+      for (int i = 0; i < EPC / 2; ++i) hw[t][i] = hq[t][i / 4][i % 4];
   float out[R2][MAXT];
 #pragma unroll
   for (int r = 0; r < R2; ++r) {
@@ -817,14 +823,15 @@ __global__ __launch_bounds__(256) void dec_phase2_bf(DecodeArgs a) {
 // j's expert is found through its slot id, whatever the lookup's group numbering).  A
 // workgroup owns R2 rows of the output and has one wavefront per pair: wavefront j
 // computes its expert's R2 rows of W_down h_j exactly as dec_phase2_bf does (the same
-// loads, bf16 rounding of h_j and dot path), parks them in LDS, and wavefront 0 sums
+// loads of the bf16 h_j and dot path), parks them in LDS, and wavefront 0 sums
 // w_j * d_j in rank order with one fused multiply-add per pair, the arithmetic of
 // dec_combine, so the result is bit-identical to the two separate kernels.
 constexpr int kP2cMaxK = 8;
+constexpr int kP2cRows = 8;  // output rows per workgroup
 
 template <int WFMT>
 __global__ __launch_bounds__(64 * kP2cMaxK) void dec_phase2_combine_bf(DecodeArgs a) {
-  constexpr int R2 = kP2RowsPerWave;
+  constexpr int R2 = kP2cRows;
   constexpr int EPC = kIsFp4<WFMT> ? 32 : 8;  // elements per lane chunk (one 16-byte weight load)
   __shared__ float s_d[kP2cMaxK][R2];
   const int H = a.H, I = a.I, k = a.k;
@@ -840,10 +847,11 @@ __global__ __launch_bounds__(64 * kP2cMaxK) void dec_phase2_combine_bf(DecodeArg
     return;
   }
   const uint8_t* rec = a.ctrl->arena + (int64_t)slot * a.rec_bytes;
-  f32x4n hq[EPC / 4];
-  const f32x4n* hp = reinterpret_cast<const f32x4n*>(a.h + (int64_t)j * I + lane * EPC);
+  constexpr int HQ = EPC / 8;  // 16-byte loads of the lane's bf16 h elements
+  u32x4n hq[HQ];
+  const u32x4n* hp = reinterpret_cast<const u32x4n*>(a.h16 + (int64_t)j * I + lane * EPC);
 #pragma unroll
-  for (int i = 0; i < EPC / 4; ++i) hq[i] = hp[i];
+  for (int i = 0; i < HQ; ++i) hq[i] = hp[i];
   uint16_t scr[R2];
   if constexpr (kIsFp4<WFMT>) {
 #pragma unroll
@@ -856,10 +864,7 @@ __global__ __launch_bounds__(64 * kP2cMaxK) void dec_phase2_combine_bf(DecodeArg
   __builtin_amdgcn_sched_barrier(0);  // every load in flight before any use
   uint32_t hw[EPC / 2];
 #pragma unroll
-  for (int i = 0; i < EPC / 2; ++i) {
-    const bf16x2 b = {(__bf16)hq[i / 2][2 * (i % 2)], (__bf16)hq[i / 2][2 * (i % 2) + 1]};
-    hw[i] = __builtin_bit_cast(uint32_t, b);
-  }
+  for (int i = 0; i < EPC / 2; ++i) hw[i] = hq[i / 4][i % 4];
   float out[R2];
 #pragma unroll
   for (int r = 0; r < R2; ++r) {
@@ -1091,7 +1096,7 @@ void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStre
 // dec_phase2_combine_bf); false: the shape or format needs the separate kernels.
 bool launch_decode_phase2_combine(int wfmt, const DecodeArgs& a, hipStream_t s, Timing tm) {
   if (a.T != 1 || a.k < 1 || a.k > kP2cMaxK || wfmt == MOE_WFMT_F32 || lane_chunks(wfmt, a.I) != 1) return false;
-  const dim3 grid((a.H + kP2RowsPerWave - 1) / kP2RowsPerWave), block(64 * a.k);
+  const dim3 grid((a.H + kP2cRows - 1) / kP2cRows), block(64 * a.k);
   if (wfmt == MOE_WFMT_BF16) launch_timed(dec_phase2_combine_bf<MOE_WFMT_BF16>, grid, block, 0, s, tm, a);
   else if (wfmt == MOE_WFMT_FP4) launch_timed(dec_phase2_combine_bf<MOE_WFMT_FP4>, grid, block, 0, s, tm, a);
   else launch_timed(dec_phase2_combine_bf<MOE_WFMT_MXFP4>, grid, block, 0, s, tm, a);

@@ -101,6 +101,7 @@ struct DecodeArgs {
   const int32_t* cnt;        // device counters (C_NGRP)
   const int32_t* slot_idx;   // [T,k] slot of each pair (or a CPU flag), as the lookup wrote it
   float* h;                  // [T*k, I] scratch
+  uint16_t* h16;             // [T*k, I] the same values rounded to bf16
   float* d;                  // [T*k, H] scratch (per-pair expert outputs)
   float* y;                  // [T,H]
   // all-resident batch-1 steps routed inside phase 1 (logits != nullptr): every workgroup
@@ -304,6 +305,7 @@ struct moe_ctx {
   // scratch (device)
   float* logits = nullptr;       // [max_tokens*E]
   float* h = nullptr;            // [decode pairs * I]
+  uint16_t* h16 = nullptr;       // [decode pairs * I] h rounded to bf16
   float* dpair = nullptr;        // [decode pairs * H]
   float* y_cpu_dev = nullptr;    // [max_tokens*H]
   // prefill scratch (device, sized for max_tokens)

@@ -11,80 +11,12 @@ namespace rmoe {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Decode-sized batches: one wavefront per expert row, activations staged in LDS
-// as fp32.  W_r rows are read with 16-byte lane loads (fully coalesced), eight
-// per lane requested before any is used, so a 16 KB row takes two memory round
-// trips rather than sixteen.
-constexpr int kRouteWaves = 4;
-constexpr int kRouteBatch = 8;  // 16-byte row chunks per lane in flight
-
-template <int AFMT>
-__global__ __launch_bounds__(256) void route_gemv(const void* __restrict__ x, const float* __restrict__ wr,
-                                                   const float* __restrict__ bias, float* __restrict__ logits,
-                                                   int T, int E, int H) {
-  extern __shared__ float s_x[];  // [T][H]
-  constexpr int EV = (AFMT == MOE_AFMT_BF16) ? 8 : 4;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = min(blockIdx.x * kRouteWaves + wave, E - 1);  // rows past E recompute the last one, unstored
-  const float4* row = reinterpret_cast<const float4*>(wr + (size_t)e * H);
-  const int nc = H / 4;  // 16-byte chunks of a row; lanes past the row's end load nothing
-  // the first batch of the row is requested before the activations are staged; chunk
-  // indices past the row's end are clamped (in bounds) and their products skipped
-  float4 w4[kRouteBatch];
-#pragma unroll
-  for (int b = 0; b < kRouteBatch; ++b) w4[b] = row[min(lane + 64 * b, nc - 1)];
-  for (int i = threadIdx.x; i < T * H / EV; i += blockDim.x) {
-    const uint4 q = reinterpret_cast<const uint4*>(x)[i];
-    float* dst = s_x + i * EV;
-    if constexpr (AFMT == MOE_AFMT_BF16) {
-      *reinterpret_cast<float4*>(dst) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
-    } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
-                                                    __uint_as_float(q.z), __uint_as_float(q.w));
-    }
-  }
-  __syncthreads();
-  float acc[kDecodeMaxTok];
-#pragma unroll
-  for (int t = 0; t < kDecodeMaxTok; ++t) acc[t] = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += 64 * kRouteBatch) {
-#pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      const int c = c0 + lane + 64 * b;
-      if (c < nc) {
-#pragma unroll
-        for (int t = 0; t < kDecodeMaxTok; ++t) {
-          if (t < T) {
-            const float4 x4 = *reinterpret_cast<const float4*>(&s_x[t * H + 4 * c]);
-            acc[t] += w4[b].x * x4.x + w4[b].y * x4.y + w4[b].z * x4.z + w4[b].w * x4.w;
-          }
-        }
-      }
-    }
-    const int c1 = c0 + 64 * kRouteBatch;
-    if (c1 < nc) {
-#pragma unroll
-      for (int b = 0; b < kRouteBatch; ++b) w4[b] = row[min(c1 + lane + 64 * b, nc - 1)];
-    }
-  }
-  if (blockIdx.x * kRouteWaves + wave >= E) return;
-#pragma unroll
-  for (int t = 0; t < kDecodeMaxTok; ++t) {
-    if (t < T) {
-      float s = wave_sum(acc[t]);
-      if (lane == 0) logits[(size_t)t * E + e] = s + (bias ? bias[(size_t)t * E + e] : 0.f);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Long prompts: fp32 MFMA (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32
-// accumulation).  A block owns 32 tokens x 64 experts; wavefront (wm, wn) of the
-// 2 x 2 grid owns 16 tokens x 32 experts (two 16x16 accumulators).  K runs in
-// chunks of 32 through double-buffered LDS; the next chunk is loaded into
-// registers while the current one is multiplied.
-constexpr int kRgT = 32, kRgE = 64, kRgK = 32, kRgP = kRgK + 4;  // padded LDS row (floats)
+// Decode-sized batches: one workgroup per expert row, each of its four wavefronts a
+// quarter of the row.  A lane's 16-byte weight chunks (four at H = 4096) and the matching
+// activations are all requested before any is used, so the whole 4 MB of an E = 256,
+// H = 4096 router is in flight at once over E workgroups (one memory round trip); the
+// quarter sums meet in LDS and are added in wavefront order.
+constexpr int kRouteBatch = 4;  // 16-byte row chunks per lane per round
 
 template <int AFMT>
 __device__ __forceinline__ float4 route_x4(const void* x, size_t i) {  // 4 activations at element i
@@ -95,6 +27,61 @@ __device__ __forceinline__ float4 route_x4(const void* x, size_t i) {  // 4 acti
     return *reinterpret_cast<const float4*>(static_cast<const float*>(x) + i);
   }
 }
+
+template <int AFMT>
+__global__ __launch_bounds__(256) void route_gemv(const void* __restrict__ x, const float* __restrict__ wr,
+                                                   const float* __restrict__ bias, float* __restrict__ logits,
+                                                   int T, int E, int H) {
+  __shared__ float s_part[4][kDecodeMaxTok];
+  const int e = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cw = H / 16;  // 16-byte chunks in a quarter row (H % 64 == 0)
+  const int c0 = wave * cw;
+  const float4* row = reinterpret_cast<const float4*>(wr + (size_t)e * H) + c0;
+  float acc[kDecodeMaxTok];
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTok; ++t) acc[t] = 0.f;
+  for (int cb = 0; cb < cw; cb += 64 * kRouteBatch) {
+    float4 w4[kRouteBatch];
+    float4 x4[kRouteBatch][kDecodeMaxTok];
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      const int c = min(cb + lane + 64 * b, cw - 1);  // clamped chunks are loaded, not added
+      w4[b] = row[c];
+#pragma unroll
+      for (int t = 0; t < kDecodeMaxTok; ++t)
+        if (t < T) x4[b][t] = route_x4<AFMT>(x, (size_t)t * H + 4 * (c0 + c));
+    }
+#pragma unroll
+    for (int b = 0; b < kRouteBatch; ++b) {
+      if (cb + lane + 64 * b < cw) {
+#pragma unroll
+        for (int t = 0; t < kDecodeMaxTok; ++t)
+          if (t < T) acc[t] += w4[b].x * x4[b][t].x + w4[b].y * x4[b][t].y + w4[b].z * x4[b][t].z + w4[b].w * x4[b][t].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTok; ++t) {
+    if (t < T) {
+      const float v = wave_sum(acc[t]);
+      if (lane == 0) s_part[wave][t] = v;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    const float z = ((s_part[0][t] + s_part[1][t]) + s_part[2][t]) + s_part[3][t];
+    logits[(size_t)t * E + e] = z + (bias ? bias[(size_t)t * E + e] : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Long prompts: fp32 MFMA (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32
+// accumulation).  A block owns 32 tokens x 64 experts; wavefront (wm, wn) of the
+// 2 x 2 grid owns 16 tokens x 32 experts (two 16x16 accumulators).  K runs in
+// chunks of 32 through double-buffered LDS; the next chunk is loaded into
+// registers while the current one is multiplied.
+constexpr int kRgT = 32, kRgE = 64, kRgK = 32, kRgP = kRgK + 4;  // padded LDS row (floats)
 
 template <int AFMT>
 __global__ __launch_bounds__(256) void route_gemm(const void* __restrict__ x, const float* __restrict__ wr,
@@ -158,12 +145,10 @@ __global__ __launch_bounds__(256) void route_gemm(const void* __restrict__ x, co
 void launch_route_logits(const void* x, int afmt, const float* wr, const float* bias, float* logits, int T, int E,
                          int H, hipStream_t s) {
   if (T <= kDecodeMaxTok && T * H <= kDecodeMaxTH) {
-    dim3 grid((E + kRouteWaves - 1) / kRouteWaves);
-    size_t lds = (size_t)T * H * sizeof(float);
     if (afmt == MOE_AFMT_BF16)
-      hipLaunchKernelGGL(route_gemv<MOE_AFMT_BF16>, grid, dim3(256), lds, s, x, wr, bias, logits, T, E, H);
+      hipLaunchKernelGGL(route_gemv<MOE_AFMT_BF16>, dim3(E), dim3(256), 0, s, x, wr, bias, logits, T, E, H);
     else
-      hipLaunchKernelGGL(route_gemv<MOE_AFMT_F32>, grid, dim3(256), lds, s, x, wr, bias, logits, T, E, H);
+      hipLaunchKernelGGL(route_gemv<MOE_AFMT_F32>, dim3(E), dim3(256), 0, s, x, wr, bias, logits, T, E, H);
   } else {
     dim3 grid((T + kRgT - 1) / kRgT, (E + kRgE - 1) / kRgE);
     if (afmt == MOE_AFMT_BF16)

@@ -524,7 +524,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->grp_slot, std::max<int64_t>(E, Pmax)) || dev_alloc(&ctx->grp_pair0, std::max<int64_t>(E, Pmax)) ||
       dev_alloc(&ctx->slot_scratch, Pmax) ||
       dev_alloc(&ctx->pair_grp, Pmax) ||
-      dev_alloc(&ctx->logits, (size_t)c.max_tokens * E) || dev_alloc(&ctx->h, (size_t)Pdec * I) ||
+      dev_alloc(&ctx->logits, (size_t)c.max_tokens * E) || dev_alloc(&ctx->h, (size_t)Pdec * I) || dev_alloc(&ctx->h16, (size_t)Pdec * I) ||
       dev_alloc(&ctx->dpair, (size_t)Pdec * H) ||
       dev_alloc(&ctx->y_cpu_dev, (size_t)c.max_tokens * H) || dev_alloc(&ctx->perm, Pmax) ||
       dev_alloc(&ctx->inv, Pmax) || dev_alloc(&ctx->offsets, std::max<int64_t>(E, Pmax) + 1) ||
@@ -620,7 +620,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   }
   for (auto e : ctx->event_pool) hipEventDestroy(e);
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
-                 ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->dpair, ctx->y_cpu_dev,
+                 ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->h16, ctx->dpair, ctx->y_cpu_dev,
                  ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
                  ctx->flags, ctx->xo, ctx->dstats, ctx->ctrl, ctx->seq_dev};
   for (void* p : dev)
@@ -851,6 +851,7 @@ MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, 
     d.cnt = ctx->cnt;
     d.slot_idx = slot_idx;
     d.h = ctx->h;
+    d.h16 = ctx->h16;
     d.d = ctx->dpair;
     d.y = y;
     d.logits = ctx->logits;
@@ -969,6 +970,7 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
   d.cnt = ctx->cnt;
   d.slot_idx = slot_idx;
   d.h = ctx->h;
+  d.h16 = ctx->h16;
   d.d = ctx->dpair;
   d.y = y;
   const int max_groups = std::min(P, E);
