@@ -107,18 +107,20 @@ __device__ __forceinline__ bool topk_better(float va, int ia, float vb, int ib) 
 }
 
 // PL logits per lane (E <= 64 * PL): the scan and the selection rounds touch only those.
+// A chosen logit (and every slot past E) is held as (-inf, INT_MAX), which loses to any
+// candidate under the order, so the rounds are branch-free selects.
 template <int PL>
 __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E, int k, int renorm,
                                              int32_t* __restrict__ idx_out, float* __restrict__ w_out, int* lds_idx) {
   const int lane = threadIdx.x & 63;
   float v[PL];
-  bool taken[PL];
+  int ev[PL];  // the logit's expert, INT_MAX once chosen or past E
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
-    int e = lane + 64 * i;
+    const int e = lane + 64 * i;
     v[i] = (e < E) ? z[e] : -INFINITY;
-    taken[i] = (e >= E);
+    ev[i] = (e < E) ? e : 0x7fffffff;
     mx = fmaxf(mx, v[i]);
   }
   mx = wave_max(mx);
@@ -136,8 +138,10 @@ __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E,
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-      int e = lane + 64 * i;
-      if (!taken[i] && topk_better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+      // topk_better without short-circuit evaluation (no exec-mask branches)
+      const bool better = (v[i] > bv) | ((v[i] == bv) & (ev[i] < bi));
+      bv = better ? v[i] : bv;
+      bi = better ? ev[i] : bi;
     }
     // wave arg-max under the same order: the largest value, then the lowest index among
     // the lanes holding it (a single holder, the usual case, is read from its lane)
@@ -148,8 +152,11 @@ __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E,
     else
       bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
 #pragma unroll
-    for (int i = 0; i < PL; ++i)
-      if (lane + 64 * i == bi) taken[i] = true;
+    for (int i = 0; i < PL; ++i) {
+      const bool hit = ev[i] == bi;
+      v[i] = hit ? -INFINITY : v[i];
+      ev[i] = hit ? 0x7fffffff : ev[i];
+    }
     if (k <= 64) {
       if (lane == j) { my_idx = bi; my_v = wv; }
     } else if (lane == 0) {  // more than one selection per lane: written as found
