@@ -1067,6 +1067,12 @@ void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_group
   }
 }
 
+// Whether phase 2 (alone or with the combine) reads the bf16 copy of h: the bf16 dot
+// kernels, chosen exactly as in p2_dispatch (T <= 4 takes M <= 4) and by the combine.
+bool decode_phase2_reads_h16(int wfmt, int I, int T, int k) {
+  return wfmt != MOE_WFMT_F32 && lane_chunks(wfmt, I) == 1 && T * k <= 64 && T <= 4;
+}
+
 template <int W, int M>
 static void p2_dispatch(const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm) {
   dim3 grid(decode_phase2_rowblocks(a.H), max_groups);

@@ -39,8 +39,8 @@ __global__ __launch_bounds__(256) void fill_pull_kernel(FillArgs a) {
       a.dstats[D_CPU] += (uint64_t)a.cnt[C_CPU];
       a.dstats[D_EVICT] += (uint64_t)a.cnt[C_EVICT];
       const uint64_t ngrp = (uint64_t)a.cnt[C_NGRP], npair = (uint64_t)a.cnt[C_NPAIR_GPU];
-      a.dstats[D_P1_BYTES] += ngrp * a.p1_grp + a.p1_fixed + npair * a.pair_bytes;
-      a.dstats[D_P2_BYTES] += ngrp * a.p2_grp + a.p2_fixed + npair * a.pair_bytes;
+      a.dstats[D_P1_BYTES] += ngrp * a.p1_grp + a.p1_fixed + npair * a.p1_pair;
+      a.dstats[D_P2_BYTES] += ngrp * a.p2_grp + a.p2_fixed + npair * a.p2_pair;
     }
   }
   if (err || f >= nfill) return;

@@ -128,8 +128,8 @@ struct FillArgs {
   int64_t rec_bytes;
   uint64_t* dstats;          // [D_COUNT] accumulated step counts, or nullptr
   // algorithmic bytes of the step's GEMV phases (zero unless profiling):
-  // phase 1 = groups * p1_grp + p1_fixed + gpu pairs * pair_bytes, phase 2 likewise
-  uint64_t p1_grp, p1_fixed, p2_grp, p2_fixed, pair_bytes;
+  // phase 1 = groups * p1_grp + p1_fixed + gpu pairs * p1_pair, phase 2 likewise
+  uint64_t p1_grp, p1_fixed, p2_grp, p2_fixed, p1_pair, p2_pair;
 };
 
 struct PrefillArgs {
@@ -169,6 +169,7 @@ struct Timing {
 void launch_decode_phase1(int wfmt, int afmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 void launch_decode_phase2(int wfmt, const DecodeArgs& a, int max_groups, hipStream_t s, Timing tm = {});
 bool decode_phase1_routed_ok(int wfmt, int afmt, int H, int k);
+bool decode_phase2_reads_h16(int wfmt, int I, int T, int k);
 bool launch_decode_phase2_combine(int wfmt, const DecodeArgs& a, hipStream_t s, Timing tm = {});
 bool launch_decode_phase1_routed(int wfmt, int afmt, const DecodeArgs& a, hipStream_t s, Timing tm = {});
 int decode_phase2_rowblocks(int H);

@@ -884,8 +884,10 @@ MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, 
         const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
         ctx->stats.phase1_launches += 1;
         ctx->stats.phase2_launches += 1;
-        ctx->stats.phase1_bytes += (uint64_t)k * 2 * I * wrow_h + (uint64_t)H * act_bytes(ctx->cfg) + (uint64_t)k * I * 4;
-        ctx->stats.phase2_bytes += (uint64_t)k * H * wrow_i + (uint64_t)k * I * 4 + (uint64_t)H * 4;
+        // h out as fp32 and bf16 (6 bytes a value); phase 2 reads one of them
+        const uint64_t h_in = decode_phase2_reads_h16(ctx->cfg.wfmt, I, 1, k) ? 2 : 4;
+        ctx->stats.phase1_bytes += (uint64_t)k * 2 * I * wrow_h + (uint64_t)H * act_bytes(ctx->cfg) + (uint64_t)k * I * 6;
+        ctx->stats.phase2_bytes += (uint64_t)k * H * wrow_i + (uint64_t)k * I * h_in + (uint64_t)H * 4;
       }
       ctx->stats.lookups += 1;
       ctx->stats.hits += k;
@@ -996,7 +998,8 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     f.p1_fixed = dprof ? (uint64_t)T * H * act_bytes(ctx->cfg) : 0;
     f.p2_grp = dprof ? (uint64_t)H * wrow_i : 0;
     f.p2_fixed = dprof ? (uint64_t)T * H * 4 : 0;
-    f.pair_bytes = dprof ? (uint64_t)I * 4 : 0;
+    f.p1_pair = dprof ? (uint64_t)I * 6 : 0;  // h out, fp32 and bf16
+    f.p2_pair = dprof ? (uint64_t)I * (decode_phase2_reads_h16(ctx->cfg.wfmt, I, T, k) ? 2 : 4) : 0;
     TimedScope tf(ctx, s, log_rec >= 0 ? TK_FILL : -1, false, log_rec);
     launch_fill_pull(f, max_groups, s, tf.tm);
   } else if (!fused) {
@@ -1044,11 +1047,12 @@ MOE_API moe_status moe_ffn_decode(moe_ctx* ctx, int32_t layer, const void* x, in
     const int64_t wrow_h = weight_row_bytes(ctx->cfg, H), wrow_i = weight_row_bytes(ctx->cfg, I);
     ctx->stats.phase1_launches += 1;
     ctx->stats.phase2_launches += 1;
-    // algorithmic bytes: the GPU experts' gate+up rows, x once, h out / down rows, h in, y out
-    ctx->stats.phase1_bytes += (uint64_t)ngrp * 2 * I * wrow_h + (uint64_t)T * H * act_bytes(ctx->cfg) +
-                               (uint64_t)ctx->h_cnt[C_NPAIR_GPU] * I * 4;
-    ctx->stats.phase2_bytes += (uint64_t)ngrp * H * wrow_i + (uint64_t)ctx->h_cnt[C_NPAIR_GPU] * I * 4 +
-                               (uint64_t)T * H * 4;
+    // algorithmic bytes: the GPU experts' gate+up rows, x once, h out (fp32 and bf16) / down
+    // rows, h in (the copy phase 2 reads), y out
+    const uint64_t npair = (uint64_t)ctx->h_cnt[C_NPAIR_GPU];
+    const uint64_t h_in = decode_phase2_reads_h16(ctx->cfg.wfmt, I, T, k) ? 2 : 4;
+    ctx->stats.phase1_bytes += (uint64_t)ngrp * 2 * I * wrow_h + (uint64_t)T * H * act_bytes(ctx->cfg) + npair * I * 6;
+    ctx->stats.phase2_bytes += (uint64_t)ngrp * H * wrow_i + npair * I * h_in + (uint64_t)T * H * 4;
   }
   ctx->stats.decode_calls += 1;
   ctx->last_lookup_layer = -1;
