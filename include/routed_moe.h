@@ -70,6 +70,26 @@ typedef enum {
 typedef enum { MOE_AFMT_F32 = 0, MOE_AFMT_BF16 = 1 } moe_afmt;
 
 /*
+ * Arithmetic and the intermediates rounded to 16 bits (every rounding is to nearest even;
+ * accumulation is fp32 everywhere):
+ *  decode gate/up: bf16 activations with bf16 / FP4 / MXFP4 weights multiply exactly
+ *    (v_dot2_f32_bf16; e2m1 codes become bf16 exactly, a bf16 block scale multiplies the fp32
+ *    block sum, an E8M0 scale is applied exactly by the convert); other combinations in fp32.
+ *  decode down projection: with bf16 / FP4 / MXFP4 weights, the SwiGLU intermediate h is
+ *    rounded to bf16 when a row of W_down is one 16-byte load per lane (inter = 2048 for e2m1
+ *    rows, 512 for bf16), T <= 4 and T*k <= 64; otherwise, and with fp32 weights, h stays fp32.
+ *  prefill, FP4 / MXFP4 weights: activations become f16, each weight (code x block scale)
+ *    is formed in f16, h is stored as f16 between the two GEMMs (f16 MFMA, fp32 accumulate).
+ *    These are exact only while the values lie in f16's normal range (magnitudes in
+ *    [2^-14, 65504]): larger ones overflow and smaller ones lose bits, with no error
+ *    reported, so FP4 pools with block scales, or activations, outside that range need the
+ *    bf16 format.  bf16 weights: bf16 activations and weights, h stored as bf16.  fp32
+ *    weights: fp32 throughout.
+ *  CPU branch: fp32 throughout (h is not rounded), so a HYBRID step's CPU and GPU experts
+ *    can differ in the last bits of h's rounding.
+ */
+
+/*
  * Backend modes ([FT-KR] usage section: --moe-backend fused|offload|cpu|hybrid):
  *  FUSED   every record is resident; slot = key; no cache.
  *  OFFLOAD LRU cache; every miss is filled over PCIe (capped by evictable slots).
