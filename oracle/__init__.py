@@ -29,6 +29,7 @@ from .qstar import MODE_FUSED, MODE_OFFLOAD, MODE_CPU, MODE_HYBRID, qstar_split,
 from .cache import (ExpertCache, NaiveListCache, LookupResult, KIND_HIT, KIND_FILL, KIND_CPU, KIND_BUF)
 from .ffn import silu, expert_ffn, moe_combine, moe_layer_dense
 from .layer import OracleMoE
+from .mx import e4m3_decode, mxfp8_quantize, mxfp8_dequant, mxfp8_round, expert_ffn_mx
 from .placement import (POLICY_LRU, POLICY_PREFILL, POLICY_STATIC, POLICY_PINNED_RING, replay as placement_replay,
                         routing_counts, top_keys, static_resident)
 
@@ -38,6 +39,7 @@ __all__ = [
     "MODE_FUSED", "MODE_OFFLOAD", "MODE_CPU", "MODE_HYBRID", "qstar_split", "qstar_real",
     "ExpertCache", "NaiveListCache", "LookupResult", "KIND_HIT", "KIND_FILL", "KIND_CPU", "KIND_BUF",
     "silu", "expert_ffn", "moe_combine", "moe_layer_dense", "OracleMoE",
+    "e4m3_decode", "mxfp8_quantize", "mxfp8_dequant", "mxfp8_round", "expert_ffn_mx",
     "POLICY_LRU", "POLICY_PREFILL", "POLICY_STATIC", "POLICY_PINNED_RING", "placement_replay",
     "routing_counts", "top_keys", "static_resident",
 ]
