@@ -78,6 +78,7 @@ def parse():
 
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 / fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA (the MX prefill's fp8 x fp4 products)
 
 
 def log(*a):
@@ -407,10 +408,13 @@ def run_workload(args, config, primary):
         R.moe_set_mode(ctx, R.MOE_MODE_OFFLOAD)
 
     # ---------------------------------------------------------------- prefill leg
-    prefill = None
-    if not args.no_prefill and mode != R.MOE_MODE_FUSED:
-        Tp = cfg.max_tokens
-        R.moe_reset_stats(ctx)
+    # The prompt through every layer: route, whole layers double-buffered from the pool,
+    # the grouped GEMMs.  MXFP4 experts also run it on a second context with the MX prefill
+    # (MXFP8 activations on the scaled MFMA), over the same pool; its MFMA fraction is
+    # against the fp8 peak.
+    def prefill_leg(c):
+        Tp = max_tokens
+        R.moe_reset_stats(c)
         xs = [torch.from_numpy(wl.prefill_activations(l, Tp).view(np.int16)).to(dev) for l in range(L)]
         pb = torch.from_numpy(np.stack([wl.zipf_bias(l) for l in range(L)])).to(dev)
         pidx = torch.empty((Tp, k), dtype=torch.int32, device=dev)
@@ -419,28 +423,48 @@ def run_workload(args, config, primary):
         pbias = torch.empty((Tp, E), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         t2 = time.perf_counter()
-        R.moe_prefill_begin(ctx, stream)
+        R.moe_prefill_begin(c, stream)
         for l in range(L):
             pbias.copy_(pb[l].expand(Tp, E))
-            R.moe_route(ctx, l, xs[l], Tp, pbias, None, pidx, pw, stream)
-            R.moe_ffn_prefill(ctx, l, xs[l], Tp, pidx, pw, py, None, None, stream)
-        R.moe_prefill_end(ctx, stream)
+            R.moe_route(c, l, xs[l], Tp, pbias, None, pidx, pw, stream)
+            R.moe_ffn_prefill(c, l, xs[l], Tp, pidx, pw, py, None, None, stream)
+        R.moe_prefill_end(c, stream)
         torch.cuda.synchronize()
         pel = time.perf_counter() - t2
-        ps = R.moe_get_stats(ctx)
+        ps = R.moe_get_stats(c)
         gemm_ms = ps["gemm1_ms"] + ps["gemm2_ms"]
         tflops = ps["gemm_flops"] / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
-        prefill = {
+        return {
             "tokens": Tp, "tokens_per_s": round(Tp / pel, 1), "wall_s": round(pel, 3),
             "copy_GBps": round(ps["copy_bytes"] / (ps["copy_ms"] * 1e-3) / 1e9, 2) if ps["copy_ms"] > 0 else None,
             "copy_bytes": ps["copy_bytes"], "copy_ms_per_layer": round(ps["copy_ms"] / L, 3),
             "gemm_ms_per_layer": round(gemm_ms / L, 3),
             "gemm1_ms_per_layer": round(ps["gemm1_ms"] / L, 3), "gemm2_ms_per_layer": round(ps["gemm2_ms"] / L, 3),
-            "gemm_TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "gemm_TFLOPs": round(tflops, 1),
             "gemm_weight_GBps": round(E * S / (gemm_ms / L * 1e-3) / 1e9, 1) if gemm_ms > 0 else None,
             "overlap": round(max(0.0, (ps["copy_ms"] + gemm_ms - pel * 1e3) / max(1e-9, min(ps["copy_ms"], gemm_ms))), 3),
         }
+
+    prefill = None
+    prefill_mx = None
+    if not args.no_prefill and mode != R.MOE_MODE_FUSED:
+        prefill = prefill_leg(ctx)
+        prefill["mfma_frac"] = round(prefill["gemm_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
         log(f"[{config}] prefill: {prefill}")
+        if wl.wfmt == W.WFMT_MXFP4:
+            cfg_m = R.make_config(L, E, k, H, wl.inter, wl.wfmt, wl.afmt, max_tokens, mode, wl.renorm,
+                                  cpu_threads=args.cpu_threads, flags=R.MOE_FLAG_PROFILE | R.MOE_FLAG_MX_PREFILL)
+            ctx_m = R.moe_create(cfg_m)
+            R.moe_pool_register(ctx_m, pool, wl.pool_records, 1)
+            arena_m = torch.empty((2 * E + 1) * S, dtype=torch.uint8, device=dev)
+            R.moe_bind(ctx_m, router, arena_m, arena_m.numel(), 2 * E + 1)
+            prefill_mx = prefill_leg(ctx_m)
+            prefill_mx["activations"] = "MXFP8 (E4M3, E8M0 per 32)"
+            prefill_mx["mfma_frac_fp8_peak"] = round(prefill_mx["gemm_TFLOPs"] / PEAK_FP8_TFLOPS, 4)
+            log(f"[{config}] prefill (MX): {prefill_mx}")
+            R.moe_destroy(ctx_m)
+            del arena_m
+            torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- elastic leg
     # The batch-4 hybrid run of the elastic configuration on the same pool: four
@@ -562,6 +586,7 @@ def run_workload(args, config, primary):
         "fused_decode": fused,
         "elastic_hybrid_batch4": elastic,
         "prefill": prefill,
+        "prefill_mx": prefill_mx,
         "hbm_ceiling": hbm,
     }
     R.moe_destroy(ctx)

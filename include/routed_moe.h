@@ -106,6 +106,16 @@ typedef enum { MOE_KIND_HIT = 0, MOE_KIND_FILL = 1, MOE_KIND_CPU = 2, MOE_KIND_B
  * its device mapping; captured steps hand their CPU branch to a library thread, so replay
  * has no host node (see moe_ffn_decode). */
 #define MOE_FLAG_DEVICE_FILLS 2
+/* MXFP4 experts only (else moe_create returns MOE_ENOTSUP): the prefill GEMMs on the GPU take
+ * their activation operands in MXFP8 and multiply them with the weights' e2m1 codes and E8M0
+ * scales as stored (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation).  The pages
+ * leave the activation format open ([FT-KR] "실험 환경" serves the experts in MXFP4); the
+ * conversion is that of the OCP Microscaling v1.0 specification: 32-element blocks along the
+ * reduction dimension, E8M0 scale 2^(floor(log2 max|v|) - 8) (clamped to [-127, 127]; -127 for
+ * a block of zeros), E4M3 elements rounded to nearest even and saturated at 448; the SwiGLU
+ * intermediate is converted from its fp32 value.  Decode and experts a CPU or HYBRID prefill
+ * round sends to the host keep their own arithmetic. */
+#define MOE_FLAG_MX_PREFILL 4
 
 typedef struct {
   int32_t n_layers, n_experts, top_k, hidden, inter; /* L, E, k, H, I */

@@ -23,6 +23,7 @@ MOE_MODE_FUSED, MOE_MODE_OFFLOAD, MOE_MODE_CPU, MOE_MODE_HYBRID = 0, 1, 2, 3
 MOE_KIND_HIT, MOE_KIND_FILL, MOE_KIND_CPU, MOE_KIND_BUF = 0, 1, 2, 3
 MOE_FLAG_PROFILE = 1
 MOE_FLAG_DEVICE_FILLS = 2
+MOE_FLAG_MX_PREFILL = 4
 
 _STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ENOMEM", -3: "MOE_EHIP", -4: "MOE_ESTATE",
            -5: "MOE_ENOPIN", -6: "MOE_ENOTSUP", -7: "MOE_ETIMEDOUT"}

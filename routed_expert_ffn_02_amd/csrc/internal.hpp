@@ -134,7 +134,9 @@ struct FillArgs {
 
 struct PrefillArgs {
   const void* x;             // [T,H] afmt
-  const void* xa;            // [T,H] 16-bit MFMA operands (x itself, or its converted copy)
+  const void* xa;            // [T,H] 16-bit MFMA operands (x itself, or its converted copy);
+                             // MX prefill: E4M3 codes
+  const uint8_t* xs;         // MX prefill: E8M0 scales of xa [T, H/32]
   const float* w;            // [T,k]
   const uint8_t* arena;
   int64_t rec_bytes;
@@ -145,7 +147,8 @@ struct PrefillArgs {
   const int32_t* offsets;    // [G+1]
   const int32_t* tile_base;  // [G+1] cumulative m-tiles
   const int32_t* cnt;        // C_NGRP, C_NPAIR_GPU
-  void* act;                 // [P, I] bf16/f16 (sorted order)
+  void* act;                 // [P, I] bf16/f16 (sorted order); MX prefill: E4M3 codes
+  uint8_t* acts;             // MX prefill: E8M0 scales of act [P, I/32]
   float* ypair;              // [P, H] fp32 (sorted order)
   float* y;                  // [T, H]
   const float* y_cpu;        // [T, H] or nullptr
@@ -226,6 +229,11 @@ bool prefill_needs_act_operands(int wfmt, int afmt);
 void launch_act_operands(int wfmt, int afmt, const void* x, void* xo, int64_t n, hipStream_t s);
 void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
 void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
+// MX prefill of MXFP4 experts: activations to MXFP8 (codes [T,H], scales [T,H/32]) and the
+// scaled-MFMA GEMMs (a.xa / a.xs in, a.act / a.acts between them)
+void launch_mx_quant(int afmt, const void* x, uint8_t* codes, uint8_t* scales, int64_t n, hipStream_t s);
+void launch_prefill_gemm1_mx(const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
+void launch_prefill_gemm2_mx(const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
 void launch_prefill_combine(const PrefillArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- CPU branch

@@ -908,6 +908,340 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// MX prefill of MXFP4 experts (opt-in): the activation operand of each GEMM in MXFP8 (E4M3
+// elements, one E8M0 scale per 32 along k) meets the weights' e2m1 codes and E8M0 scales as
+// stored in v_mfma_scale_f32_32x32x64_f8f6f4 (32 x 32 outputs over 64 k, fp32 accumulation;
+// no dequantising instructions).  The instruction's operand layout (measured on gfx950):
+// lane l holds row (A) / column (B) l % 32; A bytes 0-15 are k = 16 (l / 32) + j and bytes
+// 16-31 are k = 32 + 16 (l / 32) + j; B codes (16 bytes, low nibble first) are
+// k = 32 (l / 32) + j; lane l supplies the E8M0 scale of its row / column for the 32-k block
+// l / 32.  The accumulator layout is that of the 32 x 32 f16 MFMA (frag_row).
+//
+// The conversion to MXFP8 (OCP Microscaling v1.0): a block's scale is 2^s with
+// s = floor(log2 max|v|) - 8, clamped to [-127, 127] (-127 for a block of zeros or of
+// fp32 subnormals); each element v / 2^s goes to the nearest E4M3 value, ties to the even
+// code, magnitudes beyond 448 saturating.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  return ef == 0 ? -127 : max(-127, min(127, ef - 127 - 8));
+}
+
+// fp32 -> E4M3 code (see above); NaN -> 0x7F
+__device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fabsf(q);
+  uint32_t code;
+  if (a != a) {
+    code = 0x7Fu;
+  } else if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (8 is the smallest normal, code 0x08)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;  // -6 .. 8
+    uint32_t m = (uint32_t)__builtin_rintf((ldexpf(a, -e) - 1.0f) * 8.0f);
+    if (m == 8) {
+      m = 0;
+      ++e;
+    }
+    code = ((uint32_t)(e + 7) << 3) | m;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
+// Activations [T, H] (afmt) -> E4M3 codes [T, H] and E8M0 scales [T, H / 32]: one thread
+// per 32-element block.
+template <int AFMT>
+__global__ __launch_bounds__(256) void mx_quant_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  float v[32];
+  if constexpr (AFMT == MOE_AFMT_BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + 32 * b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 w = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * q + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + 32 * b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 w = p[q];
+      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const int s = mx_scale_exp(amax);
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    w[q] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[q] |= f32_to_e4m3(ldexpf(v[4 * q + j], -s)) << (8 * j);
+  }
+  u32x4* o = reinterpret_cast<u32x4*>(codes + 32 * b);
+  o[0] = u32x4{w[0], w[1], w[2], w[3]};
+  o[1] = u32x4{w[4], w[5], w[6], w[7]};
+  scales[b] = (uint8_t)(s + 127);
+}
+
+constexpr int MX_AW = F4_KS + 16;  // padded activation row (bytes): conflict-free 16-byte reads
+
+struct MxChunk {
+  u32x4 a[4];   // activation piece i: tile row (tid >> 4) + 16 i, 16 bytes at (tid & 15) * 16
+  u32x4 b[8];   // code piece j: block row (tid >> 3) + 32 j, 16 bytes at (tid & 7) * 16
+  uint32_t s;   // activation scales (tid < 128): tile row tid >> 1, blocks 4 (tid & 1) .. + 3
+};
+
+struct MxSrc {
+  const uint8_t* a;    // activation codes (uniform)
+  uint32_t aoff[4];    // byte offset of activation piece i at k = 0
+  uint32_t arow;       // bytes per activation row (K)
+  const uint8_t* as;   // activation scales (uniform)
+  uint32_t asoff;      // byte offset of this thread's scale word at k = 0
+  const uint8_t* b;    // expert record (uniform)
+  uint32_t boff[2];    // byte offset of code piece 0 (rows < 128) and piece 4 (rows >= 128) at k = 0
+  int64_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
+};
+
+template <int MR>
+__device__ __forceinline__ void mx_issue(MxChunk& st, const MxSrc& src, int c) {
+#pragma unroll
+  for (int i = 0; i < 2 * MR; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(src.a + c * F4_KS + src.aoff[i]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint8_t* bb = src.b + (j & 3) * src.bstep + c * (F4_KS / 2);
+    st.b[j] = *reinterpret_cast<const u32x4*>(bb + src.boff[j >> 2]);
+  }
+  if (threadIdx.x < 64 * MR) st.s = *reinterpret_cast<const uint32_t*>(src.as + c * (F4_KS / 32) + src.asoff);
+}
+
+template <int MR>
+__device__ __forceinline__ void mx_store(const MxChunk& st, uint8_t (*sA)[MX_AW], uint8_t (*sAs)[8],
+                                         uint8_t (*sB)[F4_BP], int tid) {
+#pragma unroll
+  for (int i = 0; i < 2 * MR; ++i) *reinterpret_cast<u32x4*>(&sA[(tid >> 4) + 16 * i][(tid & 15) * 16]) = st.a[i];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 3) + 32 * j][(tid & 7) * 16]) = st.b[j];
+  if (tid < 64 * MR) *reinterpret_cast<uint32_t*>(&sAs[tid >> 1][4 * (tid & 1)]) = st.s;
+}
+
+__device__ __forceinline__ f32x16 mfma_mx(const u32x4& alo, const u32x4& ahi, const u32x4& b, uint32_t sa,
+                                          uint32_t sb, const f32x16& c) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const v8i av = {(int)alo[0], (int)alo[1], (int)alo[2], (int)alo[3], (int)ahi[0], (int)ahi[1], (int)ahi[2], (int)ahi[3]};
+  const v8i bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  // A: E4M3 (format 0), B: e2m1 (format 4); each scale in byte 0 of its operand
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// One 256-k chunk: four 64-k steps; for step u the lane's weight scales are bytes 2u + h of
+// the chunk's eight (one E8M0 byte per 32-k block), its activation scales bytes 2u + h of
+// its tile row's.
+template <int MR>
+__device__ __forceinline__ void mx_compute(const uint8_t (*sA)[MX_AW], const uint8_t (*sAs)[8],
+                                           const uint8_t (*sB)[F4_BP], int rb0, int rb1, const u32x4& q0,
+                                           const u32x4& q1, int lane, f32x16 (&acc)[MR][2]) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const u32x4 b0 = *reinterpret_cast<const u32x4*>(&sB[rb0 + r][32 * u + 16 * h]);
+    const u32x4 b1 = *reinterpret_cast<const u32x4*>(&sB[rb1 + r][32 * u + 16 * h]);
+    const int sh = 8 * ((2 * u + h) & 3);
+    const uint32_t s0 = (q0[u >> 1] >> sh) & 0xffu, s1 = (q1[u >> 1] >> sh) & 0xffu;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const u32x4 alo = *reinterpret_cast<const u32x4*>(&sA[32 * m + r][64 * u + 16 * h]);
+      const u32x4 ahi = *reinterpret_cast<const u32x4*>(&sA[32 * m + r][64 * u + 32 + 16 * h]);
+      const uint32_t sa = sAs[32 * m + r][2 * u + h];
+      acc[m][0] = mfma_mx(alo, ahi, b0, sa, s0, acc[m][0]);
+      acc[m][1] = mfma_mx(alo, ahi, b1, sa, s1, acc[m][1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one step's LDS operands live at a time
+  }
+}
+
+// The k loop over nc = K / 256 chunks (the structure of f4_kloop); rb0 / rb1: the
+// wavefront's two 32-row weight fragments in the block's LDS rows; sc0 / sc1: byte offsets
+// of their E8M0 scale rows.  Refills past the end re-read the last chunk (in bounds, unused).
+template <int MR>
+__device__ __forceinline__ void mx_kloop(int nc, const MxSrc& src, uint32_t sc0, uint32_t sc1, uint8_t (*sA)[MX_AW],
+                                         uint8_t (*sAs)[8], uint8_t (*sB)[F4_BP], int rb0, int rb1, int tid,
+                                         f32x16 (&acc)[MR][2]) {
+  const int lane = tid & 63;
+  MxChunk N;
+  mx_issue<MR>(N, src, 0);
+  u32x4 q0 = f4_scales<true>(src.b, sc0, 0), q1 = f4_scales<true>(src.b, sc1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mx_store<MR>(N, sA, sAs, sB, tid);
+  u32x4 c0 = q0, c1 = q1;
+  __syncthreads();
+  mx_issue<MR>(N, src, min(1, nc - 1));
+  q0 = f4_scales<true>(src.b, sc0, min(1, nc - 1));
+  q1 = f4_scales<true>(src.b, sc1, min(1, nc - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c = 0; c < nc; ++c) {
+    mx_compute<MR>(sA, sAs, sB, rb0, rb1, c0, c1, lane, acc);
+    __syncthreads();  // every wavefront is done with chunk c
+    mx_store<MR>(N, sA, sAs, sB, tid);
+    c0 = q0;
+    c1 = q1;
+    __syncthreads();
+    mx_issue<MR>(N, src, min(c + 2, nc - 1));
+    q0 = f4_scales<true>(src.b, sc0, min(c + 2, nc - 1));
+    q1 = f4_scales<true>(src.b, sc1, min(c + 2, nc - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Activation sources of a tile: piece i of thread tid is tile row (tid >> 4) + 16 i (row 0
+// of the tile for rows past its end), the scale word tile row tid >> 1.
+template <int MR>
+__device__ __forceinline__ void mx_rows(MxSrc& src, const TileInfo& ti, int tid, bool gather, const PrefillArgs& a,
+                                        uint32_t K) {
+  auto row_of = [&](int r) -> uint32_t {
+    const int rr = r < ti.rows ? r : 0;
+    return gather ? (uint32_t)(a.perm[ti.row0 + rr] / a.k) : (uint32_t)(ti.row0 + rr);
+  };
+  src.arow = K;
+#pragma unroll
+  for (int i = 0; i < 2 * MR; ++i) src.aoff[i] = row_of((tid >> 4) + 16 * i) * K + (uint32_t)(tid & 15) * 16u;
+  src.asoff = row_of((tid >> 1) & 63) * (K / 32) + 4u * (uint32_t)(tid & 1);
+}
+
+// GEMM1 (MX): act columns n0 .. n0 + 127 of the tile as MXFP8 (codes + one scale per 32
+// columns, the wavefront's own 32); block rows 0..127 gate rows n0.., 128..255 up.
+template <int MR>
+__device__ __forceinline__ void gemm1_mx_tile(const PrefillArgs& a, const TileInfo& ti, uint8_t (*sA)[MX_AW],
+                                              uint8_t (*sAs)[8], uint8_t (*sB)[F4_BP]) {
+  const int H = a.H, I = a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = ti.nt * 128;
+  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const int64_t n = (int64_t)H * I;
+  MxSrc src;
+  src.a = reinterpret_cast<const uint8_t*>(a.xa);
+  src.as = a.xs;
+  mx_rows<MR>(src, ti, tid, true, a, (uint32_t)H);
+  src.b = rec;
+  src.boff[0] = (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(H / 2) + (uint32_t)(tid & 7) * 16u;
+  src.boff[1] = src.boff[0] + (uint32_t)(n / 2);
+  src.bstep = (int64_t)32 * (H / 2);
+  const int col = n0 + wave * 32 + (lane & 31);
+  // record: gate, up, down codes (n / 2 bytes each), then E8M0 scales (n / 32 each)
+  const uint32_t sc_g = (uint32_t)(3 * (n / 2)) + (uint32_t)col * (uint32_t)(H / 32);
+  const uint32_t sc_u = sc_g + (uint32_t)(n / 32);
+  f32x16 acc[MR][2];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
+  mx_kloop<MR>(H / F4_KS, src, sc_g, sc_u, sA, sAs, sB, wave * 32, 128 + wave * 32, tid, acc);
+
+  // SwiGLU in fp32, then MXFP8 over each row's 32 columns (held by the 32 lanes of a half)
+  uint8_t* act = reinterpret_cast<uint8_t*>(a.act);
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      const float g = acc[m][0][i];
+      const float v = g * __frcp_rn(1.0f + __expf(-g)) * acc[m][1][i];
+      float am = fabsf(v);
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) am = fmaxf(am, __shfl_xor(am, d));
+      const int s = mx_scale_exp(am);
+      const uint32_t code = f32_to_e4m3(ldexpf(v, -s));
+      if (r < ti.rows) {
+        act[(int64_t)(ti.row0 + r) * I + col] = (uint8_t)code;
+        if ((lane & 31) == 0) a.acts[(int64_t)(ti.row0 + r) * (I / 32) + (col >> 5)] = (uint8_t)(s + 127);
+      }
+    }
+  }
+}
+
+// GEMM2 (MX): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64 of them.
+template <int MR>
+__device__ __forceinline__ void gemm2_mx_tile(const PrefillArgs& a, const TileInfo& ti, uint8_t (*sA)[MX_AW],
+                                              uint8_t (*sAs)[8], uint8_t (*sB)[F4_BP]) {
+  const int H = a.H, I = a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = ti.nt * 256;
+  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const int64_t n = (int64_t)H * I;
+  MxSrc src;
+  src.a = reinterpret_cast<const uint8_t*>(a.act);
+  src.as = a.acts;
+  mx_rows<MR>(src, ti, tid, false, a, (uint32_t)I);
+  src.b = rec;
+  src.boff[0] = (uint32_t)n + (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(I / 2) + (uint32_t)(tid & 7) * 16u;
+  src.boff[1] = src.boff[0] + 128u * (uint32_t)(I / 2);
+  src.bstep = (int64_t)32 * (I / 2);
+  const int c0 = n0 + wave * 64 + (lane & 31);
+  const uint32_t sc0 = (uint32_t)(3 * (n / 2)) + 2u * (uint32_t)(n / 32) + (uint32_t)c0 * (uint32_t)(I / 32);
+  const uint32_t sc1 = sc0 + 32u * (uint32_t)(I / 32);
+  f32x16 acc[MR][2];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
+  mx_kloop<MR>(I / F4_KS, src, sc0, sc1, sA, sAs, sB, wave * 64, wave * 64 + 32, tid, acc);
+
+  int pr[MR][16];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      pr[m][i] = a.perm[ti.row0 + (r < ti.rows ? r : 0)];
+    }
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      if (r < ti.rows) {
+        float* dst = a.ypair + (int64_t)pr[m][i] * H;
+        dst[c0] = acc[m][0][i];
+        dst[c0 + 32] = acc[m][1][i];
+      }
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void gemm1_mx_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[64][MX_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sAs[64][8];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
+  TileInfo ti;
+  if (!decode_tile(a, a.I / 128, ti)) return;
+  if (ti.rows <= 32) gemm1_mx_tile<1>(a, ti, sA, sAs, sB);
+  else gemm1_mx_tile<2>(a, ti, sA, sAs, sB);
+}
+
+__global__ __launch_bounds__(256, 2) void gemm2_mx_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[64][MX_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sAs[64][8];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
+  TileInfo ti;
+  if (!decode_tile(a, a.H / 256, ti)) return;
+  if (ti.rows <= 32) gemm2_mx_tile<1>(a, ti, sA, sAs, sB);
+  else gemm2_mx_tile<2>(a, ti, sA, sAs, sB);
+}
+
+// ---------------------------------------------------------------------------
 // Activations -> 16-bit MFMA operands, once per call (FP4 weights take f16, bf16
 // weights bf16).  Same rounding as an in-GEMM conversion (round to nearest even).
 template <int AFMT, bool TO_F16>
@@ -1018,6 +1352,21 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
   else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm1_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
   else if (fp4_staged(a)) launch_timed(gemm1_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm1_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
+}
+
+void launch_mx_quant(int afmt, const void* x, uint8_t* codes, uint8_t* scales, int64_t n, hipStream_t s) {
+  const int64_t nb = n / 32;
+  const dim3 grid((unsigned)((nb + 255) / 256));
+  if (afmt == MOE_AFMT_BF16) hipLaunchKernelGGL(mx_quant_kernel<MOE_AFMT_BF16>, grid, dim3(256), 0, s, x, codes, scales, nb);
+  else hipLaunchKernelGGL(mx_quant_kernel<MOE_AFMT_F32>, grid, dim3(256), 0, s, x, codes, scales, nb);
+}
+
+void launch_prefill_gemm1_mx(const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
+  launch_timed(gemm1_mx_kernel, dim3(padded_grid(max_tiles_m, a.I / 128)), dim3(256), 0, s, tm, a);
+}
+
+void launch_prefill_gemm2_mx(const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
+  launch_timed(gemm2_mx_kernel, dim3(padded_grid(max_tiles_m, a.H / 256)), dim3(256), 0, s, tm, a);
 }
 
 void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {

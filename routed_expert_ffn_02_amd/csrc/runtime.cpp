@@ -501,6 +501,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       (int64_t)c.max_tokens * c.top_k > (1 << 22))
     return MOE_EINVAL;
   // MXFP4 runs the LDS-staged prefill GEMMs only: 256-k chunks, 32-bit byte offsets
+  if ((c.flags & MOE_FLAG_MX_PREFILL) && c.wfmt != MOE_WFMT_MXFP4) return MOE_ENOTSUP;
   if (c.wfmt == MOE_WFMT_MXFP4 &&
       (c.hidden % 256 || c.inter % 256 || (int64_t)c.max_tokens * c.hidden >= (1ll << 31) ||
        (int64_t)c.max_tokens * c.top_k * c.inter >= (1ll << 31) || record_bytes(c) >= (1ll << 32)))
@@ -1071,7 +1072,16 @@ moe_status prefill_gpu_part(moe_ctx* ctx, const void* x, int T, const float* w, 
   PrefillArgs a;
   a.x = x;
   a.xa = x;
-  if (prefill_needs_act_operands(ctx->cfg.wfmt, ctx->cfg.afmt)) {
+  a.xs = nullptr;
+  a.acts = nullptr;
+  // MX prefill: activations as MXFP8 codes (xo) with their scales after them
+  const bool mx = (ctx->cfg.flags & MOE_FLAG_MX_PREFILL) != 0;
+  if (mx) {
+    uint8_t* codes = reinterpret_cast<uint8_t*>(ctx->xo);
+    launch_mx_quant(ctx->cfg.afmt, x, codes, codes + (int64_t)T * H, (int64_t)T * H, s);
+    a.xa = codes;
+    a.xs = codes + (int64_t)T * H;
+  } else if (prefill_needs_act_operands(ctx->cfg.wfmt, ctx->cfg.afmt)) {
     launch_act_operands(ctx->cfg.wfmt, ctx->cfg.afmt, x, ctx->xo, (int64_t)T * H, s);
     a.xa = ctx->xo;
   }
@@ -1090,6 +1100,7 @@ moe_status prefill_gpu_part(moe_ctx* ctx, const void* x, int T, const float* w, 
   a.tile_base = ctx->tile_base;
   a.cnt = ctx->cnt;
   a.act = ctx->act;
+  if (mx) a.acts = reinterpret_cast<uint8_t*>(ctx->act) + (int64_t)P * I;
   a.ypair = ctx->ypair;
   a.y = y;
   a.y_cpu = y_cpu;
@@ -1097,11 +1108,13 @@ moe_status prefill_gpu_part(moe_ctx* ctx, const void* x, int T, const float* w, 
   const int max_tiles_m = (P + bm - 1) / bm + std::min(E, P);
   {
     TimedScope t(ctx, s, TK_G1);
-    launch_prefill_gemm1(ctx->cfg.wfmt, ctx->cfg.afmt, a, max_tiles_m, s, t.tm);
+    if (mx) launch_prefill_gemm1_mx(a, max_tiles_m, s, t.tm);
+    else launch_prefill_gemm1(ctx->cfg.wfmt, ctx->cfg.afmt, a, max_tiles_m, s, t.tm);
   }
   {
     TimedScope t(ctx, s, TK_G2);
-    launch_prefill_gemm2(ctx->cfg.wfmt, a, max_tiles_m, s, t.tm);
+    if (mx) launch_prefill_gemm2_mx(a, max_tiles_m, s, t.tm);
+    else launch_prefill_gemm2(ctx->cfg.wfmt, a, max_tiles_m, s, t.tm);
   }
   if (ctx->cfg.flags & MOE_FLAG_PROFILE) {
     ctx->stats.gemm1_launches += 1;

@@ -22,10 +22,13 @@ def row_rel_err(y, ref):
     return float((num / den).max())
 
 
-def oracle_outputs(wl, layer, x_np, idx, threads=None):
+def oracle_outputs(wl, layer, x_np, idx, threads=None, ffn=None):
     """Per-pair expert outputs [T,k,H] (float64) of the oracle's all-resident definition,
     with the distinct experts evaluated in parallel threads (each runs the oracle's own
-    dequantisation and SwiGLU for its rows; numpy releases the GIL in both)."""
+    dequantisation and SwiGLU for its rows; numpy releases the GIL in both).  ffn: the
+    oracle's expert function (default the plain SwiGLU; oracle.expert_ffn_mx for the MX
+    prefill)."""
+    ffn = ffn or oracle.expert_ffn
     x64 = oracle.formats.activations_f64(x_np)
     idx = np.asarray(idx)
     T, k = idx.shape
@@ -34,7 +37,7 @@ def oracle_outputs(wl, layer, x_np, idx, threads=None):
 
     def one(e):
         rows = np.argwhere(idx == e)
-        ys = oracle.expert_ffn(x64[rows[:, 0]], *oracle.expert_weights_f64(wl, layer * wl.n_experts + e))
+        ys = ffn(x64[rows[:, 0]], *oracle.expert_weights_f64(wl, layer * wl.n_experts + e))
         return rows, ys
 
     threads = threads or min(16, len(os.sched_getaffinity(0)))
