@@ -1002,27 +1002,40 @@ struct MxChunk {
   uint32_t s;   // activation scales (tid < 128): tile row tid >> 1, blocks 4 (tid & 1) .. + 3
 };
 
+// Loads go through buffer resources (base and size in scalar registers): a lane's byte
+// offset stays in one VGPR for the whole k loop and the chunk's offset is the scalar offset,
+// so the two register stages share their addressing (no per-piece 64-bit pointers).
 struct MxSrc {
-  const uint8_t* a;    // activation codes (uniform)
+  __amdgpu_buffer_rsrc_t ra;   // activation codes
+  __amdgpu_buffer_rsrc_t ras;  // activation scales
+  __amdgpu_buffer_rsrc_t rb;   // expert record
   uint32_t aoff[4];    // byte offset of activation piece i at k = 0
-  uint32_t arow;       // bytes per activation row (K)
-  const uint8_t* as;   // activation scales (uniform)
   uint32_t asoff;      // byte offset of this thread's scale word at k = 0
-  const uint8_t* b;    // expert record (uniform)
   uint32_t boff[2];    // byte offset of code piece 0 (rows < 128) and piece 4 (rows >= 128) at k = 0
-  int64_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
+  int32_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
 };
+
+// raw buffer over [p, p + 4 GiB): no size check (every offset here is in bounds by
+// construction); the last descriptor word is the gfx9 raw-buffer format word
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
+}
 
 template <int MR>
 __device__ __forceinline__ void mx_issue(MxChunk& st, const MxSrc& src, int c) {
 #pragma unroll
-  for (int i = 0; i < 2 * MR; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(src.a + c * F4_KS + src.aoff[i]);
+  for (int i = 0; i < 2 * MR; ++i) st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.aoff[i], c * F4_KS, 0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint8_t* bb = src.b + (j & 3) * src.bstep + c * (F4_KS / 2);
-    st.b[j] = *reinterpret_cast<const u32x4*>(bb + src.boff[j >> 2]);
-  }
-  if (threadIdx.x < 64 * MR) st.s = *reinterpret_cast<const uint32_t*>(src.as + c * (F4_KS / 32) + src.asoff);
+  for (int j = 0; j < 8; ++j)
+    st.b[j] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.boff[j >> 2], (j & 3) * src.bstep + c * (F4_KS / 2), 0);
+  if (threadIdx.x < 64 * MR) st.s = __builtin_amdgcn_raw_buffer_load_b32(src.ras, src.asoff, c * (F4_KS / 32), 0);
+}
+
+// the eight E8M0 weight scales of a row for chunk c (byte w: 32-k block w of the chunk)
+__device__ __forceinline__ u32x4 mx_wscales(const MxSrc& src, uint32_t soff, int c) {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(src.rb, soff, 8 * c, 0);
+  return u32x4{v[0], v[1], 0u, 0u};
 }
 
 template <int MR>
@@ -1080,14 +1093,14 @@ __device__ __forceinline__ void mx_kloop(int nc, const MxSrc& src, uint32_t sc0,
   const int lane = tid & 63;
   MxChunk N;
   mx_issue<MR>(N, src, 0);
-  u32x4 q0 = f4_scales<true>(src.b, sc0, 0), q1 = f4_scales<true>(src.b, sc1, 0);
+  u32x4 q0 = mx_wscales(src, sc0, 0), q1 = mx_wscales(src, sc1, 0);
   __builtin_amdgcn_sched_barrier(0);
   mx_store<MR>(N, sA, sAs, sB, tid);
   u32x4 c0 = q0, c1 = q1;
   __syncthreads();
   mx_issue<MR>(N, src, min(1, nc - 1));
-  q0 = f4_scales<true>(src.b, sc0, min(1, nc - 1));
-  q1 = f4_scales<true>(src.b, sc1, min(1, nc - 1));
+  q0 = mx_wscales(src, sc0, min(1, nc - 1));
+  q1 = mx_wscales(src, sc1, min(1, nc - 1));
   __builtin_amdgcn_sched_barrier(0);
   for (int c = 0; c < nc; ++c) {
     mx_compute<MR>(sA, sAs, sB, rb0, rb1, c0, c1, lane, acc);
@@ -1097,8 +1110,8 @@ __device__ __forceinline__ void mx_kloop(int nc, const MxSrc& src, uint32_t sc0,
     c1 = q1;
     __syncthreads();
     mx_issue<MR>(N, src, min(c + 2, nc - 1));
-    q0 = f4_scales<true>(src.b, sc0, min(c + 2, nc - 1));
-    q1 = f4_scales<true>(src.b, sc1, min(c + 2, nc - 1));
+    q0 = mx_wscales(src, sc0, min(c + 2, nc - 1));
+    q1 = mx_wscales(src, sc1, min(c + 2, nc - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1112,7 +1125,6 @@ __device__ __forceinline__ void mx_rows(MxSrc& src, const TileInfo& ti, int tid,
     const int rr = r < ti.rows ? r : 0;
     return gather ? (uint32_t)(a.perm[ti.row0 + rr] / a.k) : (uint32_t)(ti.row0 + rr);
   };
-  src.arow = K;
 #pragma unroll
   for (int i = 0; i < 2 * MR; ++i) src.aoff[i] = row_of((tid >> 4) + 16 * i) * K + (uint32_t)(tid & 15) * 16u;
   src.asoff = row_of((tid >> 1) & 63) * (K / 32) + 4u * (uint32_t)(tid & 1);
@@ -1129,13 +1141,13 @@ __device__ __forceinline__ void gemm1_mx_tile(const PrefillArgs& a, const TileIn
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int64_t n = (int64_t)H * I;
   MxSrc src;
-  src.a = reinterpret_cast<const uint8_t*>(a.xa);
-  src.as = a.xs;
+  src.ra = mx_rsrc(a.xa);
+  src.ras = mx_rsrc(a.xs);
   mx_rows<MR>(src, ti, tid, true, a, (uint32_t)H);
-  src.b = rec;
+  src.rb = mx_rsrc(rec);
   src.boff[0] = (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(H / 2) + (uint32_t)(tid & 7) * 16u;
   src.boff[1] = src.boff[0] + (uint32_t)(n / 2);
-  src.bstep = (int64_t)32 * (H / 2);
+  src.bstep = 32 * (H / 2);
   const int col = n0 + wave * 32 + (lane & 31);
   // record: gate, up, down codes (n / 2 bytes each), then E8M0 scales (n / 32 each)
   const uint32_t sc_g = (uint32_t)(3 * (n / 2)) + (uint32_t)col * (uint32_t)(H / 32);
@@ -1181,13 +1193,13 @@ __device__ __forceinline__ void gemm2_mx_tile(const PrefillArgs& a, const TileIn
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int64_t n = (int64_t)H * I;
   MxSrc src;
-  src.a = reinterpret_cast<const uint8_t*>(a.act);
-  src.as = a.acts;
+  src.ra = mx_rsrc(a.act);
+  src.ras = mx_rsrc(a.acts);
   mx_rows<MR>(src, ti, tid, false, a, (uint32_t)I);
-  src.b = rec;
+  src.rb = mx_rsrc(rec);
   src.boff[0] = (uint32_t)n + (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(I / 2) + (uint32_t)(tid & 7) * 16u;
   src.boff[1] = src.boff[0] + 128u * (uint32_t)(I / 2);
-  src.bstep = (int64_t)32 * (I / 2);
+  src.bstep = 32 * (I / 2);
   const int c0 = n0 + wave * 64 + (lane & 31);
   const uint32_t sc0 = (uint32_t)(3 * (n / 2)) + 2u * (uint32_t)(n / 32) + (uint32_t)c0 * (uint32_t)(I / 32);
   const uint32_t sc1 = sc0 + 32u * (uint32_t)(I / 32);
