@@ -629,28 +629,34 @@ struct F4Chunk {
   u32x4 b[8];  // code piece j: block row (tid >> 3) + 32 j, 16 bytes at (tid & 7) * 16
 };
 
-// Per-thread parts are 32-bit byte offsets from wave-uniform bases, so the loads take
-// a scalar base and one VGPR offset each.
+// Loads go through buffer resources (base and size in scalar registers): a lane's byte
+// offset stays in one VGPR for the whole k loop and the chunk's offset is the scalar
+// offset, so the register stages share their addressing (no per-piece 64-bit pointers).
 struct F4Src {
-  const uint8_t* a;    // activation base (uniform)
+  __amdgpu_buffer_rsrc_t ra;  // activations
+  __amdgpu_buffer_rsrc_t rb;  // expert record
   uint32_t aoff[8];    // byte offset of activation piece i at k = 0
-  const uint8_t* b;    // expert record (uniform)
   uint32_t boff[2];    // byte offset of code piece 0 (rows < 128) and piece 4 (rows >= 128) at k = 0
-  int64_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
+  int32_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
 };
+
+// raw buffer over [p, p + 4 GiB): no size check (every offset here is in bounds by
+// construction: records and activation operands stay below 4 GiB, see fp4_staged);
+// the last descriptor word is the gfx9 raw-buffer format word
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
+}
 
 // MR: 32-row activation fragments in the tile (1 for a tile of at most 32 rows, else 2);
 // only their rows are fetched and stored.
 template <int MR>
 __device__ __forceinline__ void f4_issue(F4Chunk& st, const F4Src& src, int c) {
-  const uint8_t* ab = src.a + c * (2 * F4_KS);
 #pragma unroll
-  for (int i = 0; i < 4 * MR; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(ab + src.aoff[i]);
+  for (int i = 0; i < 4 * MR; ++i)
+    st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.aoff[i], c * (2 * F4_KS), 0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint8_t* bb = src.b + (j & 3) * src.bstep + c * (F4_KS / 2);
-    st.b[j] = *reinterpret_cast<const u32x4*>(bb + src.boff[j >> 2]);
-  }
+  for (int j = 0; j < 8; ++j)
+    st.b[j] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.boff[j >> 2], (j & 3) * src.bstep + c * (F4_KS / 2), 0);
 }
 
 template <int MR>
@@ -666,12 +672,12 @@ __device__ __forceinline__ void f4_store(const F4Chunk& st, uint16_t (*sA)[F4_AW
 // its high half half 1.  MXFP4 (MX): 8 E8M0 bytes, byte 2w + h for sub-step w and
 // lane half h (the upper two words of the vector are unused).
 template <bool MX>
-__device__ __forceinline__ u32x4 f4_scales(const uint8_t* rec, uint32_t soff, int c) {
+__device__ __forceinline__ u32x4 f4_scales(__amdgpu_buffer_rsrc_t rec, uint32_t soff, int c) {
   if constexpr (MX) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(rec + 8 * c + soff);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rec, soff, 8 * c, 0);
     return u32x4{v[0], v[1], 0u, 0u};
   } else {
-    return *reinterpret_cast<const u32x4*>(rec + 16 * c + soff);
+    return __builtin_amdgcn_raw_buffer_load_b128(rec, soff, 16 * c, 0);
   }
 }
 
@@ -750,14 +756,14 @@ __device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0,
   F4Chunk N;
   F4Scales sc;
   f4_issue<MR>(N, src, chunk(0));
-  u32x4 q0 = f4_scales<MX>(src.b, sc0, chunk(0)), q1 = f4_scales<MX>(src.b, sc1, chunk(0));
+  u32x4 q0 = f4_scales<MX>(src.rb, sc0, chunk(0)), q1 = f4_scales<MX>(src.rb, sc1, chunk(0));
   __builtin_amdgcn_sched_barrier(0);
   f4_store<MR>(N, sA, sB, tid);
   f4_take<MX>(sc, q0, q1, h);
   __syncthreads();
   f4_issue<MR>(N, src, chunk(1));
-  q0 = f4_scales<MX>(src.b, sc0, chunk(1));
-  q1 = f4_scales<MX>(src.b, sc1, chunk(1));
+  q0 = f4_scales<MX>(src.rb, sc0, chunk(1));
+  q1 = f4_scales<MX>(src.rb, sc1, chunk(1));
   __builtin_amdgcn_sched_barrier(0);
   for (int c = 0; c < nc; ++c) {
     f4_compute<MX, MR>(sA, sB, rb0, rb1, sc, lane, acc);
@@ -766,8 +772,8 @@ __device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0,
     f4_take<MX>(sc, q0, q1, h);
     __syncthreads();
     f4_issue<MR>(N, src, chunk(c + 2));
-    q0 = f4_scales<MX>(src.b, sc0, chunk(c + 2));
-    q1 = f4_scales<MX>(src.b, sc1, chunk(c + 2));
+    q0 = f4_scales<MX>(src.rb, sc0, chunk(c + 2));
+    q1 = f4_scales<MX>(src.rb, sc1, chunk(c + 2));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -786,7 +792,7 @@ __device__ __forceinline__ void gemm1_fp4_tile(const PrefillArgs& a, const TileI
   // record: gate codes, up codes, down codes (n / 2 bytes each), then bf16 scales
 
   F4Src src;
-  src.a = reinterpret_cast<const uint8_t*>(a.xa);
+  src.ra = buf_rsrc(a.xa);
 #pragma unroll
   for (int i = 0; i < 4 * MR; ++i) {
     const int row = (tid >> 5) + 8 * i;
@@ -794,10 +800,10 @@ __device__ __forceinline__ void gemm1_fp4_tile(const PrefillArgs& a, const TileI
     src.aoff[i] = 2u * (tok * (uint32_t)H + (uint32_t)(tid & 31) * 8u);
   }
   // block rows 0..127: gate rows n0.., 128..255: up rows n0..
-  src.b = rec;
+  src.rb = buf_rsrc(rec);
   src.boff[0] = (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(H / 2) + (uint32_t)(tid & 7) * 16u;
   src.boff[1] = src.boff[0] + (uint32_t)(n / 2);
-  src.bstep = (int64_t)32 * (H / 2);
+  src.bstep = 32 * (H / 2);
   const int col = n0 + wave * 32 + (lane & 31);
   const uint32_t sc_g = (uint32_t)(3 * (n / 2)) + SB * (uint32_t)col * (uint32_t)(H / 32);
   const uint32_t sc_u = sc_g + SB * (uint32_t)(n / 32);
@@ -853,16 +859,16 @@ __device__ __forceinline__ void gemm2_fp4_tile(const PrefillArgs& a, const TileI
   // (gate, up, down: n / 32 each)
 
   F4Src src;
-  src.a = reinterpret_cast<const uint8_t*>(a.act);
+  src.ra = buf_rsrc(a.act);
 #pragma unroll
   for (int i = 0; i < 4 * MR; ++i) {
     const int row = (tid >> 5) + 8 * i;
     src.aoff[i] = 2u * ((uint32_t)(ti.row0 + (row < ti.rows ? row : 0)) * (uint32_t)I + (uint32_t)(tid & 31) * 8u);
   }
-  src.b = rec;
+  src.rb = buf_rsrc(rec);
   src.boff[0] = (uint32_t)n + (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(I / 2) + (uint32_t)(tid & 7) * 16u;
   src.boff[1] = src.boff[0] + 128u * (uint32_t)(I / 2);
-  src.bstep = (int64_t)32 * (I / 2);
+  src.bstep = 32 * (I / 2);
   const int c0 = n0 + wave * 64 + (lane & 31);
   const uint32_t sc0 = (uint32_t)(3 * (n / 2)) + SB * 2u * (uint32_t)(n / 32) + SB * (uint32_t)c0 * (uint32_t)(I / 32);
   const uint32_t sc1 = sc0 + SB * 32u * (uint32_t)(I / 32);
@@ -1015,12 +1021,6 @@ struct MxSrc {
   int32_t bstep;       // bytes from code piece j to piece j + 1 (32 rows)
 };
 
-// raw buffer over [p, p + 4 GiB): no size check (every offset here is in bounds by
-// construction); the last descriptor word is the gfx9 raw-buffer format word
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
-}
-
 template <int MR>
 __device__ __forceinline__ void mx_issue(MxChunk& st, const MxSrc& src, int c) {
 #pragma unroll
@@ -1141,10 +1141,10 @@ __device__ __forceinline__ void gemm1_mx_tile(const PrefillArgs& a, const TileIn
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int64_t n = (int64_t)H * I;
   MxSrc src;
-  src.ra = mx_rsrc(a.xa);
-  src.ras = mx_rsrc(a.xs);
+  src.ra = buf_rsrc(a.xa);
+  src.ras = buf_rsrc(a.xs);
   mx_rows<MR>(src, ti, tid, true, a, (uint32_t)H);
-  src.rb = mx_rsrc(rec);
+  src.rb = buf_rsrc(rec);
   src.boff[0] = (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(H / 2) + (uint32_t)(tid & 7) * 16u;
   src.boff[1] = src.boff[0] + (uint32_t)(n / 2);
   src.bstep = 32 * (H / 2);
@@ -1193,10 +1193,10 @@ __device__ __forceinline__ void gemm2_mx_tile(const PrefillArgs& a, const TileIn
   const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
   const int64_t n = (int64_t)H * I;
   MxSrc src;
-  src.ra = mx_rsrc(a.act);
-  src.ras = mx_rsrc(a.acts);
+  src.ra = buf_rsrc(a.act);
+  src.ras = buf_rsrc(a.acts);
   mx_rows<MR>(src, ti, tid, false, a, (uint32_t)I);
-  src.rb = mx_rsrc(rec);
+  src.rb = buf_rsrc(rec);
   src.boff[0] = (uint32_t)n + (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(I / 2) + (uint32_t)(tid & 7) * 16u;
   src.boff[1] = src.boff[0] + 128u * (uint32_t)(I / 2);
   src.bstep = 32 * (I / 2);
