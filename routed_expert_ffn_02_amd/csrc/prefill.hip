@@ -207,12 +207,19 @@ __device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int NT, TileIn
   }
   const int r = bid - a.tile_base[lo] * NT;
   const int mcount = a.tile_base[lo + 1] - a.tile_base[lo];
-  ti.g = lo;
-  ti.nt = r / mcount;
+  // the tile is the workgroup's: say so, so that addresses built from it (buffer
+  // descriptors above all) stay in scalar registers
+  ti.g = __builtin_amdgcn_readfirstlane(lo);
+  ti.nt = __builtin_amdgcn_readfirstlane(r / mcount);
   const int mt = r % mcount;
-  ti.row0 = a.offsets[lo] + mt * BM;
-  ti.rows = min(BM, a.offsets[lo + 1] - ti.row0);
+  ti.row0 = __builtin_amdgcn_readfirstlane(a.offsets[lo] + mt * BM);
+  ti.rows = __builtin_amdgcn_readfirstlane(min(BM, a.offsets[lo + 1] - ti.row0));
   return true;
+}
+
+// The arena record of tile group g (the same for the whole workgroup).
+__device__ __forceinline__ const uint8_t* group_record(const PrefillArgs& a, int g) {
+  return a.arena + (int64_t)__builtin_amdgcn_readfirstlane(a.grp_slot[g]) * a.rec_bytes;
 }
 
 template <bool F16>
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col0 = ti.nt * 128 + wave * 32;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const uint8_t* rec = group_record(a, ti.g);
 
   // A sources: token rows gathered through the permutation.  Rows past the group
   // end read the group's first token; their outputs are never stored.
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = ti.nt * 256 + wave * 64;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const uint8_t* rec = group_record(a, ti.g);
 
   // A sources: sorted act rows (already in the MFMA operand type).
   int64_t a_src[2];
@@ -667,37 +674,82 @@ __device__ __forceinline__ void f4_store(const F4Chunk& st, uint16_t (*sA)[F4_AW
   for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 3) + 32 * j][(tid & 7) * 16]) = st.b[j];
 }
 
-// Scales of one weight row for chunk c: blocks [8c, 8c + 8).  bf16 scales: 16 bytes,
-// word w covers k in [64w, 64w + 64) of the chunk, its low half the lanes of half 0,
-// its high half half 1.  MXFP4 (MX): 8 E8M0 bytes, byte 2w + h for sub-step w and
-// lane half h (the upper two words of the vector are unused).
-template <bool MX>
-__device__ __forceinline__ u32x4 f4_scales(__amdgpu_buffer_rsrc_t rec, uint32_t soff, int c) {
-  if constexpr (MX) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rec, soff, 8 * c, 0);
-    return u32x4{v[0], v[1], 0u, 0u};
-  } else {
-    return __builtin_amdgcn_raw_buffer_load_b128(rec, soff, 16 * c, 0);
+// Block scales of one weight row.  Chunk c holds blocks [8c, 8c + 8): bf16 scales, 16
+// bytes, word w covering k in [64w, 64w + 64) of the chunk with its low half for the lanes
+// of half 0 and its high half for half 1; MXFP4 (MX): 8 E8M0 bytes, byte 2w + h for
+// sub-step w and lane half h.
+//
+// They are fetched G chunks at a time (a segment): lane half h loads chunks Gs + hG/2 ..
+// Gs + hG/2 + G/2 - 1 of its row, keeps the halves it uses and trades the others with the
+// lane 32 away, so a row's scale line is touched once per G chunks.  (Fetched chunk by
+// chunk, each 128-byte line was touched eight times, far enough apart for the weight
+// stream to evict it in between: it came from memory again every time.)  Pieces past the
+// last chunk re-read the last one (in bounds, unused).
+template <bool MX, int G>
+struct F4Seg {  // the pieces in flight: G / 2 chunks (bf16: one vector each; MX: two per vector)
+  u32x4 p[MX ? (G + 3) / 4 : G / 2];
+};
+
+template <bool MX, int G>
+struct F4SegT {  // this lane's scales of the segment's chunks (c' = chunk - Gs)
+  // bf16: t[2c' + (w >> 1)], sub-step w in half w & 1; MX: t[c'], byte w = sub-step w
+  uint32_t t[MX ? G : 2 * G];
+};
+
+template <bool MX, int G>
+__device__ __forceinline__ void f4_seg_load(F4Seg<MX, G>& x, __amdgpu_buffer_rsrc_t rec, uint32_t soff, int s,
+                                            int nc, int h) {
+  static_assert(G == 2 || G == 4, "segments of two or four chunks");
+#pragma unroll
+  for (int q = 0; q < G / 2; ++q) {
+    // the chunk depends on the lane half, so the whole offset is the lane's (a scalar
+    // offset must be the same for every lane)
+    const uint32_t c = (uint32_t)min(G * s + (G / 2) * h + q, nc - 1);
+    if constexpr (MX) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rec, soff + 8u * c, 0, 0);
+      x.p[q >> 1][2 * (q & 1)] = v[0];
+      x.p[q >> 1][2 * (q & 1) + 1] = v[1];
+    } else {
+      x.p[q] = __builtin_amdgcn_raw_buffer_load_b128(rec, soff + 16u * c, 0, 0);
+    }
   }
 }
 
-struct F4Scales {
-  uint32_t w0[4], w1[4];  // this lane's scale of each sub-step for fragments rb0 and rb1 (low bits)
-};
-
-template <bool MX>
-__device__ __forceinline__ void f4_take(F4Scales& s, const u32x4& q0, const u32x4& q1, int h) {
+template <bool MX, int G>
+__device__ __forceinline__ void f4_seg_build(F4SegT<MX, G>& t, const F4Seg<MX, G>& x, int h) {
+  // MX: bytes h and 2 + h of a pair of words (one chunk) -> one word; bf16: the 16-bit
+  // halves h of a pair of words (two sub-steps) -> one word
+  const uint32_t own = MX ? (h ? 0x07050301u : 0x06040200u) : (h ? 0x07060302u : 0x05040100u);
+  const uint32_t other = MX ? (h ? 0x06040200u : 0x07050301u) : (h ? 0x05040100u : 0x07060302u);
+  constexpr int NW = MX ? G / 2 : G;  // words this lane builds from its own pieces
+  uint32_t keep[NW], give[NW];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if constexpr (MX) {
-      const int sh = 8 * (2 * (w & 1) + h);
-      s.w0[w] = (q0[w >> 1] >> sh) & 0xffu;
-      s.w1[w] = (q1[w >> 1] >> sh) & 0xffu;
-    } else {
-      s.w0[w] = q0[w] >> (16 * h);
-      s.w1[w] = q1[w] >> (16 * h);
-    }
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t lo = x.p[i >> 1][2 * (i & 1)], hi = x.p[i >> 1][2 * (i & 1) + 1];
+    keep[i] = __builtin_amdgcn_perm(hi, lo, own);
+    give[i] = __builtin_amdgcn_perm(hi, lo, other);
   }
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t recv = __shfl_xor(give[i], 32);
+    t.t[i] = h ? recv : keep[i];
+    t.t[NW + i] = h ? keep[i] : recv;
+  }
+}
+
+// Advance to the next chunk of the segment.
+template <bool MX, int G>
+__device__ __forceinline__ void f4_seg_next(F4SegT<MX, G>& t) {
+  constexpr int W = MX ? 1 : 2, N = MX ? G : 2 * G;
+#pragma unroll
+  for (int i = 0; i + W < N; ++i) t.t[i] = t.t[i + W];
+}
+
+// This lane's scale of sub-step w in the segment's current chunk (low bits).
+template <bool MX, int G>
+__device__ __forceinline__ uint32_t f4_seg_get(const F4SegT<MX, G>& t, int w) {
+  if constexpr (MX) return (t.t[0] >> (8 * w)) & 0xffu;
+  else return t.t[w >> 1] >> (16 * (w & 1));
 }
 
 // MFMA operands of a run of MXFP4 codes: the convert applies the block's power of
@@ -718,7 +770,8 @@ __device__ __forceinline__ void b_operands_mx(BOps<MOE_WFMT_FP4>& o, const BRun<
 // sub-step (one scale block) and MFMA j its slice [32h + 8j, + 8), in A and B alike.
 template <bool MX, int MR>
 __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const uint8_t (*sB)[F4_BP], int rb0, int rb1,
-                                           const F4Scales& sc, int lane, f32x16 (&acc)[MR][2]) {
+                                           const F4SegT<MX, 4>& t0, const F4SegT<MX, 4>& t1, int lane,
+                                           f32x16 (&acc)[MR][2]) {
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -726,11 +779,11 @@ __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const ui
     const BRun<MOE_WFMT_FP4> c0{*reinterpret_cast<const u32x4*>(&sB[rb0 + r][u * 32 + 16 * h])};
     const BRun<MOE_WFMT_FP4> c1{*reinterpret_cast<const u32x4*>(&sB[rb1 + r][u * 32 + 16 * h])};
     if constexpr (MX) {
-      b_operands_mx(o0, c0, sc.w0[u]);
-      b_operands_mx(o1, c1, sc.w1[u]);
+      b_operands_mx(o0, c0, f4_seg_get<MX, 4>(t0, u));
+      b_operands_mx(o1, c1, f4_seg_get<MX, 4>(t1, u));
     } else {
-      b_operands<MOE_WFMT_FP4>(o0, c0, sc.w0[u]);
-      b_operands<MOE_WFMT_FP4>(o1, c1, sc.w1[u]);
+      b_operands<MOE_WFMT_FP4>(o0, c0, f4_seg_get<MX, 4>(t0, u));
+      b_operands<MOE_WFMT_FP4>(o1, c1, f4_seg_get<MX, 4>(t1, u));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -746,7 +799,9 @@ __device__ __forceinline__ void f4_compute(const uint16_t (*sA)[F4_AW], const ui
 }
 
 // The k loop over nc = K / 256 chunks.  rb0 / rb1: the wavefront's two 32-row weight
-// fragments in the block's LDS rows; sc0 / sc1: byte offsets of their scale rows.
+// fragments in the block's LDS rows; sc0 / sc1: byte offsets of their scale rows.  Scale
+// segments are four chunks long; segment s is requested with the tiles of chunk 4s and
+// unpacked when they are stored.
 template <bool MX, int MR>
 __device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0, uint32_t sc1,
                                          uint16_t (*sA)[F4_AW], uint8_t (*sB)[F4_BP], int rb0, int rb1, int tid,
@@ -754,26 +809,35 @@ __device__ __forceinline__ void f4_kloop(int nc, const F4Src& src, uint32_t sc0,
   const int lane = tid & 63, h = lane >> 5;
   auto chunk = [&](int c) { return min(c, nc - 1); };
   F4Chunk N;
-  F4Scales sc;
+  F4Seg<MX, 4> x0, x1;
+  F4SegT<MX, 4> t0, t1;
   f4_issue<MR>(N, src, chunk(0));
-  u32x4 q0 = f4_scales<MX>(src.rb, sc0, chunk(0)), q1 = f4_scales<MX>(src.rb, sc1, chunk(0));
+  f4_seg_load<MX, 4>(x0, src.rb, sc0, 0, nc, h);
+  f4_seg_load<MX, 4>(x1, src.rb, sc1, 0, nc, h);
   __builtin_amdgcn_sched_barrier(0);
   f4_store<MR>(N, sA, sB, tid);
-  f4_take<MX>(sc, q0, q1, h);
+  f4_seg_build<MX, 4>(t0, x0, h);
+  f4_seg_build<MX, 4>(t1, x1, h);
   __syncthreads();
   f4_issue<MR>(N, src, chunk(1));
-  q0 = f4_scales<MX>(src.rb, sc0, chunk(1));
-  q1 = f4_scales<MX>(src.rb, sc1, chunk(1));
   __builtin_amdgcn_sched_barrier(0);
   for (int c = 0; c < nc; ++c) {
-    f4_compute<MX, MR>(sA, sB, rb0, rb1, sc, lane, acc);
+    f4_compute<MX, MR>(sA, sB, rb0, rb1, t0, t1, lane, acc);
     __syncthreads();  // every wavefront is done with chunk c
     f4_store<MR>(N, sA, sB, tid);
-    f4_take<MX>(sc, q0, q1, h);
+    if (((c + 1) & 3) == 0) {
+      f4_seg_build<MX, 4>(t0, x0, h);
+      f4_seg_build<MX, 4>(t1, x1, h);
+    } else {
+      f4_seg_next<MX, 4>(t0);
+      f4_seg_next<MX, 4>(t1);
+    }
     __syncthreads();
     f4_issue<MR>(N, src, chunk(c + 2));
-    q0 = f4_scales<MX>(src.rb, sc0, chunk(c + 2));
-    q1 = f4_scales<MX>(src.rb, sc1, chunk(c + 2));
+    if (((c + 2) & 3) == 0) {
+      f4_seg_load<MX, 4>(x0, src.rb, sc0, (c + 2) >> 2, nc, h);
+      f4_seg_load<MX, 4>(x1, src.rb, sc1, (c + 2) >> 2, nc, h);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -787,7 +851,7 @@ __device__ __forceinline__ void gemm1_fp4_tile(const PrefillArgs& a, const TileI
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = ti.nt * 128;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const uint8_t* rec = group_record(a, ti.g);
   const int64_t n = (int64_t)H * I;
   // record: gate codes, up codes, down codes (n / 2 bytes each), then bf16 scales
 
@@ -853,7 +917,7 @@ __device__ __forceinline__ void gemm2_fp4_tile(const PrefillArgs& a, const TileI
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = ti.nt * 256;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const uint8_t* rec = group_record(a, ti.g);
   const int64_t n = (int64_t)H * I;
   // record: gate codes, up codes, down codes (n / 2 bytes each), then bf16 scales
   // (gate, up, down: n / 32 each)
@@ -1031,13 +1095,6 @@ __device__ __forceinline__ void mx_issue(MxChunk& st, const MxSrc& src, int c) {
   if (threadIdx.x < 64 * MR) st.s = __builtin_amdgcn_raw_buffer_load_b32(src.ras, src.asoff, c * (F4_KS / 32), 0);
 }
 
-// the eight E8M0 weight scales of a row for chunk c (byte w: 32-k block w of the chunk)
-__device__ __forceinline__ u32x4 mx_wscales(const MxSrc& src, uint32_t soff, int c) {
-  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-  const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(src.rb, soff, 8 * c, 0);
-  return u32x4{v[0], v[1], 0u, 0u};
-}
-
 template <int MR>
 __device__ __forceinline__ void mx_store(const MxChunk& st, uint8_t (*sA)[MX_AW], uint8_t (*sAs)[8],
                                          uint8_t (*sB)[F4_BP], int tid) {
@@ -1062,15 +1119,14 @@ __device__ __forceinline__ f32x16 mfma_mx(const u32x4& alo, const u32x4& ahi, co
 // its tile row's.
 template <int MR>
 __device__ __forceinline__ void mx_compute(const uint8_t (*sA)[MX_AW], const uint8_t (*sAs)[8],
-                                           const uint8_t (*sB)[F4_BP], int rb0, int rb1, const u32x4& q0,
-                                           const u32x4& q1, int lane, f32x16 (&acc)[MR][2]) {
+                                           const uint8_t (*sB)[F4_BP], int rb0, int rb1, const F4SegT<true, 2>& t0,
+                                           const F4SegT<true, 2>& t1, int lane, f32x16 (&acc)[MR][2]) {
   const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const u32x4 b0 = *reinterpret_cast<const u32x4*>(&sB[rb0 + r][32 * u + 16 * h]);
     const u32x4 b1 = *reinterpret_cast<const u32x4*>(&sB[rb1 + r][32 * u + 16 * h]);
-    const int sh = 8 * ((2 * u + h) & 3);
-    const uint32_t s0 = (q0[u >> 1] >> sh) & 0xffu, s1 = (q1[u >> 1] >> sh) & 0xffu;
+    const uint32_t s0 = f4_seg_get<true, 2>(t0, u), s1 = f4_seg_get<true, 2>(t1, u);
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       const u32x4 alo = *reinterpret_cast<const u32x4*>(&sA[32 * m + r][64 * u + 16 * h]);
@@ -1083,35 +1139,45 @@ __device__ __forceinline__ void mx_compute(const uint8_t (*sA)[MX_AW], const uin
   }
 }
 
-// The k loop over nc = K / 256 chunks (the structure of f4_kloop); rb0 / rb1: the
-// wavefront's two 32-row weight fragments in the block's LDS rows; sc0 / sc1: byte offsets
-// of their E8M0 scale rows.  Refills past the end re-read the last chunk (in bounds, unused).
+// The k loop over nc = K / 256 chunks (the structure of f4_kloop, weight scales fetched
+// in two-chunk segments: four would not fit the registers); rb0 / rb1: the wavefront's two 32-row weight fragments
+// in the block's LDS rows; sc0 / sc1: byte offsets of their E8M0 scale rows.  Refills past
+// the end re-read the last chunk (in bounds, unused).
 template <int MR>
 __device__ __forceinline__ void mx_kloop(int nc, const MxSrc& src, uint32_t sc0, uint32_t sc1, uint8_t (*sA)[MX_AW],
                                          uint8_t (*sAs)[8], uint8_t (*sB)[F4_BP], int rb0, int rb1, int tid,
                                          f32x16 (&acc)[MR][2]) {
-  const int lane = tid & 63;
+  const int lane = tid & 63, h = lane >> 5;
   MxChunk N;
+  F4Seg<true, 2> x0, x1;
+  F4SegT<true, 2> t0, t1;
   mx_issue<MR>(N, src, 0);
-  u32x4 q0 = mx_wscales(src, sc0, 0), q1 = mx_wscales(src, sc1, 0);
+  f4_seg_load<true, 2>(x0, src.rb, sc0, 0, nc, h);
+  f4_seg_load<true, 2>(x1, src.rb, sc1, 0, nc, h);
   __builtin_amdgcn_sched_barrier(0);
   mx_store<MR>(N, sA, sAs, sB, tid);
-  u32x4 c0 = q0, c1 = q1;
+  f4_seg_build<true, 2>(t0, x0, h);
+  f4_seg_build<true, 2>(t1, x1, h);
   __syncthreads();
   mx_issue<MR>(N, src, min(1, nc - 1));
-  q0 = mx_wscales(src, sc0, min(1, nc - 1));
-  q1 = mx_wscales(src, sc1, min(1, nc - 1));
   __builtin_amdgcn_sched_barrier(0);
   for (int c = 0; c < nc; ++c) {
-    mx_compute<MR>(sA, sAs, sB, rb0, rb1, c0, c1, lane, acc);
+    mx_compute<MR>(sA, sAs, sB, rb0, rb1, t0, t1, lane, acc);
     __syncthreads();  // every wavefront is done with chunk c
     mx_store<MR>(N, sA, sAs, sB, tid);
-    c0 = q0;
-    c1 = q1;
+    if (((c + 1) & 1) == 0) {
+      f4_seg_build<true, 2>(t0, x0, h);
+      f4_seg_build<true, 2>(t1, x1, h);
+    } else {
+      f4_seg_next<true, 2>(t0);
+      f4_seg_next<true, 2>(t1);
+    }
     __syncthreads();
     mx_issue<MR>(N, src, min(c + 2, nc - 1));
-    q0 = mx_wscales(src, sc0, min(c + 2, nc - 1));
-    q1 = mx_wscales(src, sc1, min(c + 2, nc - 1));
+    if (((c + 2) & 1) == 0) {
+      f4_seg_load<true, 2>(x0, src.rb, sc0, (c + 2) >> 1, nc, h);
+      f4_seg_load<true, 2>(x1, src.rb, sc1, (c + 2) >> 1, nc, h);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1138,7 +1204,7 @@ __device__ __forceinline__ void gemm1_mx_tile(const PrefillArgs& a, const TileIn
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = ti.nt * 128;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const uint8_t* rec = group_record(a, ti.g);
   const int64_t n = (int64_t)H * I;
   MxSrc src;
   src.ra = buf_rsrc(a.xa);
@@ -1190,7 +1256,7 @@ __device__ __forceinline__ void gemm2_mx_tile(const PrefillArgs& a, const TileIn
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = ti.nt * 256;
-  const uint8_t* rec = a.arena + (int64_t)a.grp_slot[ti.g] * a.rec_bytes;
+  const uint8_t* rec = group_record(a, ti.g);
   const int64_t n = (int64_t)H * I;
   MxSrc src;
   src.ra = buf_rsrc(a.act);
