@@ -442,6 +442,10 @@ def run_workload(args, config, primary):
             "gemm1_ms_per_layer": round(ps["gemm1_ms"] / L, 3), "gemm2_ms_per_layer": round(ps["gemm2_ms"] / L, 3),
             "gemm_TFLOPs": round(tflops, 1),
             "gemm_weight_GBps": round(E * S / (gemm_ms / L * 1e-3) / 1e9, 1) if gemm_ms > 0 else None,
+            # every record of the layer is read once per layer: below 2.5 PFLOP/s / 8 TB/s =
+            # 312 flop per byte the GEMMs are bound by HBM, and this is their roofline fraction
+            "gemm_flop_per_byte": round(ps["gemm_flops"] / L / (E * S), 1) if gemm_ms > 0 else None,
+            "hbm_frac": round(E * S / (gemm_ms / L * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if gemm_ms > 0 else None,
             "overlap": round(max(0.0, (ps["copy_ms"] + gemm_ms - pel * 1e3) / max(1e-9, min(ps["copy_ms"], gemm_ms))), 3),
         }
 
