@@ -146,6 +146,8 @@ struct PrefillArgs {
   const int32_t* inv;        // [P] pair -> sorted position or -1
   const int32_t* offsets;    // [G+1]
   const int32_t* tile_base;  // [G+1] cumulative m-tiles
+  const int4* tiles1;        // GEMM1's tile per workgroup (group, first row, rows, column tile); rows 0: none
+  const int4* tiles2;        // GEMM2's
   const int32_t* cnt;        // C_NGRP, C_NPAIR_GPU
   void* act;                 // [P, I] bf16/f16 (sorted order); MX prefill: E4M3 codes
   uint8_t* acts;             // MX prefill: E8M0 scales of act [P, I/32]
@@ -225,6 +227,12 @@ void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp,
                               int32_t* scratch_flags, int n_slot_range, int gmax, int32_t* n_groups_out,
                               hipStream_t s);
 int prefill_bm();
+// Workgroups (table entries) of a GEMM launch over at most max_tiles_m row tiles of nt
+// column tiles each.
+int prefill_tile_slots(int max_tiles_m, int nt);
+struct PrefillArgs;
+// Both GEMMs' tile tables (a.tiles1, a.tiles2) from the permutation's counts.
+void launch_tile_tables(const PrefillArgs& a, int wfmt, bool mx, int max_tiles_m, hipStream_t s);
 bool prefill_needs_act_operands(int wfmt, int afmt);
 void launch_act_operands(int wfmt, int afmt, const void* x, void* xo, int64_t n, hipStream_t s);
 void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm = {});
@@ -319,6 +327,8 @@ struct moe_ctx {
   float* y_cpu_dev = nullptr;    // [max_tokens*H]
   // prefill scratch (device, sized for max_tokens)
   int32_t *perm = nullptr, *inv = nullptr, *offsets = nullptr, *tile_base = nullptr, *hist = nullptr;
+  int4* tiles = nullptr;         // the GEMMs' tile tables (GEMM1's, then GEMM2's)
+  int64_t tiles1_max = 0;        // entries reserved for GEMM1's
   int32_t* cand = nullptr;       // [E]
   void* act = nullptr;
   void* xo = nullptr;        // [max_tokens, H] 16-bit MFMA operands of the prefill activations

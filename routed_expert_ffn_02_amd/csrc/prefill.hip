@@ -180,40 +180,140 @@ void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp,
 }
 
 // ---------------------------------------------------------------------------
-// Tile decode shared by both GEMMs: returns false when the block has no tile.
+// Tile tables.  A GEMM's tiles are (group, column tile, row tile) in that order, so the row
+// tiles of one group's column block (which read the same weights) are adjacent; workgroup b
+// runs on XCD b % 8, and XCD x takes a contiguous range of that order, so those tiles share
+// one XCD's L2.  The ranges are split by estimated cost rather than by count: in the FP4
+// kernels with f16 operands a tile of at most BM / 2 rows (one 32-row fragment per
+// wavefront) takes about three quarters of the time of a full one, and with the uneven
+// groups of a prompt an equal-count split left some XCDs a sixth longer than others (the
+// bf16 kernels have no such tiles, and in the MX kernels the fragments' MFMAs are too cheap
+// to matter: there every tile counts the same).  One small kernel writes, for every workgroup of both
+// GEMMs' launches, its tile (or none), so a GEMM workgroup starts with one load instead of a
+// binary search over the groups.
 struct TileInfo {
   int g, row0, rows, nt;
 };
 
-__device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int NT, TileInfo& ti) {
-  const int ngrp = a.cnt[C_NGRP];
-  if (ngrp <= 0) return false;
-  // The grid is sized for the most tiles a call can have; the real count is only
-  // known here.  Blocks go to the 8 XCDs round-robin (block b to XCD b % 8), so
-  // spread the real tiles evenly: XCD x takes the contiguous range
-  // [x * per, (x + 1) * per), which keeps one group's tiles (and their shared
-  // activation rows) in one XCD's L2.  Blocks beyond the real work exit at once.
-  const int total = a.tile_base[ngrp] * NT;
-  const int per = (total + 7) >> 3;
-  const int i = blockIdx.x >> 3;
-  if (i >= per) return false;
-  const int bid = (blockIdx.x & 7) * per + i;
-  if (bid >= total) return false;
-  int lo = 0, hi = ngrp - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.tile_base[mid] * NT <= bid) lo = mid;
-    else hi = mid - 1;
+constexpr int kTileCostFull = 4;
+
+int prefill_tile_slots(int max_tiles_m, int nt) {
+  // per XCD: at most total / 6 + 2 tiles under the cost split (every tile costs at least 3 of
+  // at most 4 per tile on average), and total <= max_tiles_m * nt
+  return 8 * (int)(((int64_t)max_tiles_m * nt + 5) / 6 + 2);
+}
+
+__device__ void tile_table(int ngrp, const int* s_tb, const int* s_off, const int* s_uc, int bm, int NT, int n,
+                           int4* __restrict__ table, int* s_first) {
+  const int tid = threadIdx.x;
+  const int total = ngrp > 0 ? s_tb[ngrp] * NT : 0;
+  // first tile of XCD x: the first whose cost prefix reaches x / 8 of the total cost
+  if (tid <= 8) {
+    int b = 0;
+    if (tid == 8) {
+      b = total;
+    } else if (tid > 0 && total > 0) {
+      const int64_t target = (int64_t)s_uc[ngrp] * NT * tid / 8;
+      int lo = 0, hi = ngrp - 1;  // last group whose cost prefix is <= target
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)s_uc[mid] * NT <= target) lo = mid;
+        else hi = mid - 1;
+      }
+      const int mcount = s_tb[lo + 1] - s_tb[lo];
+      const int uc = s_uc[lo + 1] - s_uc[lo];  // cost of one column tile of group lo
+      const int64_t rem = target - (int64_t)s_uc[lo] * NT;
+      int nt = (int)(rem / uc);
+      int mt = (int)((rem - (int64_t)nt * uc + kTileCostFull - 1) / kTileCostFull);
+      if (mt >= mcount) {
+        ++nt;
+        mt = 0;
+      }
+      b = min(total, s_tb[lo] * NT + nt * mcount + mt);
+    }
+    s_first[tid] = b;
   }
-  const int r = bid - a.tile_base[lo] * NT;
-  const int mcount = a.tile_base[lo + 1] - a.tile_base[lo];
-  // the tile is the workgroup's: say so, so that addresses built from it (buffer
-  // descriptors above all) stay in scalar registers
-  ti.g = __builtin_amdgcn_readfirstlane(lo);
-  ti.nt = __builtin_amdgcn_readfirstlane(r / mcount);
-  const int mt = r % mcount;
-  ti.row0 = __builtin_amdgcn_readfirstlane(a.offsets[lo] + mt * BM);
-  ti.rows = __builtin_amdgcn_readfirstlane(min(BM, a.offsets[lo + 1] - ti.row0));
+  __syncthreads();
+  // a split that would not fit the launch's n / 8 workgroups per XCD falls back to equal
+  // counts (which always fit)
+  bool fits = true;
+  for (int x = 0; x < 8; ++x) fits &= s_first[x + 1] - s_first[x] <= n / 8;
+  __syncthreads();
+  if (!fits && tid <= 8) s_first[tid] = (int)((int64_t)total * tid / 8);
+  __syncthreads();
+  for (int e = tid; e < n; e += blockDim.x) {
+    const int x = e & 7, b = s_first[x] + (e >> 3);
+    int4 t = {0, 0, 0, 0};
+    if (b < s_first[x + 1]) {
+      int lo = 0, hi = ngrp - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tb[mid] * NT <= b) lo = mid;
+        else hi = mid - 1;
+      }
+      const int r = b - s_tb[lo] * NT, mcount = s_tb[lo + 1] - s_tb[lo];
+      const int mt = r % mcount;
+      const int row0 = s_off[lo] + mt * bm;
+      t = int4{lo, row0, min(bm, s_off[lo + 1] - row0), r / mcount};
+    }
+    table[e] = t;
+  }
+}
+
+// One workgroup of 1024 threads; groups <= 1024 (one per thread in the scans).
+__global__ __launch_bounds__(1024) void tile_tables_kernel(const int32_t* __restrict__ cnt,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ tile_base, int bm,
+                                                           int half_cost, int nt1, int n1, int4* __restrict__ t1,
+                                                           int nt2, int n2, int4* __restrict__ t2) {
+  __shared__ int s_tb[kMaxExperts + 1], s_off[kMaxExperts + 1], s_uc[kMaxExperts + 1];
+  __shared__ int s_tmp[64], s_first[9];
+  const int ngrp = min(cnt[C_NGRP], kMaxExperts);
+  const int g = threadIdx.x;
+  int uc = 0;  // cost of one column tile of group g: its row tiles
+  for (int i = g; i <= ngrp; i += blockDim.x) {
+    s_tb[i] = tile_base[i];
+    s_off[i] = offsets[i];
+  }
+  if (g < ngrp) {
+    const int rows = offsets[g + 1] - offsets[g];
+    const int mcount = tile_base[g + 1] - tile_base[g];
+    if (mcount > 0) {
+      const int last = rows - bm * (mcount - 1);
+      uc = kTileCostFull * (mcount - 1) + (2 * last <= bm ? half_cost : kTileCostFull);
+    }
+  }
+  int tot;
+  const int pre = block_excl_scan(uc, s_tmp, &tot);
+  if (g < ngrp) s_uc[g] = pre;
+  if (g == 0 && ngrp >= 0) s_uc[ngrp] = tot;
+  __syncthreads();
+  tile_table(ngrp, s_tb, s_off, s_uc, bm, nt1, n1, t1, s_first);
+  __syncthreads();
+  tile_table(ngrp, s_tb, s_off, s_uc, bm, nt2, n2, t2, s_first);
+}
+
+bool fp4_staged(const PrefillArgs& a);
+
+void launch_tile_tables(const PrefillArgs& a, int wfmt, bool mx, int max_tiles_m, hipStream_t s) {
+  const bool f16_fp4 = !mx && (wfmt == MOE_WFMT_FP4 || wfmt == MOE_WFMT_MXFP4) && fp4_staged(a);
+  const int nt1 = a.I / 128, nt2 = a.H / 256;
+  hipLaunchKernelGGL(tile_tables_kernel, dim3(1), dim3(1024), 0, s, a.cnt, a.offsets, a.tile_base, BM,
+                     f16_fp4 ? 3 : kTileCostFull, nt1, prefill_tile_slots(max_tiles_m, nt1),
+                     const_cast<int4*>(a.tiles1), nt2, prefill_tile_slots(max_tiles_m, nt2),
+                     const_cast<int4*>(a.tiles2));
+}
+
+// The workgroup's tile from its GEMM's table; false when it has none.  The fields are the
+// workgroup's: marked uniform, so addresses built from them (buffer descriptors above all)
+// stay in scalar registers.
+__device__ __forceinline__ bool decode_tile(const int4* table, TileInfo& ti) {
+  const int4 t = table[blockIdx.x];
+  if (t.z <= 0) return false;
+  ti.g = __builtin_amdgcn_readfirstlane(t.x);
+  ti.row0 = __builtin_amdgcn_readfirstlane(t.y);
+  ti.rows = __builtin_amdgcn_readfirstlane(t.z);
+  ti.nt = __builtin_amdgcn_readfirstlane(t.w);
   return true;
 }
 
@@ -508,7 +608,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
   constexpr bool F16 = (WFMT == MOE_WFMT_FP4);
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDSW];
   TileInfo ti;
-  if (!decode_tile(a, a.I / 128, ti)) return;
+  if (!decode_tile(a.tiles1, ti)) return;
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col0 = ti.nt * 128 + wave * 32;
@@ -563,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
   constexpr bool F16 = (WFMT == MOE_WFMT_FP4);
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDSW];
   TileInfo ti;
-  if (!decode_tile(a, a.H / 256, ti)) return;
+  if (!decode_tile(a.tiles2, ti)) return;
   const int H = a.H, I = a.I;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = ti.nt * 256 + wave * 64;
@@ -903,7 +1003,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_fp4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
-  if (!decode_tile(a, a.I / 128, ti)) return;
+  if (!decode_tile(a.tiles1, ti)) return;
   if (ti.rows <= 32) gemm1_fp4_tile<MX, 1>(a, ti, sA, sB);
   else gemm1_fp4_tile<MX, 2>(a, ti, sA, sB);
 }
@@ -972,7 +1072,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][F4_AW];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
-  if (!decode_tile(a, a.H / 256, ti)) return;
+  if (!decode_tile(a.tiles2, ti)) return;
   if (ti.rows <= 32) gemm2_fp4_tile<MX, 1>(a, ti, sA, sB);
   else gemm2_fp4_tile<MX, 2>(a, ti, sA, sB);
 }
@@ -1304,7 +1404,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_mx_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sAs[64][8];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
-  if (!decode_tile(a, a.I / 128, ti)) return;
+  if (!decode_tile(a.tiles1, ti)) return;
   if (ti.rows <= 32) gemm1_mx_tile<1>(a, ti, sA, sAs, sB);
   else gemm1_mx_tile<2>(a, ti, sA, sAs, sB);
 }
@@ -1314,7 +1414,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_mx_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t sAs[64][8];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
-  if (!decode_tile(a, a.H / 256, ti)) return;
+  if (!decode_tile(a.tiles2, ti)) return;
   if (ti.rows <= 32) gemm2_mx_tile<1>(a, ti, sA, sAs, sB);
   else gemm2_mx_tile<2>(a, ti, sA, sAs, sB);
 }
@@ -1412,10 +1512,6 @@ bool fp4_staged(const PrefillArgs& a) {
          (int64_t)a.T * a.k * a.I < (1ll << 31) && a.rec_bytes < (1ll << 32);
 }
 
-static int padded_grid(int tiles_m, int nt) {
-  int n = tiles_m * nt;
-  return ((n + 7) / 8) * 8;
-}
 
 void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
   if (wfmt == MOE_WFMT_F32) {
@@ -1425,7 +1521,7 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
     else launch_timed(gemm1_f32_kernel<MOE_AFMT_F32>, grid, dim3(256), 0, s, tm, a);
     return;
   }
-  const dim3 grid(padded_grid(max_tiles_m, a.I / 128));
+  const dim3 grid(prefill_tile_slots(max_tiles_m, a.I / 128));
   if (wfmt == MOE_WFMT_BF16) launch_timed(gemm1_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
   else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm1_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
   else if (fp4_staged(a)) launch_timed(gemm1_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
@@ -1440,11 +1536,11 @@ void launch_mx_quant(int afmt, const void* x, uint8_t* codes, uint8_t* scales, i
 }
 
 void launch_prefill_gemm1_mx(const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
-  launch_timed(gemm1_mx_kernel, dim3(padded_grid(max_tiles_m, a.I / 128)), dim3(256), 0, s, tm, a);
+  launch_timed(gemm1_mx_kernel, dim3(prefill_tile_slots(max_tiles_m, a.I / 128)), dim3(256), 0, s, tm, a);
 }
 
 void launch_prefill_gemm2_mx(const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
-  launch_timed(gemm2_mx_kernel, dim3(padded_grid(max_tiles_m, a.H / 256)), dim3(256), 0, s, tm, a);
+  launch_timed(gemm2_mx_kernel, dim3(prefill_tile_slots(max_tiles_m, a.H / 256)), dim3(256), 0, s, tm, a);
 }
 
 void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
@@ -1453,7 +1549,7 @@ void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipSt
     launch_timed(gemm2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tm, a);
     return;
   }
-  const dim3 grid(padded_grid(max_tiles_m, a.H / 256));
+  const dim3 grid(prefill_tile_slots(max_tiles_m, a.H / 256));
   if (wfmt == MOE_WFMT_BF16) launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
   else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm2_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
   else if (fp4_staged(a)) launch_timed(gemm2_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);

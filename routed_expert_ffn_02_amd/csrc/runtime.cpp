@@ -46,6 +46,15 @@ moe_status fail(moe_ctx* c, moe_status st, const std::string& msg) {
     if (!(cond)) return fail(ctx, MOE_EINVAL, msg); \
   } while (0)
 
+// Entries of both GEMMs' tile tables for up to Pmax prefill pairs (sets ctx->tiles1_max).
+int64_t prefill_tables_max(moe_ctx* ctx, int64_t Pmax) {
+  const moe_config& c = ctx->cfg;
+  const int bm = prefill_bm();
+  const int max_tiles_m = (int)((Pmax + bm - 1) / bm + std::min<int64_t>(c.n_experts, Pmax));
+  ctx->tiles1_max = prefill_tile_slots(max_tiles_m, c.inter / 128);
+  return ctx->tiles1_max + prefill_tile_slots(max_tiles_m, c.hidden / 256);
+}
+
 int64_t record_bytes(const moe_config& c) {
   const int64_t n = (int64_t)c.hidden * c.inter;
   switch (c.wfmt) {
@@ -530,6 +539,7 @@ MOE_API moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       dev_alloc(&ctx->y_cpu_dev, (size_t)c.max_tokens * H) || dev_alloc(&ctx->perm, Pmax) ||
       dev_alloc(&ctx->inv, Pmax) || dev_alloc(&ctx->offsets, std::max<int64_t>(E, Pmax) + 1) ||
       dev_alloc(&ctx->tile_base, std::max<int64_t>(E, Pmax) + 1) ||
+      dev_alloc(&ctx->tiles, prefill_tables_max(ctx, Pmax)) ||
       dev_alloc(&ctx->hist, (size_t)((Pmax + 255) / 256) * kMaxExperts) || dev_alloc(&ctx->cand, E) ||
       dev_alloc(reinterpret_cast<uint8_t**>(&ctx->act), (size_t)Pmax * I * 4) ||
       dev_alloc(&ctx->ypair, (size_t)Pmax * H) || dev_alloc(&ctx->flags, std::max<int64_t>((int64_t)L * E, kMaxCachedSlots)) ||
@@ -622,7 +632,7 @@ MOE_API moe_status moe_destroy(moe_ctx* ctx) {
   for (auto e : ctx->event_pool) hipEventDestroy(e);
   void* dev[] = {ctx->slot_of, ctx->key_of, ctx->stamp, ctx->reserved, ctx->counter, ctx->step_dev,
                  ctx->u_slot, ctx->u_evict, ctx->grp_slot, ctx->grp_pair0, ctx->slot_scratch, ctx->pair_grp, ctx->logits, ctx->h, ctx->h16, ctx->dpair, ctx->y_cpu_dev,
-                 ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
+                 ctx->perm, ctx->inv, ctx->offsets, ctx->tile_base, ctx->tiles, ctx->hist, ctx->cand, ctx->act, ctx->ypair,
                  ctx->flags, ctx->xo, ctx->dstats, ctx->ctrl, ctx->seq_dev};
   for (void* p : dev)
     if (p) hipFree(p);
@@ -1099,13 +1109,16 @@ moe_status prefill_gpu_part(moe_ctx* ctx, const void* x, int T, const float* w, 
   a.offsets = ctx->offsets;
   a.tile_base = ctx->tile_base;
   a.cnt = ctx->cnt;
+  const int max_tiles_m = (P + bm - 1) / bm + std::min(E, P);
+  a.tiles1 = ctx->tiles;
+  a.tiles2 = ctx->tiles + ctx->tiles1_max;
+  if (ctx->cfg.wfmt != MOE_WFMT_F32) launch_tile_tables(a, ctx->cfg.wfmt, mx, max_tiles_m, s);
   a.act = ctx->act;
   if (mx) a.acts = reinterpret_cast<uint8_t*>(ctx->act) + (int64_t)P * I;
   a.ypair = ctx->ypair;
   a.y = y;
   a.y_cpu = y_cpu;
   a.pair_gpu = pair_gpu;
-  const int max_tiles_m = (P + bm - 1) / bm + std::min(E, P);
   {
     TimedScope t(ctx, s, TK_G1);
     if (mx) launch_prefill_gemm1_mx(a, max_tiles_m, s, t.tm);
