@@ -128,3 +128,30 @@ def test_permute_is_stable_sort_by_slot():
         assert np.array_equal(perm.cpu().numpy()[: len(ref_perm)], ref_perm)
         counts = np.array([np.sum(flat == g) for g in groups])
         assert np.array_equal(offs.cpu().numpy()[: n + 1], np.concatenate([[0], np.cumsum(counts)]))
+
+
+@pytest.mark.parametrize("wl", [PF_BF16, PF_FP4_256], ids=["bf16", "fp4_staged"])
+@pytest.mark.parametrize("T", [33, 600])
+def test_prefill_skewed_groups(wl, T):
+    """Uneven groups, as a prompt's routing makes them: every token's first pick is expert
+    0 (one group of T rows: several 64-row tiles, the last possibly a short one), the second
+    alternates between experts 1 and 2, the third spreads over the rest; the GEMMs' tile
+    tables and their split of the tiles over the XCDs must cover every row exactly once."""
+    import routed_expert_ffn_02_amd as R
+    E, k = wl.n_experts, wl.top_k
+    assert k == 3 or k == 4
+    h = Harness(wl, R.MOE_MODE_OFFLOAD, n_slots=2 * E + 1, max_tokens=T)
+    rng = np.random.default_rng(T)
+    R.moe_prefill_begin(h.ctx)
+    for layer in range(wl.n_layers):
+        x = wl.prefill_activations(layer, T)
+        t = np.arange(T)
+        cols = [np.zeros(T, dtype=np.int64), 1 + t % 2, 3 + (7 * t) % (E - 3)]
+        if k == 4:
+            cols.append(3 + (7 * t + 1) % (E - 3))
+        idx = np.stack(cols, axis=1).astype(np.int32)
+        w = rng.uniform(0.1, 1.0, size=(T, k))
+        w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+        y, tr, cnt = h.prefill_layer(layer, x, idx, w)
+        assert row_rel_err(y, _expected(wl, layer, x, idx, w)) <= tol_for(wl), layer
+    R.moe_prefill_end(h.ctx)
