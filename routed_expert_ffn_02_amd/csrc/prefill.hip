@@ -241,7 +241,7 @@ __device__ void tile_table(int ngrp, const int* s_tb, const int* s_off, const in
   __syncthreads();
   if (!fits && tid <= 8) s_first[tid] = (int)((int64_t)total * tid / 8);
   __syncthreads();
-  for (int e = tid; e < n; e += blockDim.x) {
+  for (int e = blockIdx.x * blockDim.x + tid; e < n; e += gridDim.x * blockDim.x) {
     const int x = e & 7, b = s_first[x] + (e >> 3);
     int4 t = {0, 0, 0, 0};
     if (b < s_first[x + 1]) {
@@ -260,7 +260,8 @@ __device__ void tile_table(int ngrp, const int* s_tb, const int* s_off, const in
   }
 }
 
-// One workgroup of 1024 threads; groups <= 1024 (one per thread in the scans).
+// Workgroups of 1024 threads (groups <= 1024: one per thread in the scan); each computes the
+// split from the group counts and writes its slice of both tables.
 __global__ __launch_bounds__(1024) void tile_tables_kernel(const int32_t* __restrict__ cnt,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ tile_base, int bm,
@@ -298,9 +299,10 @@ bool fp4_staged(const PrefillArgs& a);
 void launch_tile_tables(const PrefillArgs& a, int wfmt, bool mx, int max_tiles_m, hipStream_t s) {
   const bool f16_fp4 = !mx && (wfmt == MOE_WFMT_FP4 || wfmt == MOE_WFMT_MXFP4) && fp4_staged(a);
   const int nt1 = a.I / 128, nt2 = a.H / 256;
-  hipLaunchKernelGGL(tile_tables_kernel, dim3(1), dim3(1024), 0, s, a.cnt, a.offsets, a.tile_base, BM,
-                     f16_fp4 ? 3 : kTileCostFull, nt1, prefill_tile_slots(max_tiles_m, nt1),
-                     const_cast<int4*>(a.tiles1), nt2, prefill_tile_slots(max_tiles_m, nt2),
+  const int n1 = prefill_tile_slots(max_tiles_m, nt1), n2 = prefill_tile_slots(max_tiles_m, nt2);
+  const int grid = (std::max(n1, n2) + 1023) / 1024;
+  hipLaunchKernelGGL(tile_tables_kernel, dim3(grid), dim3(1024), 0, s, a.cnt, a.offsets, a.tile_base, BM,
+                     f16_fp4 ? 3 : kTileCostFull, nt1, n1, const_cast<int4*>(a.tiles1), nt2, n2,
                      const_cast<int4*>(a.tiles2));
 }
 
