@@ -186,11 +186,11 @@ void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp,
 // one XCD's L2.  The ranges are split by estimated cost rather than by count: in the FP4
 // kernels with f16 operands a tile of at most BM / 2 rows (one 32-row fragment per
 // wavefront) takes about three quarters of the time of a full one, and with the uneven
-// groups of a prompt an equal-count split left some XCDs a sixth longer than others (the
-// bf16 kernels have no such tiles, and in the MX kernels the fragments' MFMAs are too cheap
-// to matter: there every tile counts the same).  One small kernel writes, for every workgroup of both
-// GEMMs' launches, its tile (or none), so a GEMM workgroup starts with one load instead of a
-// binary search over the groups.
+// groups of a prompt an equal-count split left one XCD busy 14% longer than another (the
+// bf16 kernels have no such tiles, and in the MX kernels the fragments' MFMAs are too
+// cheap to matter: there every tile counts the same).  One small kernel writes, for every
+// workgroup of both GEMMs' launches, its tile (or none), so a GEMM workgroup starts with
+// one load instead of a binary search over the groups.
 struct TileInfo {
   int g, row0, rows, nt;
 };
@@ -198,8 +198,9 @@ struct TileInfo {
 constexpr int kTileCostFull = 4;
 
 int prefill_tile_slots(int max_tiles_m, int nt) {
-  // per XCD: at most total / 6 + 2 tiles under the cost split (every tile costs at least 3 of
-  // at most 4 per tile on average), and total <= max_tiles_m * nt
+  // Tiles cost 3 or 4, so an XCD's eighth of the total cost (at most 4 * total / 8) holds
+  // at most total / 6 tiles, plus one on each side of its range's boundaries; and
+  // total <= max_tiles_m * nt.
   return 8 * (int)(((int64_t)max_tiles_m * nt + 5) / 6 + 2);
 }
 
