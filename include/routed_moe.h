@@ -178,6 +178,22 @@ MOE_API const char* moe_last_error(const moe_ctx* ctx);
  */
 MOE_API int64_t moe_record_bytes(const moe_config* cfg);
 
+/*
+ * Whether n_records records at `pool` (host memory laid out as moe_record_bytes defines,
+ * caller-owned, only read) keep the FP4 / MXFP4 prefill exact.  The prefill forms every
+ * weight e2m1(code) x scale in f16 (see the arithmetic note above), which is exact while
+ * each nonzero weight lies in f16's normal range [2^-14, 65504].  Only the block scales are
+ * read, and any code is assumed to occur in a block, so a nonzero scale s must satisfy
+ * 0.5 |s| >= 2^-14 and 6 |s| <= 65504: bf16 scales in [2^-13, 10880] (or zero), E8M0 bytes
+ * in 114..140.  Records outside that range still decode exactly (fp32 arithmetic); their
+ * prefill weights overflow or lose bits with no error, so such pools need the bf16 format.
+ * *first_bad receives the lowest failing record index, or -1.  MOE_OK when every record
+ * passes (always for fp32 and bf16 weights), MOE_EINVAL when one fails or for a bad
+ * argument.  Pure host function (several threads for a large pool).
+ */
+MOE_API moe_status moe_pool_check_f16(const moe_config* cfg, const void* pool, int64_t n_records,
+                                      int64_t* first_bad);
+
 /* ---- host expert pool (the source of truth) ---------------------------- */
 
 /*
@@ -198,6 +214,8 @@ MOE_API moe_status moe_pool_alloc(moe_ctx* ctx, int64_t n_records, void** host_p
  * FTW 포맷", last paragraph).
  */
 MOE_API moe_status moe_pool_register(moe_ctx* ctx, void* host_pool, int64_t n_records, int32_t pinned);
+/* (Neither moe_pool_register nor moe_pool_load inspects the weights: a caller that prefills
+ * FP4 / MXFP4 experts checks the pool once with moe_pool_check_f16.) */
 
 /*
  * Bind the router weights and the slot arena.

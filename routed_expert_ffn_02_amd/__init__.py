@@ -133,6 +133,7 @@ def _load():
         "moe_bench_hbm": (I32, [VP, ctypes.c_size_t, ctypes.c_size_t, I32, VP, VP]),
         "moe_placement_replay": (I32, [ctypes.POINTER(moe_replay_config), VP, I32, VP, I32, I32, VP,
                                        ctypes.POINTER(moe_replay_result)]),
+        "moe_pool_check_f16": (I32, [ctypes.POINTER(moe_config), VP, I64, ctypes.POINTER(I64)]),
         "moe_bank_write": (I32, [ctypes.c_char_p, ctypes.POINTER(moe_config), VP, I64]),
         "moe_bank_info": (I32, [ctypes.c_char_p, ctypes.POINTER(moe_bank_header)]),
         "moe_bank_read": (I32, [ctypes.c_char_p, ctypes.POINTER(moe_config), VP, I64, I32,
@@ -215,6 +216,16 @@ def moe_last_error(ctx: Ctx) -> str:
 
 def moe_record_bytes(cfg: moe_config) -> int:
     return int(lib.moe_record_bytes(ctypes.byref(cfg)))
+
+
+def moe_pool_check_f16(cfg: moe_config, pool, n_records: int) -> int:
+    """Lowest record index whose block scales could take an FP4 / MXFP4 prefill weight out of
+    f16's normal range, or -1 when every record passes."""
+    bad = ctypes.c_int64(-1)
+    st = lib.moe_pool_check_f16(ctypes.byref(cfg), _ptr(pool), n_records, ctypes.byref(bad))
+    if st not in (MOE_OK, MOE_EINVAL) or (st == MOE_EINVAL and bad.value < 0):
+        raise MoeError(st, "moe_pool_check_f16", "bad argument")
+    return int(bad.value)
 
 
 def moe_pool_alloc(ctx: Ctx, n_records: int) -> int:

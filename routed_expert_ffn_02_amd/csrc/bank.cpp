@@ -102,10 +102,65 @@ bool parallel_read(const char* path, ReadMode mode, int64_t off, uint8_t* dst, i
   return ok;
 }
 
+// Whether one block scale keeps every nonzero weight e2m1(code) * scale of its block in
+// f16's normal range [2^-14, 65504] (|code| in 0.5 .. 6).  bf16 scale bits: zero passes; a
+// nonzero |s| needs 2^-13 <= |s| (biased exponent >= 114) and 6 |s| <= 65504 (exponent
+// 140 with at most 42 of 128 mantissa steps, or below 140); inf / NaN / subnormals fail.
+// E8M0 byte e (2^(e - 127)): 114 <= e <= 140.
+bool scale_ok_bf16(uint16_t b) {
+  const int e = (b >> 7) & 0xff, m = b & 0x7f;
+  if (e == 0) return m == 0;
+  return (e >= 114 && e < 140) || (e == 140 && m <= 42);
+}
+bool scale_ok_e8m0(uint8_t e) { return e >= 114 && e <= 140; }
+
 }  // namespace
 }  // namespace rmoe
 
 using namespace rmoe;
+
+extern "C" MOE_API moe_status moe_pool_check_f16(const moe_config* cfg, const void* pool, int64_t n_records,
+                                                 int64_t* first_bad) {
+  if (!cfg || !pool || n_records < 0 || !first_bad) return MOE_EINVAL;
+  const int64_t S = moe_record_bytes(cfg);
+  if (S <= 0) return MOE_EINVAL;
+  *first_bad = -1;
+  if (cfg->wfmt != MOE_WFMT_FP4 && cfg->wfmt != MOE_WFMT_MXFP4) return MOE_OK;  // no block scales
+  const int64_t n = (int64_t)cfg->hidden * cfg->inter;
+  const int64_t scales = 3 * (n / 32), off = 3 * (n / 2);  // after the three tensors' codes
+  const bool mx = cfg->wfmt == MOE_WFMT_MXFP4;
+  const int nt = (int)std::max<int64_t>(1, std::min<int64_t>({16, n_records, (int64_t)std::thread::hardware_concurrency()}));
+  std::atomic<int64_t> bad{INT64_MAX};
+  std::vector<std::thread> ts;
+  for (int t = 0; t < nt; ++t)
+    ts.emplace_back([&, t] {
+      for (int64_t r = t; r < n_records && r < bad.load(std::memory_order_relaxed); r += nt) {
+        const uint8_t* sc = static_cast<const uint8_t*>(pool) + r * S + off;
+        bool ok = true;
+        if (mx) {
+          for (int64_t i = 0; i < scales && ok; ++i) ok = scale_ok_e8m0(sc[i]);
+        } else {
+          for (int64_t i = 0; i < scales && ok; ++i) {
+            uint16_t b;
+            std::memcpy(&b, sc + 2 * i, 2);
+            ok = scale_ok_bf16(b);
+          }
+        }
+        if (!ok) {
+          int64_t cur = bad.load();
+          while (r < cur && !bad.compare_exchange_weak(cur, r)) {
+          }
+          return;
+        }
+      }
+    });
+  for (auto& th : ts) th.join();
+  if (bad.load() != INT64_MAX) {
+    *first_bad = bad.load();
+    return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
 
 extern "C" MOE_API moe_status moe_bank_write(const char* path, const moe_config* cfg, const void* pool,
                                              int64_t n_records) {
