@@ -727,7 +727,7 @@ __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
 // activation tile (64 x 256, 32 KB) and the block's 256 weight rows x 128 B of codes
 // (32 KB), single-buffered in LDS (69 KB, two blocks per CU).  The next chunk waits in
 // registers while the current one is multiplied; block scales travel in registers,
-// 16 bytes per lane per chunk.  Refills past the end re-read the last chunk (in
+// fetched four chunks at a time (see F4Seg).  Refills past the end re-read the last chunk (in
 // bounds, unused).  Needs K % 256 == 0.
 constexpr int F4_KS = 256;                 // k per chunk
 constexpr int F4_AW = F4_KS + 8;           // padded activation row (elements)
