@@ -109,7 +109,9 @@ __device__ __forceinline__ bool topk_better(float va, int ia, float vb, int ib) 
 // PL logits per lane (E <= 64 * PL): the scan and the selection rounds touch only those.
 // A chosen logit (and every slot past E) is held as (-inf, INT_MAX), which loses to any
 // candidate under the order, so the rounds are branch-free selects.
-template <int PL>
+// GATES = false: the selection alone (lds_idx only; no softmax, no global outputs), for
+// readers that need only which experts were chosen.
+template <int PL, bool GATES = true>
 __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E, int k, int renorm,
                                              int32_t* __restrict__ idx_out, float* __restrict__ w_out, int* lds_idx) {
   const int lane = threadIdx.x & 63;
@@ -123,12 +125,14 @@ __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E,
     ev[i] = (e < E) ? e : 0x7fffffff;
     mx = fmaxf(mx, v[i]);
   }
-  mx = wave_max(mx);
   float sum = 0.f;
+  if constexpr (GATES) {
+    mx = wave_max(mx);
 #pragma unroll
-  for (int i = 0; i < PL; ++i)
-    if (lane + 64 * i < E) sum += __expf(v[i] - mx);
-  sum = wave_sum(sum);
+    for (int i = 0; i < PL; ++i)
+      if (lane + 64 * i < E) sum += __expf(v[i] - mx);
+    sum = wave_sum(sum);
+  }
   // selection rounds carry only the arg-max; lane j keeps the j-th winner (k <= 64) and
   // the gates are formed after the loop, all lanes at once
   int my_idx = 0;
@@ -159,11 +163,17 @@ __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E,
     }
     if (k <= 64) {
       if (lane == j) { my_idx = bi; my_v = wv; }
+    } else if (!GATES) {
+      if (lane == 0) lds_idx[j] = bi;
     } else if (lane == 0) {  // more than one selection per lane: written as found
       idx_out[j] = bi;
       w_out[j] = __expf(wv - mx) / sum;
       if (lds_idx) lds_idx[j] = bi;
     }
+  }
+  if (!GATES) {
+    if (k <= 64 && lane < k) lds_idx[lane] = my_idx;
+    return;
   }
   if (k <= 64) {
     const float p = __expf(my_v - mx) / sum;
@@ -192,6 +202,15 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   else if (E <= 256) topk_wave_pl<4>(z, E, k, renorm, idx_out, w_out, lds_idx);
   else if (E <= 512) topk_wave_pl<8>(z, E, k, renorm, idx_out, w_out, lds_idx);
   else topk_wave_pl<kTopkPerLane>(z, E, k, renorm, idx_out, w_out, lds_idx);
+}
+
+// The selection of topk_wave into lds_idx alone (k <= 64 or not): no softmax, no gates.
+__device__ __forceinline__ void topk_wave_select(const float* __restrict__ z, int E, int k, int* lds_idx) {
+  if (E <= 64) topk_wave_pl<1, false>(z, E, k, 0, nullptr, nullptr, lds_idx);
+  else if (E <= 128) topk_wave_pl<2, false>(z, E, k, 0, nullptr, nullptr, lds_idx);
+  else if (E <= 256) topk_wave_pl<4, false>(z, E, k, 0, nullptr, nullptr, lds_idx);
+  else if (E <= 512) topk_wave_pl<8, false>(z, E, k, 0, nullptr, nullptr, lds_idx);
+  else topk_wave_pl<kTopkPerLane, false>(z, E, k, 0, nullptr, nullptr, lds_idx);
 }
 
 // Two e2m1 codes (byte `sel` of w, low nibble first) -> two fp32 values, exact.

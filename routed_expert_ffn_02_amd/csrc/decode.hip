@@ -473,19 +473,41 @@ __global__ __launch_bounds__(256) void dec_phase1_bf(DecodeArgs a) {
   int n = 0;
   int slot;
   if constexpr (ROUTE) {
-    // all resident, one token: the activations are requested first, then wavefront 0
-    // takes the top k from the logits (the selection and gates of the top-k kernel);
-    // group g is rank g and its slot is the key.  Workgroup (0, 0) publishes the step.
+    // all resident, one token: wavefront 0 takes the top k from the logits (the selection
+    // and gates of the top-k kernel) while the other three stage the token's activation
+    // row in LDS, which every wavefront reads back after the barrier.  (Requested by each
+    // wavefront ahead of the logits, the row's loads -- one 8 KB row for every wavefront
+    // of the launch -- held the logits back, since loads complete in issue order.)  Group g
+    // is rank g and its slot is the key.  Workgroup (0, 0) publishes the step.
     static_assert(MAXT == 1, "routed phase 1 is for one token");
+    constexpr int NXP = 64 * CPL * XQ;  // 16-byte pieces of the activation row
     __shared__ int s_idx[kSmallLookupPairs];
-    __shared__ int s_tk[kSmallLookupPairs];
-    __shared__ float s_tw[kSmallLookupPairs];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) load_x_words<XQ>(a.x, H, 0, lane + 64 * c, xq[0][c]);
+    __shared__ u32x4n s_x[NXP];
     const bool first = blockIdx.x == 0 && blockIdx.y == 0;
-    if (wave == 0)
-      topk_wave(a.logits, a.E, a.k, a.renorm, first ? a.topk_out : s_tk, first ? a.topk_w_out : s_tw, s_idx);
+    if (wave == 0) {
+      // only workgroup (0, 0) publishes the gates; the others need just the selection
+      if (first) topk_wave(a.logits, a.E, a.k, a.renorm, a.topk_out, a.topk_w_out, s_idx);
+      else topk_wave_select(a.logits, a.E, a.k, s_idx);
+    } else {
+      const u32x4n* xp = reinterpret_cast<const u32x4n*>(a.x);
+      constexpr int XPT = (NXP + 191) / 192;  // pieces per thread of wavefronts 1..3
+      u32x4n xs[XPT];
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) {
+        const int i = threadIdx.x - 64 + 192 * j;
+        if (i < NXP) xs[j] = xp[i];
+      }
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) {
+        const int i = threadIdx.x - 64 + 192 * j;
+        if (i < NXP) s_x[i] = xs[j];
+      }
+    }
     __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < XQ; ++i) xq[0][c][i] = s_x[(lane + 64 * c) * XQ + i];
     const int base = a.layer * a.E;
     if (first && wave == 0 && lane < a.k) {
       const int sl = base + s_idx[lane];
