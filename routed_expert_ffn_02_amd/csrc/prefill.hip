@@ -1081,6 +1081,212 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 grouped GEMMs with the weights staged in LDS, on the plan of the FP4 kernels above:
+// every weight load covers whole 128-byte lines (eight lanes per row), the rows go to LDS
+// as they are and each lane reads its MFMA operands back from there.  (The register-direct
+// kernels above read 32 bytes of each of 32 rows per load, which bounds them by the
+// address path.)  A chunk covers 64 k: the activation tile (64 x 64 bf16, 8 KB) and the
+// block's 256 weight rows x 128 B (32 KB), single-buffered in LDS (46 KB); the next chunk
+// waits in registers while the current one is multiplied.  Refills past the end re-read
+// the last chunk (in bounds, unused).  Needs K % 64 == 0.
+constexpr int BS_KS = 64;          // k per chunk
+constexpr int BS_AW = BS_KS + 8;   // padded activation row (elements): conflict-free 16-byte reads
+
+struct BsChunk {
+  u32x4 a[2];  // activation piece i: tile row (tid >> 3) + 32 i, 8 elements at (tid & 7) * 8
+  u32x4 b[8];  // weight piece j: block row (tid >> 3) + 32 j, 16 bytes at (tid & 7) * 16
+};
+
+struct BsSrc {
+  __amdgpu_buffer_rsrc_t ra;  // activations
+  __amdgpu_buffer_rsrc_t rb;  // expert record
+  uint32_t aoff[2];    // byte offset of activation piece i at k = 0
+  uint32_t boff[2];    // byte offset of weight piece 0 (rows < 128) and piece 4 (rows >= 128) at k = 0
+  int32_t bstep;       // bytes from weight piece j to piece j + 1 (32 rows)
+};
+
+template <int MR>
+__device__ __forceinline__ void bs_issue(BsChunk& st, const BsSrc& src, int c) {
+#pragma unroll
+  for (int i = 0; i < MR; ++i) st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.aoff[i], c * (2 * BS_KS), 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    st.b[j] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.boff[j >> 2], (j & 3) * src.bstep + c * (2 * BS_KS), 0);
+}
+
+template <int MR>
+__device__ __forceinline__ void bs_store(const BsChunk& st, uint16_t (*sA)[BS_AW], uint8_t (*sB)[F4_BP], int tid) {
+#pragma unroll
+  for (int i = 0; i < MR; ++i) *reinterpret_cast<u32x4*>(&sA[(tid >> 3) + 32 * i][(tid & 7) * 8]) = st.a[i];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(&sB[(tid >> 3) + 32 * j][(tid & 7) * 16]) = st.b[j];
+}
+
+// One chunk: four 16-k MFMA steps; in step j lane half h holds k = 16 j + 8 h + [0, 8)
+// of its activation row and of its weight row alike (the operand layout of the 32 x 32 x 16
+// bf16 MFMA).
+template <int MR>
+__device__ __forceinline__ void bs_compute(const uint16_t (*sA)[BS_AW], const uint8_t (*sB)[F4_BP], int rb0, int rb1,
+                                           int lane, f32x16 (&acc)[MR][2]) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 b0 = *reinterpret_cast<const u32x4*>(&sB[rb0 + r][32 * j + 16 * h]);
+    const u32x4 b1 = *reinterpret_cast<const u32x4*>(&sB[rb1 + r][32 * j + 16 * h]);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const u32x4 am = *reinterpret_cast<const u32x4*>(&sA[32 * m + r][16 * j + 8 * h]);
+      acc[m][0] = mfma32<false>(am, b0, acc[m][0]);
+      acc[m][1] = mfma32<false>(am, b1, acc[m][1]);
+    }
+  }
+}
+
+// The k loop over nc = K / 64 chunks; rb0 / rb1: the wavefront's two 32-row weight
+// fragments in the block's LDS rows.
+template <int MR>
+__device__ __forceinline__ void bs_kloop(int nc, const BsSrc& src, uint16_t (*sA)[BS_AW], uint8_t (*sB)[F4_BP],
+                                         int rb0, int rb1, int tid, f32x16 (&acc)[MR][2]) {
+  const int lane = tid & 63;
+  BsChunk N;
+  bs_issue<MR>(N, src, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  bs_store<MR>(N, sA, sB, tid);
+  __syncthreads();
+  bs_issue<MR>(N, src, min(1, nc - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c = 0; c < nc; ++c) {
+    bs_compute<MR>(sA, sB, rb0, rb1, lane, acc);
+    __syncthreads();  // every wavefront is done with chunk c
+    bs_store<MR>(N, sA, sB, tid);
+    __syncthreads();
+    bs_issue<MR>(N, src, min(c + 2, nc - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// GEMM1 (bf16 weights): act columns n0 .. n0 + 127; block rows 0..127 gate rows n0..,
+// 128..255 up.
+template <int MR>
+__device__ __forceinline__ void gemm1_bs_tile(const PrefillArgs& a, const TileInfo& ti, uint16_t (*sA)[BS_AW],
+                                              uint8_t (*sB)[F4_BP]) {
+  const int H = a.H, I = a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = ti.nt * 128;
+  const uint8_t* rec = group_record(a, ti.g);
+  const int64_t n = (int64_t)H * I;
+  // record: gate, up, down weights (n bf16 each)
+  BsSrc src;
+  src.ra = buf_rsrc(a.xa);
+#pragma unroll
+  for (int i = 0; i < MR; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    const uint32_t tok = (uint32_t)(a.perm[ti.row0 + (row < ti.rows ? row : 0)] / a.k);
+    src.aoff[i] = 2u * (tok * (uint32_t)H + (uint32_t)(tid & 7) * 8u);
+  }
+  src.rb = buf_rsrc(rec);
+  src.boff[0] = (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(2 * H) + (uint32_t)(tid & 7) * 16u;
+  src.boff[1] = src.boff[0] + (uint32_t)(2 * n);
+  src.bstep = 32 * (2 * H);
+
+  f32x16 acc[MR][2];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
+  bs_kloop<MR>(H / BS_KS, src, sA, sB, wave * 32, 128 + wave * 32, tid, acc);
+
+  uint16_t* act = reinterpret_cast<uint16_t*>(a.act);
+  const int col = n0 + wave * 32 + (lane & 31);
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      if (r < ti.rows) {
+        const float g = acc[m][0][i];
+        const float v = g * __frcp_rn(1.0f + __expf(-g)) * acc[m][1][i];
+        act[(int64_t)(ti.row0 + r) * I + col] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+// A tile of at most 32 rows runs one 32-row fragment per wavefront.
+__global__ __launch_bounds__(256, 2) void gemm1_bs_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64][BS_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
+  TileInfo ti;
+  if (!decode_tile(a.tiles1, ti)) return;
+  if (ti.rows <= 32) gemm1_bs_tile<1>(a, ti, sA, sB);
+  else gemm1_bs_tile<2>(a, ti, sA, sB);
+}
+
+// GEMM2 (bf16 weights): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64 of
+// them.
+template <int MR>
+__device__ __forceinline__ void gemm2_bs_tile(const PrefillArgs& a, const TileInfo& ti, uint16_t (*sA)[BS_AW],
+                                              uint8_t (*sB)[F4_BP]) {
+  const int H = a.H, I = a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = ti.nt * 256;
+  const uint8_t* rec = group_record(a, ti.g);
+  const int64_t n = (int64_t)H * I;
+  BsSrc src;
+  src.ra = buf_rsrc(a.act);
+#pragma unroll
+  for (int i = 0; i < MR; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    src.aoff[i] = 2u * ((uint32_t)(ti.row0 + (row < ti.rows ? row : 0)) * (uint32_t)I + (uint32_t)(tid & 7) * 8u);
+  }
+  src.rb = buf_rsrc(rec);
+  src.boff[0] = (uint32_t)(4 * n) + (uint32_t)(n0 + (tid >> 3)) * (uint32_t)(2 * I) + (uint32_t)(tid & 7) * 16u;
+  src.boff[1] = src.boff[0] + 128u * (uint32_t)(2 * I);
+  src.bstep = 32 * (2 * I);
+
+  f32x16 acc[MR][2];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][q][i] = 0.f;
+  bs_kloop<MR>(I / BS_KS, src, sA, sB, wave * 64, wave * 64 + 32, tid, acc);
+
+  const int c0 = n0 + wave * 64 + (lane & 31);
+  int pr[MR][16];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      pr[m][i] = a.perm[ti.row0 + (r < ti.rows ? r : 0)];
+    }
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * m + frag_row(lane, i);
+      if (r < ti.rows) {
+        float* dst = a.ypair + (int64_t)pr[m][i] * H;
+        dst[c0] = acc[m][0][i];
+        dst[c0 + 32] = acc[m][1][i];
+      }
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void gemm2_bs_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64][BS_AW];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
+  TileInfo ti;
+  if (!decode_tile(a.tiles2, ti)) return;
+  if (ti.rows <= 32) gemm2_bs_tile<1>(a, ti, sA, sB);
+  else gemm2_bs_tile<2>(a, ti, sA, sB);
+}
+
+// ---------------------------------------------------------------------------
 // MX prefill of MXFP4 experts (opt-in): the activation operand of each GEMM in MXFP8 (E4M3
 // elements, one E8M0 scale per 32 along k) meets the weights' e2m1 codes and E8M0 scales as
 // stored in v_mfma_scale_f32_32x32x64_f8f6f4 (32 x 32 outputs over 64 k, fp32 accumulation;
@@ -1507,12 +1713,17 @@ __global__ void gemm2_f32_kernel(PrefillArgs a) {
   a.ypair[(int64_t)a.perm[row] * a.H + col] = s;
 }
 
-// The LDS-staged FP4 kernels take two 128-k stages per 16-byte scale load.
 // The LDS-staged FP4 kernels take 256-k chunks and hold byte offsets (activations,
 // record) in 32 bits.  MXFP4 contexts are created only for shapes that meet this.
 bool fp4_staged(const PrefillArgs& a) {
   return a.H % 256 == 0 && a.I % 256 == 0 && (int64_t)a.T * a.H < (1ll << 31) &&
          (int64_t)a.T * a.k * a.I < (1ll << 31) && a.rec_bytes < (1ll << 32);
+}
+
+// The LDS-staged bf16 kernels likewise hold byte offsets in 32 bits (64-k chunks; the
+// tiles already need I % 128 == 0 and H % 256 == 0).
+bool bf16_staged(const PrefillArgs& a) {
+  return (int64_t)a.T * a.H < (1ll << 31) && (int64_t)a.T * a.k * a.I < (1ll << 31) && a.rec_bytes < (1ll << 32);
 }
 
 
@@ -1525,7 +1736,10 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
     return;
   }
   const dim3 grid(prefill_tile_slots(max_tiles_m, a.I / 128));
-  if (wfmt == MOE_WFMT_BF16) launch_timed(gemm1_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  if (wfmt == MOE_WFMT_BF16) {
+    if (bf16_staged(a)) launch_timed(gemm1_bs_kernel, grid, dim3(256), 0, s, tm, a);
+    else launch_timed(gemm1_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  }
   else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm1_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
   else if (fp4_staged(a)) launch_timed(gemm1_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm1_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
@@ -1553,7 +1767,10 @@ void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipSt
     return;
   }
   const dim3 grid(prefill_tile_slots(max_tiles_m, a.H / 256));
-  if (wfmt == MOE_WFMT_BF16) launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  if (wfmt == MOE_WFMT_BF16) {
+    if (bf16_staged(a)) launch_timed(gemm2_bs_kernel, grid, dim3(256), 0, s, tm, a);
+    else launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
+  }
   else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm2_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
   else if (fp4_staged(a)) launch_timed(gemm2_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm2_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
