@@ -263,32 +263,37 @@ __device__ void tile_table(int ngrp, const int* s_tb, const int* s_off, const in
 
 // Workgroups of 1024 threads (groups <= 1024: one per thread in the scan); each computes the
 // split from the group counts and writes its slice of both tables.
+// Row tiles are bm rows high (a group's last one holds the rest); their count per group
+// comes from the group offsets, so a table's bm need not be the permutation's.
 __global__ __launch_bounds__(1024) void tile_tables_kernel(const int32_t* __restrict__ cnt,
-                                                           const int32_t* __restrict__ offsets,
-                                                           const int32_t* __restrict__ tile_base, int bm,
+                                                           const int32_t* __restrict__ offsets, int bm,
                                                            int half_cost, int nt1, int n1, int4* __restrict__ t1,
                                                            int nt2, int n2, int4* __restrict__ t2) {
   __shared__ int s_tb[kMaxExperts + 1], s_off[kMaxExperts + 1], s_uc[kMaxExperts + 1];
   __shared__ int s_tmp[64], s_first[9];
   const int ngrp = min(cnt[C_NGRP], kMaxExperts);
   const int g = threadIdx.x;
-  int uc = 0;  // cost of one column tile of group g: its row tiles
-  for (int i = g; i <= ngrp; i += blockDim.x) {
-    s_tb[i] = tile_base[i];
-    s_off[i] = offsets[i];
-  }
+  int uc = 0, mcount = 0;  // cost of one column tile of group g (its row tiles), their count
+  for (int i = g; i <= ngrp; i += blockDim.x) s_off[i] = offsets[i];
   if (g < ngrp) {
     const int rows = offsets[g + 1] - offsets[g];
-    const int mcount = tile_base[g + 1] - tile_base[g];
+    mcount = (rows + bm - 1) / bm;
     if (mcount > 0) {
       const int last = rows - bm * (mcount - 1);
       uc = kTileCostFull * (mcount - 1) + (2 * last <= bm ? half_cost : kTileCostFull);
     }
   }
-  int tot;
+  int tot, mtot;
   const int pre = block_excl_scan(uc, s_tmp, &tot);
-  if (g < ngrp) s_uc[g] = pre;
-  if (g == 0 && ngrp >= 0) s_uc[ngrp] = tot;
+  const int mpre = block_excl_scan(mcount, s_tmp, &mtot);
+  if (g < ngrp) {
+    s_uc[g] = pre;
+    s_tb[g] = mpre;
+  }
+  if (g == 0 && ngrp >= 0) {
+    s_uc[ngrp] = tot;
+    s_tb[ngrp] = mtot;
+  }
   __syncthreads();
   tile_table(ngrp, s_tb, s_off, s_uc, bm, nt1, n1, t1, s_first);
   __syncthreads();
@@ -296,13 +301,17 @@ __global__ __launch_bounds__(1024) void tile_tables_kernel(const int32_t* __rest
 }
 
 bool fp4_staged(const PrefillArgs& a);
+bool bf16_staged(const PrefillArgs& a);
+constexpr int BS_BM = 128;  // row tile of the LDS-staged bf16 kernels
 
 void launch_tile_tables(const PrefillArgs& a, int wfmt, bool mx, int max_tiles_m, hipStream_t s) {
   const bool f16_fp4 = !mx && (wfmt == MOE_WFMT_FP4 || wfmt == MOE_WFMT_MXFP4) && fp4_staged(a);
+  // (max_tiles_m counts BM-row tiles, an upper bound for taller ones)
+  const int bm = (wfmt == MOE_WFMT_BF16 && bf16_staged(a)) ? BS_BM : BM;
   const int nt1 = a.I / 128, nt2 = a.H / 256;
   const int n1 = prefill_tile_slots(max_tiles_m, nt1), n2 = prefill_tile_slots(max_tiles_m, nt2);
   const int grid = (std::max(n1, n2) + 1023) / 1024;
-  hipLaunchKernelGGL(tile_tables_kernel, dim3(grid), dim3(1024), 0, s, a.cnt, a.offsets, a.tile_base, BM,
+  hipLaunchKernelGGL(tile_tables_kernel, dim3(grid), dim3(1024), 0, s, a.cnt, a.offsets, bm,
                      f16_fp4 ? 3 : kTileCostFull, nt1, n1, const_cast<int4*>(a.tiles1), nt2, n2,
                      const_cast<int4*>(a.tiles2));
 }
@@ -1085,22 +1094,24 @@ __global__ __launch_bounds__(256, 2) void gemm2_fp4_kernel(PrefillArgs a) {
 // every weight load covers whole 128-byte lines (eight lanes per row), the rows go to LDS
 // as they are and each lane reads its MFMA operands back from there.  (The register-direct
 // kernels above read 32 bytes of each of 32 rows per load, which bounds them by the
-// address path.)  A chunk covers 64 k: the activation tile (64 x 64 bf16, 8 KB) and the
-// block's 256 weight rows x 128 B (32 KB), single-buffered in LDS (46 KB); the next chunk
-// waits in registers while the current one is multiplied.  Refills past the end re-read
-// the last chunk (in bounds, unused).  Needs K % 64 == 0.
+// address path.)  Row tiles are 128 high, so a group of up to 128 rows reads its weights
+// once; a tile runs ceil(rows / 32) 32-row fragments per wavefront.  A chunk covers 64 k:
+// the activation tile (up to 128 x 64 bf16, 16 KB) and the block's 256 weight rows x 128 B
+// (32 KB), single-buffered in LDS (55 KB, two blocks per CU); the next chunk waits in
+// registers while the current one is multiplied.  Refills past the end re-read the last
+// chunk (in bounds, unused).  Needs K % 64 == 0.
 constexpr int BS_KS = 64;          // k per chunk
 constexpr int BS_AW = BS_KS + 8;   // padded activation row (elements): conflict-free 16-byte reads
 
 struct BsChunk {
-  u32x4 a[2];  // activation piece i: tile row (tid >> 3) + 32 i, 8 elements at (tid & 7) * 8
+  u32x4 a[4];  // activation piece i: tile row (tid >> 3) + 32 i, 8 elements at (tid & 7) * 8
   u32x4 b[8];  // weight piece j: block row (tid >> 3) + 32 j, 16 bytes at (tid & 7) * 16
 };
 
 struct BsSrc {
   __amdgpu_buffer_rsrc_t ra;  // activations
   __amdgpu_buffer_rsrc_t rb;  // expert record
-  uint32_t aoff[2];    // byte offset of activation piece i at k = 0
+  uint32_t aoff[4];    // byte offset of activation piece i at k = 0
   uint32_t boff[2];    // byte offset of weight piece 0 (rows < 128) and piece 4 (rows >= 128) at k = 0
   int32_t bstep;       // bytes from weight piece j to piece j + 1 (32 rows)
 };
@@ -1214,14 +1225,15 @@ __device__ __forceinline__ void gemm1_bs_tile(const PrefillArgs& a, const TileIn
   }
 }
 
-// A tile of at most 32 rows runs one 32-row fragment per wavefront.
 __global__ __launch_bounds__(256, 2) void gemm1_bs_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[64][BS_AW];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[BS_BM][BS_AW];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
   if (!decode_tile(a.tiles1, ti)) return;
   if (ti.rows <= 32) gemm1_bs_tile<1>(a, ti, sA, sB);
-  else gemm1_bs_tile<2>(a, ti, sA, sB);
+  else if (ti.rows <= 64) gemm1_bs_tile<2>(a, ti, sA, sB);
+  else if (ti.rows <= 96) gemm1_bs_tile<3>(a, ti, sA, sB);
+  else gemm1_bs_tile<4>(a, ti, sA, sB);
 }
 
 // GEMM2 (bf16 weights): output columns n0 .. n0 + 255 (down rows); wavefront w owns 64 of
@@ -1278,12 +1290,14 @@ __device__ __forceinline__ void gemm2_bs_tile(const PrefillArgs& a, const TileIn
 }
 
 __global__ __launch_bounds__(256, 2) void gemm2_bs_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[64][BS_AW];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[BS_BM][BS_AW];
   __shared__ __attribute__((aligned(16))) uint8_t sB[F4_ROWS][F4_BP];
   TileInfo ti;
   if (!decode_tile(a.tiles2, ti)) return;
   if (ti.rows <= 32) gemm2_bs_tile<1>(a, ti, sA, sB);
-  else gemm2_bs_tile<2>(a, ti, sA, sB);
+  else if (ti.rows <= 64) gemm2_bs_tile<2>(a, ti, sA, sB);
+  else if (ti.rows <= 96) gemm2_bs_tile<3>(a, ti, sA, sB);
+  else gemm2_bs_tile<4>(a, ti, sA, sB);
 }
 
 // ---------------------------------------------------------------------------
