@@ -4,6 +4,8 @@
 // token (FreeToken summary, "decode co-design" section: router and cache lookup
 // on the GPU; "MoE" section: k << E).  Gates are the softmax over all E logits
 // taken at the chosen experts (renorm = 1: renormalised over the k chosen).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace rmoe {
@@ -11,12 +13,12 @@ namespace rmoe {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Decode-sized batches: one workgroup per expert row, each of its four wavefronts a
-// quarter of the row.  A lane's 16-byte weight chunks (four at H = 4096) and the matching
-// activations are all requested before any is used, so the whole 4 MB of an E = 256,
-// H = 4096 router is in flight at once over E workgroups (one memory round trip); the
-// quarter sums meet in LDS and are added in wavefront order.
-constexpr int kRouteBatch = 4;  // 16-byte row chunks per lane per round
+// Decode-sized batches: one workgroup per expert row, of up to sixteen wavefronts (one
+// 16-byte weight chunk per lane at H = 4096); thread i takes the row's chunks i, i + n,
+// ... (n threads, loads coalesced across the block) with the matching activations, so the
+// whole 4 MB of an E = 256, H = 4096 router is in flight at once over E workgroups (one
+// memory round trip).  Wavefront sums meet in LDS and are added in wavefront order.
+constexpr int kRouteWaves = 16;  // wavefronts per workgroup at most
 
 template <int AFMT>
 __device__ __forceinline__ float4 route_x4(const void* x, size_t i) {  // 4 activations at element i
@@ -29,36 +31,25 @@ __device__ __forceinline__ float4 route_x4(const void* x, size_t i) {  // 4 acti
 }
 
 template <int AFMT>
-__global__ __launch_bounds__(256) void route_gemv(const void* __restrict__ x, const float* __restrict__ wr,
-                                                   const float* __restrict__ bias, float* __restrict__ logits,
-                                                   int T, int E, int H) {
-  __shared__ float s_part[4][kDecodeMaxTok];
-  const int e = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int cw = H / 16;  // 16-byte chunks in a quarter row (H % 64 == 0)
-  const int c0 = wave * cw;
-  const float4* row = reinterpret_cast<const float4*>(wr + (size_t)e * H) + c0;
+__global__ __launch_bounds__(64 * kRouteWaves) void route_gemv(const void* __restrict__ x, const float* __restrict__ wr,
+                                                               const float* __restrict__ bias,
+                                                               float* __restrict__ logits, int T, int E, int H) {
+  __shared__ float s_part[kRouteWaves][kDecodeMaxTok];
+  const int e = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int nc = H / 4;  // 16-byte chunks in a row
+  const float4* row = reinterpret_cast<const float4*>(wr + (size_t)e * H);
   float acc[kDecodeMaxTok];
 #pragma unroll
   for (int t = 0; t < kDecodeMaxTok; ++t) acc[t] = 0.f;
-  for (int cb = 0; cb < cw; cb += 64 * kRouteBatch) {
-    float4 w4[kRouteBatch];
-    float4 x4[kRouteBatch][kDecodeMaxTok];
+  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+    const float4 w4 = row[c];
+    float4 x4[kDecodeMaxTok];
 #pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      const int c = min(cb + lane + 64 * b, cw - 1);  // clamped chunks are loaded, not added
-      w4[b] = row[c];
+    for (int t = 0; t < kDecodeMaxTok; ++t)
+      if (t < T) x4[t] = route_x4<AFMT>(x, (size_t)t * H + 4 * c);
 #pragma unroll
-      for (int t = 0; t < kDecodeMaxTok; ++t)
-        if (t < T) x4[b][t] = route_x4<AFMT>(x, (size_t)t * H + 4 * (c0 + c));
-    }
-#pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b) {
-      if (cb + lane + 64 * b < cw) {
-#pragma unroll
-        for (int t = 0; t < kDecodeMaxTok; ++t)
-          if (t < T) acc[t] += w4[b].x * x4[b][t].x + w4[b].y * x4[b][t].y + w4[b].z * x4[b][t].z + w4[b].w * x4[b][t].w;
-      }
-    }
+    for (int t = 0; t < kDecodeMaxTok; ++t)
+      if (t < T) acc[t] += w4.x * x4[t].x + w4.y * x4[t].y + w4.z * x4[t].z + w4.w * x4[t].w;
   }
 #pragma unroll
   for (int t = 0; t < kDecodeMaxTok; ++t) {
@@ -70,7 +61,8 @@ __global__ __launch_bounds__(256) void route_gemv(const void* __restrict__ x, co
   __syncthreads();
   if (threadIdx.x < T) {
     const int t = threadIdx.x;
-    const float z = ((s_part[0][t] + s_part[1][t]) + s_part[2][t]) + s_part[3][t];
+    float z = 0.f;
+    for (int w = 0; w < nw; ++w) z += s_part[w][t];
     logits[(size_t)t * E + e] = z + (bias ? bias[(size_t)t * E + e] : 0.f);
   }
 }
@@ -145,10 +137,12 @@ __global__ __launch_bounds__(256) void route_gemm(const void* __restrict__ x, co
 void launch_route_logits(const void* x, int afmt, const float* wr, const float* bias, float* logits, int T, int E,
                          int H, hipStream_t s) {
   if (T <= kDecodeMaxTok && T * H <= kDecodeMaxTH) {
+    // one chunk per lane where the row allows (H = 4096: sixteen wavefronts)
+    const int nw = std::min(kRouteWaves, std::max(1, (H / 4 + 63) / 64));
     if (afmt == MOE_AFMT_BF16)
-      hipLaunchKernelGGL(route_gemv<MOE_AFMT_BF16>, dim3(E), dim3(256), 0, s, x, wr, bias, logits, T, E, H);
+      hipLaunchKernelGGL(route_gemv<MOE_AFMT_BF16>, dim3(E), dim3(64 * nw), 0, s, x, wr, bias, logits, T, E, H);
     else
-      hipLaunchKernelGGL(route_gemv<MOE_AFMT_F32>, dim3(E), dim3(256), 0, s, x, wr, bias, logits, T, E, H);
+      hipLaunchKernelGGL(route_gemv<MOE_AFMT_F32>, dim3(E), dim3(64 * nw), 0, s, x, wr, bias, logits, T, E, H);
   } else {
     dim3 grid((T + kRgT - 1) / kRgT, (E + kRgE - 1) / kRgE);
     if (afmt == MOE_AFMT_BF16)
