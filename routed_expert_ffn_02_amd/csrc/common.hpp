@@ -93,6 +93,18 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Maximum of an int over the 64 lanes (INT_MIN is the identity).
+__device__ __forceinline__ int wave_max_i32(int v) {
+  const int id = (int)0x80000000;
+  v = max(v, dpp_move_i<0xB1, 0xf>(v, id));
+  v = max(v, dpp_move_i<0x4E, 0xf>(v, id));
+  v = max(v, dpp_move_i<0x141, 0xf>(v, id));
+  v = max(v, dpp_move_i<0x140, 0xf>(v, id));
+  v = max(v, dpp_move_i<0x142, 0xa>(v, id));
+  v = max(v, dpp_move_i<0x143, 0xc>(v, id));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------------------
@@ -106,14 +118,28 @@ __device__ __forceinline__ bool topk_better(float va, int ia, float vb, int ib) 
   return va > vb || (va == vb && ia < ib);
 }
 
-// PL logits per lane (E <= 64 * PL): the scan and the selection rounds touch only those.
-// A chosen logit (and every slot past E) is held as (-inf, INT_MAX), which loses to any
-// candidate under the order, so the rounds are branch-free selects.
+// Order-preserving int key of a finite logit or -inf (-0 taken as +0, so equal values
+// have equal keys), and back.
+__device__ __forceinline__ int topk_key(float v) {
+  const int b = __float_as_int(v == 0.f ? 0.f : v);
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float topk_unkey(int key) { return __int_as_float(key >= 0 ? key : key ^ 0x7fffffff); }
+
+// PL logits per lane (E <= 64 * PL).  A lane first sorts its own logits under the
+// selection order (PL <= 8; an insertion network of selects), so its best is always its
+// first; a round takes the wave maximum of the lanes' firsts as int keys (one DPP max
+// per step), breaks a tie between lanes by the lower index, and the winning lane shifts
+// its list up.  (PL = 16 keeps a scan of the lane's logits per round: its network would
+// cost more than the scans.)  A chosen logit (and every slot past E) is held as
+// (-inf, INT_MAX), which loses to any candidate under the order, so the rounds are
+// branch-free selects.  Logits are finite (the router's inputs are).
 // GATES = false: the selection alone (lds_idx only; no softmax, no global outputs), for
 // readers that need only which experts were chosen.
 template <int PL, bool GATES = true>
 __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E, int k, int renorm,
                                              int32_t* __restrict__ idx_out, float* __restrict__ w_out, int* lds_idx) {
+  constexpr bool SORTED = PL <= 8;
   const int lane = threadIdx.x & 63;
   float v[PL];
   int ev[PL];  // the logit's expert, INT_MAX once chosen or past E
@@ -133,33 +159,69 @@ __device__ __forceinline__ void topk_wave_pl(const float* __restrict__ z, int E,
       if (lane + 64 * i < E) sum += __expf(v[i] - mx);
     sum = wave_sum(sum);
   }
+  if constexpr (SORTED) {
+#pragma unroll
+    for (int i = 1; i < PL; ++i) {
+#pragma unroll
+      for (int j = i; j > 0; --j) {
+        // entry j before entry j - 1 under the order (no short-circuit evaluation)
+        const bool sw = (v[j] > v[j - 1]) | ((v[j] == v[j - 1]) & (ev[j] < ev[j - 1]));
+        const float va = v[j - 1], vb = v[j];
+        const int ia = ev[j - 1], ib = ev[j];
+        v[j - 1] = sw ? vb : va;
+        v[j] = sw ? va : vb;
+        ev[j - 1] = sw ? ib : ia;
+        ev[j] = sw ? ia : ib;
+      }
+    }
+  }
   // selection rounds carry only the arg-max; lane j keeps the j-th winner (k <= 64) and
   // the gates are formed after the loop, all lanes at once
   int my_idx = 0;
   float my_v = -INFINITY;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    float wv;
+    int bi;
+    if constexpr (SORTED) {
+      const int key = topk_key(v[0]);
+      const int wkey = wave_max_i32(key);
+      wv = topk_unkey(wkey);
+      const uint64_t holders = __ballot(key == wkey);
+      if (__popcll(holders) == 1)
+        bi = __builtin_amdgcn_readlane(ev[0], __ffsll((unsigned long long)holders) - 1);
+      else
+        bi = wave_min_i32(key == wkey ? ev[0] : 0x7fffffff);
+      const bool hit = ev[0] == bi;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      // topk_better without short-circuit evaluation (no exec-mask branches)
-      const bool better = (v[i] > bv) | ((v[i] == bv) & (ev[i] < bi));
-      bv = better ? v[i] : bv;
-      bi = better ? ev[i] : bi;
-    }
-    // wave arg-max under the same order: the largest value, then the lowest index among
-    // the lanes holding it (a single holder, the usual case, is read from its lane)
-    const float wv = wave_max(bv);
-    const uint64_t holders = __ballot(bv == wv);
-    if (__popcll(holders) == 1)
-      bi = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)holders) - 1);
-    else
-      bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
+      for (int i = 0; i + 1 < PL; ++i) {
+        v[i] = hit ? v[i + 1] : v[i];
+        ev[i] = hit ? ev[i + 1] : ev[i];
+      }
+      v[PL - 1] = hit ? -INFINITY : v[PL - 1];
+      ev[PL - 1] = hit ? 0x7fffffff : ev[PL - 1];
+    } else {
+      float bv = -INFINITY;
+      bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const bool hit = ev[i] == bi;
-      v[i] = hit ? -INFINITY : v[i];
-      ev[i] = hit ? 0x7fffffff : ev[i];
+      for (int i = 0; i < PL; ++i) {
+        const bool better = (v[i] > bv) | ((v[i] == bv) & (ev[i] < bi));
+        bv = better ? v[i] : bv;
+        bi = better ? ev[i] : bi;
+      }
+      // wave arg-max under the same order: the largest value, then the lowest index among
+      // the lanes holding it (a single holder, the usual case, is read from its lane)
+      wv = wave_max(bv);
+      const uint64_t holders = __ballot(bv == wv);
+      if (__popcll(holders) == 1)
+        bi = __builtin_amdgcn_readlane(bi, __ffsll((unsigned long long)holders) - 1);
+      else
+        bi = wave_min_i32(bv == wv ? bi : 0x7fffffff);
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const bool hit = ev[i] == bi;
+        v[i] = hit ? -INFINITY : v[i];
+        ev[i] = hit ? 0x7fffffff : ev[i];
+      }
     }
     if (k <= 64) {
       if (lane == j) { my_idx = bi; my_v = wv; }
