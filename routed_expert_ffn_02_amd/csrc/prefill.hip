@@ -186,9 +186,10 @@ void launch_groups_from_slots(const int32_t* slot_idx, int P, int32_t* pair_grp,
 // one XCD's L2.  The ranges are split by estimated cost rather than by count: in the FP4
 // kernels with f16 operands a tile of at most BM / 2 rows (one 32-row fragment per
 // wavefront) takes about three quarters of the time of a full one, and with the uneven
-// groups of a prompt an equal-count split left one XCD busy 14% longer than another (the
-// bf16 kernels have no such tiles, and in the MX kernels the fragments' MFMAs are too
-// cheap to matter: there every tile counts the same).  One small kernel writes, for every
+// groups of a prompt an equal-count split left one XCD busy 14% longer than another (in
+// the bf16 kernels a tile's time follows the weight bytes, which a tile of any height
+// reads in full, and in the MX kernels the fragments' MFMAs are too cheap to matter:
+// there every tile counts the same).  One small kernel writes, for every
 // workgroup of both GEMMs' launches, its tile (or none), so a GEMM workgroup starts with
 // one load instead of a binary search over the groups.
 struct TileInfo {
