@@ -357,7 +357,8 @@ MOE_API moe_status moe_decode_layer(moe_ctx* ctx, int32_t layer, const void* x, 
  * stream; otherwise prefill loads experts on demand.  moe_ffn_prefill(layer) waits for its layer's
  * copy, routes nothing itself (topk_idx / topk_w come from moe_route), permutes the token-expert
  * pairs by slot, runs the grouped SwiGLU GEMMs (bf16 / FP4 weights need hidden % 256 == 0 and
- * inter % 128 == 0, else MOE_ENOTSUP), combines into y (device fp32 [T,H]) and queues the
+ * inter % 128 == 0, and bf16 weights T * hidden < 2^31, T * top_k * inter < 2^31 and records
+ * below 4 GiB, else MOE_ENOTSUP), combines into y (device fp32 [T,H]) and queues the
  * copy of layer+2 into the buffer it frees.  trace (device, [min(T*k,E)] per round) and counts
  * (device int32 [4]) are optional.  moe_prefill_end returns the buffers to the pool with their
  * contents: the last two layers survive to seed decode.

@@ -302,13 +302,12 @@ __global__ __launch_bounds__(1024) void tile_tables_kernel(const int32_t* __rest
 }
 
 bool fp4_staged(const PrefillArgs& a);
-bool bf16_staged(const PrefillArgs& a);
 constexpr int BS_BM = 128;  // row tile of the LDS-staged bf16 kernels
 
 void launch_tile_tables(const PrefillArgs& a, int wfmt, bool mx, int max_tiles_m, hipStream_t s) {
   const bool f16_fp4 = !mx && (wfmt == MOE_WFMT_FP4 || wfmt == MOE_WFMT_MXFP4) && fp4_staged(a);
   // (max_tiles_m counts BM-row tiles, an upper bound for taller ones)
-  const int bm = (wfmt == MOE_WFMT_BF16 && bf16_staged(a)) ? BS_BM : BM;
+  const int bm = wfmt == MOE_WFMT_BF16 ? BS_BM : BM;
   const int nt1 = a.I / 128, nt2 = a.H / 256;
   const int n1 = prefill_tile_slots(max_tiles_m, nt1), n2 = prefill_tile_slots(max_tiles_m, nt2);
   const int grid = (std::max(n1, n2) + 1023) / 1024;
@@ -347,18 +346,19 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM structure (both GEMMs).  Block = 4 wavefronts, 64 sorted rows
-// (2 MFMA row fragments) x 4 * 64 weight rows; every wavefront owns 2 weight-row
-// fragments of 32 and computes the 2 x 2 fragment product.
+// Register-streamed grouped GEMMs, for FP4 shapes the LDS-staged kernels below do not take
+// (inter % 256 != 0).  Block = 4 wavefronts, 64 sorted rows (2 MFMA row fragments) x
+// 4 * 64 weight rows; every wavefront owns 2 weight-row fragments of 32 and computes the
+// 2 x 2 fragment product.
 //   * B (weights) never touches LDS: each wavefront loads its own weight rows
-//     straight into MFMA operand registers (FP4: dequantised there), so every
+//     straight into MFMA operand registers and dequantises them there, so every
 //     weight byte is read and converted exactly once.
 //   * A (activation rows, shared by the 4 wavefronts) goes global -> registers
 //     -> LDS, one 64-row x 64-k tile per k-step.
 //   * Within a k-step of 64, lane half h (lane >> 5) covers k in [32h, 32h + 32)
 //     and MFMA j takes its 8-element slice [32h + 8j, 32h + 8j + 8) from A and B
-//     alike: a lane's weight loads are one contiguous 32-element run of a row
-//     (for FP4, one 16-byte block of codes with its single scale).
+//     alike: a lane's weight loads are one contiguous 32-element run of a row (one
+//     16-byte block of codes with its single scale).
 //   * Register stages are indexed by compile-time constants (the k loop is
 //     unrolled by the pipeline depth D): D k-steps of loads are in flight while
 //     the current step's MFMAs run.
@@ -428,19 +428,12 @@ __device__ __forceinline__ void store_a(const AStage<AFMT>& st, uint16_t (*sA)[L
   }
 }
 
-// B: this lane's 32-element run of one weight row for one k-step.
-//   FP4: 16 bytes at row offset (k0 + 32 h) / 2 -- the MFMA slice j of the step is
-//        the lane's codes 8 j .. 8 j + 7, i.e. k = 32 h + 8 j + [0, 8).
-//   bf16: four 16-byte chunks 2 j + h (j = 0..3) of the step's 128-byte row segment,
-//        so lanes r and r + 32 read adjacent chunks of row r in every load; MFMA
-//        slice j of the step covers k = 16 j + 8 h + [0, 8).
-// The activation fragments use the same k order (a_koff below).
+// B: this lane's 32-element run of one weight row for one k-step: 16 bytes of FP4 codes at
+// row offset (k0 + 32 h) / 2 -- the MFMA slice j of the step is the lane's codes
+// 8 j .. 8 j + 7, i.e. k = 32 h + 8 j + [0, 8).  The activation fragments use the same k
+// order (a_koff below).
 template <int WFMT>
 struct BRun;
-template <>
-struct BRun<MOE_WFMT_BF16> {
-  u32x4 v[4];
-};
 template <>
 struct BRun<MOE_WFMT_FP4> {
   u32x4 v;  // 32 e2m1 codes, element 2i in the low nibble of byte i
@@ -448,7 +441,7 @@ struct BRun<MOE_WFMT_FP4> {
 
 template <int WFMT>
 __device__ __forceinline__ int a_koff(int h, int j) {
-  return WFMT == MOE_WFMT_FP4 ? 32 * h + 8 * j : 16 * j + 8 * h;
+  return 32 * h + 8 * j;
 }
 
 // Row source of a B run: this lane's row base (FP4: and its scale row).
@@ -460,24 +453,14 @@ struct BRow {
 template <int WFMT>
 __device__ __forceinline__ BRow b_row(const uint8_t* rec, int H, int I, int tensor, int row, int cols) {
   const int64_t n = (int64_t)H * I;
-  if constexpr (WFMT == MOE_WFMT_BF16) {
-    return {rec + tensor * n * 2 + (int64_t)row * cols * 2, nullptr};
-  } else {
-    const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2));
-    return {rec + tensor * (n / 2) + (int64_t)row * (cols / 2), scales + tensor * (n / 32) + (int64_t)row * (cols / 32)};
-  }
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(rec + 3 * (n / 2));
+  return {rec + tensor * (n / 2) + (int64_t)row * (cols / 2), scales + tensor * (n / 32) + (int64_t)row * (cols / 32)};
 }
 
 // Loads of k-step kt (h = lane half).
 template <int WFMT>
 __device__ __forceinline__ void load_b(BRun<WFMT>& r, const BRow& src, int kt, int h) {
-  if constexpr (WFMT == MOE_WFMT_BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(src.p + (int64_t)kt * (BK * 2)) + h;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.v[j] = p[2 * j];
-  } else {
-    r.v = *reinterpret_cast<const u32x4*>(src.p + kt * (BK / 2) + 16 * h);
-  }
+  r.v = *reinterpret_cast<const u32x4*>(src.p + kt * (BK / 2) + 16 * h);
 }
 
 // FP4 block scales of a row for the k-step pair (kt, kt + 1), kt even: scales
@@ -489,7 +472,7 @@ __device__ __forceinline__ u32x2 load_scales(const BRow& src, int kt) {
   return *reinterpret_cast<const u32x2*>(src.sc + 2 * kt);
 }
 
-// MFMA operand j (8 values) of a run: bf16 as stored, FP4 expanded to f16 and scaled.
+// MFMA operand j (8 values) of a run of FP4 codes, expanded to f16 and scaled.
 template <int WFMT>
 struct BOps {
   u32x4 op[4];
@@ -497,22 +480,17 @@ struct BOps {
 
 template <int WFMT>
 __device__ __forceinline__ void b_operands(BOps<WFMT>& o, const BRun<WFMT>& r, uint32_t scale_bits) {
-  if constexpr (WFMT == MOE_WFMT_BF16) {
+  const _Float16 sh = (_Float16)bf16_to_f32((uint16_t)scale_bits);
+  const f16x2 s2 = {sh, sh};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.op[j] = r.v[j];
-  } else {
-    const _Float16 sh = (_Float16)bf16_to_f32((uint16_t)scale_bits);
-    const f16x2 s2 = {sh, sh};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = r.v[j];
-      const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-      const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-      const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-      const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
-      o.op[j] = u32x4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
-                      __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
-    }
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = r.v[j];
+    const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    o.op[j] = u32x4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                    __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
   }
 }
 
@@ -618,7 +596,8 @@ __device__ __forceinline__ int frag_row(int lane, int i) { return 8 * (i >> 2) +
 // gate and the up rows of those columns, so SwiGLU runs on its own accumulators.
 template <int WFMT>
 __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
-  constexpr bool F16 = (WFMT == MOE_WFMT_FP4);
+  static_assert(WFMT == MOE_WFMT_FP4, "the register-streamed kernels serve FP4 weights only");
+  constexpr bool F16 = true;  // f16 operands and f16 act
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDSW];
   TileInfo ti;
   if (!decode_tile(a.tiles1, ti)) return;
@@ -659,10 +638,7 @@ __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
       if (r < ti.rows) {
         const float g = acc[m][0][i];
         const float v = g * __frcp_rn(1.0f + __expf(-g)) * acc[m][1][i];
-        uint16_t bits;
-        if constexpr (F16) bits = __builtin_bit_cast(uint16_t, (_Float16)v);
-        else bits = f32_to_bf16_rne(v);
-        act[(int64_t)(ti.row0 + r) * I + col] = bits;
+        act[(int64_t)(ti.row0 + r) * I + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
       }
     }
   }
@@ -673,7 +649,8 @@ __global__ __launch_bounds__(256, 2) void gemm1_kernel(PrefillArgs a) {
 // Wavefront w owns output columns n0 + 64 w .. + 63 (two weight fragments).
 template <int WFMT>
 __global__ __launch_bounds__(256, 2) void gemm2_kernel(PrefillArgs a) {
-  constexpr bool F16 = (WFMT == MOE_WFMT_FP4);
+  static_assert(WFMT == MOE_WFMT_FP4, "the register-streamed kernels serve FP4 weights only");
+  constexpr bool F16 = true;  // f16 operands
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDSW];
   TileInfo ti;
   if (!decode_tile(a.tiles2, ti)) return;
@@ -1735,11 +1712,9 @@ bool fp4_staged(const PrefillArgs& a) {
          (int64_t)a.T * a.k * a.I < (1ll << 31) && a.rec_bytes < (1ll << 32);
 }
 
-// The LDS-staged bf16 kernels likewise hold byte offsets in 32 bits (64-k chunks; the
-// tiles already need I % 128 == 0 and H % 256 == 0).
-bool bf16_staged(const PrefillArgs& a) {
-  return (int64_t)a.T * a.H < (1ll << 31) && (int64_t)a.T * a.k * a.I < (1ll << 31) && a.rec_bytes < (1ll << 32);
-}
+// The LDS-staged bf16 kernels are the only bf16 path: their 32-bit byte offsets bound
+// T * H, T * k * I and the record size, which moe_ffn_prefill checks (64-k chunks; the
+// tiles need I % 128 == 0 and H % 256 == 0).
 
 
 void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tiles_m, hipStream_t s, Timing tm) {
@@ -1751,10 +1726,7 @@ void launch_prefill_gemm1(int wfmt, int afmt, const PrefillArgs& a, int max_tile
     return;
   }
   const dim3 grid(prefill_tile_slots(max_tiles_m, a.I / 128));
-  if (wfmt == MOE_WFMT_BF16) {
-    if (bf16_staged(a)) launch_timed(gemm1_bs_kernel, grid, dim3(256), 0, s, tm, a);
-    else launch_timed(gemm1_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
-  }
+  if (wfmt == MOE_WFMT_BF16) launch_timed(gemm1_bs_kernel, grid, dim3(256), 0, s, tm, a);
   else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm1_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
   else if (fp4_staged(a)) launch_timed(gemm1_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm1_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);
@@ -1782,10 +1754,7 @@ void launch_prefill_gemm2(int wfmt, const PrefillArgs& a, int max_tiles_m, hipSt
     return;
   }
   const dim3 grid(prefill_tile_slots(max_tiles_m, a.H / 256));
-  if (wfmt == MOE_WFMT_BF16) {
-    if (bf16_staged(a)) launch_timed(gemm2_bs_kernel, grid, dim3(256), 0, s, tm, a);
-    else launch_timed(gemm2_kernel<MOE_WFMT_BF16>, grid, dim3(256), 0, s, tm, a);
-  }
+  if (wfmt == MOE_WFMT_BF16) launch_timed(gemm2_bs_kernel, grid, dim3(256), 0, s, tm, a);
   else if (wfmt == MOE_WFMT_MXFP4) launch_timed(gemm2_fp4_kernel<true>, grid, dim3(256), 0, s, tm, a);
   else if (fp4_staged(a)) launch_timed(gemm2_fp4_kernel<false>, grid, dim3(256), 0, s, tm, a);
   else launch_timed(gemm2_kernel<MOE_WFMT_FP4>, grid, dim3(256), 0, s, tm, a);

@@ -1193,6 +1193,11 @@ MOE_API moe_status moe_ffn_prefill(moe_ctx* ctx, int32_t layer, const void* x, i
   CHECK_ARG(x && topk_idx && topk_w && y, "null pointer");
   if (ctx->cfg.wfmt != MOE_WFMT_F32 && (ctx->cfg.hidden % 256 || ctx->cfg.inter % 128))
     return fail(ctx, MOE_ENOTSUP, "MFMA prefill needs hidden % 256 == 0 and inter % 128 == 0");
+  // the bf16 GEMMs (LDS-staged) hold byte offsets of activations and records in 32 bits
+  if (ctx->cfg.wfmt == MOE_WFMT_BF16 &&
+      ((int64_t)T * ctx->cfg.hidden >= (1ll << 31) || (int64_t)T * ctx->cfg.top_k * ctx->cfg.inter >= (1ll << 31) ||
+       ctx->S >= (1ll << 32)))
+    return fail(ctx, MOE_ENOTSUP, "bf16 prefill needs T * hidden and T * top_k * inter below 2^31, records below 4 GiB");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int k = ctx->cfg.top_k, E = ctx->cfg.n_experts, L = ctx->cfg.n_layers, P = T * k;
   const int mode = ctx->cfg.mode;
