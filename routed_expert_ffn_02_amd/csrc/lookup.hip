@@ -45,13 +45,26 @@ __device__ int block_sum(int v, int* s_tmp) {
   return total;
 }
 
+// Minimum of an unsigned value over the 64 lanes, by DPP row moves (all ones is the
+// identity); every lane receives it.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  auto step = [](uint32_t x, uint32_t y) { return y < x ? y : x; };
+  const int id = -1;
+  v = step(v, (uint32_t)dpp_move_i<0xB1, 0xf>((int)v, id));
+  v = step(v, (uint32_t)dpp_move_i<0x4E, 0xf>((int)v, id));
+  v = step(v, (uint32_t)dpp_move_i<0x141, 0xf>((int)v, id));
+  v = step(v, (uint32_t)dpp_move_i<0x140, 0xf>((int)v, id));
+  v = step(v, (uint32_t)dpp_move_i<0x142, 0xa>((int)v, id));
+  v = step(v, (uint32_t)dpp_move_i<0x143, 0xc>((int)v, id));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// 64-bit minimum as two 32-bit ones: the high words, then the low words of the lanes
+// holding the smallest high word (no LDS round trips).
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = (o < v) ? o : v;
-  }
-  return v;
+  const uint32_t hi = wave_min_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_min_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0xffffffffu);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {  // set bits of mask below lane
@@ -129,7 +142,7 @@ __device__ __forceinline__ void lookup_small(const LookupArgs& a, int* s_slotrow
       if (lane == 0) s_sc[0] = 0;
       int first = lane;  // first pair routed to the same expert
       for (int q = 0; q < P; ++q) {
-        const int eq = __shfl(e, q);
+        const int eq = __builtin_amdgcn_readlane(e, q);
         if (q < first && eq == e) first = q;
       }
       const uint64_t fmask = __ballot(valid && first == lane);
@@ -261,7 +274,7 @@ __device__ __forceinline__ void lookup_small(const LookupArgs& a, int* s_slotrow
   // group id: GPU entries ordered by slot
   int g = 0;
   for (int u = 0; u < nU; ++u) {
-    const int su = __shfl(slot, u);
+    const int su = __builtin_amdgcn_readlane(slot, u);
     if (((gmask >> u) & 1ull) && su < slot) ++g;
   }
   if (is_gpu) {
